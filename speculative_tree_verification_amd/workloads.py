@@ -1,0 +1,325 @@
+"""Seeded synthetic workloads for packed-tree SSD verification.
+
+This module is data only: tree shapes, accepted paths and random tensors with
+the distributions of the five workload configurations, plus bf16 encoding.
+It holds none of the method's arithmetic (no decay, no recurrence, no
+contraction), so both the HIP path and the CPU oracle can consume what it
+produces without sharing computation.
+
+Method context: "STree: Speculative Tree Decoding for Hybrid State Space
+Models" (atlas.scime.ai summary, section "Approach"): a draft token tree is
+packed into one sequence (nodes in topological order, root first) and verified
+in one pass of a Mamba2/SSD layer. The pages print no workload recipe; the
+shapes and distributions below are the five named configurations.
+
+Layouts (all C-contiguous, row-major):
+    x      [B, T, H, P]   bf16 bits (uint16) or float32
+    dt     [B, T, H]      bf16 bits or float32 (already positive: softplus)
+    A, D   [H]            float32
+    Bm, Cm [B, T, G, N]   bf16 bits or float32
+    h0     [B, H, P, N]   float32 (state stored P x N, n fastest)
+    parent [B, T]         int32, parent[b, 0] == -1, 0 <= parent[b, i] < i
+    accepted     [B, Lmax] int32 (root-path node list, -1 padded)
+    accepted_len [B]       int32
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Optional
+
+import numpy as np
+
+F32 = "f32"
+BF16 = "bf16"
+
+
+@dataclasses.dataclass(frozen=True)
+class WorkloadConfig:
+    cid: int
+    name: str
+    batch: int
+    n_heads: int
+    head_dim: int
+    d_state: int
+    n_groups: int
+    n_nodes: int
+    dtype: str
+    layers: int
+    max_path_len: int
+    description: str
+
+
+CONFIGS: Dict[int, WorkloadConfig] = {
+    0: WorkloadConfig(0, "toy-binary-7", 1, 1, 16, 8, 1, 7, F32, 1, 3,
+                      "toy fp32 tree scan, complete binary tree of 7 nodes"),
+    1: WorkloadConfig(1, "mamba2-2.7b-tree15-x64layers", 1, 80, 64, 128, 1, 15, BF16, 64, 5,
+                      "Mamba2-2.7B-shaped layer, 15-node static tree, 64 layer calls"),
+    2: WorkloadConfig(2, "mamba2-2.7b-b16-tree31", 16, 80, 64, 128, 1, 31, BF16, 1, 5,
+                      "batched Mamba2-2.7B-shaped layer, 31-node random recursive trees"),
+    3: WorkloadConfig(3, "hybrid-8b-b32-tree63-g8", 32, 64, 64, 64, 8, 63, BF16, 1, 7,
+                      "8B-hybrid-scale layer, 63-node geometric-branching trees, 8 groups"),
+    4: WorkloadConfig(4, "mamba2-2.7b-b64-tree255-wide", 64, 80, 64, 128, 1, 255, BF16, 1, 9,
+                      "wide-tree stress, 255-node level-structured trees"),
+}
+
+# Static 15-node tree of the Mamba2-2.7B workload: root; 3 children; 6
+# grandchildren (2 per child); the first 4 grandchildren in breadth-first
+# order get one child each; node 10 gets the single depth-4 leaf.
+TREE15 = np.array([-1, 0, 0, 0, 1, 1, 2, 2, 3, 3, 4, 5, 6, 7, 10], dtype=np.int32)
+TREE7 = np.array([-1, 0, 0, 1, 1, 2, 2], dtype=np.int32)
+LEVELS255 = (1, 8, 32, 64, 64, 48, 24, 10, 4)
+
+
+# --------------------------------------------------------------------------
+# bf16 encoding (round to nearest, ties to even) -- data encoding only
+# --------------------------------------------------------------------------
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (RNE) and return the 16-bit patterns."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    out = rounded.astype(np.uint16)
+    nan = np.isnan(a)
+    if nan.any():
+        out[nan] = 0x7FC0
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float32 exactly."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def to_f64(arr: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact widening of a stored tensor (bf16 bits or float32) to float64."""
+    if dtype == BF16:
+        return bf16_bits_to_f32(arr).astype(np.float64)
+    return np.asarray(arr, dtype=np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# tree shapes (parent pointers in topological order, root = node 0)
+# --------------------------------------------------------------------------
+def depths_of(parent: np.ndarray) -> np.ndarray:
+    """Depth (edges to the root) of each node; parent[i] < i is assumed."""
+    d = np.zeros(len(parent), dtype=np.int64)
+    for i in range(1, len(parent)):
+        d[i] = d[parent[i]] + 1
+    return d
+
+
+def root_path(parent: np.ndarray, node: int) -> List[int]:
+    """Node list from the root down to ``node``."""
+    path = []
+    j = int(node)
+    while j >= 0:
+        path.append(j)
+        j = int(parent[j])
+    return path[::-1]
+
+
+def random_recursive_tree(rng: np.random.Generator, T: int, max_depth: int) -> np.ndarray:
+    """parent[i] ~ U{0..i-1}, redrawn until the node's depth is <= max_depth."""
+    parent = np.full(T, -1, dtype=np.int32)
+    depth = np.zeros(T, dtype=np.int64)
+    for i in range(1, T):
+        while True:
+            p = int(rng.integers(0, i))
+            if depth[p] + 1 <= max_depth:
+                break
+        parent[i] = p
+        depth[i] = depth[p] + 1
+    return parent
+
+
+def geometric_tree(rng: np.random.Generator, T: int, depth_cap: int, p_stop: float = 1.0 / 3.0) -> np.ndarray:
+    """Random frontier expansion with Geometric(p) children on {0,1,...}.
+
+    Mean branching (1-p)/p = 2 at p = 1/3. A uniformly chosen unexpanded node is
+    expanded next; nodes at ``depth_cap`` get no children; growth stops at T
+    nodes. Trees that do not reach exactly T nodes and depth ``depth_cap`` are
+    redrawn.
+    """
+    while True:
+        parent = [-1]
+        depth = [0]
+        frontier = [0]
+        while frontier and len(parent) < T:
+            u = frontier.pop(int(rng.integers(0, len(frontier))))
+            if depth[u] >= depth_cap:
+                continue
+            k = int(rng.geometric(p_stop)) - 1  # numpy's geometric is on {1,2,...}
+            k = min(k, T - len(parent))
+            for _ in range(k):
+                parent.append(u)
+                depth.append(depth[u] + 1)
+                frontier.append(len(parent) - 1)
+        if len(parent) == T and max(depth) == depth_cap:
+            return np.array(parent, dtype=np.int32)
+
+
+def level_tree(rng: np.random.Generator, levels=LEVELS255) -> np.ndarray:
+    """Nodes numbered level by level; each picks a parent uniformly in the level above."""
+    parent = [-1]
+    prev = [0]
+    for size in levels[1:]:
+        cur = []
+        for _ in range(size):
+            parent.append(int(prev[int(rng.integers(0, len(prev)))]))
+            cur.append(len(parent) - 1)
+        prev = cur
+    return np.array(parent, dtype=np.int32)
+
+
+def path_of_length(rng: np.random.Generator, parent: np.ndarray, max_len: int) -> List[int]:
+    """L ~ U{1..min(max_len, maxdepth+1)}, then a uniform node at depth L-1 -> its root path."""
+    d = depths_of(parent)
+    top = min(max_len, int(d.max()) + 1)
+    L = int(rng.integers(1, top + 1))
+    cands = np.nonzero(d == L - 1)[0]
+    node = int(cands[int(rng.integers(0, len(cands)))])
+    return root_path(parent, node)
+
+
+def _draw_tree_and_path(cfg: WorkloadConfig, rng: np.random.Generator):
+    B, T = cfg.batch, cfg.n_nodes
+    parents = np.zeros((B, T), dtype=np.int32)
+    paths: List[List[int]] = []
+    for b in range(B):
+        if cfg.cid == 0:
+            par = TREE7.copy()
+            path = [0, 1, 4]
+        elif cfg.cid == 1:
+            par = TREE15.copy()
+            leaves = [i for i in range(T) if not np.any(par == i)]
+            leaf = leaves[int(rng.integers(0, len(leaves)))]
+            path = root_path(par, leaf)
+        elif cfg.cid == 2:
+            par = random_recursive_tree(rng, T, max_depth=8)
+            path = path_of_length(rng, par, cfg.max_path_len)
+        elif cfg.cid == 3:
+            par = geometric_tree(rng, T, depth_cap=6)
+            node = int(rng.integers(0, T))
+            path = root_path(par, node)
+        elif cfg.cid == 4:
+            par = level_tree(rng)
+            path = path_of_length(rng, par, cfg.max_path_len)
+        else:
+            raise ValueError(cfg.cid)
+        parents[b] = par
+        paths.append(path)
+    acc = np.full((B, cfg.max_path_len), -1, dtype=np.int32)
+    acc_len = np.zeros(B, dtype=np.int32)
+    for b, path in enumerate(paths):
+        acc[b, :len(path)] = path
+        acc_len[b] = len(path)
+    return parents, acc, acc_len
+
+
+def softplus(z: np.ndarray) -> np.ndarray:
+    """log(1 + e^z), the dt distribution's transform (input generation only)."""
+    z = np.asarray(z, dtype=np.float64)
+    return np.where(z > 20.0, z, np.log1p(np.exp(np.minimum(z, 20.0))))
+
+
+def make_inputs(cid: int, layer: int = 0) -> Dict[str, np.ndarray]:
+    """Seeded inputs of configuration ``cid`` (one layer instance).
+
+    Draw order: tree -> path -> A -> D -> dt bias -> dt -> x -> B -> C -> h0,
+    from ``numpy.random.default_rng([1000 + cid, layer])``. Layers of the same
+    configuration share the layer-0 tree and accepted path.
+    """
+    cfg = CONFIGS[cid]
+    rng = np.random.default_rng([1000 + cid, layer])
+    parents, acc, acc_len = _draw_tree_and_path(cfg, rng)
+    if layer != 0:
+        parents, acc, acc_len = make_tree_and_path(cid)
+    B, T, H, P, N, G = cfg.batch, cfg.n_nodes, cfg.n_heads, cfg.head_dim, cfg.d_state, cfg.n_groups
+    A = (-np.exp(rng.uniform(0.0, np.log(16.0), size=H))).astype(np.float32)
+    D = rng.standard_normal(H).astype(np.float32)
+    if cfg.cid == 3:
+        bias = rng.uniform(-6.0, -2.0, size=H)
+        z = rng.standard_normal((B, T, H)) + bias[None, None, :]
+    else:
+        z = rng.standard_normal((B, T, H)) - 4.0
+    dt = softplus(z).astype(np.float32)
+    x = rng.standard_normal((B, T, H, P), dtype=np.float32)
+    Bm = rng.standard_normal((B, T, G, N), dtype=np.float32)
+    Cm = rng.standard_normal((B, T, G, N), dtype=np.float32)
+    h0 = (0.1 * rng.standard_normal((B, H, P, N), dtype=np.float32)).astype(np.float32)
+    out = dict(parent=parents, accepted=acc, accepted_len=acc_len, A=A, D=D, h0=h0)
+    if cfg.dtype == BF16:
+        out.update(x=f32_to_bf16_bits(x), dt=f32_to_bf16_bits(dt),
+                   B=f32_to_bf16_bits(Bm), C=f32_to_bf16_bits(Cm))
+    else:
+        out.update(x=x, dt=dt, B=Bm, C=Cm)
+    return out
+
+
+def make_tree_and_path(cid: int):
+    """The layer-0 tree and accepted path of configuration ``cid``."""
+    cfg = CONFIGS[cid]
+    rng = np.random.default_rng([1000 + cid, 0])
+    return _draw_tree_and_path(cfg, rng)
+
+
+def make_custom(seed: int, batch: int, n_nodes: int, n_heads: int, head_dim: int, d_state: int,
+                n_groups: int, dtype: str, parents: Optional[np.ndarray] = None,
+                tree: str = "recursive", max_depth: int = 8, max_path_len: int = 9,
+                dt_shift: float = -4.0) -> Dict[str, np.ndarray]:
+    """Inputs of an arbitrary shape with the configurations' distributions.
+
+    ``tree`` selects the shape when ``parents`` is not given: "recursive"
+    (uniform earlier parent, depth <= max_depth), "chain", "star", "level"
+    (the 255-node level layout) or "geometric".
+    """
+    rng = np.random.default_rng([7000, seed])
+    B, T, H, P, N, G = batch, n_nodes, n_heads, head_dim, d_state, n_groups
+    if parents is None:
+        parents = np.zeros((B, T), dtype=np.int32)
+        for b in range(B):
+            if T == 0:
+                continue
+            if tree == "recursive":
+                parents[b] = random_recursive_tree(rng, T, max_depth)
+            elif tree == "chain":
+                parents[b] = np.arange(-1, T - 1, dtype=np.int32)
+            elif tree == "star":
+                parents[b] = np.array([-1] + [0] * (T - 1), dtype=np.int32)
+            elif tree == "level":
+                parents[b] = level_tree(rng)
+            elif tree == "geometric":
+                parents[b] = geometric_tree(rng, T, depth_cap=max_depth)
+            else:
+                raise ValueError(tree)
+    parents = np.ascontiguousarray(parents, dtype=np.int32).reshape(B, T)
+    acc = np.full((B, max_path_len), -1, dtype=np.int32)
+    acc_len = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        if T == 0:
+            continue
+        path = path_of_length(rng, parents[b], max_path_len)
+        acc[b, :len(path)] = path
+        acc_len[b] = len(path)
+    A = (-np.exp(rng.uniform(0.0, np.log(16.0), size=H))).astype(np.float32)
+    D = rng.standard_normal(H).astype(np.float32)
+    dt = softplus(rng.standard_normal((B, T, H)) + dt_shift).astype(np.float32)
+    x = rng.standard_normal((B, T, H, P), dtype=np.float32)
+    Bm = rng.standard_normal((B, T, G, N), dtype=np.float32)
+    Cm = rng.standard_normal((B, T, G, N), dtype=np.float32)
+    h0 = (0.1 * rng.standard_normal((B, H, P, N), dtype=np.float32)).astype(np.float32)
+    out = dict(parent=parents, accepted=acc, accepted_len=acc_len, A=A, D=D, h0=h0)
+    if dtype == BF16:
+        out.update(x=f32_to_bf16_bits(x), dt=f32_to_bf16_bits(dt),
+                   B=f32_to_bf16_bits(Bm), C=f32_to_bf16_bits(Cm))
+    else:
+        out.update(x=x, dt=dt, B=Bm, C=Cm)
+    return out
+
+
+def shape_of(inp: Dict[str, np.ndarray]):
+    """(B, T, H, P, N, G) of an input dict."""
+    B, T, H, P = inp["x"].shape
+    G, N = inp["B"].shape[2], inp["B"].shape[3]
+    return B, T, H, P, N, G
