@@ -1,0 +1,160 @@
+/*
+ * tree_ssd.h -- C ABI of libtree_ssd.so: packed-tree verification and commit
+ * for one Mamba2/SSD layer on AMD MI355X (gfx950).
+ *
+ * Method: "STree: Speculative Tree Decoding for Hybrid State Space Models"
+ * (atlas.scime.ai summary, sections "Problem" and "Approach"; mlsanity
+ * abstract). A draft token tree is packed into one sequence of T nodes, node 0
+ * the root and every parent listed before its children. One pass gives every
+ * node the exact output the SSM recurrence would give on that node's root path
+ * alone. The tree mask L (ancestor-or-self) accumulates the per-token log
+ * decays along root paths ("A_tree = L log A", read with log A_j = dt_j * A_h,
+ * the log of the discrete transition exp(dt_j * A_h)). Commit ("activation
+ * replay for state backtracking") rebuilds only the accepted path's final
+ * state from the retained inputs; no per-node state is ever stored.
+ *
+ * Per batch item b and head h (group g = h / (H / G)), with the state stored
+ * as H[p][n] (P x N, n fastest):
+ *   H_i = exp(cum_i) h0 + sum_{j on path(i)} exp(cum_i - cum_j) dt_j x_j (outer) B_j
+ *   y_i = H_i C_i + D_h x_i,      cum_i = sum_{j on path(i)} dt_j A_h
+ * which is the recurrence H <- exp(dt A) H + dt x (outer) B, y = H C + D x run
+ * from h0 along the root path of node i.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller, contiguous
+ *     row-major. The library allocates nothing, keeps no state between calls,
+ *     and is reentrant. Work is enqueued on `stream` (a hipStream_t; NULL means
+ *     the null stream) without synchronising; results are ready when the
+ *     stream reaches that point.
+ *   - Host-detectable errors (NULL pointers, bad sizes, bad dtype) return a
+ *     tsv_status other than TSV_OK before anything is enqueued.
+ *   - Data-dependent errors are reported per batch item in device memory
+ *     tree_status[b] (a bit set, see TSV_ST_*). The outputs of an item with any
+ *     bit set are left bitwise untouched. tree_status may be NULL (no report;
+ *     invalid items are still skipped).
+ *   - Nodes are limited to T <= 256 (four 64-bit ancestor words per node).
+ *   - The launch runs on the device current to the calling thread.
+ */
+#ifndef TREE_SSD_H
+#define TREE_SSD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* dtype of x, dt, B, C and y */
+typedef enum { TSV_F32 = 0, TSV_BF16 = 1 } tsv_dtype;
+
+/* Return codes */
+typedef enum {
+    TSV_OK = 0,
+    TSV_E_NULL = 1,        /* a required pointer is NULL */
+    TSV_E_SHAPE = 2,       /* a size is out of range, H % G != 0, or T > 256 */
+    TSV_E_DTYPE = 3,       /* in_dtype is not a tsv_dtype */
+    TSV_E_UNSUPPORTED = 4, /* the size combination has no kernel */
+    TSV_E_LAUNCH = 5       /* the HIP launch failed (see hipGetLastError) */
+} tsv_status;
+
+/* Per-item status bits written to tree_status[b] */
+#define TSV_ST_BAD_ROOT 1   /* parent[b][0] != -1 */
+#define TSV_ST_BAD_PARENT 2 /* some parent[b][i] (i >= 1) is not in [0, i) */
+#define TSV_ST_BAD_PATH 4   /* accepted path: len not in [0, max_path_len],
+                               first node not 0, an index not in [0, T), or a
+                               node whose parent is not the previous entry */
+
+/* Flags (tsv_shape.flags) */
+#define TSV_FLAG_FORCE_GENERIC 1 /* use the plain VALU verify kernel even where
+                                    the MFMA kernel applies (testing aid) */
+
+typedef struct {
+    int32_t batch;           /* Bt >= 0 (0: nothing to do) */
+    int32_t n_nodes;         /* T in [0, 256] (0: nothing to do) */
+    int32_t n_heads;         /* H >= 1 */
+    int32_t head_dim;        /* P >= 1 */
+    int32_t d_state;         /* N >= 1 */
+    int32_t n_groups;        /* G >= 1, H % G == 0; head h uses group h / (H/G) */
+    int32_t in_dtype;        /* tsv_dtype of x, dt, B, C, y */
+    int32_t flags;           /* TSV_FLAG_* (0 = automatic choice) */
+    int32_t heads_per_block; /* launch hint: heads one work-group handles for the
+                                MFMA verify kernel; 0 = automatic. Must divide
+                                H / G when given. */
+} tsv_shape;
+
+/*
+ * tree_ssd_verify -- every node's output of one SSD layer over a packed tree
+ * (the summary's "Approach": accumulated log decays along ancestor paths give
+ * exact per-path outputs in one pass).
+ *
+ *   x      [Bt][T][H][P]   in_dtype   token inputs
+ *   dt     [Bt][T][H]      in_dtype   step sizes, already positive (after any
+ *                                     softplus / bias of the caller)
+ *   A      [H]             float      per-head decay rate (normally < 0)
+ *   B, C   [Bt][T][G][N]   in_dtype   input / output projections
+ *   D      [H]             float      skip weight
+ *   h0     [Bt][H][P][N]   float      state before the root (read only)
+ *   parent [Bt][T]         int32      parent[b][0] = -1, parent[b][i] in [0, i)
+ *   y      [Bt][T][H][P]   in_dtype   output (bf16 results rounded to nearest
+ *                                     even from fp32 accumulators)
+ *   tree_status [Bt]       int32      optional; set to bits 1|2 of the item's tree
+ *
+ * Arithmetic: fp32 accumulation. For bf16 inputs with P == 64 and N in {64, 128}
+ * the h0 read-out C h0^T runs on bf16 MFMA with h0 split into a bf16 high and
+ * low part (about 16 significant bits); everything else is fp32.
+ */
+tsv_status tree_ssd_verify(const tsv_shape* s, const void* x, const void* dt, const float* A,
+                           const void* B, const void* C, const float* D, const float* h0,
+                           const int32_t* parent, void* y, int32_t* tree_status, void* stream);
+
+/*
+ * tree_ssd_commit -- activation replay: overwrite h0 with the state at the end
+ * of the accepted root path (the summary's "activation replay for state
+ * backtracking"), using the same inputs the verify call read:
+ *   H' = exp(cum_l) h0 + sum_k exp(cum_l - cum_{j_k}) dt_{j_k} x_{j_k} (outer) B_{j_k}
+ * for the path j_0 = 0, ..., j_{len-1} = l. len == 0 leaves h0 unchanged.
+ *
+ *   x, dt, A, B, parent   as for tree_ssd_verify (only path rows are read)
+ *   h0_inout [Bt][H][P][N] float   read, then overwritten in place
+ *   accepted [Bt][max_path_len] int32  root-path node list of each item
+ *   accepted_len [Bt]      int32   number of valid entries of each row
+ *   max_path_len           >= 0    row length of `accepted` (1 <= ... <= 256
+ *                                  when Bt > 0; 0 allowed with all len == 0)
+ *   tree_status [Bt]       int32   optional; bits 1|2|4 of the item
+ *
+ * Not idempotent: a second call advances the state again. It must be ordered
+ * after every verify that reads the same h0 (same stream, or an event).
+ */
+tsv_status tree_ssd_commit(const tsv_shape* s, const void* x, const void* dt, const float* A,
+                           const void* B, float* h0_inout, const int32_t* parent,
+                           const int32_t* accepted, const int32_t* accepted_len,
+                           int32_t max_path_len, int32_t* tree_status, void* stream);
+
+/*
+ * tree_ssd_tree_info -- the tree mask of each item (the summary's L): depth of
+ * every node (edges from the root) and its ancestor-or-self set as four 64-bit
+ * words (bit j of word j/64 set iff node j is on the root path of node i).
+ *
+ *   parent   [batch][n_nodes] int32
+ *   depth    [batch][n_nodes] int32     output
+ *   anc_bits [batch][n_nodes][4] uint64 output (unused words are zero)
+ *   tree_status [batch] int32           optional; bits 1|2
+ * Invalid items leave depth and anc_bits untouched.
+ */
+tsv_status tree_ssd_tree_info(int32_t batch, int32_t n_nodes, const int32_t* parent,
+                              int32_t* depth, uint64_t* anc_bits, int32_t* tree_status,
+                              void* stream);
+
+/* Static, human-readable name of a tsv_status value. */
+const char* tree_ssd_status_string(int32_t status);
+
+/* ABI version of this header (incremented on any incompatible change). */
+int32_t tree_ssd_abi_version(void);
+
+#define TREE_SSD_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREE_SSD_H */

@@ -1,0 +1,211 @@
+"""Python binding of libtree_ssd.so (argument marshalling only).
+
+Every step of the computation runs in the HIP library; this module checks
+tensor placement / dtype / shape, fills the ``tsv_shape`` struct and passes raw
+device pointers and torch's current HIP stream through ctypes. PyTorch is used
+for device memory and streams only. There is no fallback: if the library is
+missing, importing this module raises.
+
+Entry points mirror include/tree_ssd.h: ``verify``, ``commit``, ``tree_info``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libtree_ssd.so")
+
+TSV_F32 = 0
+TSV_BF16 = 1
+TSV_FLAG_FORCE_GENERIC = 1
+ST_BAD_ROOT, ST_BAD_PARENT, ST_BAD_PATH = 1, 2, 4
+STATUS_NAMES = {0: "TSV_OK", 1: "TSV_E_NULL", 2: "TSV_E_SHAPE", 3: "TSV_E_DTYPE",
+                4: "TSV_E_UNSUPPORTED", 5: "TSV_E_LAUNCH"}
+EXPORTS = ("tree_ssd_verify", "tree_ssd_commit", "tree_ssd_tree_info", "tree_ssd_status_string",
+           "tree_ssd_abi_version")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_nodes", ctypes.c_int32),
+                ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("d_state", ctypes.c_int32), ("n_groups", ctypes.c_int32),
+                ("in_dtype", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("heads_per_block", ctypes.c_int32)]
+
+
+class TreeSSDError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {STATUS_NAMES.get(code, code)} ({status_string(code)})")
+
+
+_VP = ctypes.c_void_p
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m speculative_tree_verification_amd.build`"
+            " (there is no CPU fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    L.tree_ssd_verify.argtypes = [ctypes.POINTER(Shape)] + [_VP] * 11
+    L.tree_ssd_verify.restype = ctypes.c_int
+    L.tree_ssd_commit.argtypes = [ctypes.POINTER(Shape)] + [_VP] * 8 + [ctypes.c_int32, _VP, _VP]
+    L.tree_ssd_commit.restype = ctypes.c_int
+    L.tree_ssd_tree_info.argtypes = [ctypes.c_int32, ctypes.c_int32] + [_VP] * 5
+    L.tree_ssd_tree_info.restype = ctypes.c_int
+    L.tree_ssd_status_string.argtypes = [ctypes.c_int32]
+    L.tree_ssd_status_string.restype = ctypes.c_char_p
+    L.tree_ssd_abi_version.argtypes = []
+    L.tree_ssd_abi_version.restype = ctypes.c_int32
+    return L
+
+
+lib = _load()
+
+
+def status_string(code: int) -> str:
+    return lib.tree_ssd_status_string(int(code)).decode()
+
+
+def abi_version() -> int:
+    return int(lib.tree_ssd_abi_version())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr()) if t.numel() > 0 else None
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return TSV_F32
+    if t.dtype == torch.bfloat16:
+        return TSV_BF16
+    raise TypeError(f"unsupported input dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _check(t: torch.Tensor, name: str, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype} != {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: device {t.device} != {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def make_shape(x: torch.Tensor, Bm: torch.Tensor, flags: int = 0, heads_per_block: int = 0) -> Shape:
+    Bt, T, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    return Shape(Bt, T, H, P, N, G, _dtype_code(x), flags, heads_per_block)
+
+
+def verify(x, dt, A, B, C, D, h0, parent, y=None, tree_status=None, stream=None,
+           force_generic: bool = False, heads_per_block: int = 0, check: bool = True):
+    """y [Bt,T,H,P] of one SSD layer over packed trees (tree_ssd_verify)."""
+    Bt, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev, io = x.device, x.dtype
+    if check:
+        _check(dt, "dt", (Bt, T, H), io, dev)
+        _check(B, "B", (Bt, T, G, N), io, dev)
+        _check(C, "C", (Bt, T, G, N), io, dev)
+        _check(A, "A", (H,), torch.float32, dev)
+        _check(D, "D", (H,), torch.float32, dev)
+        _check(h0, "h0", (Bt, H, P, N), torch.float32, dev)
+        _check(parent, "parent", (Bt, T), torch.int32, dev)
+        _check(x, "x", (Bt, T, H, P), io, dev)
+    if y is None:
+        y = torch.empty_like(x)
+    elif check:
+        _check(y, "y", (Bt, T, H, P), io, dev)
+    if tree_status is not None and check:
+        _check(tree_status, "tree_status", (Bt,), torch.int32, dev)
+    shape = make_shape(x, B, TSV_FLAG_FORCE_GENERIC if force_generic else 0, heads_per_block)
+    rc = lib.tree_ssd_verify(ctypes.byref(shape), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                             _ptr(D), _ptr(h0), _ptr(parent), _ptr(y), _ptr(tree_status),
+                             _stream(stream))
+    if rc != 0:
+        raise TreeSSDError(rc, "tree_ssd_verify")
+    return y
+
+
+def commit(x, dt, A, B, h0, parent, accepted, accepted_len, tree_status=None, stream=None,
+           check: bool = True):
+    """Overwrite h0 [Bt,H,P,N] with the state after each item's accepted path."""
+    Bt, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev, io = x.device, x.dtype
+    Lmax = accepted.shape[1] if accepted.dim() == 2 else 0
+    if check:
+        _check(dt, "dt", (Bt, T, H), io, dev)
+        _check(B, "B", (Bt, T, G, N), io, dev)
+        _check(A, "A", (H,), torch.float32, dev)
+        _check(h0, "h0", (Bt, H, P, N), torch.float32, dev)
+        _check(parent, "parent", (Bt, T), torch.int32, dev)
+        _check(accepted, "accepted", (Bt, Lmax), torch.int32, dev)
+        _check(accepted_len, "accepted_len", (Bt,), torch.int32, dev)
+        if tree_status is not None:
+            _check(tree_status, "tree_status", (Bt,), torch.int32, dev)
+    shape = make_shape(x, B)
+    rc = lib.tree_ssd_commit(ctypes.byref(shape), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(h0),
+                             _ptr(parent), _ptr(accepted), _ptr(accepted_len), int(Lmax),
+                             _ptr(tree_status), _stream(stream))
+    if rc != 0:
+        raise TreeSSDError(rc, "tree_ssd_commit")
+    return h0
+
+
+def tree_info(parent: torch.Tensor, depth=None, anc=None, tree_status=None, stream=None):
+    """(depth [Bt,T] int32, anc [Bt,T,4] int64 bit patterns, status [Bt] int32)."""
+    Bt, T = parent.shape
+    dev = parent.device
+    if depth is None:
+        depth = torch.zeros((Bt, T), dtype=torch.int32, device=dev)
+    if anc is None:
+        anc = torch.zeros((Bt, T, 4), dtype=torch.int64, device=dev)
+    if tree_status is None:
+        tree_status = torch.zeros((Bt,), dtype=torch.int32, device=dev)
+    rc = lib.tree_ssd_tree_info(int(Bt), int(T), _ptr(parent), _ptr(depth), _ptr(anc),
+                                _ptr(tree_status), _stream(stream))
+    if rc != 0:
+        raise TreeSSDError(rc, "tree_ssd_tree_info")
+    return depth, anc, tree_status
+
+
+# ---------------------------------------------------------------------------
+# host <-> device marshalling of the seeded workloads
+# ---------------------------------------------------------------------------
+def to_device(inp: Dict[str, np.ndarray], device="cuda") -> Dict[str, torch.Tensor]:
+    """Upload a workload dict: bf16 bit patterns become torch.bfloat16 tensors."""
+    out = {}
+    for k, v in inp.items():
+        if v.dtype == np.uint16:
+            t = torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).view(torch.bfloat16)
+        else:
+            t = torch.from_numpy(np.ascontiguousarray(v))
+        out[k] = t.to(device)
+    return out
+
+
+def to_numpy_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact float64 copy of a device tensor (bf16 widened exactly)."""
+    return t.detach().to("cpu", torch.float32).double().numpy()

@@ -1,0 +1,95 @@
+// api.hip -- extern "C" entry points of libtree_ssd.so (declared in
+// include/tree_ssd.h). Host-side validation happens here, before anything is
+// enqueued; the kernels themselves only see consistent shapes.
+#include "../../include/tree_ssd.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int kMaxNodes = 256;
+constexpr int kMaxDim = 256;
+
+tsv_status check_shape(const tsv_shape* s) {
+    if (!s) return TSV_E_NULL;
+    if (s->in_dtype != TSV_F32 && s->in_dtype != TSV_BF16) return TSV_E_DTYPE;
+    if (s->batch < 0 || s->n_nodes < 0 || s->n_nodes > kMaxNodes) return TSV_E_SHAPE;
+    if (s->n_heads < 1 || s->head_dim < 1 || s->d_state < 1 || s->n_groups < 1) return TSV_E_SHAPE;
+    if (s->n_heads % s->n_groups != 0) return TSV_E_SHAPE;
+    if (s->heads_per_block < 0) return TSV_E_SHAPE;
+    if (s->heads_per_block > 0 && (s->n_heads / s->n_groups) % s->heads_per_block != 0)
+        return TSV_E_SHAPE;
+    if (s->head_dim > kMaxDim || s->d_state > kMaxDim) return TSV_E_UNSUPPORTED;
+    // the per-launch grid stays well inside 2^31 work-groups
+    if ((long long)s->batch * s->n_heads * 64 > 0x7fffffffLL) return TSV_E_UNSUPPORTED;
+    return TSV_OK;
+}
+
+bool use_mfma(const tsv_shape* s) {
+    return s->in_dtype == TSV_BF16 && !(s->flags & TSV_FLAG_FORCE_GENERIC) &&
+           tsv::verify_mfma_supported(s->head_dim, s->d_state);
+}
+
+}  // namespace
+
+extern "C" {
+
+tsv_status tree_ssd_verify(const tsv_shape* s, const void* x, const void* dt, const float* A,
+                           const void* B, const void* C, const float* D, const float* h0,
+                           const int32_t* parent, void* y, int32_t* tree_status, void* stream) {
+    tsv_status st = check_shape(s);
+    if (st != TSV_OK) return st;
+    if (s->batch == 0 || s->n_nodes == 0) return TSV_OK;
+    if (!x || !dt || !A || !B || !C || !D || !h0 || !parent || !y) return TSV_E_NULL;
+    tsv::VerifyArgs a{x,  dt, A,           B,        C,          D,          h0,
+                      parent, y, tree_status, s->batch, s->n_nodes, s->n_heads, s->head_dim,
+                      s->d_state, s->n_groups};
+    hipStream_t hs = (hipStream_t)stream;
+    hipError_t e = use_mfma(s) ? tsv::launch_verify_mfma(a, s->heads_per_block, hs)
+                               : tsv::launch_verify_generic(a, s->in_dtype == TSV_BF16, hs);
+    return e == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
+}
+
+tsv_status tree_ssd_commit(const tsv_shape* s, const void* x, const void* dt, const float* A,
+                           const void* B, float* h0_inout, const int32_t* parent,
+                           const int32_t* accepted, const int32_t* accepted_len,
+                           int32_t max_path_len, int32_t* tree_status, void* stream) {
+    tsv_status st = check_shape(s);
+    if (st != TSV_OK) return st;
+    if (max_path_len < 0 || max_path_len > kMaxNodes) return TSV_E_SHAPE;
+    if (s->batch == 0 || s->n_nodes == 0) return TSV_OK;
+    if (!x || !dt || !A || !B || !h0_inout || !parent || !accepted_len) return TSV_E_NULL;
+    if (max_path_len > 0 && !accepted) return TSV_E_NULL;
+    tsv::CommitArgs a{x,          dt,           A,           B,          h0_inout,
+                      parent,     accepted,     accepted_len, tree_status, s->batch,
+                      s->n_nodes, s->n_heads,   s->head_dim,  s->d_state, s->n_groups,
+                      max_path_len};
+    hipError_t e = tsv::launch_commit(a, s->in_dtype == TSV_BF16, (hipStream_t)stream);
+    return e == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
+}
+
+tsv_status tree_ssd_tree_info(int32_t batch, int32_t n_nodes, const int32_t* parent,
+                              int32_t* depth, uint64_t* anc_bits, int32_t* tree_status,
+                              void* stream) {
+    if (batch < 0 || n_nodes < 0 || n_nodes > kMaxNodes) return TSV_E_SHAPE;
+    if (batch == 0 || n_nodes == 0) return TSV_OK;
+    if (!parent || !depth || !anc_bits) return TSV_E_NULL;
+    hipError_t e = tsv::launch_tree_info(batch, n_nodes, parent, depth, anc_bits, tree_status,
+                                         (hipStream_t)stream);
+    return e == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
+}
+
+const char* tree_ssd_status_string(int32_t status) {
+    switch (status) {
+        case TSV_OK: return "ok";
+        case TSV_E_NULL: return "null pointer argument";
+        case TSV_E_SHAPE: return "size out of range (T > 256, H % G != 0, negative size, bad heads_per_block or max_path_len)";
+        case TSV_E_DTYPE: return "unknown input dtype";
+        case TSV_E_UNSUPPORTED: return "unsupported size combination (head_dim or d_state > 256)";
+        case TSV_E_LAUNCH: return "HIP kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int32_t tree_ssd_abi_version(void) { return TREE_SSD_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,143 @@
+// common.hpp -- device helpers shared by the tree-SSD kernels (gfx950, wave64).
+//
+// Tree topology of a packed draft tree ("STree: Speculative Tree Decoding for
+// Hybrid State Space Models", atlas.scime.ai summary, section "Approach": the
+// tree mask L over the packed sequence): node 0 is the root, every parent is
+// listed before its children, T <= 256. One work-group of 256 threads holds
+// one tree in LDS, one node per thread.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tsv {
+
+constexpr int kMaxNodes = 256;
+constexpr int kBlock = 256;
+constexpr int kWave = 64;
+
+constexpr int kStBadRoot = 1;
+constexpr int kStBadParent = 2;
+constexpr int kStBadPath = 4;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
+    return __uint_as_float(b16 << 16);
+}
+
+// round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+}
+
+// element access for the two input dtypes (float, or bf16 stored as uint16_t)
+template <typename TIO>
+struct Elem;
+
+template <>
+struct Elem<float> {
+    static __device__ __forceinline__ float ld(const float* p, size_t i) { return p[i]; }
+    static __device__ __forceinline__ void st(float* p, size_t i, float v) { p[i] = v; }
+};
+
+template <>
+struct Elem<uint16_t> {
+    static __device__ __forceinline__ float ld(const uint16_t* p, size_t i) {
+        return bf16_bits_to_f32(p[i]);
+    }
+    static __device__ __forceinline__ void st(uint16_t* p, size_t i, float v) {
+        p[i] = f32_to_bf16_bits(v);
+    }
+};
+
+// ---------------------------------------------------------------- sync helpers
+// Order LDS traffic between the lanes of one wave (no hardware barrier).
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Exclusive prefix sum over the 256 threads of the block. `scratch` holds at
+// least 4 ints of LDS. Returns the exclusive prefix; *total gets the sum.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        int o = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += o;
+    }
+    if (lane == kWave - 1) scratch[wave] = incl;
+    __syncthreads();
+    int base = 0, sum = 0;
+#pragma unroll
+    for (int w = 0; w < kBlock / kWave; ++w) {
+        int t = scratch[w];
+        if (w < wave) base += t;
+        sum += t;
+    }
+    *total = sum;
+    __syncthreads();
+    return base + incl - v;
+}
+
+// ---------------------------------------------------------------- topology
+// Stage parent[0..T) into LDS and validate it: returns the status bits
+// (kStBadRoot | kStBadParent), identical in every thread. Acts as a barrier.
+__device__ __forceinline__ int load_tree(const int32_t* __restrict__ parent_b, int T,
+                                         int* s_par) {
+    const int i = threadIdx.x;
+    int bad_root = 0, bad_par = 0;
+    if (i < T) {
+        int p = parent_b[i];
+        s_par[i] = p;
+        if (i == 0)
+            bad_root = (p != -1);
+        else
+            bad_par = (p < 0 || p >= i);
+    }
+    int r = __syncthreads_or(bad_root) ? kStBadRoot : 0;
+    r |= __syncthreads_or(bad_par) ? kStBadParent : 0;
+    return r;
+}
+
+// Depth (edges from the root) of node threadIdx.x by pointer jumping over the
+// validated tree in LDS: after round r every node knows its distance to the
+// ancestor 2^r steps up. At most ceil(log2 T) rounds; stops early when every
+// node has reached the root. s_nxt and s_dep are LDS scratch of kMaxNodes.
+__device__ __forceinline__ int tree_depth(const int* s_par, int T, int* s_nxt, int* s_dep) {
+    const int i = threadIdx.x;
+    int nxt = -1, dep = 0;
+    if (i < T) {
+        nxt = s_par[i];
+        dep = (nxt >= 0) ? 1 : 0;
+        s_nxt[i] = nxt;
+        s_dep[i] = dep;
+    }
+    while (__syncthreads_or(nxt >= 0)) {
+        int n2 = nxt, d2 = dep;
+        if (nxt >= 0) {
+            d2 = dep + s_dep[nxt];
+            n2 = s_nxt[nxt];
+        }
+        __syncthreads();
+        if (i < T) {
+            s_dep[i] = d2;
+            s_nxt[i] = n2;
+        }
+        nxt = n2;
+        dep = d2;
+    }
+    return dep;
+}
+
+}  // namespace tsv

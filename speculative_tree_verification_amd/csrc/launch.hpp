@@ -1,0 +1,50 @@
+// launch.hpp -- host-side launchers of the tree-SSD kernels (one per .hip file).
+// Shapes are validated by the C-ABI layer (api.hip) before any of these runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tsv {
+
+struct VerifyArgs {
+    const void* x;
+    const void* dt;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const float* h0;
+    const int32_t* parent;
+    void* y;
+    int32_t* tree_status;
+    int batch, T, H, P, N, G;
+};
+
+struct CommitArgs {
+    const void* x;
+    const void* dt;
+    const float* A;
+    const void* B;
+    float* h;
+    const int32_t* parent;
+    const int32_t* accepted;
+    const int32_t* accepted_len;
+    int32_t* tree_status;
+    int batch, T, H, P, N, G, Lmax;
+};
+
+hipError_t launch_tree_info(int batch, int T, const int32_t* parent, int32_t* depth,
+                            uint64_t* anc, int32_t* tree_status, hipStream_t stream);
+
+// plain VALU verify, any P, N <= 256; bf16 selects the bf16 input dtype
+hipError_t launch_verify_generic(const VerifyArgs& a, bool bf16, hipStream_t stream);
+
+// bf16 MFMA verify; requires P == 64, N in {64, 128}
+bool verify_mfma_supported(int P, int N);
+hipError_t launch_verify_mfma(const VerifyArgs& a, int heads_per_block, hipStream_t stream);
+int verify_mfma_default_heads_per_block(int batch, int T, int H, int G);
+
+hipError_t launch_commit(const CommitArgs& a, bool bf16, hipStream_t stream);
+
+}  // namespace tsv

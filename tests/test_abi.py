@@ -1,0 +1,127 @@
+"""The C-ABI library: loads, exports every symbol include/*.h declares, and
+rejects bad host-side arguments before enqueuing anything (no GPU needed:
+these calls return before any HIP runtime call)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "speculative_tree_verification_amd", "libtree_ssd.so")
+
+
+def declared_functions():
+    names = set()
+    for hdr in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(hdr).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b(tree_ssd_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIB):
+        from speculative_tree_verification_amd.build import build
+        build()
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    assert {"tree_ssd_verify", "tree_ssd_commit", "tree_ssd_tree_info",
+            "tree_ssd_status_string", "tree_ssd_abi_version"} <= names
+
+
+def test_every_declared_symbol_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings_and_version(L):
+    L.tree_ssd_status_string.restype = ctypes.c_char_p
+    for code in range(6):
+        assert L.tree_ssd_status_string(code)
+    assert L.tree_ssd_status_string(99) == b"unknown status"
+    assert L.tree_ssd_abi_version() == 1
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("batch", "n_nodes", "n_heads", "head_dim", "d_state",
+                                             "n_groups", "in_dtype", "flags", "heads_per_block")]
+
+
+def call_verify(L, shape, ptrs=None):
+    vp = ctypes.c_void_p
+    L.tree_ssd_verify.argtypes = [ctypes.POINTER(Shape)] + [vp] * 11
+    L.tree_ssd_verify.restype = ctypes.c_int
+    ptrs = ptrs if ptrs is not None else [None] * 11
+    return L.tree_ssd_verify(ctypes.byref(shape) if shape is not None else None, *ptrs)
+
+
+def call_commit(L, shape, lmax=4, ptrs=None):
+    vp = ctypes.c_void_p
+    L.tree_ssd_commit.argtypes = [ctypes.POINTER(Shape)] + [vp] * 8 + [ctypes.c_int32, vp, vp]
+    L.tree_ssd_commit.restype = ctypes.c_int
+    ptrs = ptrs if ptrs is not None else [None] * 8
+    return L.tree_ssd_commit(ctypes.byref(shape), *ptrs, lmax, None, None)
+
+
+def good():
+    return Shape(2, 15, 8, 64, 128, 1, 1, 0, 0)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("n_nodes", 257, 2), ("n_nodes", -1, 2), ("batch", -3, 2), ("n_heads", 0, 2),
+    ("head_dim", 0, 2), ("d_state", 0, 2), ("n_groups", 3, 2), ("in_dtype", 7, 3),
+    ("heads_per_block", 3, 2), ("heads_per_block", -1, 2), ("head_dim", 512, 4),
+    ("d_state", 300, 4)])
+def test_verify_rejects_bad_shapes(L, field, value, code):
+    s = good()
+    setattr(s, field, value)
+    assert call_verify(L, s) == code
+
+
+def test_verify_null_checks(L):
+    assert call_verify(L, None) == 1
+    assert call_verify(L, good()) == 1  # all tensor pointers NULL
+    fake = [ctypes.c_void_p(0x1000)] * 11
+    fake[4] = None  # C missing
+    assert call_verify(L, good(), fake) == 1
+
+
+def test_empty_inputs_are_noops(L):
+    s = good()
+    s.batch = 0
+    assert call_verify(L, s) == 0
+    assert call_commit(L, s) == 0
+    s = good()
+    s.n_nodes = 0
+    assert call_verify(L, s) == 0
+    assert call_commit(L, s) == 0
+    L.tree_ssd_tree_info.argtypes = [ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 5
+    assert L.tree_ssd_tree_info(0, 5, None, None, None, None, None) == 0
+    assert L.tree_ssd_tree_info(3, 0, None, None, None, None, None) == 0
+
+
+def test_commit_checks(L):
+    s = good()
+    assert call_commit(L, s, lmax=-1) == 2
+    assert call_commit(L, s, lmax=257) == 2
+    assert call_commit(L, s, lmax=4) == 1
+    L.tree_ssd_tree_info.argtypes = [ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 5
+    assert L.tree_ssd_tree_info(2, 300, None, None, None, None, None) == 2
+    assert L.tree_ssd_tree_info(2, 10, None, None, None, None, None) == 1
+
+
+def test_product_path_never_reaches_the_oracle():
+    """No file of the package imports, loads or names the oracle's modules."""
+    pkg = os.path.join(ROOT, "speculative_tree_verification_amd")
+    pat = re.compile(r"(^\s*(from|import)\s+oracle)|liboracle|oracle\.(py|c)\b|oracle_verify", re.M)
+    for path in glob.glob(os.path.join(pkg, "**", "*"), recursive=True):
+        if not os.path.isfile(path) or path.endswith((".so", ".o", ".pyc")):
+            continue
+        assert not pat.search(open(path, errors="ignore").read()), path
