@@ -1,0 +1,329 @@
+#!/usr/bin/env python3
+"""Throughput of packed-tree SSD verification + commit on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+tree_ssd_verify for every layer of the workload, then tree_ssd_commit for
+every layer (the accepted path is part of the input). Inputs are resident in
+HBM before the timed region; several copies of the input set rotate so the
+256 MB Infinity Cache cannot serve them.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
+
+Prints one JSON line (metric, value in tree nodes/s, roofline of the dominant
+kernel from HIP events, CPU-oracle baseline). Diagnostics go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tree-verify nodes/sec (batch×nodes×heads×layers) at 1 GPU; % peak HBM GB/s"
+PEAK_HBM_GBS = 8000.0
+ROTATE_BYTES = 640 << 20   # rotating input sets must exceed the 256 MB Infinity Cache
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=1,
+                    help="workload configuration id (0-4); default 1, the 64-layer Mamba2-2.7B step")
+    ap.add_argument("--secondary", default="2,4",
+                    help="comma list of further workloads measured in the same run ('' for none)")
+    ap.add_argument("--secondary-steps", type=int, default=20)
+    ap.add_argument("--no-oracle", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--oracle-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--heads-per-block", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (HBM counter calibration)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic bytes per launch (what the method must move; no per-node state)
+# ---------------------------------------------------------------------------
+def verify_bytes(B, T, H, P, N, G, io):
+    return (io * (2 * B * T * H * P + B * T * H + 2 * B * T * G * N) + 4 * B * H * P * N
+            + 8 * H + 4 * B * T)
+
+
+def commit_bytes(B, T, H, P, N, G, io, path_lens, Lmax):
+    L = int(sum(path_lens))
+    return (8 * B * H * P * N + L * io * (H * P + H + G * N) + 4 * B * T + 4 * B * Lmax + 4 * B
+            + 4 * H)
+
+
+def source_sha(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "speculative_tree_verification_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(kernel, workload, sha):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        recs = json.load(f)
+    for r in recs.get("records", []):
+        if r.get("kernel") == kernel and r.get("workload") == workload and r.get("source_sha") == sha:
+            return r
+    return None
+
+
+# ---------------------------------------------------------------------------
+class Workload:
+    """All layers of one configuration, resident on the GPU, in S rotating sets."""
+
+    def __init__(self, cid, torch, bnd, W, heads_per_block=0, keep_host=False):
+        self.cid = cid
+        self.cfg = cfg = W.CONFIGS[cid]
+        self.io = 2 if cfg.dtype == W.BF16 else 4
+        t0 = time.time()
+        self.host = []
+        layers = []
+        for l in range(cfg.layers):
+            inp = W.make_inputs(cid, l)
+            if keep_host:
+                self.host.append(inp)
+            layers.append(bnd.to_device(inp))
+        log(f"[bench] workload {cid} ({cfg.name}): generated {cfg.layers} layer(s) in {time.time() - t0:.1f}s")
+        B, T, H, P = layers[0]["x"].shape
+        G, N = layers[0]["B"].shape[2], layers[0]["B"].shape[3]
+        self.dims = (B, T, H, P, N, G)
+        self.path_lens = [int(v) for v in layers[0]["accepted_len"].cpu().tolist()]
+        self.Lmax = layers[0]["accepted"].shape[1]
+        set_bytes = sum(t.numel() * t.element_size() for d in layers for t in d.values())
+        set_bytes += sum(d["x"].numel() * d["x"].element_size() for d in layers)  # y
+        self.n_sets = max(2, -(-ROTATE_BYTES // set_bytes))
+        self.sets = [layers]
+        for s in range(1, self.n_sets):
+            self.sets.append([{k: v.clone() for k, v in d.items()} for d in layers])
+        self.verify_calls, self.commit_calls = [], []
+        for layers_s in self.sets:
+            vc, cc = [], []
+            for d in layers_s:
+                y = torch.empty_like(d["x"])
+                d["y"] = y
+                vc.append(bnd.PreparedVerify(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"],
+                                             d["h0"], d["parent"], y,
+                                             heads_per_block=heads_per_block))
+                cc.append(bnd.PreparedCommit(d["x"], d["dt"], d["A"], d["B"], d["h0"], d["parent"],
+                                             d["accepted"], d["accepted_len"]))
+            self.verify_calls.append(vc)
+            self.commit_calls.append(cc)
+        torch.cuda.synchronize()
+        log(f"[bench] {self.n_sets} rotating sets of {set_bytes / 2**20:.1f} MiB")
+
+    @property
+    def nodes_per_step(self):
+        B, T, H, P, N, G = self.dims
+        return B * T * H * self.cfg.layers
+
+    def step(self, s, ev=None):
+        """Enqueue one step on input set s; ev = (v0, v1, c0, c1) events around layer 0."""
+        vc, cc = self.verify_calls[s], self.commit_calls[s]
+        for l, f in enumerate(vc):
+            if ev is not None and l == 0:
+                ev[0].record()
+                f()
+                ev[1].record()
+            else:
+                f()
+        for l, f in enumerate(cc):
+            if ev is not None and l == 0:
+                ev[2].record()
+                f()
+                ev[3].record()
+            else:
+                f()
+
+    def algorithmic_bytes(self):
+        B, T, H, P, N, G = self.dims
+        return (verify_bytes(B, T, H, P, N, G, self.io),
+                commit_bytes(B, T, H, P, N, G, self.io, self.path_lens, self.Lmax))
+
+
+def sleep_cycles_for(torch, ms):
+    """Cycles of torch.cuda._sleep that keep the GPU busy for about ms."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    torch.cuda._sleep(1_000_000)
+    e1.record()
+    torch.cuda.synchronize()
+    per = max(e0.elapsed_time(e1), 1e-3) / 1_000_000
+    return int(ms / per)
+
+
+def time_steps(torch, wl, steps, warmup):
+    """Warm up, then time exactly `steps` steps with HIP events; the stream is
+    pre-loaded with a spin kernel so the host enqueues ahead of the GPU and the
+    region measures GPU execution of back-to-back launches."""
+    host_t = []
+    for i in range(warmup):
+        t0 = time.perf_counter()
+        wl.step(i % wl.n_sets)
+        host_t.append(time.perf_counter() - t0)
+        torch.cuda.synchronize()
+    host_per_step = min(host_t) if host_t else 5e-3
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()  # barrier (one rank) + synchronize before the timed region
+    cyc = sleep_cycles_for(torch, 1.5e3 * host_per_step * steps + 20.0)
+    torch.cuda._sleep(cyc)
+    start.record()
+    t_host = time.perf_counter()
+    for i in range(steps):
+        wl.step(i % wl.n_sets, evs[i])
+    end.record()
+    t_host = time.perf_counter() - t_host
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    v_us = [evs[i][0].elapsed_time(evs[i][1]) * 1e3 for i in range(steps)]
+    c_us = [evs[i][2].elapsed_time(evs[i][3]) * 1e3 for i in range(steps)]
+    return dict(ms_per_step=ms, verify_us=sum(v_us) / steps, commit_us=sum(c_us) / steps,
+                verify_us_min=min(v_us), commit_us_min=min(c_us), host_ms=1e3 * t_host / steps)
+
+
+def kernel_report(name, us, nbytes, workload, sha):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    rec = traffic_record(name, workload, sha)
+    traffic = None
+    if rec is not None:
+        traffic = int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+            "kernel": name, "avg_us": round(us, 3), "algorithmic_bytes": int(nbytes)}
+
+
+def cpu_baseline(wl, W, seconds):
+    """The fp64 oracle timed on a bounded sample of the same workload on the host."""
+    from oracle import oracle as O
+    B, T, H, P, N, G = wl.dims
+    done_nodes, used, parts = 0, 0.0, 0
+    # sample unit: one layer's verify + commit for a block of items (all heads)
+    units = [(l, b0) for l in range(wl.cfg.layers) for b0 in range(B)]
+    items_per_unit = 1 if B > 1 else 1
+    for (l, b) in units:
+        inp = wl.host[l]
+        sel = [(b, h) for h in range(H)]
+        s = O.gather_slices(inp, wl.cfg.dtype, sel)
+        t0 = time.perf_counter()
+        O.verify_slices(s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"], s["h0"], s["parent"])
+        O.commit_slices(s["x"], s["dt"], s["A"], s["B"], s["h0"], s["parent"], s["accepted"],
+                        s["accepted_len"], Lmax=inp["accepted"].shape[-1])
+        used += time.perf_counter() - t0
+        done_nodes += T * H * items_per_unit
+        parts += 1
+        if used >= seconds:
+            break
+    what = (f"{parts} of {len(units)} (layer, item) units of the workload, all {H} heads each: "
+            f"verify + commit in fp64")
+    return {"value": round(done_nodes / used, 1), "unit": "nodes/s", "cores": O.num_threads(),
+            "kind": "oracle", "sample": what, "seconds": round(used, 2)}
+
+
+def run_workload(torch, bnd, W, cid, steps, warmup, hpb, keep_host):
+    wl = Workload(cid, torch, bnd, W, heads_per_block=hpb, keep_host=keep_host)
+    t = time_steps(torch, wl, steps, warmup)
+    vb, cb = wl.algorithmic_bytes()
+    name = wl.cfg.name
+    v = kernel_report("verify", t["verify_us"], vb, name, source_sha("verify_mfma.hip", "common.hpp"))
+    c = kernel_report("commit", t["commit_us"], cb, name, source_sha("commit.hip", "common.hpp"))
+    nodes_s = wl.nodes_per_step / (t["ms_per_step"] * 1e-3)
+    log(f"[bench] workload {cid}: {t['ms_per_step']:.4f} ms/step, {nodes_s:.4g} nodes/s; "
+        f"verify {t['verify_us']:.2f} us ({v['achieved']:.0f} GB/s), "
+        f"commit {t['commit_us']:.2f} us ({c['achieved']:.0f} GB/s); host {t['host_ms']:.3f} ms/step")
+    return wl, t, v, c, nodes_s
+
+
+def copy_calibration(torch):
+    n = 256 << 20
+    a = torch.empty(n // 4, dtype=torch.float32, device="cuda").normal_()
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": n, "launches": 5}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path has no "
+              "multi-GPU mode: heads or items would be sharded with no exchange inside it.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from speculative_tree_verification_amd import binding as bnd
+    from speculative_tree_verification_amd import workloads as W
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+
+    wl, t, v, c, nodes_s = run_workload(torch, bnd, W, args.workload, args.steps, args.warmup,
+                                        args.heads_per_block, keep_host=not args.no_oracle)
+    B, T, H, P, N, G = wl.dims
+    layers = wl.cfg.layers
+    dominant = v if v["avg_us"] >= c["avg_us"] else c
+    roofline = {k: dominant[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
+    roofline["kernel"] = dominant["kernel"]
+    out = {
+        "metric": METRIC,
+        "value": round(nodes_s, 1),
+        "unit": "nodes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.cfg.dtype,
+        "data": "synthetic (seeded generator; shapes and distributions of the named workload)",
+        "config": {"workload": wl.cfg.name, "batch": B, "nodes": T, "heads": H, "head_dim": P,
+                   "d_state": N, "groups": G, "layers": layers,
+                   "step": f"{layers} x tree_ssd_verify + {layers} x tree_ssd_commit",
+                   "rotating_sets": wl.n_sets},
+        "roofline": roofline,
+        "kernels": {"verify": v, "commit": c},
+    }
+    secondary = []
+    for sid in [int(s) for s in args.secondary.split(",") if s.strip()]:
+        if sid == args.workload:
+            continue
+        wl2, t2, v2, c2, ns2 = run_workload(torch, bnd, W, sid, args.secondary_steps, 3,
+                                            0, keep_host=False)
+        secondary.append({"workload": wl2.cfg.name, "nodes_per_s": round(ns2, 1),
+                          "ms_per_step": round(t2["ms_per_step"], 5),
+                          "verify": v2, "commit": c2})
+        del wl2
+        torch.cuda.empty_cache()
+    if secondary:
+        out["secondary"] = secondary
+    if not args.no_oracle:
+        log("[bench] timing the CPU oracle on a sample of the workload")
+        out["cpu_baseline"] = cpu_baseline(wl, W, args.oracle_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

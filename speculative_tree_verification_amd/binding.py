@@ -209,3 +209,62 @@ def to_device(inp: Dict[str, np.ndarray], device="cuda") -> Dict[str, torch.Tens
 def to_numpy_f64(t: torch.Tensor) -> np.ndarray:
     """Exact float64 copy of a device tensor (bf16 widened exactly)."""
     return t.detach().to("cpu", torch.float32).double().numpy()
+
+
+# ---------------------------------------------------------------------------
+# prepared calls: arguments checked and marshalled once, launched many times
+# ---------------------------------------------------------------------------
+class PreparedVerify:
+    """tree_ssd_verify with fixed buffers; calling it enqueues one launch."""
+
+    def __init__(self, x, dt, A, B, C, D, h0, parent, y, tree_status=None, stream=None,
+                 force_generic: bool = False, heads_per_block: int = 0):
+        Bt, T, H, P = x.shape
+        G, N = B.shape[2], B.shape[3]
+        io, dev = x.dtype, x.device
+        for t, name, shp, dty in ((dt, "dt", (Bt, T, H), io), (B, "B", (Bt, T, G, N), io),
+                                  (C, "C", (Bt, T, G, N), io), (A, "A", (H,), torch.float32),
+                                  (D, "D", (H,), torch.float32),
+                                  (h0, "h0", (Bt, H, P, N), torch.float32),
+                                  (parent, "parent", (Bt, T), torch.int32),
+                                  (y, "y", (Bt, T, H, P), io)):
+            _check(t, name, shp, dty, dev)
+        self.shape = make_shape(x, B, TSV_FLAG_FORCE_GENERIC if force_generic else 0,
+                                heads_per_block)
+        self._keep = (x, dt, A, B, C, D, h0, parent, y, tree_status)
+        self.args = (ctypes.byref(self.shape), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                     _ptr(D), _ptr(h0), _ptr(parent), _ptr(y), _ptr(tree_status),
+                     _stream(stream))
+
+    def __call__(self):
+        rc = lib.tree_ssd_verify(*self.args)
+        if rc != 0:
+            raise TreeSSDError(rc, "tree_ssd_verify")
+
+
+class PreparedCommit:
+    """tree_ssd_commit with fixed buffers; calling it enqueues one launch."""
+
+    def __init__(self, x, dt, A, B, h0, parent, accepted, accepted_len, tree_status=None,
+                 stream=None):
+        Bt, T, H, P = x.shape
+        G, N = B.shape[2], B.shape[3]
+        io, dev = x.dtype, x.device
+        Lmax = accepted.shape[1]
+        for t, name, shp, dty in ((dt, "dt", (Bt, T, H), io), (B, "B", (Bt, T, G, N), io),
+                                  (A, "A", (H,), torch.float32),
+                                  (h0, "h0", (Bt, H, P, N), torch.float32),
+                                  (parent, "parent", (Bt, T), torch.int32),
+                                  (accepted, "accepted", (Bt, Lmax), torch.int32),
+                                  (accepted_len, "accepted_len", (Bt,), torch.int32)):
+            _check(t, name, shp, dty, dev)
+        self.shape = make_shape(x, B)
+        self._keep = (x, dt, A, B, h0, parent, accepted, accepted_len, tree_status)
+        self.args = (ctypes.byref(self.shape), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(h0),
+                     _ptr(parent), _ptr(accepted), _ptr(accepted_len), int(Lmax),
+                     _ptr(tree_status), _stream(stream))
+
+    def __call__(self):
+        rc = lib.tree_ssd_commit(*self.args)
+        if rc != 0:
+            raise TreeSSDError(rc, "tree_ssd_commit")

@@ -26,7 +26,35 @@ tsv_status check_shape(const tsv_shape* s) {
 
 bool use_mfma(const tsv_shape* s) {
     return s->in_dtype == TSV_BF16 && !(s->flags & TSV_FLAG_FORCE_GENERIC) &&
-           tsv::verify_mfma_supported(s->head_dim, s->d_state);
+           s->head_dim == 64 && (s->d_state == 64 || s->d_state == 128);
+}
+
+int compute_units() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return 256;
+    return n;
+}
+
+// Heads per work-group: the largest divisor of the heads of one group that
+// still fills every resident work-group slot of the GPU at least once.
+int default_heads_per_block(const tsv_shape* s, int blocks_per_cu) {
+    const long slots = (long)compute_units() * blocks_per_cu;
+    const int hpg = s->n_heads / s->n_groups;
+    int best = 1;
+    for (int d = 1; d <= hpg; ++d)
+        if (hpg % d == 0 && (long)s->batch * (s->n_heads / d) >= slots) best = d;
+    return best;
+}
+
+hipError_t launch_mfma(const tsv_shape* s, const tsv::VerifyArgs& a, hipStream_t hs) {
+    const bool small = s->n_nodes <= 64;
+    int hb = s->heads_per_block;
+    if (hb == 0)
+        hb = default_heads_per_block(s, small ? tsv::verify_small_blocks_per_cu(a.T, a.N)
+                                              : tsv::verify_wide_blocks_per_cu(a.T, a.N));
+    return small ? tsv::launch_verify_small(a, hb, hs) : tsv::launch_verify_wide(a, hb, hs);
 }
 
 }  // namespace
@@ -44,7 +72,7 @@ tsv_status tree_ssd_verify(const tsv_shape* s, const void* x, const void* dt, co
                       parent, y, tree_status, s->batch, s->n_nodes, s->n_heads, s->head_dim,
                       s->d_state, s->n_groups};
     hipStream_t hs = (hipStream_t)stream;
-    hipError_t e = use_mfma(s) ? tsv::launch_verify_mfma(a, s->heads_per_block, hs)
+    hipError_t e = use_mfma(s) ? launch_mfma(s, a, hs)
                                : tsv::launch_verify_generic(a, s->in_dtype == TSV_BF16, hs);
     return e == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
 }

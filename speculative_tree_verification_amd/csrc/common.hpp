@@ -3,8 +3,8 @@
 // Tree topology of a packed draft tree ("STree: Speculative Tree Decoding for
 // Hybrid State Space Models", atlas.scime.ai summary, section "Approach": the
 // tree mask L over the packed sequence): node 0 is the root, every parent is
-// listed before its children, T <= 256. One work-group of 256 threads holds
-// one tree in LDS, one node per thread.
+// listed before its children, T <= 256. One work-group of at least 256
+// threads holds one tree in LDS, one node per thread.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -33,8 +33,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
     return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// two floats -> packed bf16 pair (a in the low half), one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
 // element access for the two input dtypes (float, or bf16 stored as uint16_t)
@@ -65,8 +69,9 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Exclusive prefix sum over the 256 threads of the block. `scratch` holds at
-// least 4 ints of LDS. Returns the exclusive prefix; *total gets the sum.
+// Exclusive prefix sum over the NT threads of the block. `scratch` holds at
+// least NT/64 ints of LDS. Returns the exclusive prefix; *total gets the sum.
+template <int NT = kBlock>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -80,7 +85,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
     __syncthreads();
     int base = 0, sum = 0;
 #pragma unroll
-    for (int w = 0; w < kBlock / kWave; ++w) {
+    for (int w = 0; w < NT / kWave; ++w) {
         int t = scratch[w];
         if (w < wave) base += t;
         sum += t;

@@ -40,10 +40,12 @@ hipError_t launch_tree_info(int batch, int T, const int32_t* parent, int32_t* de
 // plain VALU verify, any P, N <= 256; bf16 selects the bf16 input dtype
 hipError_t launch_verify_generic(const VerifyArgs& a, bool bf16, hipStream_t stream);
 
-// bf16 MFMA verify; requires P == 64, N in {64, 128}
-bool verify_mfma_supported(int P, int N);
-hipError_t launch_verify_mfma(const VerifyArgs& a, int heads_per_block, hipStream_t stream);
-int verify_mfma_default_heads_per_block(int batch, int T, int H, int G);
+// bf16 MFMA verify (head_dim 64, d_state 64 or 128): trees of <= 64 nodes use
+// the per-wave head_dim-slice kernel, wider trees the LDS-staged kernel
+hipError_t launch_verify_small(const VerifyArgs& a, int heads_per_block, hipStream_t stream);
+int verify_small_blocks_per_cu(int T, int N);
+hipError_t launch_verify_wide(const VerifyArgs& a, int heads_per_block, hipStream_t stream);
+int verify_wide_blocks_per_cu(int T, int N);
 
 hipError_t launch_commit(const CommitArgs& a, bool bf16, hipStream_t stream);
 

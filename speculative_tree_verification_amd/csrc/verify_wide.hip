@@ -1,0 +1,341 @@
+// verify_wide.hip -- packed-tree verification of one Mamba2/SSD layer for wide
+// trees (65..256 nodes), bf16 inputs, head_dim 64, d_state 64 or 128.
+//
+// Method: "STree: Speculative Tree Decoding for Hybrid State Space Models"
+// (atlas.scime.ai summary, section "Approach"): per (item b, head h)
+//   y_i = exp(cum_i) (h0 C_i) + sum_{j on path(i)} G_ij exp(cum_i - cum_j) dt_j x_j + D x_i,
+// G = C B^T on ancestor pairs only, cum = L (dt A) along root paths.
+//
+// Mapping for MI355X (one work-group of NW = 8 or 16 waves per CU, i.e. two or
+// four waves per SIMD, ~145 KB of LDS):
+//  * work-group = (item b, block of HB heads of one group). The tree set-up
+//    (validation, depth by pointer jumping, ancestor-pair lists, pair scores
+//    G_ij) runs once and serves all HB heads.
+//  * wave w owns node tile w (nodes 16w .. 16w+15) and all 64 rows of
+//    head_dim; its C operands (exact bf16 B-matrix of the read-out MFMA) stay
+//    in registers for every head of the work-group.
+//  * per head, double buffered (head h+1 streams in while head h computes):
+//    x (T x 64 bf16) goes straight from HBM to LDS (global_load_lds_dwordx4,
+//    whole 128-byte rows); h0 (64 x N fp32) is read once into registers and
+//    split once per work-group into bf16 high and low planes in LDS. Tiles are
+//    stored with an XOR swizzle of their 16-byte chunks so that the operand
+//    and ancestor-row reads below spread over the LDS banks.
+//  * read-out (h0 C^T) on 16x16x32 bf16 MFMA (hi and lo planes). The A-operand
+//    rows are permuted so that lane (r, q) owns 16 contiguous head_dim columns
+//    16q..16q+15 of node 16w + r: ancestor rows of x are two 16-byte LDS reads
+//    and y leaves as two 16-byte stores.
+//  * the sparse intra-tree term is summed over each node's ancestor-pair list
+//    (D x_i joins the node's own term); exp is evaluated on ancestor pairs only
+//    and the decay is summed along the path (no cancellation). Two ancestors
+//    are taken at a time: their x rows are interleaved into bf16 pairs and
+//    dotted (v_dot2_f32_bf16, fp32 accumulate) with the two weights, each
+//    split into bf16 high and low parts (about 16 significant bits).
+#include "launch.hpp"
+#include "verify_common.hpp"
+
+namespace tsv {
+
+constexpr int kWideMaxPairs = 2048;
+
+template <int NW, int KS>
+struct WideCfg {
+    static constexpr int NT = NW * kWave;  // threads per work-group
+    static constexpr int N = 32 * KS;
+    static constexpr int TPM = 16 * NW;    // nodes covered: one 16-node tile per wave
+    static constexpr int CPR = N / 8;      // 16-byte bf16 chunks per row of an h0 plane / of C
+    static constexpr int HL_BYTES = kHeadDim * N * 2;  // one bf16 plane (hi or lo) of h0
+    static constexpr int X_BYTES = TPM * kHeadDim * 2;  // x tile, 128-byte rows
+    static constexpr int H0_F4 = kHeadDim * N / 4 / NT; // float4 of h0 per thread
+    static constexpr int X_INSTR = TPM * 8 / kWave / NW; // 1 KB async loads per wave
+    static_assert(kHeadDim * N / 4 % NT == 0, "h0 tile must split evenly over the threads");
+    static_assert(TPM * N * 2 <= 4 * HL_BYTES, "C tile must fit the two h0 buffers");
+};
+
+// byte offset of 16-byte chunk c of row r in a tile with `cpr` chunks per row
+// (a power of two), chunk index XOR-ed with `key`
+__device__ __forceinline__ int swz_off(int r, int c, int cpr, int key) {
+    return (r * cpr + (c ^ (key & (cpr - 1)))) * 16;
+}
+// swizzle key of head_dim row p: distinct for the 16 rows one MFMA operand read touches
+__device__ __forceinline__ int row_key(int p) { return (p >> 4) | ((p & 3) << 2); }
+// swizzle key of x row j: with the row parity it spreads 16 random rows over
+// all sixteen 16-byte bank groups
+__device__ __forceinline__ int x_key(int j) { return (j >> 1) & 7; }
+// head_dim row fed as MFMA A-operand row m of p-tile pt
+__device__ __forceinline__ int perm_row(int pt, int m) { return 16 * (m >> 2) + 4 * pt + (m & 3); }
+
+template <int NW, int KS>
+__global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const float* __restrict__ A,
+    const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
+    const float* __restrict__ D, const float* __restrict__ h0, const int32_t* __restrict__ parent,
+    uint16_t* __restrict__ y, int32_t* __restrict__ tree_status, int T, int H, int G, int HB) {
+    using Cfg = WideCfg<NW, KS>;
+    constexpr int NT = Cfg::NT;
+    constexpr int N = Cfg::N;
+    constexpr int TPM = Cfg::TPM;
+    constexpr int CPR = Cfg::CPR;
+    constexpr int MAXP = kWideMaxPairs;
+
+    __shared__ __attribute__((aligned(16))) unsigned char s_hl[2][2][Cfg::HL_BYTES];  // [buf][hi,lo]
+    __shared__ __attribute__((aligned(16))) unsigned char s_x[2][Cfg::X_BYTES];
+    __shared__ float s_dt[2][TPM];
+    __shared__ int s_par[kMaxNodes];
+    __shared__ int s_dep[kMaxNodes];
+    __shared__ int s_off[kMaxNodes];
+    __shared__ int s_scratch[kMaxNodes];
+    __shared__ int s_scan[NW];
+    __shared__ uint16_t s_pair[MAXP];  // node i in the low byte, ancestor j in the high byte
+    __shared__ float s_G[MAXP];
+
+    const int nblk = H / HB;
+    const int b = blockIdx.x / nblk;
+    const int h_first = (blockIdx.x % nblk) * HB;
+    const int g = h_first / (H / G);
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int w = tid / kWave;
+    const int r16 = lane & 15;
+    const int q = lane >> 4;
+    const int i = 16 * w + r16;  // this lane's node
+    const size_t bc_row0 = ((size_t)b * T) * G + g;
+
+    // ---- per-head staging
+    // x rows of head h straight into LDS buffer `buf` (asynchronous, swizzled)
+    auto stage_x = [&](int h, int buf) {
+        unsigned char* xbase = s_x[buf];
+#pragma unroll
+        for (int m = 0; m < Cfg::X_INSTR; ++m) {
+            const int blk = w * Cfg::X_INSTR + m;  // 1 KB block of the tile
+            const int pos = blk * kWave + lane;     // 16-byte chunk position in LDS
+            const int r = pos >> 3, slot = pos & 7;
+            if (r < T)
+                __builtin_amdgcn_global_load_lds(
+                    (const void*)(x + (((size_t)b * T + r) * H + h) * kHeadDim + 8 * (slot ^ x_key(r))),
+                    (__attribute__((address_space(3))) void*)(xbase + blk * 1024), 16, 0, 0);
+        }
+    };
+    // h0 of head h into registers (consecutive threads, consecutive float4)
+    float4 hreg[Cfg::H0_F4];
+    uint32_t dreg;
+    auto prefetch = [&](int h) {
+        const float4* src = (const float4*)(h0 + ((size_t)b * H + h) * kHeadDim * N);
+#pragma unroll
+        for (int m = 0; m < Cfg::H0_F4; ++m) hreg[m] = src[tid + NT * m];
+        dreg = (tid < T) ? dt[((size_t)b * T + tid) * H + h] : 0u;
+    };
+    // split the registers into bf16 hi / lo planes of buffer `buf`, and dt
+    auto stage_h0 = [&](int buf) {
+        unsigned char* hib = s_hl[buf][0];
+        unsigned char* lob = s_hl[buf][1];
+#pragma unroll
+        for (int m = 0; m < Cfg::H0_F4; ++m) {
+            const int gi = tid + NT * m;  // float4 index in the 64 x N tile
+            const int p = gi / (N / 4), c4 = gi % (N / 4);
+            const int off = swz_off(p, c4 >> 1, CPR, row_key(p)) + 8 * (c4 & 1);
+            const float4 v = hreg[m];
+            const uint32_t h01 = pack_bf16x2(v.x, v.y), h23 = pack_bf16x2(v.z, v.w);
+            const uint32_t l01 = pack_bf16x2(v.x - lo_bf16(h01), v.y - hi_bf16(h01));
+            const uint32_t l23 = pack_bf16x2(v.z - lo_bf16(h23), v.w - hi_bf16(h23));
+            *(uint2*)(hib + off) = make_uint2(h01, h23);
+            *(uint2*)(lob + off) = make_uint2(l01, l23);
+        }
+        if (tid < TPM) s_dt[buf][tid] = bf16_bits_to_f32(dreg);
+    };
+
+    // head 0 streams in while the tree is set up (x into buffer 0; h0 into registers)
+    stage_x(h_first, 0);
+    prefetch(h_first);
+
+    // ---------------------------------------------------------------- set-up
+    const int st = load_tree(parent + (size_t)b * T, T, s_par);
+    if (h_first == 0 && tid == 0 && tree_status) tree_status[b] = st;
+    if (st) {
+        __builtin_amdgcn_s_waitcnt(0);  // drain the asynchronous LDS loads before leaving
+        return;
+    }
+    // C tile (T x N bf16, rows swizzled) in the h0 buffers, which are still free
+    unsigned char* cbase = &s_hl[0][0][0];
+    for (int c = tid; c < TPM * CPR; c += NT) {
+        const int r = c / CPR, ch = c % CPR;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (r < T) v = *(const uint4*)(Cm + (bc_row0 + (size_t)r * G) * N + 8 * ch);
+        *(uint4*)(cbase + swz_off(r, ch, CPR, r)) = v;
+    }
+    const int total_pairs = build_pairs<NT>(s_par, T, s_dep, s_off, s_scratch, s_scan, s_pair, MAXP);
+    const bool cached = total_pairs <= MAXP;
+    __syncthreads();
+    if (cached) {
+        for (int pq = tid; pq < total_pairs; pq += NT) {
+            const int pr = s_pair[pq];
+            const int pi = pr & 255, pj = pr >> 8;
+            const uint16_t* Bj = Bm + (bc_row0 + (size_t)pj * G) * N;
+            uint4 vb[CPR];
+#pragma unroll
+            for (int ch = 0; ch < CPR; ++ch) vb[ch] = *(const uint4*)(Bj + 8 * ch);
+            float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+            for (int ch = 0; ch < CPR; ch += 2) {
+                s0 = dot8_bf16(*(const uint4*)(cbase + swz_off(pi, ch, CPR, pi)), vb[ch], s0);
+                s1 = dot8_bf16(*(const uint4*)(cbase + swz_off(pi, ch + 1, CPR, pi)), vb[ch + 1], s1);
+            }
+            s_G[pq] = s0 + s1;
+        }
+    }
+    bf16x8 creg[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) creg[ks] = *(const bf16x8*)(cbase + swz_off(i, 4 * ks + q, CPR, i));
+    const int my_base = (i < T) ? s_off[i] : 0;
+    const int my_cnt = (i < T) ? s_dep[i] + 1 : 0;
+    __syncthreads();  // C tile consumed: the h0 buffers are free
+    stage_h0(0);
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's x chunks of head 0 have landed
+    __syncthreads();
+
+    // ---------------------------------------------------------------- heads
+    const bool tile_live = 16 * w < T;
+    for (int hh = 0; hh < HB; ++hh) {
+        const int h = h_first + hh;
+        const int buf = hh & 1;
+        const bool more = hh + 1 < HB;
+        if (more) {
+            stage_x(h + 1, buf ^ 1);
+            prefetch(h + 1);
+        }
+        if (tile_live) {
+            const unsigned char* hib = s_hl[buf][0];
+            const unsigned char* lob = s_hl[buf][1];
+            const unsigned char* sx = s_x[buf];
+            const float* sdt = s_dt[buf];
+
+            // read-out: acc[pt] holds (h0 C^T) rows p = 16q + 4pt + r, column i
+            f32x4 acc[4];
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) {
+                    const int p = perm_row(pt, r16);
+                    const int off = swz_off(p, 4 * ks + q, CPR, row_key(p));
+                    acc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(hib + off), creg[ks], acc[pt], 0, 0, 0);
+                }
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) {
+                    const int p = perm_row(pt, r16);
+                    const int off = swz_off(p, 4 * ks + q, CPR, row_key(p));
+                    acc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(lob + off), creg[ks], acc[pt], 0, 0, 0);
+                }
+            }
+
+            // intra-tree term + D x_i over node i's ancestor list, columns 16q .. 16q+15,
+            // two ancestors at a time: their x rows are interleaved into bf16 pairs and
+            // multiplied by the two weights, each split into bf16 high + low parts
+            const float Ah = A[h];
+            const float Dh = D[h];
+            float ta[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) ta[e] = 0.f;
+            auto add_rows = [&](int j0, float w0, int j1, float w1) {
+                const int a0 = swz_off(j0, 2 * q, 8, x_key(j0));
+                const int a1 = swz_off(j1, 2 * q, 8, x_key(j1));
+                const uint4 p0 = *(const uint4*)(sx + a0), q0 = *(const uint4*)(sx + (a0 ^ 16));
+                const uint4 p1 = *(const uint4*)(sx + a1), q1 = *(const uint4*)(sx + (a1 ^ 16));
+                const uint32_t u0[8] = {p0.x, p0.y, p0.z, p0.w, q0.x, q0.y, q0.z, q0.w};
+                const uint32_t u1[8] = {p1.x, p1.y, p1.z, p1.w, q1.x, q1.y, q1.z, q1.w};
+                const uint32_t whi = pack_bf16x2(w0, w1);
+                const uint32_t wlo = pack_bf16x2(w0 - lo_bf16(whi), w1 - hi_bf16(whi));
+                const bf16x2 wh = __builtin_bit_cast(bf16x2, whi), wl = __builtin_bit_cast(bf16x2, wlo);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const bf16x2 xl = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(u1[e], u0[e], 0x05040100u));
+                    const bf16x2 xh = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(u1[e], u0[e], 0x07060302u));
+                    ta[2 * e] = __builtin_amdgcn_fdot2_f32_bf16(xl, wh, ta[2 * e], false);
+                    ta[2 * e] = __builtin_amdgcn_fdot2_f32_bf16(xl, wl, ta[2 * e], false);
+                    ta[2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(xh, wh, ta[2 * e + 1], false);
+                    ta[2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(xh, wl, ta[2 * e + 1], false);
+                }
+            };
+            float s = 0.f;  // sum of dt*A over the path nodes from i up to (excluding) j
+            if (i < T) {
+                if (cached) {
+                    // entry k = 0 is the node itself: weight G_ii dt_i + D
+                    int k = 0;
+                    int j0 = i;
+                    float w0 = 0.f;
+                    for (; k < my_cnt; k += 2) {
+                        j0 = s_pair[my_base + k] >> 8;
+                        const float dj0 = sdt[j0];
+                        w0 = s_G[my_base + k] * __expf(s) * dj0 + (k == 0 ? Dh : 0.f);
+                        s += dj0 * Ah;
+                        int j1 = j0;
+                        float w1 = 0.f;
+                        if (k + 1 < my_cnt) {
+                            j1 = s_pair[my_base + k + 1] >> 8;
+                            const float dj1 = sdt[j1];
+                            w1 = s_G[my_base + k + 1] * __expf(s) * dj1;
+                            s += dj1 * Ah;
+                        }
+                        add_rows(j0, w0, j1, w1);
+                    }
+                } else {
+                    // pair list too long for LDS (very deep trees): chase parents and
+                    // score each pair from the B and C rows in memory
+                    const uint16_t* Ci = Cm + (bc_row0 + (size_t)i * G) * N;
+                    for (int j = i; j >= 0; j = s_par[j]) {
+                        const float dj = sdt[j];
+                        const float gij = dot_rows_lean<N>(Ci, Bm + (bc_row0 + (size_t)j * G) * N);
+                        add_rows(j, gij * __expf(s) * dj + (j == i ? Dh : 0.f), j, 0.f);
+                        s += dj * Ah;
+                    }
+                }
+            }
+            const float sc = __expf(s);
+            uint32_t o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int pt = e >> 1, r = 2 * (e & 1);  // columns 4pt + r, 4pt + r + 1
+                o[e] = pack_bf16x2(acc[pt][r] * sc + ta[2 * e], acc[pt][r + 1] * sc + ta[2 * e + 1]);
+            }
+            if (i < T) {
+                uint4* dst = (uint4*)(y + (((size_t)b * T + i) * H + h) * kHeadDim + 16 * q);
+                dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+                dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+            }
+        }
+        if (more) {
+            __builtin_amdgcn_s_waitcnt(0);  // head h+1: this thread's h0, x chunks and dt landed
+            stage_h0(buf ^ 1);
+        }
+        __syncthreads();  // head h+1 staged; buffer buf free for head h+2
+    }
+}
+
+template <int NW, int KS>
+static const void* wide_kernel() { return (const void*)verify_wide_kernel<NW, KS>; }
+
+static int wide_waves(int T) { return T <= 128 ? 8 : 16; }
+
+static const void* pick_wide(int T, int N) {
+    if (N == 64) return wide_waves(T) == 8 ? wide_kernel<8, 2>() : wide_kernel<16, 2>();
+    return wide_waves(T) == 8 ? wide_kernel<8, 4>() : wide_kernel<16, 4>();
+}
+
+hipError_t launch_verify_wide(const VerifyArgs& a, int HB, hipStream_t stream) {
+    const void* k = pick_wide(a.T, a.N);
+    dim3 grid((unsigned)(a.batch * (a.H / HB)));
+    void* args[] = {(void*)&a.x, (void*)&a.dt, (void*)&a.A, (void*)&a.B, (void*)&a.C, (void*)&a.D,
+                    (void*)&a.h0, (void*)&a.parent, (void*)&a.y, (void*)&a.tree_status,
+                    (void*)&a.T, (void*)&a.H, (void*)&a.G, (void*)&HB};
+    return hipLaunchKernel(k, grid, dim3(wide_waves(a.T) * kWave), args, 0, stream);
+}
+
+int verify_wide_blocks_per_cu(int T, int N) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pick_wide(T, N), wide_waves(T) * kWave, 0) !=
+        hipSuccess)
+        n = 1;
+    return n > 0 ? n : 1;
+}
+
+}  // namespace tsv
