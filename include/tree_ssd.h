@@ -67,6 +67,8 @@ typedef enum {
 /* Flags (tsv_shape.flags) */
 #define TSV_FLAG_FORCE_GENERIC 1 /* use the plain VALU verify kernel even where
                                     the MFMA kernel applies (testing aid) */
+#define TSV_FLAG_FORCE_WIDE 2    /* use the wide-tree MFMA verify kernel for any
+                                    tree size it supports (testing / tuning aid) */
 
 typedef struct {
     int32_t batch;           /* Bt >= 0 (0: nothing to do) */

@@ -1,7 +1,7 @@
 // api.hip -- extern "C" entry points of libtree_ssd.so (declared in
 // include/tree_ssd.h). Host-side validation happens here, before anything is
 // enqueued; the kernels themselves only see consistent shapes.
-#include "../../include/tree_ssd.h"
+#include "tree_ssd.h"
 #include "launch.hpp"
 
 namespace {
@@ -49,7 +49,7 @@ int default_heads_per_block(const tsv_shape* s, int blocks_per_cu) {
 }
 
 hipError_t launch_mfma(const tsv_shape* s, const tsv::VerifyArgs& a, hipStream_t hs) {
-    const bool small = s->n_nodes <= 64;
+    const bool small = s->n_nodes <= 64 && !(s->flags & TSV_FLAG_FORCE_WIDE);
     int hb = s->heads_per_block;
     if (hb == 0)
         hb = default_heads_per_block(s, small ? tsv::verify_small_blocks_per_cu(a.T, a.N)

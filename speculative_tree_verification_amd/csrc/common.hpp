@@ -69,6 +69,15 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Work-group barrier that orders LDS traffic only: global stores still in
+// flight are not waited for (a plain __syncthreads waits for every
+// outstanding vector memory operation, stores included).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Exclusive prefix sum over the NT threads of the block. `scratch` holds at
 // least NT/64 ints of LDS. Returns the exclusive prefix; *total gets the sum.
 template <int NT = kBlock>

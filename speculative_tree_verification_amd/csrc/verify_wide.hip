@@ -51,6 +51,11 @@ struct WideCfg {
     static_assert(TPM * N * 2 <= 4 * HL_BYTES, "C tile must fit the two h0 buffers");
 };
 
+template <int V>
+struct BufC {
+    static constexpr int value = V;
+};
+
 // byte offset of 16-byte chunk c of row r in a tile with `cpr` chunks per row
 // (a power of two), chunk index XOR-ed with `key`
 __device__ __forceinline__ int swz_off(int r, int c, int cpr, int key) {
@@ -78,7 +83,11 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
     constexpr int MAXP = kWideMaxPairs;
 
     __shared__ __attribute__((aligned(16))) unsigned char s_hl[2][2][Cfg::HL_BYTES];  // [buf][hi,lo]
-    __shared__ __attribute__((aligned(16))) unsigned char s_x[2][Cfg::X_BYTES];
+    // two distinct arrays (not one indexed by a runtime buffer number) so the
+    // compiler can tell that reads of one x buffer never alias the asynchronous
+    // loads into the other, and does not wait for the prefetch before them
+    __shared__ __attribute__((aligned(16))) unsigned char s_x0[Cfg::X_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char s_x1[Cfg::X_BYTES];
     __shared__ float s_dt[2][TPM];
     __shared__ int s_par[kMaxNodes];
     __shared__ int s_dep[kMaxNodes];
@@ -94,7 +103,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
     const int g = h_first / (H / G);
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int w = tid / kWave;
+    const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
     const int r16 = lane & 15;
     const int q = lane >> 4;
     const int i = 16 * w + r16;  // this lane's node
@@ -102,8 +111,8 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
 
     // ---- per-head staging
     // x rows of head h straight into LDS buffer `buf` (asynchronous, swizzled)
-    auto stage_x = [&](int h, int buf) {
-        unsigned char* xbase = s_x[buf];
+    auto stage_x = [&](int h, auto bufc) {
+        unsigned char* xbase = decltype(bufc)::value == 0 ? s_x0 : s_x1;
 #pragma unroll
         for (int m = 0; m < Cfg::X_INSTR; ++m) {
             const int blk = w * Cfg::X_INSTR + m;  // 1 KB block of the tile
@@ -144,7 +153,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
     };
 
     // head 0 streams in while the tree is set up (x into buffer 0; h0 into registers)
-    stage_x(h_first, 0);
+    stage_x(h_first, BufC<0>{});
     prefetch(h_first);
 
     // ---------------------------------------------------------------- set-up
@@ -194,18 +203,19 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
 
     // ---------------------------------------------------------------- heads
     const bool tile_live = 16 * w < T;
-    for (int hh = 0; hh < HB; ++hh) {
+    auto head = [&](int hh, auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
         const int h = h_first + hh;
-        const int buf = hh & 1;
         const bool more = hh + 1 < HB;
         if (more) {
-            stage_x(h + 1, buf ^ 1);
+            stage_x(h + 1, BufC<buf ^ 1>{});
             prefetch(h + 1);
         }
+        uint32_t o[8];
         if (tile_live) {
             const unsigned char* hib = s_hl[buf][0];
             const unsigned char* lob = s_hl[buf][1];
-            const unsigned char* sx = s_x[buf];
+            const unsigned char* sx = buf == 0 ? s_x0 : s_x1;
             const float* sdt = s_dt[buf];
 
             // read-out: acc[pt] holds (h0 C^T) rows p = 16q + 4pt + r, column i
@@ -291,23 +301,30 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
                 }
             }
             const float sc = __expf(s);
-            uint32_t o[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int pt = e >> 1, r = 2 * (e & 1);  // columns 4pt + r, 4pt + r + 1
                 o[e] = pack_bf16x2(acc[pt][r] * sc + ta[2 * e], acc[pt][r + 1] * sc + ta[2 * e + 1]);
             }
-            if (i < T) {
-                uint4* dst = (uint4*)(y + (((size_t)b * T + i) * H + h) * kHeadDim + 16 * q);
-                dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-                dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-            }
         }
-        if (more) {
-            __builtin_amdgcn_s_waitcnt(0);  // head h+1: this thread's h0, x chunks and dt landed
-            stage_h0(buf ^ 1);
+        // Stage head h+1 before storing y: on gfx9 the wait also counts stores, so
+        // stores issued first would be waited for here. The wait sits outside every
+        // branch so that no path reaches the barrier with an asynchronous LDS load
+        // still in flight (the compiler would otherwise wait for the y stores too).
+        __builtin_amdgcn_s_waitcnt(0);  // head h+1: this thread's h0, x chunks and dt landed
+        if (more) stage_h0(buf ^ 1);
+        if (tile_live && i < T) {
+            uint4* dst = (uint4*)(y + (((size_t)b * T + i) * H + h) * kHeadDim + 16 * q);
+            dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+            dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
         }
-        __syncthreads();  // head h+1 staged; buffer buf free for head h+2
+        // head h+1 staged (its asynchronous x loads were waited for above); buffer
+        // buf free for head h+2. The y stores of head h stay in flight.
+        lds_barrier();
+    };
+    for (int hh = 0; hh < HB; hh += 2) {
+        head(hh, BufC<0>{});
+        if (hh + 1 < HB) head(hh + 1, BufC<1>{});
     }
 }
 
