@@ -66,21 +66,33 @@ def commit_bytes(B, T, H, P, N, G, io, path_lens, Lmax):
             + 4 * H)
 
 
-def source_sha(*names):
+def source_sha():
+    """Digest of every kernel source (HBM counters are void once any changes)."""
     h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "speculative_tree_verification_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+    csrc = os.path.join(ROOT, "speculative_tree_verification_amd", "csrc")
+    for n in sorted(os.listdir(csrc)):
+        if n.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, n), "rb") as f:
+                h.update(n.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
 def traffic_record(kernel, workload, sha):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    """HBM bytes per launch from the committed rocprofv3 counter runs (the fenced
+    JSON block of profiles/hbm_traffic.md), if taken on the current sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        recs = json.load(f)
+        text = f.read()
+    a = text.find("```json")
+    if a < 0:
+        return None
+    b = text.find("```", a + 7)
+    try:
+        recs = json.loads(text[a + 7:b])
+    except ValueError:
+        return None
     for r in recs.get("records", []):
         if r.get("kernel") == kernel and r.get("workload") == workload and r.get("source_sha") == sha:
             return r
@@ -137,22 +149,20 @@ class Workload:
         return B * T * H * self.cfg.layers
 
     def step(self, s, ev=None):
-        """Enqueue one step on input set s; ev = (v0, v1, c0, c1) events around layer 0."""
+        """Enqueue one step on input set s; ev = (v0, v1, c0, c1) events around the
+        verify launches of all layers and around the commit launches."""
         vc, cc = self.verify_calls[s], self.commit_calls[s]
-        for l, f in enumerate(vc):
-            if ev is not None and l == 0:
-                ev[0].record()
-                f()
-                ev[1].record()
-            else:
-                f()
-        for l, f in enumerate(cc):
-            if ev is not None and l == 0:
-                ev[2].record()
-                f()
-                ev[3].record()
-            else:
-                f()
+        if ev is not None:
+            ev[0].record()
+        for f in vc:
+            f()
+        if ev is not None:
+            ev[1].record()
+            ev[2].record()
+        for f in cc:
+            f()
+        if ev is not None:
+            ev[3].record()
 
     def algorithmic_bytes(self):
         B, T, H, P, N, G = self.dims
@@ -195,8 +205,10 @@ def time_steps(torch, wl, steps, warmup):
     t_host = time.perf_counter() - t_host
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
-    v_us = [evs[i][0].elapsed_time(evs[i][1]) * 1e3 for i in range(steps)]
-    c_us = [evs[i][2].elapsed_time(evs[i][3]) * 1e3 for i in range(steps)]
+    # average launch duration: each event pair spans all layers' launches of one kernel
+    nl = len(wl.verify_calls[0])
+    v_us = [evs[i][0].elapsed_time(evs[i][1]) * 1e3 / nl for i in range(steps)]
+    c_us = [evs[i][2].elapsed_time(evs[i][3]) * 1e3 / nl for i in range(steps)]
     return dict(ms_per_step=ms, verify_us=sum(v_us) / steps, commit_us=sum(c_us) / steps,
                 verify_us_min=min(v_us), commit_us_min=min(c_us), host_ms=1e3 * t_host / steps)
 
@@ -212,29 +224,27 @@ def kernel_report(name, us, nbytes, workload, sha):
             "kernel": name, "avg_us": round(us, 3), "algorithmic_bytes": int(nbytes)}
 
 
-def cpu_baseline(wl, W, seconds):
-    """The fp64 oracle timed on a bounded sample of the same workload on the host."""
+def cpu_baseline(wl, seconds):
+    """The fp64 oracle timed on a bounded sample of the same workload on the host:
+    (layer, item) units, all heads each, verify + commit, cycled until about
+    `seconds` of oracle time have been spent."""
     from oracle import oracle as O
     B, T, H, P, N, G = wl.dims
+    units = [(l, b) for l in range(wl.cfg.layers) for b in range(B)]
     done_nodes, used, parts = 0, 0.0, 0
-    # sample unit: one layer's verify + commit for a block of items (all heads)
-    units = [(l, b0) for l in range(wl.cfg.layers) for b0 in range(B)]
-    items_per_unit = 1 if B > 1 else 1
-    for (l, b) in units:
+    while used < seconds:
+        l, b = units[parts % len(units)]
         inp = wl.host[l]
-        sel = [(b, h) for h in range(H)]
-        s = O.gather_slices(inp, wl.cfg.dtype, sel)
+        s = O.gather_slices(inp, wl.cfg.dtype, [(b, h) for h in range(H)])
         t0 = time.perf_counter()
         O.verify_slices(s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"], s["h0"], s["parent"])
         O.commit_slices(s["x"], s["dt"], s["A"], s["B"], s["h0"], s["parent"], s["accepted"],
                         s["accepted_len"], Lmax=inp["accepted"].shape[-1])
         used += time.perf_counter() - t0
-        done_nodes += T * H * items_per_unit
+        done_nodes += T * H
         parts += 1
-        if used >= seconds:
-            break
-    what = (f"{parts} of {len(units)} (layer, item) units of the workload, all {H} heads each: "
-            f"verify + commit in fp64")
+    what = (f"{parts} (layer, item) units cycled over the workload's {len(units)}, all {H} heads "
+            f"each: verify + commit in fp64, {used:.1f} s of oracle time")
     return {"value": round(done_nodes / used, 1), "unit": "nodes/s", "cores": O.num_threads(),
             "kind": "oracle", "sample": what, "seconds": round(used, 2)}
 
@@ -244,8 +254,9 @@ def run_workload(torch, bnd, W, cid, steps, warmup, hpb, keep_host):
     t = time_steps(torch, wl, steps, warmup)
     vb, cb = wl.algorithmic_bytes()
     name = wl.cfg.name
-    v = kernel_report("verify", t["verify_us"], vb, name, source_sha("verify_mfma.hip", "common.hpp"))
-    c = kernel_report("commit", t["commit_us"], cb, name, source_sha("commit.hip", "common.hpp"))
+    sha = source_sha()
+    v = kernel_report("verify", t["verify_us"], vb, name, sha)
+    c = kernel_report("commit", t["commit_us"], cb, name, sha)
     nodes_s = wl.nodes_per_step / (t["ms_per_step"] * 1e-3)
     log(f"[bench] workload {cid}: {t['ms_per_step']:.4f} ms/step, {nodes_s:.4g} nodes/s; "
         f"verify {t['verify_us']:.2f} us ({v['achieved']:.0f} GB/s), "
@@ -321,7 +332,7 @@ def main():
         out["secondary"] = secondary
     if not args.no_oracle:
         log("[bench] timing the CPU oracle on a sample of the workload")
-        out["cpu_baseline"] = cpu_baseline(wl, W, args.oracle_seconds)
+        out["cpu_baseline"] = cpu_baseline(wl, args.oracle_seconds)
     print(json.dumps(out), flush=True)
 
 
