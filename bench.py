@@ -66,14 +66,21 @@ def commit_bytes(B, T, H, P, N, G, io, path_lens, Lmax):
             + 4 * H)
 
 
-def source_sha():
-    """Digest of every kernel source (HBM counters are void once any changes)."""
+KERNEL_SOURCES = {
+    "verify": ("api.hip", "launch.hpp", "common.hpp", "verify_common.hpp", "verify_mfma.hip",
+               "verify_wide.hip", "verify_generic.hip"),
+    "commit": ("api.hip", "launch.hpp", "common.hpp", "commit.hip"),
+}
+
+
+def source_sha(kernel):
+    """Digest of the sources a kernel is built from (its HBM counters are void
+    once any of them changes)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "speculative_tree_verification_amd", "csrc")
-    for n in sorted(os.listdir(csrc)):
-        if n.endswith((".hip", ".hpp")):
-            with open(os.path.join(csrc, n), "rb") as f:
-                h.update(n.encode() + b"\0" + f.read())
+    for n in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(csrc, n), "rb") as f:
+            h.update(n.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -149,8 +156,8 @@ class Workload:
         return B * T * H * self.cfg.layers
 
     def step(self, s, ev=None):
-        """Enqueue one step on input set s; ev = (v0, v1, c0, c1) events around the
-        verify launches of all layers and around the commit launches."""
+        """Enqueue one step on input set s; ev = (e0, e1, e2): e0..e1 spans the
+        verify launches of all layers, e1..e2 the commit launches."""
         vc, cc = self.verify_calls[s], self.commit_calls[s]
         if ev is not None:
             ev[0].record()
@@ -158,11 +165,10 @@ class Workload:
             f()
         if ev is not None:
             ev[1].record()
-            ev[2].record()
         for f in cc:
             f()
         if ev is not None:
-            ev[3].record()
+            ev[2].record()
 
     def algorithmic_bytes(self):
         B, T, H, P, N, G = self.dims
@@ -192,7 +198,7 @@ def time_steps(torch, wl, steps, warmup):
         host_t.append(time.perf_counter() - t0)
         torch.cuda.synchronize()
     host_per_step = min(host_t) if host_t else 5e-3
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()  # barrier (one rank) + synchronize before the timed region
     cyc = sleep_cycles_for(torch, 1.5e3 * host_per_step * steps + 20.0)
@@ -208,7 +214,7 @@ def time_steps(torch, wl, steps, warmup):
     # average launch duration: each event pair spans all layers' launches of one kernel
     nl = len(wl.verify_calls[0])
     v_us = [evs[i][0].elapsed_time(evs[i][1]) * 1e3 / nl for i in range(steps)]
-    c_us = [evs[i][2].elapsed_time(evs[i][3]) * 1e3 / nl for i in range(steps)]
+    c_us = [evs[i][1].elapsed_time(evs[i][2]) * 1e3 / nl for i in range(steps)]
     return dict(ms_per_step=ms, verify_us=sum(v_us) / steps, commit_us=sum(c_us) / steps,
                 verify_us_min=min(v_us), commit_us_min=min(c_us), host_ms=1e3 * t_host / steps)
 
@@ -254,9 +260,8 @@ def run_workload(torch, bnd, W, cid, steps, warmup, hpb, keep_host):
     t = time_steps(torch, wl, steps, warmup)
     vb, cb = wl.algorithmic_bytes()
     name = wl.cfg.name
-    sha = source_sha()
-    v = kernel_report("verify", t["verify_us"], vb, name, sha)
-    c = kernel_report("commit", t["commit_us"], cb, name, sha)
+    v = kernel_report("verify", t["verify_us"], vb, name, source_sha("verify"))
+    c = kernel_report("commit", t["commit_us"], cb, name, source_sha("commit"))
     nodes_s = wl.nodes_per_step / (t["ms_per_step"] * 1e-3)
     log(f"[bench] workload {cid}: {t['ms_per_step']:.4f} ms/step, {nodes_s:.4g} nodes/s; "
         f"verify {t['verify_us']:.2f} us ({v['achieved']:.0f} GB/s), "
