@@ -61,6 +61,17 @@ struct Elem<uint16_t> {
     }
 };
 
+// ---------------------------------------------------------------- launch helpers
+// Work-groups go to the 8 XCDs (each with its own L2) in turn: block x runs on
+// XCD x % 8. This renumbering gives consecutive logical indices to the blocks
+// of one XCD (a bijection of [0, n)), so that neighbouring work-groups that read
+// the same rows (an item's tree and B/C tile) share one L2.
+__device__ __forceinline__ int xcd_block(int x, int n) {
+    constexpr int kXcd = 8;
+    const int q = n / kXcd, r = n % kXcd, c = x % kXcd;
+    return c * q + min(c, r) + x / kXcd;
+}
+
 // ---------------------------------------------------------------- sync helpers
 // Order LDS traffic between the lanes of one wave (no hardware barrier).
 __device__ __forceinline__ void wave_sync() {

@@ -24,7 +24,8 @@
 //  * the intra-tree term is sparse (depth+1 terms per node), so it is summed
 //    over each node's ancestor-pair list in fp32 VALU, with exp evaluated only
 //    on ancestor pairs and the decay summed along the path (no cancellation).
-//  * the next head's h0 / x / dt are loaded while the current one computes.
+//  * the next head's h0 and x are loaded while the current one computes; the
+//    step sizes of all HB heads are staged once, at set-up.
 #include "launch.hpp"
 #include "verify_common.hpp"
 
@@ -32,13 +33,13 @@ namespace tsv {
 
 constexpr int kP = kHeadDim;
 constexpr int kXStride = 20;  // LDS row stride (uint16) of a wave's 16-column x slice
+constexpr int kSmallMaxHeads = 16;  // heads per work-group at most (LDS step-size table)
 
 template <int TI>
 struct MfmaCfg {
     static constexpr int TP = 16 * TI;  // node count padded to whole 16-node tiles
     static constexpr int kMaxPairs = TP * (TP + 1) / 2;  // every tree of TP nodes fits
     static constexpr int kXChunks = (2 * TP + kWave - 1) / kWave;
-    static constexpr int kDtChunks = (TP + kWave - 1) / kWave;
 };
 
 template <int TI, int KS>
@@ -60,15 +61,17 @@ __global__ __launch_bounds__(kBlock) void verify_mfma_kernel(
     __shared__ uint16_t s_pair[MAXP];  // node i in the low byte, ancestor j in the high byte
     __shared__ float s_G[MAXP];
     __shared__ __attribute__((aligned(16))) uint16_t s_x[4][TP * kXStride];
-    __shared__ float s_dtw[4][TP];
+    // dt of every head of the work-group, bf16 [head][node], staged once
+    __shared__ uint16_t s_dth[kSmallMaxHeads * TP];
     // B and C rows of the item's group, padded by 16 bytes per row
     constexpr int BCS = N + 8;
     __shared__ __attribute__((aligned(16))) uint16_t s_Bt[TP * BCS];
     __shared__ __attribute__((aligned(16))) uint16_t s_Ct[TP * BCS];
 
     const int nblk = H / HB;
-    const int b = blockIdx.x / nblk;
-    const int h_first = (blockIdx.x % nblk) * HB;
+    const int blk = xcd_block(blockIdx.x, gridDim.x);
+    const int b = blk / nblk;
+    const int h_first = (blk % nblk) * HB;
     const int g = h_first / (H / G);
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -78,13 +81,12 @@ __global__ __launch_bounds__(kBlock) void verify_mfma_kernel(
     const size_t bc_row0 = ((size_t)b * T) * G + g;  // row (b, node 0, g) of B and C
 
     // Loads that do not depend on the tree are issued first so that their
-    // latency overlaps the tree set-up: the first head's h0 / x / dt and the C
-    // operands (exact bf16 B-matrix of the read-out MFMA, shared by all heads).
+    // latency overlaps the tree set-up: the first head's h0 / x, the step sizes
+    // of all heads and the C operands (exact bf16 B-matrix of the read-out MFMA,
+    // shared by all heads).
     uint16_t* sx = s_x[w];
-    float* sdt = s_dtw[w];
     float4 hr[KS][2];
     uint4 xr[Cfg::kXChunks];
-    uint32_t dr[Cfg::kDtChunks];
 
     auto load_head = [&](int h) {
         const float* hrow = h0 + (((size_t)b * H + h) * kP + 16 * w + r16) * N + 8 * q;
@@ -101,13 +103,12 @@ __global__ __launch_bounds__(kBlock) void verify_mfma_kernel(
             if (row < T)
                 xr[m] = *(const uint4*)(x + (((size_t)b * T + row) * H + h) * kP + 16 * w + 8 * half);
         }
-#pragma unroll
-        for (int m = 0; m < Cfg::kDtChunks; ++m) {
-            const int i = lane + kWave * m;
-            dr[m] = (i < T) ? dt[((size_t)b * T + i) * H + h] : 0u;
-        }
     };
     load_head(h_first);
+    for (int e = tid; e < T * HB; e += kBlock) {
+        const int n = e / HB, hh = e - n * HB;  // consecutive threads: consecutive heads of node n
+        s_dth[hh * TP + n] = dt[((size_t)b * T + n) * H + h_first + hh];
+    }
 
     // B and C tiles: loaded with the first head, before the tree is known
     constexpr int CPR = N / 8;
@@ -164,7 +165,8 @@ __global__ __launch_bounds__(kBlock) void verify_mfma_kernel(
     // ---------------------------------------------------------------- heads
     for (int hh = 0; hh < HB; ++hh) {
         const int h = h_first + hh;
-        // stage this head's x slice and dt in the wave's own LDS region
+        const uint16_t* sdt = s_dth + hh * TP;
+        // stage this head's x slice in the wave's own LDS region
         wave_sync();
 #pragma unroll
         for (int m = 0; m < Cfg::kXChunks; ++m) {
@@ -175,11 +177,6 @@ __global__ __launch_bounds__(kBlock) void verify_mfma_kernel(
                 dst[0] = make_uint2(xr[m].x, xr[m].y);
                 dst[1] = make_uint2(xr[m].z, xr[m].w);
             }
-        }
-#pragma unroll
-        for (int m = 0; m < Cfg::kDtChunks; ++m) {
-            const int i = lane + kWave * m;
-            if (i < T) sdt[i] = bf16_bits_to_f32(dr[m]);
         }
         bf16x8 hi[KS], lo[KS];
 #pragma unroll
@@ -211,7 +208,7 @@ __global__ __launch_bounds__(kBlock) void verify_mfma_kernel(
             const int cnt = s_dep[i] + 1;
             for (int k = 0; k < cnt; ++k) {
                 const int j = s_pair[base + k] >> 8;
-                const float dtj = sdt[j];
+                const float dtj = bf16_bits_to_f32(sdt[j]);
                 const float wt = s_G[base + k] * __expf(s) * dtj;
                 const uint2 xv = *(const uint2*)(sx + j * kXStride + 4 * q);
                 t0 += wt * lo_bf16(xv.x);
@@ -244,6 +241,12 @@ static const void* pick_small(int T, int N) {
 }
 
 hipError_t launch_verify_small(const VerifyArgs& a, int HB, hipStream_t stream) {
+    // heads per work-group: the largest divisor of the requested count that the
+    // LDS step-size table holds (results do not depend on it)
+    int hb = 1;
+    for (int d = 1; d <= kSmallMaxHeads && d <= HB; ++d)
+        if (HB % d == 0) hb = d;
+    HB = hb;
     const void* k = pick_small(a.T, a.N);
     dim3 grid((unsigned)(a.batch * (a.H / HB)));
     void* args[] = {(void*)&a.x, (void*)&a.dt, (void*)&a.A, (void*)&a.B, (void*)&a.C, (void*)&a.D,

@@ -36,6 +36,9 @@
 namespace tsv {
 
 constexpr int kWideMaxPairs = 2048;
+// heads one work-group handles at most: the step sizes of all of them are
+// staged once, at set-up, as a bf16 [head][node] table in LDS
+constexpr int kWideMaxHeads = 20;
 
 template <int NW, int KS>
 struct WideCfg {
@@ -88,7 +91,9 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
     // loads into the other, and does not wait for the prefetch before them
     __shared__ __attribute__((aligned(16))) unsigned char s_x0[Cfg::X_BYTES];
     __shared__ __attribute__((aligned(16))) unsigned char s_x1[Cfg::X_BYTES];
-    __shared__ float s_dt[2][TPM];
+    // dt of every head of the work-group, bf16 [head][node]: one coalesced pass
+    // at set-up (a per-head read would touch one cache sector per node per head)
+    __shared__ uint16_t s_dth[kWideMaxHeads * TPM];
     __shared__ int s_par[kMaxNodes];
     __shared__ int s_dep[kMaxNodes];
     __shared__ int s_off[kMaxNodes];
@@ -98,8 +103,9 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
     __shared__ float s_G[MAXP];
 
     const int nblk = H / HB;
-    const int b = blockIdx.x / nblk;
-    const int h_first = (blockIdx.x % nblk) * HB;
+    const int blk = xcd_block(blockIdx.x, gridDim.x);
+    const int b = blk / nblk;
+    const int h_first = (blk % nblk) * HB;
     const int g = h_first / (H / G);
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -126,14 +132,12 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
     };
     // h0 of head h into registers (consecutive threads, consecutive float4)
     float4 hreg[Cfg::H0_F4];
-    uint32_t dreg;
     auto prefetch = [&](int h) {
         const float4* src = (const float4*)(h0 + ((size_t)b * H + h) * kHeadDim * N);
 #pragma unroll
         for (int m = 0; m < Cfg::H0_F4; ++m) hreg[m] = src[tid + NT * m];
-        dreg = (tid < T) ? dt[((size_t)b * T + tid) * H + h] : 0u;
     };
-    // split the registers into bf16 hi / lo planes of buffer `buf`, and dt
+    // split the registers into bf16 hi / lo planes of buffer `buf`
     auto stage_h0 = [&](int buf) {
         unsigned char* hib = s_hl[buf][0];
         unsigned char* lob = s_hl[buf][1];
@@ -149,12 +153,15 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
             *(uint2*)(hib + off) = make_uint2(h01, h23);
             *(uint2*)(lob + off) = make_uint2(l01, l23);
         }
-        if (tid < TPM) s_dt[buf][tid] = bf16_bits_to_f32(dreg);
     };
 
     // head 0 streams in while the tree is set up (x into buffer 0; h0 into registers)
     stage_x(h_first, BufC<0>{});
     prefetch(h_first);
+    for (int e = tid; e < T * HB; e += NT) {
+        const int n = e / HB, hh = e - n * HB;  // consecutive threads: consecutive heads of node n
+        s_dth[hh * TPM + n] = dt[((size_t)b * T + n) * H + h_first + hh];
+    }
 
     // ---------------------------------------------------------------- set-up
     const int st = load_tree(parent + (size_t)b * T, T, s_par);
@@ -216,7 +223,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
             const unsigned char* hib = s_hl[buf][0];
             const unsigned char* lob = s_hl[buf][1];
             const unsigned char* sx = buf == 0 ? s_x0 : s_x1;
-            const float* sdt = s_dt[buf];
+            const uint16_t* sdt = s_dth + hh * TPM;
 
             // read-out: acc[pt] holds (h0 C^T) rows p = 16q + 4pt + r, column i
             f32x4 acc[4];
@@ -275,14 +282,14 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
                     float w0 = 0.f;
                     for (; k < my_cnt; k += 2) {
                         j0 = s_pair[my_base + k] >> 8;
-                        const float dj0 = sdt[j0];
+                        const float dj0 = bf16_bits_to_f32(sdt[j0]);
                         w0 = s_G[my_base + k] * __expf(s) * dj0 + (k == 0 ? Dh : 0.f);
                         s += dj0 * Ah;
                         int j1 = j0;
                         float w1 = 0.f;
                         if (k + 1 < my_cnt) {
                             j1 = s_pair[my_base + k + 1] >> 8;
-                            const float dj1 = sdt[j1];
+                            const float dj1 = bf16_bits_to_f32(sdt[j1]);
                             w1 = s_G[my_base + k + 1] * __expf(s) * dj1;
                             s += dj1 * Ah;
                         }
@@ -293,7 +300,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
                     // score each pair from the B and C rows in memory
                     const uint16_t* Ci = Cm + (bc_row0 + (size_t)i * G) * N;
                     for (int j = i; j >= 0; j = s_par[j]) {
-                        const float dj = sdt[j];
+                        const float dj = bf16_bits_to_f32(sdt[j]);
                         const float gij = dot_rows_lean<N>(Ci, Bm + (bc_row0 + (size_t)j * G) * N);
                         add_rows(j, gij * __expf(s) * dj + (j == i ? Dh : 0.f), j, 0.f);
                         s += dj * Ah;
@@ -311,7 +318,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
         // stores issued first would be waited for here. The wait sits outside every
         // branch so that no path reaches the barrier with an asynchronous LDS load
         // still in flight (the compiler would otherwise wait for the y stores too).
-        __builtin_amdgcn_s_waitcnt(0);  // head h+1: this thread's h0, x chunks and dt landed
+        __builtin_amdgcn_s_waitcnt(0);  // head h+1: this thread's h0 and x chunks landed
         if (more) stage_h0(buf ^ 1);
         if (tile_live && i < T) {
             uint4* dst = (uint4*)(y + (((size_t)b * T + i) * H + h) * kHeadDim + 16 * q);
@@ -339,6 +346,12 @@ static const void* pick_wide(int T, int N) {
 }
 
 hipError_t launch_verify_wide(const VerifyArgs& a, int HB, hipStream_t stream) {
+    // heads per work-group: the largest divisor of the requested count that the
+    // LDS step-size table holds (results do not depend on it)
+    int hb = 1;
+    for (int d = 1; d <= kWideMaxHeads && d <= HB; ++d)
+        if (HB % d == 0) hb = d;
+    HB = hb;
     const void* k = pick_wide(a.T, a.N);
     dim3 grid((unsigned)(a.batch * (a.H / HB)));
     void* args[] = {(void*)&a.x, (void*)&a.dt, (void*)&a.A, (void*)&a.B, (void*)&a.C, (void*)&a.D,
