@@ -6,12 +6,12 @@
 // with c_k = sum_{m >= k} dt_{j_m} A the log decay from token j_k to the end
 // of the path (suffix sums, so no cancellation).
 //
-// Work-group = (batch item, head, chunk of the P x N state). The state chunk is
-// loaded first; meanwhile the tree and the path are validated bit-exactly from
-// LDS and the path rows of x, dt and B are staged, so the dependency chain is
-// two memory round trips (tree + path indices, then path rows). The state is
-// streamed once: each element is read and written by the same thread (rank-L
-// update in registers). Invalid items leave h0 untouched.
+// Work-group = (batch item, head, chunk of the P x N state). The state chunk,
+// the tree and the path indices are loaded together; the tree and the path are
+// validated bit-exactly from LDS; then dt, x and B of the path rows are staged
+// in one more round trip (two in all for paths of up to 16 entries). The state
+// is streamed once: each element is read and written by the same thread
+// (rank-L update in registers). Invalid items leave h0 untouched.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -30,7 +30,7 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
     __shared__ int s_path[kMaxNodes];
     __shared__ float s_w[kMaxNodes];
     __shared__ float s_w0;
-    // [kPathChunk][P] weighted x rows, then [kPathChunk][N] B rows
+    // [kPathChunk][P] x rows, then [kPathChunk][N] B rows, of the path
     extern __shared__ __attribute__((aligned(16))) float s_dyn[];
     float* s_wx = s_dyn;
     float* s_B = s_dyn + kPathChunk * P;
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
         }
     }
 
-    // tree and path indices (one round trip)
+    // tree and path indices (one round trip, with the state chunk)
     const int len = accepted_len[b];
     const bool len_ok = len >= 0 && len <= Lmax;
     if (len_ok && tid < len) s_path[tid] = accepted[(size_t)b * Lmax + tid];
@@ -84,40 +84,73 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
     if (hd == 0 && chunk == 0 && tid == 0 && tree_status) tree_status[b] = st;
     if (st || len == 0) return;
 
-    // decay weights along the path: w_k = exp(c_{k+1}) dt_{j_k}, w0 = exp(c_0)
+    // path rows, one round trip per chunk of kPathChunk entries: dt of every
+    // entry, raw x rows and B rows; the decay weights are formed once all dt are in
     const float Ah = A[hd];
-    if (tid < len) s_w[tid] = Elem<TIO>::ld(dt, ((size_t)b * T + s_path[tid]) * H + hd);
-    __syncthreads();
-    if (tid == 0) {
-        float c = 0.f;
-        for (int k = len - 1; k >= 0; --k) {
-            const float dtk = s_w[k];
-            s_w[k] = expf(c) * dtk;
-            c += dtk * Ah;
+    auto stage_rows = [&](int k0, int kn) {
+        if (sizeof(TIO) == 2 && P % 8 == 0 && N % 8 == 0) {
+            // bf16 rows in 16-byte pieces: one x piece and one B piece per thread
+            // and pass, both loads issued before either is used (one pass for
+            // head_dim 64 and d_state 128)
+            const int px = P / 8, pb = N / 8;
+            const int nx = kn * px, nb = kn * pb;
+            auto put8 = [](float* dst, uint4 v) {
+                *(float4*)dst = make_float4(bf16_bits_to_f32(v.x & 0xffff), bf16_bits_to_f32(v.x >> 16),
+                                            bf16_bits_to_f32(v.y & 0xffff), bf16_bits_to_f32(v.y >> 16));
+                *(float4*)(dst + 4) = make_float4(bf16_bits_to_f32(v.z & 0xffff), bf16_bits_to_f32(v.z >> 16),
+                                                  bf16_bits_to_f32(v.w & 0xffff), bf16_bits_to_f32(v.w >> 16));
+            };
+            for (int e = tid; e < max(nx, nb); e += kBlock) {
+                uint4 vx = make_uint4(0, 0, 0, 0), vb = vx;
+                if (e < nx) {
+                    const int k = e / px, c = e - k * px;
+                    vx = *(const uint4*)(x + (((size_t)b * T + s_path[k0 + k]) * H + hd) * P + 8 * c);
+                }
+                if (e < nb) {
+                    const int k = e / pb, c = e - k * pb;
+                    vb = *(const uint4*)(Bm + (((size_t)b * T + s_path[k0 + k]) * G + g) * N + 8 * c);
+                }
+                if (e < nx) put8(s_wx + 8 * e, vx);  // piece e: row e / px, columns 8 (e % px) ..
+                if (e < nb) put8(s_B + 8 * e, vb);
+            }
+            return;
         }
-        s_w0 = expf(c);
-    }
-
-    for (int k0 = 0; k0 < len; k0 += kPathChunk) {
-        const int kn = min(kPathChunk, len - k0);
-        __syncthreads();  // weights ready / previous chunk consumed
         for (int e = tid; e < kn * P; e += kBlock) {
             const int k = e / P, p = e - k * P;
-            s_wx[k * P + p] =
-                s_w[k0 + k] * Elem<TIO>::ld(x, (((size_t)b * T + s_path[k0 + k]) * H + hd) * P + p);
+            s_wx[k * P + p] = Elem<TIO>::ld(x, (((size_t)b * T + s_path[k0 + k]) * H + hd) * P + p);
         }
         for (int e = tid; e < kn * N; e += kBlock) {
             const int k = e / N, n = e - k * N;
             s_B[k * N + n] = Elem<TIO>::ld(Bm, (((size_t)b * T + s_path[k0 + k]) * G + g) * N + n);
         }
+    };
+    for (int k0 = 0; k0 < len; k0 += kPathChunk) {
+        const int kn = min(kPathChunk, len - k0);
+        if (k0 > 0) __syncthreads();  // previous chunk consumed
+        if (k0 == 0 && tid < len) s_w[tid] = Elem<TIO>::ld(dt, ((size_t)b * T + s_path[tid]) * H + hd);
+        stage_rows(k0, kn);
         __syncthreads();
         if (k0 == 0) {
+            // decay weights along the path: w_k = exp(c_{k+1}) dt_{j_k}, w0 = exp(c_0)
+            if (tid == 0) {
+                float c = 0.f;
+                for (int k = len - 1; k >= 0; --k) {
+                    const float dtk = s_w[k];
+                    s_w[k] = expf(c) * dtk;
+                    c += dtk * Ah;
+                }
+                s_w0 = expf(c);
+            }
+            __syncthreads();
             const float w0 = s_w0;
 #pragma unroll
             for (int v = 0; v < kVec; ++v)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) acc[v][c] *= w0;
         }
+        // weight the staged x rows in place
+        for (int e = tid; e < kn * P; e += kBlock) s_wx[e] *= s_w[k0 + e / P];
+        __syncthreads();
 #pragma unroll
         for (int v = 0; v < kVec; ++v) {
             if (VEC) {

@@ -116,14 +116,29 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
 }
 
 // ---------------------------------------------------------------- topology
-// Stage parent[0..T) into LDS and validate it: returns the status bits
+// parent[threadIdx.x] of a tree (0 for threads past T; T >= 1): issue this
+// load early and hand the value to check_tree, so that other loads overlap its
+// latency. The load is unconditional (clamped index), which lets the compiler
+// count exactly how many later loads it may leave in flight; the empty asm
+// hides the pointer's provenance so that the load is not treated as invariant
+// and moved next to its use, behind the loads issued after it, and the
+// scheduling barrier keeps it first.
+__device__ __forceinline__ int load_parent(const int32_t* parent_b, int T) {
+    typedef const int32_t __attribute__((address_space(1))) gint;
+    const int i = threadIdx.x;
+    uint64_t u = (uint64_t)parent_b;
+    asm volatile("" : "+s"(u));
+    const int p = ((gint*)u)[i < T ? i : T - 1];
+    __builtin_amdgcn_sched_barrier(0);
+    return i < T ? p : 0;
+}
+
+// Stage the parents into LDS and validate them: returns the status bits
 // (kStBadRoot | kStBadParent), identical in every thread. Acts as a barrier.
-__device__ __forceinline__ int load_tree(const int32_t* __restrict__ parent_b, int T,
-                                         int* s_par) {
+__device__ __forceinline__ int check_tree(int p, int T, int* s_par) {
     const int i = threadIdx.x;
     int bad_root = 0, bad_par = 0;
     if (i < T) {
-        int p = parent_b[i];
         s_par[i] = p;
         if (i == 0)
             bad_root = (p != -1);
@@ -133,6 +148,12 @@ __device__ __forceinline__ int load_tree(const int32_t* __restrict__ parent_b, i
     int r = __syncthreads_or(bad_root) ? kStBadRoot : 0;
     r |= __syncthreads_or(bad_par) ? kStBadParent : 0;
     return r;
+}
+
+// load_parent + check_tree in one step.
+__device__ __forceinline__ int load_tree(const int32_t* __restrict__ parent_b, int T,
+                                         int* s_par) {
+    return check_tree(load_parent(parent_b, T), T, s_par);
 }
 
 // Depth (edges from the root) of node threadIdx.x by pointer jumping over the

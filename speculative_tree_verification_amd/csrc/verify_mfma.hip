@@ -75,15 +75,17 @@ __global__ __launch_bounds__(kBlock) void verify_mfma_kernel(
     const int g = h_first / (H / G);
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int w = tid / kWave;
+    const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
     const int r16 = lane & 15;
     const int q = lane >> 4;
     const size_t bc_row0 = ((size_t)b * T) * G + g;  // row (b, node 0, g) of B and C
 
-    // Loads that do not depend on the tree are issued first so that their
-    // latency overlaps the tree set-up: the first head's h0 / x, the step sizes
-    // of all heads and the C operands (exact bf16 B-matrix of the read-out MFMA,
-    // shared by all heads).
+    // No set-up load depends on the tree, so all of them leave at once: the
+    // parents first, then the first head's h0 and x, the B and C tiles of the
+    // item's group and the step sizes of all HB heads. Vector memory operations
+    // complete in order and every load is unconditional (clamped rows), so the
+    // tree check waits for the parents only and the tree work overlaps the rest.
+    const int par_i = load_parent(parent + (size_t)b * T, T);
     uint16_t* sx = s_x[w];
     float4 hr[KS][2];
     uint4 xr[Cfg::kXChunks];
@@ -98,47 +100,52 @@ __global__ __launch_bounds__(kBlock) void verify_mfma_kernel(
 #pragma unroll
         for (int m = 0; m < Cfg::kXChunks; ++m) {
             const int c = lane + kWave * m;
-            const int row = c >> 1, half = c & 1;
-            xr[m] = make_uint4(0, 0, 0, 0);
-            if (row < T)
-                xr[m] = *(const uint4*)(x + (((size_t)b * T + row) * H + h) * kP + 16 * w + 8 * half);
+            const int row = min(c >> 1, T - 1), half = c & 1;  // rows past T are not staged
+            xr[m] = *(const uint4*)(x + (((size_t)b * T + row) * H + h) * kP + 16 * w + 8 * half);
         }
     };
     load_head(h_first);
-    for (int e = tid; e < T * HB; e += kBlock) {
-        const int n = e / HB, hh = e - n * HB;  // consecutive threads: consecutive heads of node n
-        s_dth[hh * TP + n] = dt[((size_t)b * T + n) * H + h_first + hh];
-    }
 
-    // B and C tiles: loaded with the first head, before the tree is known
     constexpr int CPR = N / 8;
     constexpr int BC_PER_THREAD = (TP * CPR + kBlock - 1) / kBlock;
+    constexpr int DT_PT = (kSmallMaxHeads * TP + kBlock - 1) / kBlock;
     uint4 breg[BC_PER_THREAD], cregt[BC_PER_THREAD];
+    uint32_t dtr[DT_PT];
 #pragma unroll
     for (int m = 0; m < BC_PER_THREAD; ++m) {
         const int c = tid + kBlock * m;
-        const int r = c / CPR, ch = c % CPR;
-        breg[m] = cregt[m] = make_uint4(0, 0, 0, 0);
-        if (r < T) {
-            breg[m] = *(const uint4*)(Bm + (bc_row0 + (size_t)r * G) * N + 8 * ch);
-            cregt[m] = *(const uint4*)(Cm + (bc_row0 + (size_t)r * G) * N + 8 * ch);
-        }
+        const int r = min(c / CPR, T - 1), ch = c % CPR;
+        breg[m] = *(const uint4*)(Bm + (bc_row0 + (size_t)r * G) * N + 8 * ch);
+        cregt[m] = *(const uint4*)(Cm + (bc_row0 + (size_t)r * G) * N + 8 * ch);
+    }
+#pragma unroll
+    for (int m = 0; m < DT_PT; ++m) {
+        const int e = min(tid + kBlock * m, T * HB - 1);
+        const int n = e / HB, hh = e - n * HB;  // consecutive threads: consecutive heads of node n
+        dtr[m] = dt[((size_t)b * T + n) * H + h_first + hh];
     }
 
     // ---------------------------------------------------------------- set-up
-    const int st = load_tree(parent + (size_t)b * T, T, s_par);
+    const int st = check_tree(par_i, T, s_par);
     if (h_first == 0 && tid == 0 && tree_status) tree_status[b] = st;
     if (st) return;
+    const int total_pairs = build_pairs(s_par, T, s_dep, s_off, s_scratch, s_scan, s_pair, MAXP);
 #pragma unroll
     for (int m = 0; m < BC_PER_THREAD; ++m) {
         const int c = tid + kBlock * m;
         const int r = c / CPR, ch = c % CPR;
         if (r < TP) {
-            *(uint4*)(s_Bt + r * BCS + 8 * ch) = breg[m];
-            *(uint4*)(s_Ct + r * BCS + 8 * ch) = cregt[m];
+            const bool live = r < T;
+            *(uint4*)(s_Bt + r * BCS + 8 * ch) = live ? breg[m] : make_uint4(0, 0, 0, 0);
+            *(uint4*)(s_Ct + r * BCS + 8 * ch) = live ? cregt[m] : make_uint4(0, 0, 0, 0);
         }
     }
-    const int total_pairs = build_pairs(s_par, T, s_dep, s_off, s_scratch, s_scan, s_pair, MAXP);
+#pragma unroll
+    for (int m = 0; m < DT_PT; ++m) {
+        const int e = tid + kBlock * m;
+        const int n = e / HB, hh = e - n * HB;
+        if (e < T * HB) s_dth[hh * TP + n] = (uint16_t)dtr[m];
+    }
     __syncthreads();
     // ancestor-pair scores G_ij = C_i . B_j from the LDS tiles, once for all heads
     for (int pq = tid; pq < total_pairs; pq += kBlock) {

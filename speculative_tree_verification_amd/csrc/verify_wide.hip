@@ -7,7 +7,7 @@
 // G = C B^T on ancestor pairs only, cum = L (dt A) along root paths.
 //
 // Mapping for MI355X (one work-group of NW = 8 or 16 waves per CU, i.e. two or
-// four waves per SIMD, ~145 KB of LDS):
+// four waves per SIMD, up to ~155 KB of LDS):
 //  * work-group = (item b, block of HB heads of one group). The tree set-up
 //    (validation, depth by pointer jumping, ancestor-pair lists, pair scores
 //    G_ij) runs once and serves all HB heads.
@@ -28,8 +28,13 @@
 //    (D x_i joins the node's own term); exp is evaluated on ancestor pairs only
 //    and the decay is summed along the path (no cancellation). Two ancestors
 //    are taken at a time: their x rows are interleaved into bf16 pairs and
-//    dotted (v_dot2_f32_bf16, fp32 accumulate) with the two weights, each
-//    split into bf16 high and low parts (about 16 significant bits).
+//    dotted (v_dot2_f32_bf16, fp32 accumulate) with the two weights. The masked
+//    decay weights are rounded once to bf16, except those of the node's own
+//    row (which carries D) and its parent, which keep a bf16 residual as well
+//    (about 16 significant bits).
+//  * set-up loads (C and B tiles, parents, the step sizes of all HB heads)
+//    are independent of the tree and leave together; pair scores are formed
+//    from LDS with the B tile passing through the second x buffer.
 #include "launch.hpp"
 #include "verify_common.hpp"
 
@@ -155,48 +160,95 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
         }
     };
 
-    // head 0 streams in while the tree is set up (x into buffer 0; h0 into registers)
-    stage_x(h_first, BufC<0>{});
-    prefetch(h_first);
-    for (int e = tid; e < T * HB; e += NT) {
-        const int n = e / HB, hh = e - n * HB;  // consecutive threads: consecutive heads of node n
-        s_dth[hh * TPM + n] = dt[((size_t)b * T + n) * H + h_first + hh];
-    }
-
     // ---------------------------------------------------------------- set-up
-    const int st = load_tree(parent + (size_t)b * T, T, s_par);
+    // No set-up load depends on the tree, so all of them leave at once: the
+    // parents first, then the item's C and B tiles (chunk c = tid + NT m is row
+    // c / CPR, chunk column c % CPR), the step sizes of all HB heads and head 0's
+    // h0. Vector memory operations complete in order, so the tree check waits
+    // for the parents only. Head 0's x goes out right after it: while an
+    // asynchronous LDS load is in flight the compiler waits for every
+    // outstanding load at each register use, so the tree work that needs no
+    // memory comes first and overlaps the rest of the traffic.
+    const int par_i = load_parent(parent + (size_t)b * T, T);
+    constexpr int BC_PT = TPM * CPR / NT;                       // tile chunks per thread
+    constexpr int DT_PT = (kWideMaxHeads * TPM + NT - 1) / NT;  // step sizes per thread
+    uint4 ct[BC_PT], bt[BC_PT];
+    uint32_t dtr[DT_PT];
+    // (loads are unconditional, from clamped rows, so that the compiler can
+    // count the loads still in flight at each later wait; rows past T are zeroed)
+#pragma unroll
+    for (int m = 0; m < BC_PT; ++m) {
+        const int c = tid + NT * m, r = c / CPR, ch = c % CPR;
+        const size_t off = (bc_row0 + (size_t)min(r, T - 1) * G) * N + 8 * ch;
+        ct[m] = *(const uint4*)(Cm + off);
+        bt[m] = *(const uint4*)(Bm + off);
+    }
+#pragma unroll
+    for (int m = 0; m < DT_PT; ++m) {
+        const int e = min(tid + NT * m, T * HB - 1);
+        const int n = e / HB, hh = e - n * HB;  // consecutive threads: consecutive heads of node n
+        dtr[m] = dt[((size_t)b * T + n) * H + h_first + hh];
+    }
+    prefetch(h_first);
+    const int st = check_tree(par_i, T, s_par);
     if (h_first == 0 && tid == 0 && tree_status) tree_status[b] = st;
-    if (st) {
-        __builtin_amdgcn_s_waitcnt(0);  // drain the asynchronous LDS loads before leaving
-        return;
-    }
-    // C tile (T x N bf16, rows swizzled) in the h0 buffers, which are still free
-    unsigned char* cbase = &s_hl[0][0][0];
-    for (int c = tid; c < TPM * CPR; c += NT) {
-        const int r = c / CPR, ch = c % CPR;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (r < T) v = *(const uint4*)(Cm + (bc_row0 + (size_t)r * G) * N + 8 * ch);
-        *(uint4*)(cbase + swz_off(r, ch, CPR, r)) = v;
-    }
+    if (st) return;
+    stage_x(h_first, BufC<0>{});
     const int total_pairs = build_pairs<NT>(s_par, T, s_dep, s_off, s_scratch, s_scan, s_pair, MAXP);
     const bool cached = total_pairs <= MAXP;
-    __syncthreads();
-    if (cached) {
-        for (int pq = tid; pq < total_pairs; pq += NT) {
-            const int pr = s_pair[pq];
-            const int pi = pr & 255, pj = pr >> 8;
-            const uint16_t* Bj = Bm + (bc_row0 + (size_t)pj * G) * N;
-            uint4 vb[CPR];
+    // C tile (TPM x N bf16, rows swizzled) in the h0 buffers, which are still free
+    unsigned char* cbase = &s_hl[0][0][0];
 #pragma unroll
-            for (int ch = 0; ch < CPR; ++ch) vb[ch] = *(const uint4*)(Bj + 8 * ch);
-            float s0 = 0.f, s1 = 0.f;
+    for (int m = 0; m < BC_PT; ++m) {
+        const int c = tid + NT * m, r = c / CPR, ch = c % CPR;
+        if (r >= T) ct[m] = bt[m] = make_uint4(0, 0, 0, 0);
+        *(uint4*)(cbase + swz_off(r, ch, CPR, r)) = ct[m];
+    }
 #pragma unroll
-            for (int ch = 0; ch < CPR; ch += 2) {
-                s0 = dot8_bf16(*(const uint4*)(cbase + swz_off(pi, ch, CPR, pi)), vb[ch], s0);
-                s1 = dot8_bf16(*(const uint4*)(cbase + swz_off(pi, ch + 1, CPR, pi)), vb[ch + 1], s1);
-            }
-            s_G[pq] = s0 + s1;
+    for (int m = 0; m < DT_PT; ++m) {
+        const int e = tid + NT * m;
+        const int n = e / HB, hh = e - n * HB;
+        if (e < T * HB) s_dth[hh * TPM + n] = (uint16_t)dtr[m];
+    }
+    // pair scores G_ij = C_i . B_j from LDS: the B tile passes through x buffer 1
+    // (free until head 1 is staged) 64 columns at a time
+    constexpr int PPT = MAXP / NT;  // pairs per thread
+    float gacc[PPT];
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) gacc[k] = 0.f;
+#pragma unroll
+    for (int pass = 0; pass < N / 64; ++pass) {
+#pragma unroll
+        for (int m = 0; m < BC_PT; ++m) {
+            const int c = tid + NT * m, r = c / CPR, ch = c % CPR;
+            if ((ch >> 3) == pass) *(uint4*)(s_x1 + swz_off(r, ch & 7, 8, r)) = bt[m];
         }
+        __syncthreads();  // pass columns of B (and, first time, the C tile and pair lists) visible
+        if (cached) {
+#pragma unroll
+            for (int k = 0; k < PPT; ++k) {
+                const int pq = tid + NT * k;
+                if (pq < total_pairs) {
+                    const int pr = s_pair[pq];
+                    const int pi = pr & 255, pj = pr >> 8;
+                    float g0 = 0.f, g1 = 0.f;
+#pragma unroll
+                    for (int cc = 0; cc < 8; cc += 2) {
+                        g0 = dot8_bf16(*(const uint4*)(cbase + swz_off(pi, 8 * pass + cc, CPR, pi)),
+                                       *(const uint4*)(s_x1 + swz_off(pj, cc, 8, pj)), g0);
+                        g1 = dot8_bf16(*(const uint4*)(cbase + swz_off(pi, 8 * pass + cc + 1, CPR, pi)),
+                                       *(const uint4*)(s_x1 + swz_off(pj, cc + 1, 8, pj)), g1);
+                    }
+                    gacc[k] += g0 + g1;
+                }
+            }
+        }
+        __syncthreads();  // B columns consumed
+    }
+    if (cached) {
+#pragma unroll
+        for (int k = 0; k < PPT; ++k)
+            if (tid + NT * k < total_pairs) s_G[tid + NT * k] = gacc[k];
     }
     bf16x8 creg[KS];
 #pragma unroll
@@ -247,13 +299,17 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
 
             // intra-tree term + D x_i over node i's ancestor list, columns 16q .. 16q+15,
             // two ancestors at a time: their x rows are interleaved into bf16 pairs and
-            // multiplied by the two weights, each split into bf16 high + low parts
+            // multiplied by the two weights (v_dot2_f32_bf16, fp32 accumulate)
             const float Ah = A[h];
             const float Dh = D[h];
             float ta[16];
 #pragma unroll
             for (int e = 0; e < 16; ++e) ta[e] = 0.f;
-            auto add_rows = [&](int j0, float w0, int j1, float w1) {
+            // LO: also multiply by the bf16 residuals of the weights (about 16
+            // significant bits in all); used for the node's own row, which carries
+            // D, and its parent
+            auto add_rows = [&](int j0, float w0, int j1, float w1, auto loc) {
+                constexpr bool LO = decltype(loc)::value != 0;
                 const int a0 = swz_off(j0, 2 * q, 8, x_key(j0));
                 const int a1 = swz_off(j1, 2 * q, 8, x_key(j1));
                 const uint4 p0 = *(const uint4*)(sx + a0), q0 = *(const uint4*)(sx + (a0 ^ 16));
@@ -261,29 +317,30 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
                 const uint32_t u0[8] = {p0.x, p0.y, p0.z, p0.w, q0.x, q0.y, q0.z, q0.w};
                 const uint32_t u1[8] = {p1.x, p1.y, p1.z, p1.w, q1.x, q1.y, q1.z, q1.w};
                 const uint32_t whi = pack_bf16x2(w0, w1);
-                const uint32_t wlo = pack_bf16x2(w0 - lo_bf16(whi), w1 - hi_bf16(whi));
-                const bf16x2 wh = __builtin_bit_cast(bf16x2, whi), wl = __builtin_bit_cast(bf16x2, wlo);
+                const bf16x2 wh = __builtin_bit_cast(bf16x2, whi);
+                const bf16x2 wl = __builtin_bit_cast(bf16x2, pack_bf16x2(w0 - lo_bf16(whi), w1 - hi_bf16(whi)));
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const bf16x2 xl = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(u1[e], u0[e], 0x05040100u));
                     const bf16x2 xh = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(u1[e], u0[e], 0x07060302u));
                     ta[2 * e] = __builtin_amdgcn_fdot2_f32_bf16(xl, wh, ta[2 * e], false);
-                    ta[2 * e] = __builtin_amdgcn_fdot2_f32_bf16(xl, wl, ta[2 * e], false);
                     ta[2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(xh, wh, ta[2 * e + 1], false);
-                    ta[2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(xh, wl, ta[2 * e + 1], false);
+                    if (LO) {
+                        ta[2 * e] = __builtin_amdgcn_fdot2_f32_bf16(xl, wl, ta[2 * e], false);
+                        ta[2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(xh, wl, ta[2 * e + 1], false);
+                    }
                 }
             };
             float s = 0.f;  // sum of dt*A over the path nodes from i up to (excluding) j
             if (i < T) {
                 if (cached) {
-                    // entry k = 0 is the node itself: weight G_ii dt_i + D
-                    int k = 0;
-                    int j0 = i;
-                    float w0 = 0.f;
-                    for (; k < my_cnt; k += 2) {
-                        j0 = s_pair[my_base + k] >> 8;
+                    // entries k and k+1 of the list; entry 0 is the node itself with
+                    // weight G_ii dt_i + D. The first two rows take the weights to
+                    // about 16 bits, the older ancestors to bf16.
+                    auto pair_step = [&](int k, auto loc) {
+                        const int j0 = s_pair[my_base + k] >> 8;
                         const float dj0 = bf16_bits_to_f32(sdt[j0]);
-                        w0 = s_G[my_base + k] * __expf(s) * dj0 + (k == 0 ? Dh : 0.f);
+                        const float w0 = s_G[my_base + k] * __expf(s) * dj0 + (k == 0 ? Dh : 0.f);
                         s += dj0 * Ah;
                         int j1 = j0;
                         float w1 = 0.f;
@@ -293,8 +350,10 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
                             w1 = s_G[my_base + k + 1] * __expf(s) * dj1;
                             s += dj1 * Ah;
                         }
-                        add_rows(j0, w0, j1, w1);
-                    }
+                        add_rows(j0, w0, j1, w1, loc);
+                    };
+                    pair_step(0, BufC<1>{});
+                    for (int k = 2; k < my_cnt; k += 2) pair_step(k, BufC<0>{});
                 } else {
                     // pair list too long for LDS (very deep trees): chase parents and
                     // score each pair from the B and C rows in memory
@@ -302,7 +361,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
                     for (int j = i; j >= 0; j = s_par[j]) {
                         const float dj = bf16_bits_to_f32(sdt[j]);
                         const float gij = dot_rows_lean<N>(Ci, Bm + (bc_row0 + (size_t)j * G) * N);
-                        add_rows(j, gij * __expf(s) * dj + (j == i ? Dh : 0.f), j, 0.f);
+                        add_rows(j, gij * __expf(s) * dj + (j == i ? Dh : 0.f), j, 0.f, BufC<1>{});
                         s += dj * Ah;
                     }
                 }

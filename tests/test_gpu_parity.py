@@ -117,6 +117,8 @@ def test_ragged_bf16(bnd, oracle_mod, T, N, G):
                         n_groups=G, dtype=W.BF16, tree="recursive", max_depth=10)
     check_full(bnd, oracle_mod, inp, W.BF16, f"ragged T={T}")
     check_full(bnd, oracle_mod, inp, W.BF16, f"ragged T={T} generic", force_generic=True)
+    if T <= 64:  # the wide-tree kernel also takes small trees when asked
+        check_full(bnd, oracle_mod, inp, W.BF16, f"ragged T={T} wide", force_wide=True)
 
 
 @pytest.mark.parametrize("T,P,N,G,H", [(7, 16, 8, 1, 1), (45, 24, 12, 1, 3), (70, 64, 128, 2, 4),
