@@ -155,20 +155,13 @@ class Workload:
         B, T, H, P, N, G = self.dims
         return B * T * H * self.cfg.layers
 
-    def step(self, s, ev=None):
-        """Enqueue one step on input set s; ev = (e0, e1, e2): e0..e1 spans the
-        verify launches of all layers, e1..e2 the commit launches."""
-        vc, cc = self.verify_calls[s], self.commit_calls[s]
-        if ev is not None:
-            ev[0].record()
-        for f in vc:
+    def step(self, s):
+        """Enqueue one step on input set s: verify for every layer, then commit
+        for every layer."""
+        for f in self.verify_calls[s]:
             f()
-        if ev is not None:
-            ev[1].record()
-        for f in cc:
+        for f in self.commit_calls[s]:
             f()
-        if ev is not None:
-            ev[2].record()
 
     def algorithmic_bytes(self):
         B, T, H, P, N, G = self.dims
@@ -190,7 +183,13 @@ def sleep_cycles_for(torch, ms):
 def time_steps(torch, wl, steps, warmup):
     """Warm up, then time exactly `steps` steps with HIP events; the stream is
     pre-loaded with a spin kernel so the host enqueues ahead of the GPU and the
-    region measures GPU execution of back-to-back launches."""
+    region measures GPU execution of back-to-back launches.
+
+    The average launch duration of each kernel comes from two further timed
+    regions of the same kind: the step's verify launches alone, then its commit
+    launches alone, `steps` rounds each over the rotating input sets, one event
+    pair around each region (events between single launches would add their
+    own overhead to every launch)."""
     host_t = []
     for i in range(warmup):
         t0 = time.perf_counter()
@@ -198,25 +197,31 @@ def time_steps(torch, wl, steps, warmup):
         host_t.append(time.perf_counter() - t0)
         torch.cuda.synchronize()
     host_per_step = min(host_t) if host_t else 5e-3
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()  # barrier (one rank) + synchronize before the timed region
-    cyc = sleep_cycles_for(torch, 1.5e3 * host_per_step * steps + 20.0)
-    torch.cuda._sleep(cyc)
-    start.record()
-    t_host = time.perf_counter()
-    for i in range(steps):
-        wl.step(i % wl.n_sets, evs[i])
-    end.record()
-    t_host = time.perf_counter() - t_host
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
-    # average launch duration: each event pair spans all layers' launches of one kernel
+
+    def region(fn, rounds):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()  # barrier (one rank) + synchronize before the timed region
+        torch.cuda._sleep(sleep_cycles_for(torch, 1.5e3 * host_per_step * rounds + 20.0))
+        start.record()
+        t_host = time.perf_counter()
+        for i in range(rounds):
+            fn(i % wl.n_sets)
+        end.record()
+        t_host = time.perf_counter() - t_host
+        torch.cuda.synchronize()
+        return start.elapsed_time(end), t_host
+
+    ms, t_host = region(wl.step, steps)
     nl = len(wl.verify_calls[0])
-    v_us = [evs[i][0].elapsed_time(evs[i][1]) * 1e3 / nl for i in range(steps)]
-    c_us = [evs[i][1].elapsed_time(evs[i][2]) * 1e3 / nl for i in range(steps)]
-    return dict(ms_per_step=ms, verify_us=sum(v_us) / steps, commit_us=sum(c_us) / steps,
-                verify_us_min=min(v_us), commit_us_min=min(c_us), host_ms=1e3 * t_host / steps)
+
+    def run_all(calls):
+        for f in calls:
+            f()
+
+    v_ms, _ = region(lambda s: run_all(wl.verify_calls[s]), steps)
+    c_ms, _ = region(lambda s: run_all(wl.commit_calls[s]), steps)
+    return dict(ms_per_step=ms / steps, verify_us=v_ms * 1e3 / (steps * nl),
+                commit_us=c_ms * 1e3 / (steps * nl), host_ms=1e3 * t_host / steps)
 
 
 def kernel_report(name, us, nbytes, workload, sha):
@@ -227,7 +232,8 @@ def kernel_report(name, us, nbytes, workload, sha):
         traffic = int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
     return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
-            "kernel": name, "avg_us": round(us, 3), "algorithmic_bytes": int(nbytes)}
+            "kernel": name, "avg_us": round(us, 3), "algorithmic_bytes": int(nbytes),
+            "timing": "HIP events around back-to-back launches of this kernel alone"}
 
 
 def cpu_baseline(wl, seconds):

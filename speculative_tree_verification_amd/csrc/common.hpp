@@ -127,7 +127,7 @@ __device__ __forceinline__ int load_parent(const int32_t* parent_b, int T) {
     typedef const int32_t __attribute__((address_space(1))) gint;
     const int i = threadIdx.x;
     uint64_t u = (uint64_t)parent_b;
-    asm volatile("" : "+s"(u));
+    asm volatile("" : "+v"(u));
     const int p = ((gint*)u)[i < T ? i : T - 1];
     __builtin_amdgcn_sched_barrier(0);
     return i < T ? p : 0;

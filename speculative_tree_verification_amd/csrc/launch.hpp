@@ -43,9 +43,7 @@ hipError_t launch_verify_generic(const VerifyArgs& a, bool bf16, hipStream_t str
 // bf16 MFMA verify (head_dim 64, d_state 64 or 128): trees of <= 64 nodes use
 // the per-wave head_dim-slice kernel, wider trees the LDS-staged kernel
 hipError_t launch_verify_small(const VerifyArgs& a, int heads_per_block, hipStream_t stream);
-int verify_small_blocks_per_cu(int T, int N);
 hipError_t launch_verify_wide(const VerifyArgs& a, int heads_per_block, hipStream_t stream);
-int verify_wide_blocks_per_cu(int T, int N);
 
 hipError_t launch_commit(const CommitArgs& a, bool bf16, hipStream_t stream);
 

@@ -81,8 +81,8 @@ __global__ __launch_bounds__(kBlock) void verify_mfma_kernel(
     const size_t bc_row0 = ((size_t)b * T) * G + g;  // row (b, node 0, g) of B and C
 
     // No set-up load depends on the tree, so all of them leave at once: the
-    // parents first, then the first head's h0 and x, the B and C tiles of the
-    // item's group and the step sizes of all HB heads. Vector memory operations
+    // parents first, then the B and C tiles of the item's group, the step sizes
+    // of all HB heads, and last the first head's h0 and x. Vector memory operations
     // complete in order and every load is unconditional (clamped rows), so the
     // tree check waits for the parents only and the tree work overlaps the rest.
     const int par_i = load_parent(parent + (size_t)b * T, T);
@@ -104,7 +104,6 @@ __global__ __launch_bounds__(kBlock) void verify_mfma_kernel(
             xr[m] = *(const uint4*)(x + (((size_t)b * T + row) * H + h) * kP + 16 * w + 8 * half);
         }
     };
-    load_head(h_first);
 
     constexpr int CPR = N / 8;
     constexpr int BC_PER_THREAD = (TP * CPR + kBlock - 1) / kBlock;
@@ -124,6 +123,8 @@ __global__ __launch_bounds__(kBlock) void verify_mfma_kernel(
         const int n = e / HB, hh = e - n * HB;  // consecutive threads: consecutive heads of node n
         dtr[m] = dt[((size_t)b * T + n) * H + h_first + hh];
     }
+    __builtin_amdgcn_sched_barrier(0);  // the set-up rows first: the first head's stream is larger
+    load_head(h_first);
 
     // ---------------------------------------------------------------- set-up
     const int st = check_tree(par_i, T, s_par);
@@ -260,12 +261,6 @@ hipError_t launch_verify_small(const VerifyArgs& a, int HB, hipStream_t stream) 
                     (void*)&a.h0, (void*)&a.parent, (void*)&a.y, (void*)&a.tree_status,
                     (void*)&a.T, (void*)&a.H, (void*)&a.G, (void*)&HB};
     return hipLaunchKernel(k, grid, dim3(kBlock), args, 0, stream);
-}
-
-int verify_small_blocks_per_cu(int T, int N) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pick_small(T, N), kBlock, 0) != hipSuccess) n = 1;
-    return n > 0 ? n : 1;
 }
 
 }  // namespace tsv

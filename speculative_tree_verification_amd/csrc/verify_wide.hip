@@ -419,12 +419,4 @@ hipError_t launch_verify_wide(const VerifyArgs& a, int HB, hipStream_t stream) {
     return hipLaunchKernel(k, grid, dim3(wide_waves(a.T) * kWave), args, 0, stream);
 }
 
-int verify_wide_blocks_per_cu(int T, int N) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pick_wide(T, N), wide_waves(T) * kWave, 0) !=
-        hipSuccess)
-        n = 1;
-    return n > 0 ? n : 1;
-}
-
 }  // namespace tsv
