@@ -38,13 +38,13 @@ int compute_units() {
 }
 
 // Heads per work-group: the largest divisor of the heads of one group that
-// still gives every compute unit `per_cu` work-groups. More heads per
-// work-group amortise the tree set-up (validation, pair lists, pair scores)
-// and let each work-group stream the next head while it computes the current
-// one; fewer leave more work-groups to hide memory latency. The small-tree
-// kernel does best with two work-groups per compute unit (measured on the
-// batched Mamba2-2.7B and 8B-hybrid shapes), the wide-tree kernel, which fills
-// a compute unit's LDS, with one.
+// still gives the GPU `per_cu` work-groups per compute unit. More heads per
+// work-group amortise the tree set-up (validation, pair lists, pair scores);
+// fewer leave more work-groups to hide memory latency. Measured on the
+// batched Mamba2-2.7B and 8B-hybrid shapes: the small-tree kernel (which
+// computes a work-group's heads side by side) does best at four work-groups
+// per compute unit, the wide-tree kernel (which fills a compute unit's LDS
+// and takes its heads one after another) at one.
 int default_heads_per_block(const tsv_shape* s, int per_cu) {
     const long want = (long)compute_units() * per_cu;
     const int hpg = s->n_heads / s->n_groups;
@@ -56,7 +56,7 @@ int default_heads_per_block(const tsv_shape* s, int per_cu) {
 hipError_t launch_mfma(const tsv_shape* s, const tsv::VerifyArgs& a, hipStream_t hs) {
     const bool small = s->n_nodes <= 64 && !(s->flags & TSV_FLAG_FORCE_WIDE);
     int hb = s->heads_per_block;
-    if (hb == 0) hb = default_heads_per_block(s, small ? 2 : 1);
+    if (hb == 0) hb = default_heads_per_block(s, small ? 4 : 1);
     return small ? tsv::launch_verify_small(a, hb, hs) : tsv::launch_verify_wide(a, hb, hs);
 }
 }  // namespace

@@ -43,6 +43,7 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
     const int tid = threadIdx.x;
     const int PN = P * N;
 
+    const float Ah = A[hd];  // issued with the first loads, off the dependency chain
     // state chunk first (written back only for a valid item)
     float* hb = h + ((size_t)b * H + hd) * PN;
     const int e0 = chunk * (kBlock * kVec * 4);
@@ -86,7 +87,6 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
 
     // path rows, one round trip per chunk of kPathChunk entries: dt of every
     // entry, raw x rows and B rows; the decay weights are formed once all dt are in
-    const float Ah = A[hd];
     auto stage_rows = [&](int k0, int kn) {
         if (sizeof(TIO) == 2 && P % 8 == 0 && N % 8 == 0) {
             // bf16 rows in 16-byte pieces: one x piece and one B piece per thread

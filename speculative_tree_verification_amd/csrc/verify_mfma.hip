@@ -11,44 +11,49 @@
 //       + D x_i,                     G = C B^T of the head's group.
 //
 // Mapping (MI355X: 64-wide waves, 16x16x32 bf16 MFMA, 160 KB LDS):
-//  * work-group = (item b, block of HB heads of one group); 256 threads.
+//  * work-group = (item b, HW heads of one group), 4 HW waves: the four waves
+//    of head slot s = w / 4 own head_dim rows 16 (w % 4) .. +15 of that head.
+//    Every head of the work-group is computed at the same time; small trees
+//    give too little work per head to hide memory latency head after head.
 //  * set-up, once per work-group: the tree is validated and its depths found
 //    by pointer jumping in LDS; the ancestor pairs (i, j) are enumerated by a
 //    block scan of depth+1; G_ij is formed on those pairs only (never on the
-//    dense T x T square) and kept in LDS for all HB heads.
-//  * per head, wave w owns head_dim rows 16w..16w+15 and streams its own
-//    16 x N slice of h0 straight from HBM into registers (each byte read once,
-//    128-byte contiguous row pieces). The read-out C h0^T runs on MFMA with h0
-//    split into bf16 high + low halves (about 16 significant bits); C is an
-//    exact bf16 operand kept in registers.
+//    dense T x T square) and kept in LDS for all HW heads.
+//  * every load leaves at the start, the parents first: no load depends on
+//    the tree, and vector memory operations complete in order, so the tree
+//    check waits for the parents only while the rest (B and C tiles, step
+//    sizes, each wave's 16 x N slice of h0 and its x rows) streams in.
+//  * the read-out C h0^T runs on MFMA with h0 split into bf16 high + low
+//    halves (about 16 significant bits), one k-step at a time; C is an exact
+//    bf16 operand kept in registers.
 //  * the intra-tree term is sparse (depth+1 terms per node), so it is summed
 //    over each node's ancestor-pair list in fp32 VALU, with exp evaluated only
 //    on ancestor pairs and the decay summed along the path (no cancellation).
-//  * the next head's h0 and x are loaded while the current one computes; the
-//    step sizes of all HB heads are staged once, at set-up.
 #include "launch.hpp"
 #include "verify_common.hpp"
 
 namespace tsv {
 
 constexpr int kP = kHeadDim;
-constexpr int kXStride = 20;  // LDS row stride (uint16) of a wave's 16-column x slice
-constexpr int kSmallMaxHeads = 16;  // heads per work-group at most (LDS step-size table)
+constexpr int kXStride = 20;        // LDS row stride (uint16) of a wave's 16-column x slice
+constexpr int kSmallMaxHeads = 4;   // heads per work-group at most (16 waves)
 
-template <int TI>
+template <int TI, int HW>
 struct MfmaCfg {
-    static constexpr int TP = 16 * TI;  // node count padded to whole 16-node tiles
+    static constexpr int NT = 4 * HW * kWave;  // threads per work-group
+    static constexpr int TP = 16 * TI;         // node count padded to whole 16-node tiles
     static constexpr int kMaxPairs = TP * (TP + 1) / 2;  // every tree of TP nodes fits
     static constexpr int kXChunks = (2 * TP + kWave - 1) / kWave;
 };
 
-template <int TI, int KS>
-__global__ __launch_bounds__(kBlock) void verify_mfma_kernel(
+template <int TI, int KS, int HW>
+__global__ __launch_bounds__(4 * HW * 64) void verify_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const float* __restrict__ A,
     const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
     const float* __restrict__ D, const float* __restrict__ h0, const int32_t* __restrict__ parent,
-    uint16_t* __restrict__ y, int32_t* __restrict__ tree_status, int T, int H, int G, int HB) {
-    using Cfg = MfmaCfg<TI>;
+    uint16_t* __restrict__ y, int32_t* __restrict__ tree_status, int T, int H, int G) {
+    using Cfg = MfmaCfg<TI, HW>;
+    constexpr int NT = Cfg::NT;
     constexpr int N = 32 * KS;
     constexpr int TP = Cfg::TP;
     constexpr int MAXP = Cfg::kMaxPairs;
@@ -57,83 +62,79 @@ __global__ __launch_bounds__(kBlock) void verify_mfma_kernel(
     __shared__ int s_scratch[kMaxNodes];
     __shared__ int s_dep[kMaxNodes];
     __shared__ int s_off[kMaxNodes];
-    __shared__ int s_scan[4];
+    __shared__ int s_scan[NT / kWave];
     __shared__ uint16_t s_pair[MAXP];  // node i in the low byte, ancestor j in the high byte
     __shared__ float s_G[MAXP];
-    __shared__ __attribute__((aligned(16))) uint16_t s_x[4][TP * kXStride];
-    // dt of every head of the work-group, bf16 [head][node], staged once
-    __shared__ uint16_t s_dth[kSmallMaxHeads * TP];
+    __shared__ __attribute__((aligned(16))) uint16_t s_x[4 * HW][TP * kXStride];
+    __shared__ uint16_t s_dth[HW * TP];  // dt of the work-group's heads, bf16 [slot][node]
     // B and C rows of the item's group, padded by 16 bytes per row
     constexpr int BCS = N + 8;
     __shared__ __attribute__((aligned(16))) uint16_t s_Bt[TP * BCS];
     __shared__ __attribute__((aligned(16))) uint16_t s_Ct[TP * BCS];
 
-    const int nblk = H / HB;
+    const int nblk = H / HW;
     const int blk = xcd_block(blockIdx.x, gridDim.x);
     const int b = blk / nblk;
-    const int h_first = (blk % nblk) * HB;
+    const int h_first = (blk % nblk) * HW;
     const int g = h_first / (H / G);
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
+    const int wl = w & 3;                                        // head_dim slice of this wave
+    const int slot = w >> 2;                                     // head slot of this wave
+    const int h = h_first + slot;
     const int r16 = lane & 15;
     const int q = lane >> 4;
     const size_t bc_row0 = ((size_t)b * T) * G + g;  // row (b, node 0, g) of B and C
 
-    // No set-up load depends on the tree, so all of them leave at once: the
-    // parents first, then the B and C tiles of the item's group, the step sizes
-    // of all HB heads, and last the first head's h0 and x. Vector memory operations
-    // complete in order and every load is unconditional (clamped rows), so the
-    // tree check waits for the parents only and the tree work overlaps the rest.
+    // ---------------------------------------------------------------- loads
+    // (unconditional, from clamped rows, so that the compiler can count the
+    // loads still in flight at each wait; rows past T are zeroed or unused)
     const int par_i = load_parent(parent + (size_t)b * T, T);
-    uint16_t* sx = s_x[w];
+    constexpr int CPR = N / 8;
+    constexpr int BC_PT = (TP * CPR + NT - 1) / NT;
+    constexpr int DT_PT = (HW * TP + NT - 1) / NT;
+    uint4 breg[BC_PT], cregt[BC_PT];
+#pragma unroll
+    for (int m = 0; m < BC_PT; ++m) {
+        const int c = tid + NT * m;
+        const int r = min(c / CPR, T - 1), ch = c % CPR;
+        breg[m] = *(const uint4*)(Bm + (bc_row0 + (size_t)r * G) * N + 8 * ch);
+        cregt[m] = *(const uint4*)(Cm + (bc_row0 + (size_t)r * G) * N + 8 * ch);
+    }
+    uint32_t dtr[DT_PT];
+#pragma unroll
+    for (int m = 0; m < DT_PT; ++m) {
+        const int e = min(tid + NT * m, T * HW - 1);
+        const int n = e / HW, hh = e - n * HW;  // consecutive threads: consecutive heads of node n
+        dtr[m] = dt[((size_t)b * T + n) * H + h_first + hh];
+    }
+    // this wave's 16 x N slice of h0 (rows 16 wl + r16) and its 16 columns of x
     float4 hr[KS][2];
-    uint4 xr[Cfg::kXChunks];
-
-    auto load_head = [&](int h) {
-        const float* hrow = h0 + (((size_t)b * H + h) * kP + 16 * w + r16) * N + 8 * q;
+    {
+        const float* hrow = h0 + (((size_t)b * H + h) * kP + 16 * wl + r16) * N + 8 * q;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             hr[ks][0] = *(const float4*)(hrow + 32 * ks);
             hr[ks][1] = *(const float4*)(hrow + 32 * ks + 4);
         }
-#pragma unroll
-        for (int m = 0; m < Cfg::kXChunks; ++m) {
-            const int c = lane + kWave * m;
-            const int row = min(c >> 1, T - 1), half = c & 1;  // rows past T are not staged
-            xr[m] = *(const uint4*)(x + (((size_t)b * T + row) * H + h) * kP + 16 * w + 8 * half);
-        }
-    };
-
-    constexpr int CPR = N / 8;
-    constexpr int BC_PER_THREAD = (TP * CPR + kBlock - 1) / kBlock;
-    constexpr int DT_PT = (kSmallMaxHeads * TP + kBlock - 1) / kBlock;
-    uint4 breg[BC_PER_THREAD], cregt[BC_PER_THREAD];
-    uint32_t dtr[DT_PT];
-#pragma unroll
-    for (int m = 0; m < BC_PER_THREAD; ++m) {
-        const int c = tid + kBlock * m;
-        const int r = min(c / CPR, T - 1), ch = c % CPR;
-        breg[m] = *(const uint4*)(Bm + (bc_row0 + (size_t)r * G) * N + 8 * ch);
-        cregt[m] = *(const uint4*)(Cm + (bc_row0 + (size_t)r * G) * N + 8 * ch);
     }
+    uint4 xr[Cfg::kXChunks];
 #pragma unroll
-    for (int m = 0; m < DT_PT; ++m) {
-        const int e = min(tid + kBlock * m, T * HB - 1);
-        const int n = e / HB, hh = e - n * HB;  // consecutive threads: consecutive heads of node n
-        dtr[m] = dt[((size_t)b * T + n) * H + h_first + hh];
+    for (int m = 0; m < Cfg::kXChunks; ++m) {
+        const int c = lane + kWave * m;
+        const int row = min(c >> 1, T - 1), half = c & 1;  // rows past T are not staged
+        xr[m] = *(const uint4*)(x + (((size_t)b * T + row) * H + h) * kP + 16 * wl + 8 * half);
     }
-    __builtin_amdgcn_sched_barrier(0);  // the set-up rows first: the first head's stream is larger
-    load_head(h_first);
 
     // ---------------------------------------------------------------- set-up
     const int st = check_tree(par_i, T, s_par);
     if (h_first == 0 && tid == 0 && tree_status) tree_status[b] = st;
     if (st) return;
-    const int total_pairs = build_pairs(s_par, T, s_dep, s_off, s_scratch, s_scan, s_pair, MAXP);
+    const int total_pairs = build_pairs<NT>(s_par, T, s_dep, s_off, s_scratch, s_scan, s_pair, MAXP);
 #pragma unroll
-    for (int m = 0; m < BC_PER_THREAD; ++m) {
-        const int c = tid + kBlock * m;
+    for (int m = 0; m < BC_PT; ++m) {
+        const int c = tid + NT * m;
         const int r = c / CPR, ch = c % CPR;
         if (r < TP) {
             const bool live = r < T;
@@ -143,13 +144,13 @@ __global__ __launch_bounds__(kBlock) void verify_mfma_kernel(
     }
 #pragma unroll
     for (int m = 0; m < DT_PT; ++m) {
-        const int e = tid + kBlock * m;
-        const int n = e / HB, hh = e - n * HB;
-        if (e < T * HB) s_dth[hh * TP + n] = (uint16_t)dtr[m];
+        const int e = tid + NT * m;
+        const int n = e / HW, hh = e - n * HW;
+        if (e < T * HW) s_dth[hh * TP + n] = (uint16_t)dtr[m];
     }
     __syncthreads();
     // ancestor-pair scores G_ij = C_i . B_j from the LDS tiles, once for all heads
-    for (int pq = tid; pq < total_pairs; pq += kBlock) {
+    for (int pq = tid; pq < total_pairs; pq += NT) {
         const int pr = s_pair[pq];
         const uint16_t* ci = s_Ct + (pr & 255) * BCS;
         const uint16_t* bj = s_Bt + (pr >> 8) * BCS;
@@ -161,106 +162,101 @@ __global__ __launch_bounds__(kBlock) void verify_mfma_kernel(
         }
         s_G[pq] = s0 + s1;
     }
-    // C operands of the read-out MFMA, kept in registers for every head
+    // C operands of the read-out MFMA
     bf16x8 creg[TI][KS];
 #pragma unroll
     for (int it = 0; it < TI; ++it)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             creg[it][ks] = *(const bf16x8*)(s_Ct + (16 * it + r16) * BCS + 32 * ks + 8 * q);
+    // this wave's x slice in its own LDS region
+    uint16_t* sx = s_x[w];
+#pragma unroll
+    for (int m = 0; m < Cfg::kXChunks; ++m) {
+        const int c = lane + kWave * m;
+        const int row = c >> 1, half = c & 1;
+        if (row < T) {
+            uint2* dst = (uint2*)(sx + row * kXStride + 8 * half);
+            dst[0] = make_uint2(xr[m].x, xr[m].y);
+            dst[1] = make_uint2(xr[m].z, xr[m].w);
+        }
+    }
     __syncthreads();
 
-    // ---------------------------------------------------------------- heads
-    for (int hh = 0; hh < HB; ++hh) {
-        const int h = h_first + hh;
-        const uint16_t* sdt = s_dth + hh * TP;
-        // stage this head's x slice in the wave's own LDS region
-        wave_sync();
+    // ---------------------------------------------------------------- head
+    // state read-out: acc[it] = (h0 C^T) tile, rows p = 16 wl + 4q + r, column
+    // i; h0 is split into bf16 high and low halves one k-step at a time
+    f32x4 acc[TI];
 #pragma unroll
-        for (int m = 0; m < Cfg::kXChunks; ++m) {
-            const int c = lane + kWave * m;
-            const int row = c >> 1, half = c & 1;
-            if (row < T) {
-                uint2* dst = (uint2*)(sx + row * kXStride + 8 * half);
-                dst[0] = make_uint2(xr[m].x, xr[m].y);
-                dst[1] = make_uint2(xr[m].z, xr[m].w);
-            }
-        }
-        bf16x8 hi[KS], lo[KS];
+    for (int it = 0; it < TI; ++it) acc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) split_hi_lo(hr[ks][0], hr[ks][1], hi[ks], lo[ks]);
-        if (hh + 1 < HB) load_head(h + 1);
-        wave_sync();
-
-        // state read-out: acc[it] = (h0 C^T) tile, rows p = 16w + 4q + r, column i
-        f32x4 acc[TI];
+    for (int ks = 0; ks < KS; ++ks) {
+        bf16x8 hi, lo;
+        split_hi_lo(hr[ks][0], hr[ks][1], hi, lo);
 #pragma unroll
         for (int it = 0; it < TI; ++it) {
-            acc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                acc[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi[ks], creg[it][ks], acc[it], 0, 0, 0);
-                acc[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo[ks], creg[it][ks], acc[it], 0, 0, 0);
-            }
+            acc[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, creg[it][ks], acc[it], 0, 0, 0);
+            acc[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, creg[it][ks], acc[it], 0, 0, 0);
         }
+    }
 
-        const float Ah = A[h];
-        const float Dh = D[h];
+    const uint16_t* sdt = s_dth + slot * TP;
+    const float Ah = A[h];
+    const float Dh = D[h];
 #pragma unroll
-        for (int it = 0; it < TI; ++it) {
-            const int i = 16 * it + r16;
-            if (i >= T) continue;
-            float t0 = 0.f, t1 = 0.f, t2 = 0.f, t3 = 0.f;
-            float s = 0.f;  // sum of dt*A over the path nodes from i up to (excluding) j
-            const int base = s_off[i];
-            const int cnt = s_dep[i] + 1;
-            for (int k = 0; k < cnt; ++k) {
-                const int j = s_pair[base + k] >> 8;
-                const float dtj = bf16_bits_to_f32(sdt[j]);
-                const float wt = s_G[base + k] * __expf(s) * dtj;
-                const uint2 xv = *(const uint2*)(sx + j * kXStride + 4 * q);
-                t0 += wt * lo_bf16(xv.x);
-                t1 += wt * hi_bf16(xv.x);
-                t2 += wt * lo_bf16(xv.y);
-                t3 += wt * hi_bf16(xv.y);
-                s += dtj * Ah;
-            }
-            const float sc = __expf(s);
-            const uint2 xi = *(const uint2*)(sx + i * kXStride + 4 * q);
-            const float o0 = acc[it][0] * sc + t0 + Dh * lo_bf16(xi.x);
-            const float o1 = acc[it][1] * sc + t1 + Dh * hi_bf16(xi.x);
-            const float o2 = acc[it][2] * sc + t2 + Dh * lo_bf16(xi.y);
-            const float o3 = acc[it][3] * sc + t3 + Dh * hi_bf16(xi.y);
-            *(uint2*)(y + (((size_t)b * T + i) * H + h) * kP + 16 * w + 4 * q) =
-                make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+    for (int it = 0; it < TI; ++it) {
+        const int i = 16 * it + r16;
+        if (i >= T) continue;
+        float t0 = 0.f, t1 = 0.f, t2 = 0.f, t3 = 0.f;
+        float s = 0.f;  // sum of dt*A over the path nodes from i up to (excluding) j
+        const int base = s_off[i];
+        const int cnt = s_dep[i] + 1;
+        for (int k = 0; k < cnt; ++k) {
+            const int j = s_pair[base + k] >> 8;
+            const float dtj = bf16_bits_to_f32(sdt[j]);
+            const float wt = s_G[base + k] * __expf(s) * dtj;
+            const uint2 xv = *(const uint2*)(sx + j * kXStride + 4 * q);
+            t0 += wt * lo_bf16(xv.x);
+            t1 += wt * hi_bf16(xv.x);
+            t2 += wt * lo_bf16(xv.y);
+            t3 += wt * hi_bf16(xv.y);
+            s += dtj * Ah;
         }
+        const float sc = __expf(s);
+        const uint2 xi = *(const uint2*)(sx + i * kXStride + 4 * q);
+        const float o0 = acc[it][0] * sc + t0 + Dh * lo_bf16(xi.x);
+        const float o1 = acc[it][1] * sc + t1 + Dh * hi_bf16(xi.x);
+        const float o2 = acc[it][2] * sc + t2 + Dh * lo_bf16(xi.y);
+        const float o3 = acc[it][3] * sc + t3 + Dh * hi_bf16(xi.y);
+        *(uint2*)(y + (((size_t)b * T + i) * H + h) * kP + 16 * wl + 4 * q) =
+            make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
     }
 }
 
 bool verify_mfma_small_supported(int T) { return T <= 64; }
 
-template <int TI, int KS>
-static const void* small_kernel() { return (const void*)verify_mfma_kernel<TI, KS>; }
+template <int TI, int KS, int HW>
+static const void* small_kernel() { return (const void*)verify_mfma_kernel<TI, KS, HW>; }
 
-static const void* pick_small(int T, int N) {
+template <int HW>
+static const void* pick_small_hw(int T, int N) {
     const int tiles = (T + 15) / 16;
-    if (N == 64) return tiles <= 1 ? small_kernel<1, 2>() : tiles <= 2 ? small_kernel<2, 2>() : small_kernel<4, 2>();
-    return tiles <= 1 ? small_kernel<1, 4>() : tiles <= 2 ? small_kernel<2, 4>() : small_kernel<4, 4>();
+    if (N == 64)
+        return tiles <= 1 ? small_kernel<1, 2, HW>() : tiles <= 2 ? small_kernel<2, 2, HW>() : small_kernel<4, 2, HW>();
+    return tiles <= 1 ? small_kernel<1, 4, HW>() : tiles <= 2 ? small_kernel<2, 4, HW>() : small_kernel<4, 4, HW>();
 }
 
 hipError_t launch_verify_small(const VerifyArgs& a, int HB, hipStream_t stream) {
-    // heads per work-group: the largest divisor of the requested count that the
-    // LDS step-size table holds (results do not depend on it)
-    int hb = 1;
-    for (int d = 1; d <= kSmallMaxHeads && d <= HB; ++d)
-        if (HB % d == 0) hb = d;
-    HB = hb;
-    const void* k = pick_small(a.T, a.N);
-    dim3 grid((unsigned)(a.batch * (a.H / HB)));
+    // heads per work-group: the largest of 4, 2, 1 that divides the requested
+    // count (results do not depend on it)
+    const int hw = HB % 4 == 0 ? 4 : HB % 2 == 0 ? 2 : 1;
+    const void* k = hw == 4 ? pick_small_hw<4>(a.T, a.N) : hw == 2 ? pick_small_hw<2>(a.T, a.N)
+                                                                 : pick_small_hw<1>(a.T, a.N);
+    dim3 grid((unsigned)(a.batch * (a.H / hw)));
     void* args[] = {(void*)&a.x, (void*)&a.dt, (void*)&a.A, (void*)&a.B, (void*)&a.C, (void*)&a.D,
                     (void*)&a.h0, (void*)&a.parent, (void*)&a.y, (void*)&a.tree_status,
-                    (void*)&a.T, (void*)&a.H, (void*)&a.G, (void*)&HB};
-    return hipLaunchKernel(k, grid, dim3(kBlock), args, 0, stream);
+                    (void*)&a.T, (void*)&a.H, (void*)&a.G};
+    return hipLaunchKernel(k, grid, dim3(4 * hw * kWave), args, 0, stream);
 }
 
 }  // namespace tsv
