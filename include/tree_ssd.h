@@ -86,8 +86,9 @@ typedef struct {
 
 /*
  * tree_ssd_verify -- every node's output of one SSD layer over a packed tree
- * (the summary's "Approach": accumulated log decays along ancestor paths give
- * exact per-path outputs in one pass).
+ * (the summary's section "Approach": log decays summed along ancestor paths let
+ * one pass over the packed tree give each node the output of its own root path,
+ * exactly).
  *
  *   x      [Bt][T][H][P]   in_dtype   token inputs
  *   dt     [Bt][T][H]      in_dtype   step sizes, already positive (after any
@@ -101,18 +102,23 @@ typedef struct {
  *                                     even from fp32 accumulators)
  *   tree_status [Bt]       int32      optional; set to bits 1|2 of the item's tree
  *
- * Arithmetic: fp32 accumulation. For bf16 inputs with P == 64 and N in {64, 128}
- * the h0 read-out C h0^T runs on bf16 MFMA with h0 split into a bf16 high and
- * low part (about 16 significant bits); everything else is fp32.
+ * Arithmetic: fp32 accumulation throughout. For bf16 inputs with P == 64 and
+ * N in {64, 128} the h0 read-out C h0^T runs on bf16 MFMA with h0 split into a
+ * bf16 high and low part (about 16 significant bits). For trees of more than
+ * 64 nodes the masked decay weights of the intra-tree term are rounded once to
+ * bf16 for the bf16 dot-product instruction, except the node's own weight
+ * (which carries D) and its parent's, which keep about 16 bits. Other inputs
+ * and shapes use fp32 arithmetic on the (exact) input values.
  */
 tsv_status tree_ssd_verify(const tsv_shape* s, const void* x, const void* dt, const float* A,
                            const void* B, const void* C, const float* D, const float* h0,
                            const int32_t* parent, void* y, int32_t* tree_status, void* stream);
 
 /*
- * tree_ssd_commit -- activation replay: overwrite h0 with the state at the end
- * of the accepted root path (the summary's "activation replay for state
- * backtracking"), using the same inputs the verify call read:
+ * tree_ssd_commit -- overwrite h0 with the state at the end of the accepted
+ * root path by replaying the path's tokens (the summary's section "Approach":
+ * state is restored from the retained activations rather than from per-node
+ * snapshots), using the same inputs the verify call read:
  *   H' = exp(cum_l) h0 + sum_k exp(cum_l - cum_{j_k}) dt_{j_k} x_{j_k} (outer) B_{j_k}
  * for the path j_0 = 0, ..., j_{len-1} = l. len == 0 leaves h0 unchanged.
  *

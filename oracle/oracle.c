@@ -13,19 +13,21 @@
  *   A draft token tree is packed into one sequence of T nodes (node 0 = root,
  *   parents before children). Every node's output must equal what the ordinary
  *   SSM recurrence gives when the root-to-node path is run as a sequence on its
- *   own ("exact per-path SSM outputs"). The recurrence of one Mamba2/SSD head
+ *   own: the packed pass must be exact, not an approximation of the unrolled
+ *   paths. The recurrence of one Mamba2/SSD head
  *   with scalar decay A, step dt, input x (P), in/out projections B, C (N) and
  *   state H (P x N) is
  *       H <- exp(dt*A) * H + dt * x (outer) B,      y = H . C + D * x.
  *   The state before the root is the shared initial state h0.
- *   Commit ("activation replay for state backtracking") rebuilds the state at
- *   the end of the accepted root path by running the same recurrence along it.
+ *   Commit rebuilds the state at the end of the accepted root path by running
+ *   the same recurrence along it again (the summary restores state by
+ *   replaying the accepted tokens' activations, keeping no per-node state).
  *
  * oracle_verify / oracle_commit do exactly that, literally: they unroll every
  * root-to-node path and run the sequential recurrence in double precision.
  * oracle_packed_verify is a second, independent formulation used only to check
  * the first: the packed-tree closed form with an explicit ancestor mask L and
- * accumulated log-decays cum = L * (dt*A) (the summary's "A_tree = L log A",
+ * accumulated log-decays cum = L * (dt*A) (the summary's formula A_tree = L log A,
  * read as the log of the per-token discrete transition exp(dt*A)).
  *
  * Every problem instance ("slice") is one (batch item, head): its own tree,

@@ -1,7 +1,8 @@
-// commit.hip -- activation replay: rebuild, in place, the state at the end of
-// the accepted root path ("STree: Speculative Tree Decoding for Hybrid State
-// Space Models", atlas.scime.ai summary, section "Approach": "activation replay
-// for state backtracking"). For the path j_0 = 0, ..., j_{L-1} = l:
+// commit.hip -- rebuild, in place, the state at the end of the accepted root
+// path by replaying the accepted tokens ("STree: Speculative Tree Decoding for
+// Hybrid State Space Models", atlas.scime.ai summary, section "Approach": the
+// state is restored from the retained activations, not from stored per-node
+// states). For the path j_0 = 0, ..., j_{L-1} = l:
 //   H' = exp(c_0) h0 + sum_k exp(c_{k+1}) dt_{j_k} x_{j_k} (outer) B_{j_k},
 // with c_k = sum_{m >= k} dt_{j_m} A the log decay from token j_k to the end
 // of the path (suffix sums, so no cancellation).
