@@ -73,14 +73,22 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(text):
+    """Source text without comments and with whitespace collapsed."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_sha(kernel):
-    """Digest of the sources a kernel is built from (its HBM counters are void
-    once any of them changes)."""
+    """Digest of the code (comments aside) of the sources a kernel is built
+    from: its HBM counters are void once any of that code changes."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "speculative_tree_verification_amd", "csrc")
     for n in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(csrc, n), "rb") as f:
-            h.update(n.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, n)) as f:
+            h.update(n.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
