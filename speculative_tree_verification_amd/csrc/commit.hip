@@ -152,6 +152,30 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
         // weight the staged x rows in place
         for (int e = tid; e < kn * P; e += kBlock) s_wx[e] *= s_w[k0 + e / P];
         __syncthreads();
+        if (VEC && (kBlock * 4) % N == 0 && pe[kVec - 1] < PN) {
+            // every float4 of this thread covers the same columns n .. n+3 of
+            // its own row p_v: one B read per path entry serves all of them,
+            // and the reads of an entry leave together
+            const int n = pe[0] % N;
+            int pv[kVec];
+#pragma unroll
+            for (int v = 0; v < kVec; ++v) pv[v] = pe[v] / N;
+#pragma unroll 1
+            for (int k = 0; k < kn; ++k) {
+                const float4 bb = *(const float4*)(s_B + k * N + n);
+                float wx[kVec];
+#pragma unroll
+                for (int v = 0; v < kVec; ++v) wx[v] = s_wx[k * P + pv[v]];
+#pragma unroll
+                for (int v = 0; v < kVec; ++v) {
+                    acc[v][0] += wx[v] * bb.x;
+                    acc[v][1] += wx[v] * bb.y;
+                    acc[v][2] += wx[v] * bb.z;
+                    acc[v][3] += wx[v] * bb.w;
+                }
+            }
+            continue;
+        }
 #pragma unroll
         for (int v = 0; v < kVec; ++v) {
             if (VEC) {
