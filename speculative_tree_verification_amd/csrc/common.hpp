@@ -145,9 +145,10 @@ __device__ __forceinline__ int check_tree(int p, int T, int* s_par) {
         else
             bad_par = (p < 0 || p >= i);
     }
+    // one barrier on the common path; a second one tells the two errors apart
+    if (!__syncthreads_or(bad_root | bad_par)) return 0;
     int r = __syncthreads_or(bad_root) ? kStBadRoot : 0;
-    r |= __syncthreads_or(bad_par) ? kStBadParent : 0;
-    return r;
+    return r | (__syncthreads_or(bad_par) ? kStBadParent : 0);
 }
 
 // load_parent + check_tree in one step.

@@ -15,10 +15,11 @@
 //    of head slot s = w / 4 own head_dim rows 16 (w % 4) .. +15 of that head.
 //    Every head of the work-group is computed at the same time; small trees
 //    give too little work per head to hide memory latency head after head.
-//  * set-up, once per work-group: the tree is validated and its depths found
-//    by pointer jumping in LDS; the ancestor pairs (i, j) are enumerated by a
-//    block scan of depth+1; G_ij is formed on those pairs only (never on the
-//    dense T x T square) and kept in LDS for all HW heads.
+//  * set-up, once per work-group: the tree is validated; wave 0 alone (one
+//    lane per node) finds the depths by pointer jumping with cross-lane reads
+//    and enumerates the ancestor pairs (i, j) with a wave prefix sum of
+//    depth+1; G_ij is formed on those pairs only (never on the dense T x T
+//    square) and kept in LDS for all HW heads.
 //  * every load leaves at the start, the parents first: no load depends on
 //    the tree, and vector memory operations complete in order, so the tree
 //    check waits for the parents only while the rest (B and C tiles, step
@@ -59,7 +60,6 @@ __global__ __launch_bounds__(4 * HW * 64) void verify_mfma_kernel(
     constexpr int MAXP = Cfg::kMaxPairs;
 
     __shared__ int s_par[kMaxNodes];
-    __shared__ int s_scratch[kMaxNodes];
     __shared__ int s_dep[kMaxNodes];
     __shared__ int s_off[kMaxNodes];
     __shared__ int s_scan[NT / kWave];
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(4 * HW * 64) void verify_mfma_kernel(
     const int st = check_tree(par_i, T, s_par);
     if (h_first == 0 && tid == 0 && tree_status) tree_status[b] = st;
     if (st) return;
-    const int total_pairs = build_pairs<NT>(s_par, T, s_dep, s_off, s_scratch, s_scan, s_pair, MAXP);
+    const int total_pairs = build_pairs_wave(par_i, T, s_dep, s_off, s_pair, MAXP, &s_scan[0]);
 #pragma unroll
     for (int m = 0; m < BC_PT; ++m) {
         const int c = tid + NT * m;

@@ -130,7 +130,8 @@ def test_fp32_generic(bnd, oracle_mod, T, P, N, G, H):
 
 
 @pytest.mark.parametrize("T,tree", [(256, "chain"), (100, "chain"), (256, "star"),
-                                    (255, "level"), (63, "geometric")])
+                                    (255, "level"), (63, "geometric"), (64, "chain"),
+                                    (64, "star"), (17, "chain"), (1, "chain")])
 def test_tree_shapes_bf16(bnd, oracle_mod, T, tree):
     """Deep chains exceed the cached ancestor-pair budget and take the on-the-fly
     score path; stars and level trees are the wide extremes."""
