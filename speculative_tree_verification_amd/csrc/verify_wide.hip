@@ -11,9 +11,12 @@
 //  * work-group = (item b, block of HB heads of one group). The tree set-up
 //    (validation, depth by pointer jumping, ancestor-pair lists, pair scores
 //    G_ij) runs once and serves all HB heads.
-//  * wave w owns node tile w (nodes 16w .. 16w+15) and all 64 rows of
-//    head_dim; its C operands (exact bf16 B-matrix of the read-out MFMA) stay
-//    in registers for every head of the work-group.
+//  * wave w owns node tile NW-1-w (16 nodes) and all 64 rows of head_dim; its
+//    C operands (exact bf16 B-matrix of the read-out MFMA) stay in registers for
+//    every head of the work-group. Nodes are in topological order, so the last
+//    tiles hold the deepest nodes and the longest ancestor walks: they go to the
+//    first wave of each SIMD, whose LDS reads are served first in the read-out,
+//    so their walks start earliest.
 //  * per head, double buffered (head h+1 streams in while head h computes):
 //    x (T x 64 bf16) goes straight from HBM to LDS (global_load_lds_dwordx4,
 //    whole 128-byte rows); h0 (64 x N fp32) is read once into registers and
@@ -69,8 +72,12 @@ struct BufC {
 __device__ __forceinline__ int swz_off(int r, int c, int cpr, int key) {
     return (r * cpr + (c ^ (key & (cpr - 1)))) * 16;
 }
-// swizzle key of head_dim row p: distinct for the 16 rows one MFMA operand read touches
-__device__ __forceinline__ int row_key(int p) { return (p >> 4) | ((p & 3) << 2); }
+// swizzle key of head_dim row p: the 16 rows one MFMA operand read touches
+// (16 (m >> 2) + 4 pt + (m & 3), m = 0..15) get key m, which spreads every
+// 16-byte read of the wave over the LDS banks without conflicts (a key that
+// is a different bijection of m, such as ((m & 3) << 2) | (m >> 2), leaves
+// two-way conflicts)
+__device__ __forceinline__ int row_key(int p) { return ((p >> 4) << 2) | (p & 3); }
 // swizzle key of x row j: with the row parity it spreads 16 random rows over
 // all sixteen 16-byte bank groups
 __device__ __forceinline__ int x_key(int j) { return (j >> 1) & 7; }
@@ -117,7 +124,8 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
     const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
     const int r16 = lane & 15;
     const int q = lane >> 4;
-    const int i = 16 * w + r16;  // this lane's node
+    const int tile = NW - 1 - w;  // deepest tiles on the first wave of each SIMD
+    const int i = 16 * tile + r16;  // this lane's node
     const size_t bc_row0 = ((size_t)b * T) * G + g;
 
     // ---- per-head staging
@@ -261,7 +269,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
     __syncthreads();
 
     // ---------------------------------------------------------------- heads
-    const bool tile_live = 16 * w < T;
+    const bool tile_live = 16 * tile < T;
     auto head = [&](int hh, auto bufc) {
         constexpr int buf = decltype(bufc)::value;
         const int h = h_first + hh;
