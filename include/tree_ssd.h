@@ -138,6 +138,42 @@ tsv_status tree_ssd_commit(const tsv_shape* s, const void* x, const void* dt, co
                            const int32_t* accepted, const int32_t* accepted_len,
                            int32_t max_path_len, int32_t* tree_status, void* stream);
 
+/* One layer's operands for tree_ssd_commit_layers: device pointers with the
+ * layouts of tree_ssd_commit (x, dt, B in in_dtype; A float; h0 float). */
+typedef struct {
+    const void* x;   /* [Bt][T][H][P] */
+    const void* dt;  /* [Bt][T][H]    */
+    const float* A;  /* [H]           */
+    const void* B;   /* [Bt][T][G][N] */
+    float* h0_inout; /* [Bt][H][P][N] read, then overwritten in place */
+} tsv_commit_layer;
+
+/*
+ * tree_ssd_commit_layers -- tree_ssd_commit for n_layers layers of one model
+ * step in a single launch. All layers share the shape, the draft tree and the
+ * accepted path: one decoding step accepts the same tokens in every layer
+ * (the summary's section "Approach": every layer's state is rebuilt from its
+ * own retained inputs along that path). Once the path is known the layers are
+ * independent, so their commits need not run one after another; each layer's
+ * result is exactly that of tree_ssd_commit on its operands.
+ *
+ *   n_layers    >= 0    number of entries of `layers` (0: nothing to do)
+ *   layers      device array [n_layers] of tsv_commit_layer, owned by the
+ *               caller, read by the kernel (so it must stay valid until the
+ *               stream passes this call); no two entries may share h0_inout
+ *   parent, accepted, accepted_len, max_path_len
+ *               as for tree_ssd_commit, shared by all layers
+ *   tree_status [Bt]    optional; written once per item (bits 1|2|4)
+ *
+ * An item whose tree or path is invalid keeps h0 untouched in every layer.
+ * Returns TSV_E_NULL for a NULL `layers` with n_layers > 0 and TSV_E_SHAPE for
+ * n_layers < 0; the pointers inside the table are not checked on the host.
+ */
+tsv_status tree_ssd_commit_layers(const tsv_shape* s, int32_t n_layers,
+                                  const tsv_commit_layer* layers, const int32_t* parent,
+                                  const int32_t* accepted, const int32_t* accepted_len,
+                                  int32_t max_path_len, int32_t* tree_status, void* stream);
+
 /*
  * tree_ssd_tree_info -- the tree mask of each item (the summary's L): depth of
  * every node (edges from the root) and its ancestor-or-self set as four 64-bit

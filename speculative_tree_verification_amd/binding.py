@@ -6,7 +6,8 @@ device pointers and torch's current HIP stream through ctypes. PyTorch is used
 for device memory and streams only. There is no fallback: if the library is
 missing, importing this module raises.
 
-Entry points mirror include/tree_ssd.h: ``verify``, ``commit``, ``tree_info``.
+Entry points mirror include/tree_ssd.h: ``verify``, ``commit``,
+``commit_layers``, ``tree_info``.
 """
 from __future__ import annotations
 
@@ -27,8 +28,8 @@ TSV_FLAG_FORCE_WIDE = 2
 ST_BAD_ROOT, ST_BAD_PARENT, ST_BAD_PATH = 1, 2, 4
 STATUS_NAMES = {0: "TSV_OK", 1: "TSV_E_NULL", 2: "TSV_E_SHAPE", 3: "TSV_E_DTYPE",
                 4: "TSV_E_UNSUPPORTED", 5: "TSV_E_LAUNCH"}
-EXPORTS = ("tree_ssd_verify", "tree_ssd_commit", "tree_ssd_tree_info", "tree_ssd_status_string",
-           "tree_ssd_abi_version")
+EXPORTS = ("tree_ssd_verify", "tree_ssd_commit", "tree_ssd_commit_layers", "tree_ssd_tree_info",
+           "tree_ssd_status_string", "tree_ssd_abi_version")
 
 
 class Shape(ctypes.Structure):
@@ -37,6 +38,12 @@ class Shape(ctypes.Structure):
                 ("d_state", ctypes.c_int32), ("n_groups", ctypes.c_int32),
                 ("in_dtype", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("heads_per_block", ctypes.c_int32)]
+
+
+class CommitLayer(ctypes.Structure):
+    """tsv_commit_layer: one layer's device pointers for tree_ssd_commit_layers."""
+    _fields_ = [("x", ctypes.c_void_p), ("dt", ctypes.c_void_p), ("A", ctypes.c_void_p),
+                ("B", ctypes.c_void_p), ("h0_inout", ctypes.c_void_p)]
 
 
 class TreeSSDError(RuntimeError):
@@ -58,6 +65,9 @@ def _load():
     L.tree_ssd_verify.restype = ctypes.c_int
     L.tree_ssd_commit.argtypes = [ctypes.POINTER(Shape)] + [_VP] * 8 + [ctypes.c_int32, _VP, _VP]
     L.tree_ssd_commit.restype = ctypes.c_int
+    L.tree_ssd_commit_layers.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32] + [_VP] * 4 + \
+        [ctypes.c_int32, _VP, _VP]
+    L.tree_ssd_commit_layers.restype = ctypes.c_int
     L.tree_ssd_tree_info.argtypes = [ctypes.c_int32, ctypes.c_int32] + [_VP] * 5
     L.tree_ssd_tree_info.restype = ctypes.c_int
     L.tree_ssd_status_string.argtypes = [ctypes.c_int32]
@@ -180,6 +190,56 @@ def commit(x, dt, A, B, h0, parent, accepted, accepted_len, tree_status=None, st
     return h0
 
 
+def layer_table(layers, device) -> torch.Tensor:
+    """Device array of tsv_commit_layer for ``layers``, a sequence of
+    (x, dt, A, B, h0) tensor tuples (the caller keeps the tensors alive)."""
+    n = len(layers)
+    table = (CommitLayer * max(n, 1))()
+    for i, (x, dt, A, B, h0) in enumerate(layers):
+        table[i] = CommitLayer(x.data_ptr(), dt.data_ptr(), A.data_ptr(), B.data_ptr(), h0.data_ptr())
+    raw = np.frombuffer(bytes(table), dtype=np.uint8)[: n * ctypes.sizeof(CommitLayer)].copy()
+    return torch.from_numpy(raw).to(device)
+
+
+def _check_commit_layer(x, dt, A, B, h0, x0, B0, i):
+    Bt, T, H, P = x0.shape
+    G, N = B0.shape[2], B0.shape[3]
+    io, dev = x0.dtype, x0.device
+    for t, name, shp, dty in ((x, "x", (Bt, T, H, P), io), (dt, "dt", (Bt, T, H), io),
+                              (B, "B", (Bt, T, G, N), io), (A, "A", (H,), torch.float32),
+                              (h0, "h0", (Bt, H, P, N), torch.float32)):
+        _check(t, f"layers[{i}].{name}", shp, dty, dev)
+
+
+def commit_layers(layers, parent, accepted, accepted_len, tree_status=None, stream=None,
+                  table: Optional[torch.Tensor] = None):
+    """tree_ssd_commit for every (x, dt, A, B, h0) of ``layers`` in one launch;
+    all layers share the tree and the accepted path. ``table`` may be a table
+    already built by ``layer_table`` for these layers."""
+    n = len(layers)
+    if n == 0:
+        return
+    x0, _, _, B0, _ = layers[0]
+    Bt, T = parent.shape
+    dev = x0.device
+    Lmax = accepted.shape[1] if accepted.dim() == 2 else 0
+    for i, (x, dt, A, B, h0) in enumerate(layers):
+        _check_commit_layer(x, dt, A, B, h0, x0, B0, i)
+    _check(parent, "parent", (x0.shape[0], x0.shape[1]), torch.int32, dev)
+    _check(accepted, "accepted", (Bt, Lmax), torch.int32, dev)
+    _check(accepted_len, "accepted_len", (Bt,), torch.int32, dev)
+    if tree_status is not None:
+        _check(tree_status, "tree_status", (Bt,), torch.int32, dev)
+    if table is None:
+        table = layer_table(layers, dev)
+    shape = make_shape(x0, B0)
+    rc = lib.tree_ssd_commit_layers(ctypes.byref(shape), int(n), _ptr(table), _ptr(parent),
+                                    _ptr(accepted), _ptr(accepted_len), int(Lmax),
+                                    _ptr(tree_status), _stream(stream))
+    if rc != 0:
+        raise TreeSSDError(rc, "tree_ssd_commit_layers")
+
+
 def tree_info(parent: torch.Tensor, depth=None, anc=None, tree_status=None, stream=None):
     """(depth [Bt,T] int32, anc [Bt,T,4] int64 bit patterns, status [Bt] int32)."""
     Bt, T = parent.shape
@@ -273,3 +333,33 @@ class PreparedCommit:
         rc = lib.tree_ssd_commit(*self.args)
         if rc != 0:
             raise TreeSSDError(rc, "tree_ssd_commit")
+
+
+class PreparedCommitLayers:
+    """tree_ssd_commit_layers with fixed buffers and a resident layer table;
+    calling it enqueues one launch that commits every layer."""
+
+    def __init__(self, layers, parent, accepted, accepted_len, tree_status=None, stream=None):
+        n = len(layers)
+        if n == 0:
+            raise ValueError("PreparedCommitLayers needs at least one layer")
+        x0, _, _, B0, _ = layers[0]
+        Bt = x0.shape[0]
+        dev = x0.device
+        Lmax = accepted.shape[1]
+        for i, (x, dt, A, B, h0) in enumerate(layers):
+            _check_commit_layer(x, dt, A, B, h0, x0, B0, i)
+        _check(parent, "parent", (Bt, x0.shape[1]), torch.int32, dev)
+        _check(accepted, "accepted", (Bt, Lmax), torch.int32, dev)
+        _check(accepted_len, "accepted_len", (Bt,), torch.int32, dev)
+        self.table = layer_table(layers, dev)
+        self.shape = make_shape(x0, B0)
+        self._keep = (list(layers), parent, accepted, accepted_len, tree_status)
+        self.args = (ctypes.byref(self.shape), int(n), _ptr(self.table), _ptr(parent),
+                     _ptr(accepted), _ptr(accepted_len), int(Lmax), _ptr(tree_status),
+                     _stream(stream))
+
+    def __call__(self):
+        rc = lib.tree_ssd_commit_layers(*self.args)
+        if rc != 0:
+            raise TreeSSDError(rc, "tree_ssd_commit_layers")

@@ -89,10 +89,28 @@ tsv_status tree_ssd_commit(const tsv_shape* s, const void* x, const void* dt, co
     if (s->batch == 0 || s->n_nodes == 0) return TSV_OK;
     if (!x || !dt || !A || !B || !h0_inout || !parent || !accepted_len) return TSV_E_NULL;
     if (max_path_len > 0 && !accepted) return TSV_E_NULL;
-    tsv::CommitArgs a{x,          dt,           A,           B,          h0_inout,
-                      parent,     accepted,     accepted_len, tree_status, s->batch,
-                      s->n_nodes, s->n_heads,   s->head_dim,  s->d_state, s->n_groups,
-                      max_path_len};
+    tsv::CommitArgs a{x,        dt,          A,           B,           h0_inout,   nullptr,
+                      1,        parent,      accepted,    accepted_len, tree_status, s->batch,
+                      s->n_nodes, s->n_heads, s->head_dim, s->d_state,  s->n_groups, max_path_len};
+    hipError_t e = tsv::launch_commit(a, s->in_dtype == TSV_BF16, (hipStream_t)stream);
+    return e == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
+}
+
+tsv_status tree_ssd_commit_layers(const tsv_shape* s, int32_t n_layers,
+                                  const tsv_commit_layer* layers, const int32_t* parent,
+                                  const int32_t* accepted, const int32_t* accepted_len,
+                                  int32_t max_path_len, int32_t* tree_status, void* stream) {
+    tsv_status st = check_shape(s);
+    if (st != TSV_OK) return st;
+    if (n_layers < 0 || max_path_len < 0 || max_path_len > kMaxNodes) return TSV_E_SHAPE;
+    if (n_layers == 0 || s->batch == 0 || s->n_nodes == 0) return TSV_OK;
+    if (!layers || !parent || !accepted_len) return TSV_E_NULL;
+    if (max_path_len > 0 && !accepted) return TSV_E_NULL;
+    // the grid (layers x items x heads x state chunks) stays inside 2^31 work-groups
+    if ((long long)n_layers * s->batch * s->n_heads * 64 > 0x7fffffffLL) return TSV_E_UNSUPPORTED;
+    tsv::CommitArgs a{nullptr,  nullptr,     nullptr,     nullptr,      nullptr,     layers,
+                      n_layers, parent,      accepted,    accepted_len, tree_status, s->batch,
+                      s->n_nodes, s->n_heads, s->head_dim, s->d_state,  s->n_groups, max_path_len};
     hipError_t e = tsv::launch_commit(a, s->in_dtype == TSV_BF16, (hipStream_t)stream);
     return e == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
 }

@@ -7,7 +7,9 @@
 // with c_k = sum_{m >= k} dt_{j_m} A the log decay from token j_k to the end
 // of the path (suffix sums, so no cancellation).
 //
-// Work-group = (batch item, head, chunk of the P x N state). The state chunk,
+// Work-group = (layer, batch item, head, chunk of the P x N state); the layer
+// is 0 for a single-layer call, and for a multi-layer call the work-group reads
+// its layer's operand pointers from the caller's table. The state chunk,
 // the tree and the path indices are loaded together; the tree and the path are
 // validated bit-exactly from LDS; then dt, x and B of the path rows are staged
 // in one more round trip (two in all for paths of up to 16 entries). The state
@@ -23,10 +25,11 @@ constexpr int kVec = 4;         // float4 per thread per work-group
 
 template <typename TIO, bool VEC>
 __global__ __launch_bounds__(kBlock) void commit_kernel(
-    const TIO* __restrict__ x, const TIO* __restrict__ dt, const float* __restrict__ A,
-    const TIO* __restrict__ Bm, float* __restrict__ h, const int32_t* __restrict__ parent,
-    const int32_t* __restrict__ accepted, const int32_t* __restrict__ accepted_len,
-    int32_t* __restrict__ tree_status, int T, int H, int P, int N, int G, int Lmax, int chunks) {
+    const TIO* __restrict__ x_arg, const TIO* __restrict__ dt_arg, const float* __restrict__ A_arg,
+    const TIO* __restrict__ B_arg, float* __restrict__ h_arg, const tsv_commit_layer* __restrict__ layers,
+    const int32_t* __restrict__ parent, const int32_t* __restrict__ accepted,
+    const int32_t* __restrict__ accepted_len, int32_t* __restrict__ tree_status, int BH, int T,
+    int H, int P, int N, int G, int Lmax, int chunks) {
     __shared__ int s_par[kMaxNodes];
     __shared__ int s_path[kMaxNodes];
     __shared__ float s_w[kMaxNodes];
@@ -37,7 +40,21 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
     float* s_B = s_dyn + kPathChunk * P;
 
     const int chunk = blockIdx.x % chunks;
-    const int bh = blockIdx.x / chunks;
+    const int bh = (blockIdx.x / chunks) % BH;
+    const int layer = blockIdx.x / (chunks * BH);
+    const TIO* __restrict__ x = x_arg;
+    const TIO* __restrict__ dt = dt_arg;
+    const float* __restrict__ A = A_arg;
+    const TIO* __restrict__ Bm = B_arg;
+    float* __restrict__ h = h_arg;
+    if (layers) {  // uniform over the launch
+        const tsv_commit_layer L = layers[layer];
+        x = (const TIO*)L.x;
+        dt = (const TIO*)L.dt;
+        A = L.A;
+        Bm = (const TIO*)L.B;
+        h = L.h0_inout;
+    }
     const int b = bh / H;
     const int hd = bh % H;
     const int g = hd / (H / G);
@@ -83,7 +100,7 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
         }
     }
     if (__syncthreads_or(bad_path)) st |= kStBadPath;
-    if (hd == 0 && chunk == 0 && tid == 0 && tree_status) tree_status[b] = st;
+    if (layer == 0 && hd == 0 && chunk == 0 && tid == 0 && tree_status) tree_status[b] = st;
     if (st || len == 0) return;
 
     // path rows, one round trip per chunk of kPathChunk entries: dt of every
@@ -223,14 +240,15 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
 hipError_t launch_commit(const CommitArgs& a, bool bf16, hipStream_t stream) {
     const int per_wg = kBlock * kVec * 4;
     const int chunks = (a.P * a.N + per_wg - 1) / per_wg;
-    dim3 grid((unsigned)(a.batch * a.H * chunks));
+    const int BH = a.batch * a.H;
+    dim3 grid((unsigned)((size_t)a.n_layers * BH * chunks));
     const size_t lds = sizeof(float) * kPathChunk * (size_t)(a.P + a.N);
     const bool vec = (a.N % 4) == 0;
 #define TSV_COMMIT(TIO, V)                                                                   \
     hipLaunchKernelGGL((commit_kernel<TIO, V>), grid, dim3(kBlock), lds, stream,             \
-                       (const TIO*)a.x, (const TIO*)a.dt, a.A, (const TIO*)a.B, a.h, a.parent, \
-                       a.accepted, a.accepted_len, a.tree_status, a.T, a.H, a.P, a.N, a.G,   \
-                       a.Lmax, chunks)
+                       (const TIO*)a.x, (const TIO*)a.dt, a.A, (const TIO*)a.B, a.h, a.layers, \
+                       a.parent, a.accepted, a.accepted_len, a.tree_status, BH, a.T, a.H, a.P, \
+                       a.N, a.G, a.Lmax, chunks)
     if (bf16) {
         if (vec) TSV_COMMIT(uint16_t, true);
         else TSV_COMMIT(uint16_t, false);

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "tree_ssd.h"
+
 namespace tsv {
 
 struct VerifyArgs {
@@ -21,12 +23,16 @@ struct VerifyArgs {
     int batch, T, H, P, N, G;
 };
 
+// One layer's operands (x, dt, A, B, h), or, with `layers` set, a device table
+// of n_layers of them (the five direct pointers are then unused).
 struct CommitArgs {
     const void* x;
     const void* dt;
     const float* A;
     const void* B;
     float* h;
+    const tsv_commit_layer* layers;
+    int n_layers;
     const int32_t* parent;
     const int32_t* accepted;
     const int32_t* accepted_len;

@@ -32,7 +32,7 @@ def L():
 
 def test_header_declares_entry_points():
     names = declared_functions()
-    assert {"tree_ssd_verify", "tree_ssd_commit", "tree_ssd_tree_info",
+    assert {"tree_ssd_verify", "tree_ssd_commit", "tree_ssd_commit_layers", "tree_ssd_tree_info",
             "tree_ssd_status_string", "tree_ssd_abi_version"} <= names
 
 
@@ -115,6 +115,33 @@ def test_commit_checks(L):
     L.tree_ssd_tree_info.argtypes = [ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 5
     assert L.tree_ssd_tree_info(2, 300, None, None, None, None, None) == 2
     assert L.tree_ssd_tree_info(2, 10, None, None, None, None, None) == 1
+
+
+def call_commit_layers(L, shape, n_layers, table=None, lmax=4, parent=None, alen=None):
+    vp = ctypes.c_void_p
+    L.tree_ssd_commit_layers.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32] + [vp] * 4 + \
+        [ctypes.c_int32, vp, vp]
+    L.tree_ssd_commit_layers.restype = ctypes.c_int
+    return L.tree_ssd_commit_layers(ctypes.byref(shape), n_layers, table, parent, None, alen, lmax,
+                                    None, None)
+
+
+def test_commit_layers_checks(L):
+    """Host-side checks of the multi-layer commit (all return before any launch)."""
+    s = good()
+    fake = ctypes.c_void_p(0x1000)
+    assert call_commit_layers(L, s, -1) == 2                 # negative layer count
+    assert call_commit_layers(L, s, 0) == 0                  # no layers: nothing to do
+    assert call_commit_layers(L, s, 3) == 1                  # NULL table
+    assert call_commit_layers(L, s, 3, fake, parent=fake) == 1            # NULL accepted_len
+    assert call_commit_layers(L, s, 3, fake, lmax=4, parent=fake, alen=fake) == 1  # NULL accepted
+    assert call_commit_layers(L, s, 3, fake, lmax=300, parent=fake, alen=fake) == 2
+    bad = good()
+    bad.n_groups = 3
+    assert call_commit_layers(L, bad, 3, fake, parent=fake, alen=fake) == 2
+    empty = good()
+    empty.batch = 0
+    assert call_commit_layers(L, empty, 3) == 0
 
 
 def test_product_path_never_reaches_the_oracle():
