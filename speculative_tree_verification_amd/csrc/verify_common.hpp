@@ -134,54 +134,4 @@ __device__ __forceinline__ int build_pairs(const int* s_par, int T, int* s_dep, 
     return total;
 }
 
-// build_pairs for trees of at most 64 nodes, done by wave 0 alone in
-// registers (lane = node): depth by pointer jumping with cross-lane reads,
-// offsets by a wave prefix sum, then each lane writes its node's pairs. The
-// other waves only wait at the closing barrier. p is the calling thread's
-// parent (validated). Writes s_dep, s_off and s_pair (when the pairs fit in
-// max_pairs) and returns the pair count in every thread. s_total is one int of
-// LDS.
-__device__ __forceinline__ int build_pairs_wave(int p, int T, int* s_dep, int* s_off,
-                                                uint16_t* s_pair, int max_pairs, int* s_total) {
-    if (threadIdx.x < kWave) {
-        const int lane = threadIdx.x;
-        const bool live = lane < T;
-        int nxt = live ? p : -1;
-        int dep = nxt >= 0 ? 1 : 0;
-        // after round r, nxt is the ancestor 2^r steps up and dep the distance to it
-        while (__builtin_amdgcn_ballot_w64(nxt >= 0)) {
-            const int src = nxt >= 0 ? nxt : lane;
-            const int d2 = __shfl(dep, src, kWave), n2 = __shfl(nxt, src, kWave);
-            if (nxt >= 0) {
-                dep += d2;
-                nxt = n2;
-            }
-        }
-        const int v = live ? dep + 1 : 0;
-        int incl = v;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const int o = __shfl_up(incl, off, kWave);
-            if (lane >= off) incl += o;
-        }
-        const int total = __shfl(incl, kWave - 1, kWave);
-        const int off = incl - v;
-        if (live) {
-            s_off[lane] = off;
-            s_dep[lane] = dep;
-        }
-        if (total <= max_pairs) {
-            int j = lane;  // node i's ancestor at step k, from i itself up to the root
-            for (int k = 0; __builtin_amdgcn_ballot_w64(live && k <= dep); ++k) {
-                if (live && k <= dep) s_pair[off + k] = (uint16_t)(lane | (j << 8));
-                const int pj = __shfl(p, j < 0 ? 0 : j, kWave);
-                j = (live && k < dep) ? pj : j;
-            }
-        }
-        if (lane == 0) *s_total = total;
-    }
-    __syncthreads();
-    return *s_total;
-}
-
 }  // namespace tsv

@@ -15,11 +15,12 @@
 //    of head slot s = w / 4 own head_dim rows 16 (w % 4) .. +15 of that head.
 //    Every head of the work-group is computed at the same time; small trees
 //    give too little work per head to hide memory latency head after head.
-//  * set-up, once per work-group: the tree is validated; wave 0 alone (one
-//    lane per node) finds the depths by pointer jumping with cross-lane reads
-//    and enumerates the ancestor pairs (i, j) with a wave prefix sum of
-//    depth+1; G_ij is formed on those pairs only (never on the dense T x T
-//    square) and kept in LDS for all HW heads.
+//  * set-up, once per work-group: the tree is validated, and the pair scores
+//    G = C B^T of the lower-triangular 16 x 16 node tiles are formed on MFMA
+//    (at most ten 16 x 16 tiles for 64 nodes, a few MFMAs per wave) and kept
+//    in LDS for all HW heads. No pair list is built: each lane walks its
+//    node's root path through the parents in LDS, and the next parent, the
+//    step size, the x row and the score of an ancestor are read in one round.
 //  * every load leaves at the start, the parents first: no load depends on
 //    the tree, and vector memory operations complete in order, so the tree
 //    check waits for the parents only while the rest (B and C tiles, step
@@ -28,8 +29,8 @@
 //    halves (about 16 significant bits), one k-step at a time; C is an exact
 //    bf16 operand kept in registers.
 //  * the intra-tree term is sparse (depth+1 terms per node), so it is summed
-//    over each node's ancestor-pair list in fp32 VALU, with exp evaluated only
-//    on ancestor pairs and the decay summed along the path (no cancellation).
+//    along each node's root path in fp32 VALU, with exp evaluated only on
+//    ancestor pairs and the decay summed along the path (no cancellation).
 #include "launch.hpp"
 #include "verify_common.hpp"
 
@@ -43,7 +44,6 @@ template <int TI, int HW>
 struct MfmaCfg {
     static constexpr int NT = 4 * HW * kWave;  // threads per work-group
     static constexpr int TP = 16 * TI;         // node count padded to whole 16-node tiles
-    static constexpr int kMaxPairs = TP * (TP + 1) / 2;  // every tree of TP nodes fits
     static constexpr int kXChunks = (2 * TP + kWave - 1) / kWave;
 };
 
@@ -57,14 +57,10 @@ __global__ __launch_bounds__(4 * HW * 64) void verify_mfma_kernel(
     constexpr int NT = Cfg::NT;
     constexpr int N = 32 * KS;
     constexpr int TP = Cfg::TP;
-    constexpr int MAXP = Cfg::kMaxPairs;
 
     __shared__ int s_par[kMaxNodes];
-    __shared__ int s_dep[kMaxNodes];
-    __shared__ int s_off[kMaxNodes];
-    __shared__ int s_scan[NT / kWave];
-    __shared__ uint16_t s_pair[MAXP];  // node i in the low byte, ancestor j in the high byte
-    __shared__ float s_G[MAXP];
+    // pair scores G_ij = C_i . B_j, fp32 [i][j], lower-triangular 16 x 16 tiles
+    __shared__ float s_G[TP * TP];
     __shared__ __attribute__((aligned(16))) uint16_t s_x[4 * HW][TP * kXStride];
     __shared__ uint16_t s_dth[HW * TP];  // dt of the work-group's heads, bf16 [slot][node]
     // B and C rows of the item's group, padded by 16 bytes per row
@@ -131,7 +127,6 @@ __global__ __launch_bounds__(4 * HW * 64) void verify_mfma_kernel(
     const int st = check_tree(par_i, T, s_par);
     if (h_first == 0 && tid == 0 && tree_status) tree_status[b] = st;
     if (st) return;
-    const int total_pairs = build_pairs_wave(par_i, T, s_dep, s_off, s_pair, MAXP, &s_scan[0]);
 #pragma unroll
     for (int m = 0; m < BC_PT; ++m) {
         const int c = tid + NT * m;
@@ -149,19 +144,6 @@ __global__ __launch_bounds__(4 * HW * 64) void verify_mfma_kernel(
         if (e < T * HW) s_dth[hh * TP + n] = (uint16_t)dtr[m];
     }
     __syncthreads();
-    // ancestor-pair scores G_ij = C_i . B_j from the LDS tiles, once for all heads
-    for (int pq = tid; pq < total_pairs; pq += NT) {
-        const int pr = s_pair[pq];
-        const uint16_t* ci = s_Ct + (pr & 255) * BCS;
-        const uint16_t* bj = s_Bt + (pr >> 8) * BCS;
-        float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-        for (int ch = 0; ch < CPR; ch += 2) {
-            s0 = dot8_bf16(*(const uint4*)(ci + 8 * ch), *(const uint4*)(bj + 8 * ch), s0);
-            s1 = dot8_bf16(*(const uint4*)(ci + 8 * ch + 8), *(const uint4*)(bj + 8 * ch + 8), s1);
-        }
-        s_G[pq] = s0 + s1;
-    }
     // C operands of the read-out MFMA
     bf16x8 creg[TI][KS];
 #pragma unroll
@@ -169,6 +151,25 @@ __global__ __launch_bounds__(4 * HW * 64) void verify_mfma_kernel(
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             creg[it][ks] = *(const bf16x8*)(s_Ct + (16 * it + r16) * BCS + 32 * ks + 8 * q);
+    // pair scores G = C B^T on MFMA, once for all heads: the TI (TI + 1) / 2
+    // lower-triangular 16 x 16 tiles (ti, tj <= ti) go round the waves in a
+    // plain loop, both operands read from the LDS tiles (C rows of tile ti as
+    // the A operand, B rows of tile tj as the B operand); output row 4q + r,
+    // column r16 is G_ij for i = 16 ti + 4q + r, j = 16 tj + r16. Each G_ij
+    // depends on C_i and B_j only.
+    constexpr int kTiles = TI * (TI + 1) / 2;
+    for (int tt = w; tt < kTiles; tt += 4 * HW) {
+        int ti = 0, tj = tt;  // tt = ti (ti + 1) / 2 + tj
+        while (tj > ti) tj -= ++ti;
+        f32x4 g4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            g4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                *(const bf16x8*)(s_Ct + (16 * ti + r16) * BCS + 32 * ks + 8 * q),
+                *(const bf16x8*)(s_Bt + (16 * tj + r16) * BCS + 32 * ks + 8 * q), g4, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s_G[(16 * ti + 4 * q + r) * TP + 16 * tj + r16] = g4[r];
+    }
     // this wave's x slice in its own LDS region
     uint16_t* sx = s_x[w];
 #pragma unroll
@@ -207,20 +208,22 @@ __global__ __launch_bounds__(4 * HW * 64) void verify_mfma_kernel(
     for (int it = 0; it < TI; ++it) {
         const int i = 16 * it + r16;
         if (i >= T) continue;
+        // walk up the root path of node i: the next ancestor, its step size, its
+        // x row and its pair score are read in the same round
         float t0 = 0.f, t1 = 0.f, t2 = 0.f, t3 = 0.f;
         float s = 0.f;  // sum of dt*A over the path nodes from i up to (excluding) j
-        const int base = s_off[i];
-        const int cnt = s_dep[i] + 1;
-        for (int k = 0; k < cnt; ++k) {
-            const int j = s_pair[base + k] >> 8;
+        const float* Gi = s_G + i * TP;
+        for (int j = i; j >= 0;) {
+            const int pj = s_par[j];
             const float dtj = bf16_bits_to_f32(sdt[j]);
-            const float wt = s_G[base + k] * __expf(s) * dtj;
+            const float wt = Gi[j] * __expf(s) * dtj;
             const uint2 xv = *(const uint2*)(sx + j * kXStride + 4 * q);
             t0 += wt * lo_bf16(xv.x);
             t1 += wt * hi_bf16(xv.x);
             t2 += wt * lo_bf16(xv.y);
             t3 += wt * hi_bf16(xv.y);
             s += dtj * Ah;
+            j = pj;
         }
         const float sc = __expf(s);
         const uint2 xi = *(const uint2*)(sx + i * kXStride + 4 * q);

@@ -140,17 +140,23 @@ def test_tree_shapes_bf16(bnd, oracle_mod, T, tree):
     check_full(bnd, oracle_mod, inp, W.BF16, f"{tree} T={T}")
 
 
-def test_heads_per_block_bitwise_invariant(bnd):
+@pytest.mark.parametrize("T", [15, 40, 200])
+def test_heads_per_block_bitwise_invariant(bnd, T):
+    """Every heads-per-block choice gives the same bits, call after call, into
+    NaN-filled outputs (a missed write or a race shows up as a difference)."""
     import torch
-    inp = W.make_custom(3, batch=2, n_nodes=40, n_heads=20, head_dim=64, d_state=128, n_groups=1,
-                        dtype=W.BF16)
+    inp = W.make_custom(3 + T, batch=2, n_nodes=T, n_heads=20, head_dim=64, d_state=128,
+                        n_groups=1, dtype=W.BF16)
     dev = bnd.to_device(inp)
-    ys = []
-    for hb in (1, 2, 4, 5, 10, 20):
-        say(f"[verify] heads_per_block={hb}")
-        ys.append(run_verify(bnd, dev, heads_per_block=hb).view(torch.int16).cpu())
-    for y in ys[1:]:
-        assert torch.equal(y, ys[0])
+    ref = None
+    for rep in range(3):
+        for hb in (1, 2, 4, 5, 10, 20):
+            say(f"[verify] T={T} heads_per_block={hb} rep {rep}")
+            y = torch.full_like(dev["x"], float("nan"))
+            run_verify(bnd, dev, heads_per_block=hb, y=y)
+            y = y.view(torch.int16).cpu()
+            ref = y if ref is None else ref
+            assert torch.equal(y, ref), (T, hb, rep)
 
 
 def test_invalid_trees_leave_outputs_untouched(bnd, oracle_mod):
