@@ -47,8 +47,11 @@ struct MfmaCfg {
     static constexpr int kXChunks = (2 * TP + kWave - 1) / kWave;
 };
 
+// One-head work-groups (HW = 1) are sized for five per compute unit, so that
+// the batch-16 layer (1,280 work-groups) is resident in a single round.
 template <int TI, int KS, int HW>
-__global__ __launch_bounds__(4 * HW * 64) void verify_mfma_kernel(
+__global__ __launch_bounds__(4 * HW * 64) __attribute__((amdgpu_waves_per_eu(HW == 1 ? 5 : 1)))
+void verify_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const float* __restrict__ A,
     const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
     const float* __restrict__ D, const float* __restrict__ h0, const int32_t* __restrict__ parent,
