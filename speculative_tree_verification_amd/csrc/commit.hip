@@ -9,9 +9,10 @@
 //
 // Work-group = (layer, batch item, head, chunk of the P x N state); the layer
 // is 0 for a single-layer call, and for a multi-layer call the work-group reads
-// its layer's operand pointers from the caller's table. The state chunk,
-// the tree and the path indices are loaded together; the tree and the path are
-// validated bit-exactly from LDS; then dt, x and B of the path rows are staged
+// its layer's operand pointers from the caller's table. The path indices and
+// the parents leave first (the accepted row without waiting for its length),
+// then the state chunk; the tree and the path are validated bit-exactly from
+// LDS; then dt, x and B of the path rows are staged
 // in one more round trip (two in all for paths of up to 16 entries). The state
 // is streamed once: each element is read and written by the same thread
 // (rank-L update in registers). Invalid items leave h0 untouched.
@@ -62,7 +63,13 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
     const int PN = P * N;
 
     const float Ah = A[hd];  // issued with the first loads, off the dependency chain
-    // state chunk first (written back only for a valid item)
+    // the path indices and the parents head the only dependent chain (indices,
+    // then the path's rows), so they leave first, the accepted row without
+    // waiting for its length
+    const int len = accepted_len[b];
+    const int acc_i = Lmax > 0 ? accepted[(size_t)b * Lmax + min(tid, Lmax - 1)] : 0;
+    const int par_i = load_parent(parent + (size_t)b * T, T);
+    // state chunk (written back only for a valid item)
     float* hb = h + ((size_t)b * H + hd) * PN;
     const int e0 = chunk * (kBlock * kVec * 4);
     float acc[kVec][4];
@@ -83,10 +90,9 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
     }
 
     // tree and path indices (one round trip, with the state chunk)
-    const int len = accepted_len[b];
     const bool len_ok = len >= 0 && len <= Lmax;
-    if (len_ok && tid < len) s_path[tid] = accepted[(size_t)b * Lmax + tid];
-    int st = load_tree(parent + (size_t)b * T, T, s_par);  // barrier: s_path visible too
+    if (len_ok && tid < len) s_path[tid] = acc_i;
+    int st = check_tree(par_i, T, s_par);  // barrier: s_path visible too
     int bad_path = 0;
     if (!st) {
         if (!len_ok) {
