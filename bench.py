@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "tree-verify nodes/sec (batch×nodes×heads×layers) at 1 GPU; % peak HBM GB/s"
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA (no sparsity)
 ROTATE_BYTES = 640 << 20   # rotating input sets must exceed the 256 MB Infinity Cache
 
 
@@ -68,6 +69,29 @@ def commit_bytes(B, T, H, P, N, G, io, path_lens, Lmax):
     L = int(sum(path_lens))
     return (8 * B * H * P * N + L * io * (H * P + H + G * N) + 4 * B * T + 4 * B * Lmax + 4 * B
             + 4 * H)
+
+
+def ancestor_pairs(parent):
+    """Sum over nodes of (depth + 1) for each row of parent [B][T]: the
+    (node, ancestor-or-self) pairs of each item's tree."""
+    import numpy as np
+    parent = np.asarray(parent)
+    out = []
+    for row in parent:
+        depth = np.zeros(len(row), dtype=np.int64)
+        for i in range(1, len(row)):
+            depth[i] = depth[row[i]] + 1
+        out.append(int(depth.sum() + len(row)))
+    return out
+
+
+def verify_flops(B, T, H, P, N, G, pairs):
+    """Algorithmic flops of one verify launch: the dense read-out C h0^T
+    (2 T N P per item and head), the pair scores C_i . B_j on ancestor pairs
+    only (2 N per pair, per item and group) and the weighted sum over x rows on
+    ancestor pairs only (2 P per pair, per item and head)."""
+    npairs = sum(pairs)
+    return 2 * B * H * T * N * P + 2 * N * G * npairs + 2 * P * H * npairs
 
 
 KERNEL_SOURCES = {
@@ -139,6 +163,7 @@ class Workload:
         G, N = layers[0]["B"].shape[2], layers[0]["B"].shape[3]
         self.dims = (B, T, H, P, N, G)
         self.path_lens = [int(v) for v in layers[0]["accepted_len"].cpu().tolist()]
+        self.pairs = ancestor_pairs(layers[0]["parent"].cpu().numpy())
         self.Lmax = layers[0]["accepted"].shape[1]
         set_bytes = sum(t.numel() * t.element_size() for d in layers for t in d.values())
         set_bytes += sum(d["x"].numel() * d["x"].element_size() for d in layers)  # y
@@ -293,6 +318,12 @@ def run_workload(torch, bnd, W, cid, steps, warmup, hpb, keep_host):
     vb, cb = wl.algorithmic_bytes()
     name = wl.cfg.name
     v = kernel_report("verify", t["verify_us"], vb, name, source_sha("verify"), t["verify_launches"])
+    B, T, H, P, N, G = wl.dims
+    fl = verify_flops(B, T, H, P, N, G, wl.pairs)
+    tf = fl / (t["verify_us"] * 1e-6) / 1e12
+    v["mfma"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(tf / PEAK_BF16_TFLOPS, 5), "algorithmic_flops": int(fl),
+                 "intensity_flop_per_byte": round(fl / vb, 2)}
     c = kernel_report("commit", t["commit_us"], cb, name, source_sha("commit"), t["commit_launches"])
     nodes_s = wl.nodes_per_step / (t["ms_per_step"] * 1e-3)
     log(f"[bench] workload {cid}: {t['ms_per_step']:.4f} ms/step, {nodes_s:.4g} nodes/s; "
