@@ -229,6 +229,47 @@ def sleep_cycles_for(torch, ms):
     return int(ms / per)
 
 
+def graph_step_timing(torch, bnd, wl, steps):
+    """The same step captured once per rotating input set as a HIP graph (the
+    launches re-pointed at a side stream for the capture), replayed `steps`
+    times between two events. Reported beside the stream-launch figure."""
+    cap = torch.cuda.Stream()
+    graphs, keep = [], []
+    for layers_s in wl.sets:
+        with torch.cuda.stream(cap):
+            vc = [bnd.PreparedVerify(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"],
+                                     d["parent"], d["y"], stream=cap) for d in layers_s]
+            d0 = layers_s[0]
+            if len(layers_s) > 1:
+                cc = bnd.PreparedCommitLayers([(d["x"], d["dt"], d["A"], d["B"], d["h0"]) for d in layers_s],
+                                              d0["parent"], d0["accepted"], d0["accepted_len"], stream=cap)
+            else:
+                cc = bnd.PreparedCommit(d0["x"], d0["dt"], d0["A"], d0["B"], d0["h0"], d0["parent"],
+                                        d0["accepted"], d0["accepted_len"], stream=cap)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for f in vc:
+                f()
+            cc()
+        graphs.append(g)
+        keep.append((vc, cc))
+    torch.cuda.synchronize()
+    for i in range(2 * len(graphs)):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(sleep_cycles_for(torch, 2.0))
+    start.record()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    del graphs, keep
+    return ms
+
+
 def time_steps(torch, wl, steps, warmup):
     """Warm up, then time exactly `steps` steps with HIP events; the stream is
     pre-loaded with a spin kernel so the host enqueues ahead of the GPU and the
@@ -387,6 +428,11 @@ def main():
         "roofline": roofline,
         "kernels": {"verify": v, "commit": c},
     }
+    if layers > 1:
+        gms = graph_step_timing(torch, bnd, wl, args.steps)
+        out["graph"] = {"ms_per_step": round(gms, 5), "nodes_per_s": round(wl.nodes_per_step / (gms * 1e-3), 1),
+                        "timing": "one HIP graph per input set holding the whole step, replayed back to back"}
+        log(f"[bench] same step as a captured HIP graph: {gms:.4f} ms/step")
     secondary = []
     for sid in [int(s) for s in args.secondary.split(",") if s.strip()]:
         if sid == args.workload:
