@@ -175,6 +175,37 @@ tsv_status tree_ssd_commit_layers(const tsv_shape* s, int32_t n_layers,
                                   int32_t max_path_len, int32_t* tree_status, void* stream);
 
 /*
+ * tree_ssd_accept_greedy -- the accepted root path of each verified tree at
+ * temperature 0, the input of tree_ssd_commit. The target model's choice
+ * after node i is target_tokens[i] (its argmax next token); a child c of an
+ * accepted node i is accepted when draft_tokens[c] == target_tokens[i]
+ * ("TreeSpark: Adaptive Draft Trees Accelerate Speculative Decoding by
+ * 8-14%", section on the lossless guarantee: the target model keeps or rejects
+ * draft tokens, and a draft tree offers several candidate paths checked in one
+ * pass). The root (node 0, the token the tree grows from) is always accepted.
+ * The path is the deepest root path whose every non-root node is accepted; a
+ * tree without repeated sibling tokens has at most one, and with repeats the
+ * deepest accepted node of smallest index ends the path.
+ *
+ *   parent        [Bt][T] int32   as for tree_ssd_verify
+ *   draft_tokens  [Bt][T] int32   token of each node (node 0: the root token)
+ *   target_tokens [Bt][T] int32   target model's greedy next token after each node
+ *   max_path_len  in [1, 256]     row length of `accepted`
+ *   accepted      [Bt][max_path_len] int32  output: node indices of the path,
+ *                                 root first, cut after max_path_len entries;
+ *                                 entries past the length are -1
+ *   accepted_len  [Bt] int32      output: entries of the path kept (>= 1)
+ *   next_token    [Bt] int32      optional output: target token after the last
+ *                                 kept node (the token the next step starts from)
+ *   tree_status   [Bt] int32      optional; bits 1|2 of the item's tree
+ * Invalid items leave accepted, accepted_len and next_token untouched.
+ */
+tsv_status tree_ssd_accept_greedy(int32_t batch, int32_t n_nodes, const int32_t* parent,
+                                  const int32_t* draft_tokens, const int32_t* target_tokens,
+                                  int32_t max_path_len, int32_t* accepted, int32_t* accepted_len,
+                                  int32_t* next_token, int32_t* tree_status, void* stream);
+
+/*
  * tree_ssd_tree_info -- the tree mask of each item (the summary's L): depth of
  * every node (edges from the root) and its ancestor-or-self set as four 64-bit
  * words (bit j of word j/64 set iff node j is on the root path of node i).

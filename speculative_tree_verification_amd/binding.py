@@ -7,7 +7,7 @@ for device memory and streams only. There is no fallback: if the library is
 missing, importing this module raises.
 
 Entry points mirror include/tree_ssd.h: ``verify``, ``commit``,
-``commit_layers``, ``tree_info``.
+``commit_layers``, ``accept_greedy``, ``tree_info``.
 """
 from __future__ import annotations
 
@@ -28,8 +28,8 @@ TSV_FLAG_FORCE_WIDE = 2
 ST_BAD_ROOT, ST_BAD_PARENT, ST_BAD_PATH = 1, 2, 4
 STATUS_NAMES = {0: "TSV_OK", 1: "TSV_E_NULL", 2: "TSV_E_SHAPE", 3: "TSV_E_DTYPE",
                 4: "TSV_E_UNSUPPORTED", 5: "TSV_E_LAUNCH"}
-EXPORTS = ("tree_ssd_verify", "tree_ssd_commit", "tree_ssd_commit_layers", "tree_ssd_tree_info",
-           "tree_ssd_status_string", "tree_ssd_abi_version")
+EXPORTS = ("tree_ssd_verify", "tree_ssd_commit", "tree_ssd_commit_layers", "tree_ssd_accept_greedy",
+           "tree_ssd_tree_info", "tree_ssd_status_string", "tree_ssd_abi_version")
 
 
 class Shape(ctypes.Structure):
@@ -68,6 +68,9 @@ def _load():
     L.tree_ssd_commit_layers.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32] + [_VP] * 4 + \
         [ctypes.c_int32, _VP, _VP]
     L.tree_ssd_commit_layers.restype = ctypes.c_int
+    L.tree_ssd_accept_greedy.argtypes = [ctypes.c_int32, ctypes.c_int32] + [_VP] * 3 + \
+        [ctypes.c_int32] + [_VP] * 5
+    L.tree_ssd_accept_greedy.restype = ctypes.c_int
     L.tree_ssd_tree_info.argtypes = [ctypes.c_int32, ctypes.c_int32] + [_VP] * 5
     L.tree_ssd_tree_info.restype = ctypes.c_int
     L.tree_ssd_status_string.argtypes = [ctypes.c_int32]
@@ -238,6 +241,37 @@ def commit_layers(layers, parent, accepted, accepted_len, tree_status=None, stre
                                     _ptr(tree_status), _stream(stream))
     if rc != 0:
         raise TreeSSDError(rc, "tree_ssd_commit_layers")
+
+
+def accept_greedy(parent, draft_tokens, target_tokens, max_path_len: int, accepted=None,
+                  accepted_len=None, next_token=None, tree_status=None, stream=None):
+    """Greedy (temperature 0) acceptance of each item's verified tree:
+    (accepted [Bt, max_path_len] int32, accepted_len [Bt], next_token [Bt],
+    tree_status [Bt]). Outputs of invalid items are left as passed in."""
+    Bt, T = parent.shape
+    dev = parent.device
+    _check(parent, "parent", (Bt, T), torch.int32, dev)
+    _check(draft_tokens, "draft_tokens", (Bt, T), torch.int32, dev)
+    _check(target_tokens, "target_tokens", (Bt, T), torch.int32, dev)
+    if accepted is None:
+        accepted = torch.full((Bt, max_path_len), -1, dtype=torch.int32, device=dev)
+    if accepted_len is None:
+        accepted_len = torch.zeros((Bt,), dtype=torch.int32, device=dev)
+    if next_token is None:
+        next_token = torch.full((Bt,), -1, dtype=torch.int32, device=dev)
+    if tree_status is None:
+        tree_status = torch.zeros((Bt,), dtype=torch.int32, device=dev)
+    _check(accepted, "accepted", (Bt, max_path_len), torch.int32, dev)
+    _check(accepted_len, "accepted_len", (Bt,), torch.int32, dev)
+    _check(next_token, "next_token", (Bt,), torch.int32, dev)
+    _check(tree_status, "tree_status", (Bt,), torch.int32, dev)
+    rc = lib.tree_ssd_accept_greedy(int(Bt), int(T), _ptr(parent), _ptr(draft_tokens),
+                                    _ptr(target_tokens), int(max_path_len), _ptr(accepted),
+                                    _ptr(accepted_len), _ptr(next_token), _ptr(tree_status),
+                                    _stream(stream))
+    if rc != 0:
+        raise TreeSSDError(rc, "tree_ssd_accept_greedy")
+    return accepted, accepted_len, next_token, tree_status
 
 
 def tree_info(parent: torch.Tensor, depth=None, anc=None, tree_status=None, stream=None):

@@ -115,6 +115,20 @@ tsv_status tree_ssd_commit_layers(const tsv_shape* s, int32_t n_layers,
     return e == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
 }
 
+tsv_status tree_ssd_accept_greedy(int32_t batch, int32_t n_nodes, const int32_t* parent,
+                                  const int32_t* draft_tokens, const int32_t* target_tokens,
+                                  int32_t max_path_len, int32_t* accepted, int32_t* accepted_len,
+                                  int32_t* next_token, int32_t* tree_status, void* stream) {
+    if (batch < 0 || n_nodes < 0 || n_nodes > kMaxNodes) return TSV_E_SHAPE;
+    if (max_path_len < 1 || max_path_len > kMaxNodes) return TSV_E_SHAPE;
+    if (batch == 0 || n_nodes == 0) return TSV_OK;
+    if (!parent || !draft_tokens || !target_tokens || !accepted || !accepted_len) return TSV_E_NULL;
+    hipError_t e = tsv::launch_accept_greedy(batch, n_nodes, parent, draft_tokens, target_tokens,
+                                             max_path_len, accepted, accepted_len, next_token,
+                                             tree_status, (hipStream_t)stream);
+    return e == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
+}
+
 tsv_status tree_ssd_tree_info(int32_t batch, int32_t n_nodes, const int32_t* parent,
                               int32_t* depth, uint64_t* anc_bits, int32_t* tree_status,
                               void* stream) {

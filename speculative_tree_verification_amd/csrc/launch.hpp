@@ -53,4 +53,10 @@ hipError_t launch_verify_wide(const VerifyArgs& a, int heads_per_block, hipStrea
 
 hipError_t launch_commit(const CommitArgs& a, bool bf16, hipStream_t stream);
 
+// greedy acceptance of a verified tree (one work-group per item)
+hipError_t launch_accept_greedy(int batch, int T, const int32_t* parent, const int32_t* draft,
+                                const int32_t* target, int Lmax, int32_t* accepted,
+                                int32_t* accepted_len, int32_t* next_token, int32_t* tree_status,
+                                hipStream_t stream);
+
 }  // namespace tsv

@@ -323,3 +323,38 @@ def shape_of(inp: Dict[str, np.ndarray]):
     B, T, H, P = inp["x"].shape
     G, N = inp["B"].shape[2], inp["B"].shape[3]
     return B, T, H, P, N, G
+
+
+def make_tokens(seed: int, parent: np.ndarray, vocab: int = 32000, p_hit: float = 0.7,
+                repeats: bool = False):
+    """Seeded draft and target tokens for trees ``parent`` [B][T] (int32 each).
+
+    Siblings get distinct draft tokens (a draft tree proposes different tokens
+    at one position) unless ``repeats``, in which case they are drawn from a
+    vocabulary of 3 with replacement. Each node's target token is, with
+    probability ``p_hit``, the draft token of one of its children (uniform),
+    otherwise a uniform token.
+    """
+    rng = np.random.default_rng([8100, seed])
+    parent = np.asarray(parent)
+    B, T = parent.shape
+    draft = np.zeros((B, T), np.int32)
+    target = np.zeros((B, T), np.int32)
+    for b in range(B):
+        kids = [[] for _ in range(T)]
+        for c in range(1, T):
+            kids[parent[b, c]].append(c)
+        draft[b, 0] = rng.integers(0, vocab)
+        for i in range(T):
+            if not kids[i]:
+                continue
+            if repeats:
+                draft[b, kids[i]] = rng.integers(0, 3, size=len(kids[i]))
+            else:
+                draft[b, kids[i]] = rng.choice(vocab, size=len(kids[i]), replace=False)
+        for i in range(T):
+            if kids[i] and rng.random() < p_hit:
+                target[b, i] = draft[b, kids[i][rng.integers(0, len(kids[i]))]]
+            else:
+                target[b, i] = rng.integers(0, 3 if repeats else vocab)
+    return draft, target

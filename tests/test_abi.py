@@ -32,8 +32,8 @@ def L():
 
 def test_header_declares_entry_points():
     names = declared_functions()
-    assert {"tree_ssd_verify", "tree_ssd_commit", "tree_ssd_commit_layers", "tree_ssd_tree_info",
-            "tree_ssd_status_string", "tree_ssd_abi_version"} <= names
+    assert {"tree_ssd_verify", "tree_ssd_commit", "tree_ssd_commit_layers", "tree_ssd_accept_greedy",
+            "tree_ssd_tree_info", "tree_ssd_status_string", "tree_ssd_abi_version"} <= names
 
 
 def test_every_declared_symbol_exported(L):
@@ -142,6 +142,29 @@ def test_commit_layers_checks(L):
     empty = good()
     empty.batch = 0
     assert call_commit_layers(L, empty, 3) == 0
+
+
+def test_accept_greedy_checks(L):
+    vp = ctypes.c_void_p
+    L.tree_ssd_accept_greedy.argtypes = [ctypes.c_int32, ctypes.c_int32] + [vp] * 3 + \
+        [ctypes.c_int32] + [vp] * 5
+    L.tree_ssd_accept_greedy.restype = ctypes.c_int
+    fake = vp(0x1000)
+
+    def call(batch, T, lmax, ptrs):
+        return L.tree_ssd_accept_greedy(batch, T, *ptrs[:3], lmax, *ptrs[3:], None, None, None)
+
+    full = [fake] * 5
+    assert call(2, 300, 4, full) == 2       # more than 256 nodes
+    assert call(-1, 5, 4, full) == 2
+    assert call(2, 5, 0, full) == 2         # the root is always kept: at least one entry
+    assert call(2, 5, 257, full) == 2
+    assert call(0, 5, 4, [None] * 5) == 0   # nothing to do
+    assert call(2, 0, 4, [None] * 5) == 0
+    for k in range(5):
+        ptrs = list(full)
+        ptrs[k] = None
+        assert call(2, 5, 4, ptrs) == 1, k
 
 
 def test_product_path_never_reaches_the_oracle():

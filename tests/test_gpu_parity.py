@@ -122,7 +122,7 @@ def test_ragged_bf16(bnd, oracle_mod, T, N, G):
 
 
 @pytest.mark.parametrize("T,P,N,G,H", [(7, 16, 8, 1, 1), (45, 24, 12, 1, 3), (70, 64, 128, 2, 4),
-                                       (1, 8, 4, 1, 2), (130, 32, 16, 3, 6)])
+                                       (1, 8, 4, 1, 2), (130, 32, 16, 3, 6), (5, 256, 256, 1, 1)])
 def test_fp32_generic(bnd, oracle_mod, T, P, N, G, H):
     inp = W.make_custom(T + P, batch=2, n_nodes=T, n_heads=H, head_dim=P, d_state=N, n_groups=G,
                         dtype=W.F32, tree="recursive", max_depth=12)
@@ -303,7 +303,7 @@ def test_nondefault_stream(bnd, oracle_mod):
     assert slice_err(gpu_y_slices(y, sel), ref) <= TOL[W.BF16]
 
 
-@pytest.mark.parametrize("T,P,N,G,H", [(37, 32, 16, 1, 2), (9, 128, 64, 2, 2)])
+@pytest.mark.parametrize("T,P,N,G,H", [(37, 32, 16, 1, 2), (9, 128, 64, 2, 2), (6, 256, 256, 1, 2)])
 def test_bf16_generic_shapes(bnd, oracle_mod, T, P, N, G, H):
     """bf16 inputs whose head_dim / d_state have no MFMA kernel use the VALU kernel."""
     inp = W.make_custom(T * 3 + P, batch=2, n_nodes=T, n_heads=H, head_dim=P, d_state=N,
