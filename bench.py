@@ -315,6 +315,35 @@ def time_steps(torch, wl, steps, warmup):
                 verify_launches=nv, commit_launches=nc)
 
 
+def accept_timing(torch, bnd, W, wl, rounds):
+    """Greedy acceptance on the workload's trees with seeded draft and target
+    tokens: average duration of back-to-back launches (one per step, outside
+    the step: the step's accepted paths come from the workload)."""
+    import numpy as np
+    par = wl.sets[0][0]["parent"]
+    B, T = par.shape
+    draft, target = W.make_tokens(17, par.cpu().numpy(), p_hit=0.7)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(par.device)
+    pa = bnd.PreparedAccept(par, dev(draft), dev(target), min(T, 16))
+    for _ in range(3):
+        pa()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(sleep_cycles_for(torch, 2.0))
+    start.record()
+    for _ in range(rounds):
+        pa()
+    end.record()
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) * 1e3 / rounds
+    nbytes = 4 * (3 * B * T + B * min(T, 16) + 3 * B)
+    mean_len = float(pa.accepted_len.float().mean().item())
+    return {"kernel": "accept_greedy", "avg_us": round(us, 3), "algorithmic_bytes": nbytes,
+            "achieved_GBps": round(nbytes / (us * 1e-6) / 1e9, 2), "mean_accepted_len": round(mean_len, 3),
+            "timing": "HIP events around back-to-back launches of this kernel alone",
+            "bound": "latency (a few KB per launch)"}
+
+
 def kernel_report(name, us, nbytes, workload, sha, launches):
     gbs = nbytes / (us * 1e-6) / 1e9
     rec = traffic_record(name, workload, sha)
@@ -366,6 +395,7 @@ def run_workload(torch, bnd, W, cid, steps, warmup, hpb, keep_host):
                  "frac": round(tf / PEAK_BF16_TFLOPS, 5), "algorithmic_flops": int(fl),
                  "intensity_flop_per_byte": round(fl / vb, 2)}
     c = kernel_report("commit", t["commit_us"], cb, name, source_sha("commit"), t["commit_launches"])
+    t["accept"] = accept_timing(torch, bnd, W, wl, steps)
     nodes_s = wl.nodes_per_step / (t["ms_per_step"] * 1e-3)
     log(f"[bench] workload {cid}: {t['ms_per_step']:.4f} ms/step, {nodes_s:.4g} nodes/s; "
         f"verify {t['verify_us']:.2f} us ({v['achieved']:.0f} GB/s), "
@@ -427,6 +457,7 @@ def main():
                    "rotating_sets": wl.n_sets},
         "roofline": roofline,
         "kernels": {"verify": v, "commit": c},
+        "accept": t["accept"],
     }
     if layers > 1:
         gms = graph_step_timing(torch, bnd, wl, args.steps)
@@ -441,7 +472,7 @@ def main():
                                             0, keep_host=False)
         secondary.append({"workload": wl2.cfg.name, "nodes_per_s": round(ns2, 1),
                           "ms_per_step": round(t2["ms_per_step"], 5),
-                          "verify": v2, "commit": c2})
+                          "verify": v2, "commit": c2, "accept": t2["accept"]})
         del wl2
         torch.cuda.empty_cache()
     if secondary:

@@ -397,3 +397,27 @@ class PreparedCommitLayers:
         rc = lib.tree_ssd_commit_layers(*self.args)
         if rc != 0:
             raise TreeSSDError(rc, "tree_ssd_commit_layers")
+
+
+class PreparedAccept:
+    """tree_ssd_accept_greedy with fixed buffers; calling it enqueues one launch."""
+
+    def __init__(self, parent, draft_tokens, target_tokens, max_path_len: int, stream=None):
+        Bt, T = parent.shape
+        dev = parent.device
+        for t, name in ((parent, "parent"), (draft_tokens, "draft_tokens"),
+                        (target_tokens, "target_tokens")):
+            _check(t, name, (Bt, T), torch.int32, dev)
+        self.accepted = torch.full((Bt, max_path_len), -1, dtype=torch.int32, device=dev)
+        self.accepted_len = torch.zeros((Bt,), dtype=torch.int32, device=dev)
+        self.next_token = torch.full((Bt,), -1, dtype=torch.int32, device=dev)
+        self.tree_status = torch.zeros((Bt,), dtype=torch.int32, device=dev)
+        self._keep = (parent, draft_tokens, target_tokens)
+        self.args = (int(Bt), int(T), _ptr(parent), _ptr(draft_tokens), _ptr(target_tokens),
+                     int(max_path_len), _ptr(self.accepted), _ptr(self.accepted_len),
+                     _ptr(self.next_token), _ptr(self.tree_status), _stream(stream))
+
+    def __call__(self):
+        rc = lib.tree_ssd_accept_greedy(*self.args)
+        if rc != 0:
+            raise TreeSSDError(rc, "tree_ssd_accept_greedy")
