@@ -309,3 +309,17 @@ def test_bf16_generic_shapes(bnd, oracle_mod, T, P, N, G, H):
     inp = W.make_custom(T * 3 + P, batch=2, n_nodes=T, n_heads=H, head_dim=P, d_state=N,
                         n_groups=G, dtype=W.BF16)
     check_full(bnd, oracle_mod, inp, W.BF16, f"bf16 generic T={T} P={P} N={N}")
+
+
+@pytest.mark.parametrize("T,dtype", [(31, W.BF16), (200, W.BF16), (40, W.F32)])
+def test_linear_attention_special_case(bnd, oracle_mod, T, dtype):
+    """Tree linear attention (no decay, no skip): y_i = h0 q_i + sum over the root
+    path of (q_i . k_j) v_j is the verify call with A = 0, dt = 1, D = 0 and
+    (x, B, C) = (v, k, q). Commit then gives h0 + sum of v_j k_j^T on the path."""
+    inp = W.make_custom(800 + T, batch=3, n_nodes=T, n_heads=4, head_dim=64, d_state=128,
+                        n_groups=1, dtype=dtype)
+    inp["A"] = np.zeros_like(inp["A"])
+    inp["D"] = np.zeros_like(inp["D"])
+    one = np.ones(inp["dt"].shape, np.float32)
+    inp["dt"] = W.f32_to_bf16_bits(one) if dtype == W.BF16 else one
+    check_full(bnd, oracle_mod, inp, dtype, f"linear attention T={T}")
