@@ -358,3 +358,32 @@ def make_tokens(seed: int, parent: np.ndarray, vocab: int = 32000, p_hit: float 
             else:
                 target[b, i] = rng.integers(0, 3 if repeats else vocab)
     return draft, target
+
+
+def make_gdn(seed: int, batch: int, n_nodes: int, n_heads: int, dk: int, dv: int,
+             tree: str = "recursive", max_depth: int = 8, max_path_len: int = 9,
+             parents: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Seeded fp32 inputs of a gated-delta-rule layer over packed trees:
+    q, k [B][T][H][dk] (k scaled to unit length, q by 1/sqrt(dk)), v [B][T][H][dv]
+    ~ N(0, 1), log gate g = log U(0.9, 1), step beta = sigmoid(N(0, 1)), state
+    S0 [B][H][dv][dk] ~ 0.1 N(0, 1); trees and accepted paths as make_custom."""
+    rng = np.random.default_rng([9100, seed])
+    B, T, H = batch, n_nodes, n_heads
+    if parents is None:
+        base = make_custom(seed, batch=B, n_nodes=T, n_heads=1, head_dim=4, d_state=4, n_groups=1,
+                           dtype=F32, tree=tree, max_depth=max_depth, max_path_len=max_path_len)
+        parents, acc, acc_len = base["parent"], base["accepted"], base["accepted_len"]
+    else:
+        parents = np.asarray(parents, np.int32)
+        acc = np.full((B, max_path_len), -1, np.int32)
+        acc_len = np.zeros(B, np.int32)
+    k = rng.standard_normal((B, T, H, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    q = rng.standard_normal((B, T, H, dk)) / np.sqrt(dk)
+    v = rng.standard_normal((B, T, H, dv))
+    g = np.log(rng.uniform(0.9, 1.0, size=(B, T, H)))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H))))
+    S0 = 0.1 * rng.standard_normal((B, H, dv, dk))
+    f = lambda a: np.ascontiguousarray(a, dtype=np.float32)
+    return dict(q=f(q), k=f(k), v=f(v), g=f(g), beta=f(beta), S0=f(S0), parent=parents,
+                accepted=acc, accepted_len=acc_len)

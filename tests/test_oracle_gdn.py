@@ -1,0 +1,112 @@
+"""Pins of the gated-delta-rule oracle (oracle/gdn.py), no GPU: closed forms
+(no write: pure decay; unit gate and step with orthonormal keys: the value of
+the latest key is read back exactly), the WY closed form against the unrolled
+recurrence, verify/commit consistency, linearity and status bits."""
+import itertools
+
+import numpy as np
+import pytest
+
+from oracle import gdn as O
+from speculative_tree_verification_amd import workloads as W
+
+
+def f64(d):
+    return {k: (v.astype(np.float64) if v.dtype == np.float32 else v) for k, v in d.items()}
+
+
+def verify(d):
+    return O.verify_unrolled(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], d["parent"])
+
+
+def test_no_write_is_pure_decay():
+    d = f64(W.make_gdn(1, batch=2, n_nodes=12, n_heads=2, dk=8, dv=5))
+    d["beta"][:] = 0.0
+    o, st = verify(d)
+    assert not st.any()
+    for b in range(2):
+        for i in range(12):
+            path = O.root_path(d["parent"][b], i)
+            for h in range(2):
+                G = sum(d["g"][b, j, h] for j in path)
+                want = np.exp(G) * d["S0"][b, h] @ d["q"][b, i, h]
+                assert np.allclose(o[b, i, h], want, rtol=1e-13, atol=1e-15)
+
+
+def test_unit_gate_and_step_store_values_exactly():
+    """g = 0, beta = 1 and orthonormal keys along each path: after writing key
+    k_j the state maps k_j to v_j, so querying an ancestor's key returns its value."""
+    rng = np.random.default_rng(2)
+    T, dk, dv = 10, 16, 4
+    d = f64(W.make_gdn(2, batch=1, n_nodes=T, n_heads=1, dk=dk, dv=dv))
+    basis, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    d["k"][0, :, 0] = basis[:T]          # every node its own orthonormal key
+    d["g"][:] = 0.0
+    d["beta"][:] = 1.0
+    par = d["parent"][0]
+    for i in range(T):
+        path = O.root_path(par, i)
+        j = path[int(rng.integers(0, len(path)))]
+        d["q"][0, i, 0] = d["k"][0, j, 0]
+        o, _ = verify(d)
+        assert np.allclose(o[0, i, 0], d["v"][0, j, 0], atol=1e-12), (i, j)
+
+
+@pytest.mark.parametrize("T,tree", [(1, "recursive"), (9, "chain"), (20, "star"), (31, "recursive"),
+                                    (40, "geometric")])
+def test_wy_closed_form_equals_unrolled(T, tree):
+    d = f64(W.make_gdn(T, batch=2, n_nodes=T, n_heads=2, dk=12, dv=7, tree=tree, max_depth=6))
+    o, st = verify(d)
+    o2, e = O.verify_wy(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], d["parent"])
+    assert not st.any()
+    assert np.max(np.abs(o - o2)) <= 1e-12 * np.max(np.abs(o))
+    S1, st = O.commit_unrolled(d["k"], d["v"], d["g"], d["beta"], d["S0"], d["parent"],
+                               d["accepted"], d["accepted_len"])
+    S2 = O.commit_wy(d["k"], e, d["g"], d["S0"], d["parent"], d["accepted"], d["accepted_len"])
+    assert not st.any()
+    assert np.max(np.abs(S1 - S2)) <= 1e-12 * np.max(np.abs(S1))
+
+
+def test_all_small_trees_wy_equals_unrolled():
+    """Every topologically labelled tree of up to 5 nodes."""
+    for T in range(1, 6):
+        for choice in itertools.product(*[range(i) for i in range(1, T)]):
+            par = np.array([[-1] + list(choice)], np.int32)
+            d = f64(W.make_gdn(T * 100 + sum(choice), batch=1, n_nodes=T, n_heads=1, dk=4, dv=3,
+                               parents=par))
+            o, _ = verify(d)
+            o2, _ = O.verify_wy(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], d["parent"])
+            assert np.max(np.abs(o - o2)) <= 1e-12 * max(np.max(np.abs(o)), 1e-30)
+
+
+def test_commit_consistent_with_verify_and_linear():
+    d = f64(W.make_gdn(5, batch=3, n_nodes=25, n_heads=2, dk=10, dv=6))
+    o, _ = verify(d)
+    S, st = O.commit_unrolled(d["k"], d["v"], d["g"], d["beta"], d["S0"], d["parent"],
+                              d["accepted"], d["accepted_len"])
+    assert not st.any()
+    for b in range(3):
+        n = int(d["accepted_len"][b])
+        if n == 0:
+            continue
+        last = int(d["accepted"][b, n - 1])
+        for h in range(2):
+            assert np.allclose(S[b, h] @ d["q"][b, last, h], o[b, last, h], rtol=1e-12, atol=1e-14)
+    d2 = dict(d, v=3.0 * d["v"], S0=3.0 * d["S0"])
+    o3, _ = verify(d2)
+    assert np.allclose(o3, 3.0 * o, rtol=1e-12, atol=1e-14)
+
+
+def test_status_bits():
+    d = f64(W.make_gdn(6, batch=4, n_nodes=8, n_heads=1, dk=4, dv=3, max_path_len=4))
+    d["parent"][1, 0] = 2
+    d["parent"][2, 5] = 6
+    d["accepted"][3, 0] = 1
+    d["accepted_len"][3] = max(int(d["accepted_len"][3]), 1)
+    o, st = verify(d)
+    assert st.tolist() == [0, 1, 2, 0] and not o[1].any() and not o[2].any()
+    S, st = O.commit_unrolled(d["k"], d["v"], d["g"], d["beta"], d["S0"], d["parent"],
+                              d["accepted"], d["accepted_len"])
+    assert st.tolist() == [0, 1, 2, 4]
+    for b in (1, 2, 3):
+        assert np.array_equal(S[b], d["S0"][b])
