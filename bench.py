@@ -49,6 +49,7 @@ def parse():
                     help="comma list of further workloads measured in the same run ('' for none)")
     ap.add_argument("--secondary-steps", type=int, default=20)
     ap.add_argument("--no-oracle", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--no-gdn", action="store_true", help="skip the gated-delta-rule tree kernels")
     ap.add_argument("--oracle-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--heads-per-block", type=int, default=0)
@@ -315,6 +316,53 @@ def time_steps(torch, wl, steps, warmup):
                 verify_launches=nv, commit_launches=nc)
 
 
+GDN_SHAPE = dict(batch=16, n_nodes=31, n_heads=16, dk=128, dv=128)
+
+
+def gdn_timing(torch, bnd, W, rounds):
+    """Gated-delta-rule tree verify and commit on a batch-16 layer over the
+    31-node random trees (16 heads, dk = dv = 128, fp32), rotating input sets;
+    average durations of back-to-back launches of each kernel alone."""
+    sh = GDN_SHAPE
+    base = W.make_gdn(31, **sh, max_path_len=5)
+    B, T, H, dk, dv = sh["batch"], sh["n_nodes"], sh["n_heads"], sh["dk"], sh["dv"]
+    one = sum(a.nbytes for a in base.values()) + 2 * base["v"].nbytes
+    nsets = max(2, -(-ROTATE_BYTES // one))
+    sets = []
+    for i in range(nsets):
+        d = {k: torch.from_numpy(v).cuda() for k, v in base.items()}
+        d["o"], d["e"] = torch.empty_like(d["v"]), torch.empty_like(d["v"])
+        sets.append(d)
+
+    def ver(d):
+        bnd.gdn_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], d["parent"], o=d["o"], e=d["e"])
+
+    def com(d):
+        bnd.gdn_commit(d["k"], d["g"], d["e"], d["S0"], d["parent"], d["accepted"], d["accepted_len"])
+
+    out = {"workload": f"gdn-b{B}-tree{T}-h{H}-dk{dk}-dv{dv}", "dtype": "f32"}
+    L = int(base["accepted_len"].sum())
+    nbytes = {"verify": 4 * (B * T * H * (2 * dk + 3 * dv + 2) + B * H * dv * dk) + 4 * B * T,
+              "commit": 4 * (2 * B * H * dv * dk + L * H * (dk + dv + 1)) + 4 * B * (T + 6)}
+    for name, fn in (("verify", ver), ("commit", com)):
+        for d in sets:
+            fn(d)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(sleep_cycles_for(torch, 2.0))
+        start.record()
+        for r in range(rounds):
+            fn(sets[r % nsets])
+        end.record()
+        torch.cuda.synchronize()
+        us = start.elapsed_time(end) * 1e3 / rounds
+        gbs = nbytes[name] / (us * 1e-6) / 1e9
+        out[name] = {"avg_us": round(us, 3), "algorithmic_bytes": nbytes[name], "achieved": round(gbs, 1),
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    out["nodes_per_s"] = round(B * T * H / ((out["verify"]["avg_us"] + out["commit"]["avg_us"]) * 1e-6), 1)
+    return out
+
+
 def accept_timing(torch, bnd, W, wl, rounds):
     """Greedy acceptance on the workload's trees with seeded draft and target
     tokens: average duration of back-to-back launches (one per step, outside
@@ -477,6 +525,10 @@ def main():
         torch.cuda.empty_cache()
     if secondary:
         out["secondary"] = secondary
+    if not args.no_gdn:
+        out["gdn"] = gdn_timing(torch, bnd, W, args.secondary_steps)
+        log(f"[bench] gated delta rule {out['gdn']['workload']}: verify {out['gdn']['verify']['avg_us']:.2f} us, "
+            f"commit {out['gdn']['commit']['avg_us']:.2f} us")
     if not args.no_oracle:
         log("[bench] timing the CPU oracle on a sample of the workload")
         out["cpu_baseline"] = cpu_baseline(wl, args.oracle_seconds)

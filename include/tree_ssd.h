@@ -175,6 +175,51 @@ tsv_status tree_ssd_commit_layers(const tsv_shape* s, int32_t n_layers,
                                   int32_t max_path_len, int32_t* tree_status, void* stream);
 
 /*
+ * tree_gdn_verify -- every node's output of one gated-delta-rule layer over a
+ * packed tree ("TreeWY: Speculative Verification for Gated DeltaNet Hybrids",
+ * fugumt page, abstract: one triangular solve over the tree gives every draft
+ * node's output, and a small pseudo-value matrix is kept for commit). Per head
+ * the state S (dv x dk, stored [p][n]) follows
+ *   S <- exp(g) S (I - beta k k^T) + beta v k^T,   o = S q
+ * from S0 along each node's root path. With G_i the sum of g over that path,
+ * the pseudo-values e solve
+ *   e_i + beta_i sum_{j strict ancestor of i} exp(G_i - G_j) (k_i . k_j) e_j
+ *       = beta_i (v_i - exp(G_i) S0 k_i)
+ * and o_i = exp(G_i) S0 q_i + sum_{j on path(i)} exp(G_i - G_j) (q_i . k_j) e_j.
+ *
+ * The shape uses tsv_shape with head_dim = dv, d_state = dk, n_groups = 1,
+ * in_dtype = TSV_F32 (all tensors fp32); n_nodes <= 64, dk and dv <= 128
+ * (TSV_E_UNSUPPORTED otherwise).
+ *   q, k   [Bt][T][H][dk]   queries and keys (keys normally of unit length)
+ *   v      [Bt][T][H][dv]   values
+ *   g      [Bt][T][H]       log gate (<= 0)
+ *   beta   [Bt][T][H]       step in [0, 1]
+ *   S0     [Bt][H][dv][dk]  state before the root (read only)
+ *   parent [Bt][T]          as for tree_ssd_verify
+ *   o      [Bt][T][H][dv]   output
+ *   e      [Bt][T][H][dv]   optional output: the pseudo-values, input of commit
+ *   tree_status [Bt]        optional; bits 1|2
+ * fp32 arithmetic throughout.
+ */
+tsv_status tree_gdn_verify(const tsv_shape* s, const float* q, const float* k, const float* v,
+                           const float* g, const float* beta, const float* S0,
+                           const int32_t* parent, float* o, float* e, int32_t* tree_status,
+                           void* stream);
+
+/*
+ * tree_gdn_commit -- overwrite S0 with the state at the end of each item's
+ * accepted root path from the pseudo-values tree_gdn_verify wrote:
+ *   S' = exp(G_l) S0 + sum_{j on the path} exp(G_l - G_j) e_j k_j^T.
+ * k, g, parent as for tree_gdn_verify; e from it; accepted, accepted_len,
+ * max_path_len and tree_status (bits 1|2|4) as for tree_ssd_commit. len == 0
+ * leaves S0 unchanged; invalid items leave it untouched.
+ */
+tsv_status tree_gdn_commit(const tsv_shape* s, const float* k, const float* g, const float* e,
+                           float* S0_inout, const int32_t* parent, const int32_t* accepted,
+                           const int32_t* accepted_len, int32_t max_path_len, int32_t* tree_status,
+                           void* stream);
+
+/*
  * tree_ssd_accept_greedy -- the accepted root path of each verified tree at
  * temperature 0, the input of tree_ssd_commit. The target model's choice
  * after node i is target_tokens[i] (its argmax next token); a child c of an

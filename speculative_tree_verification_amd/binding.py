@@ -7,7 +7,8 @@ for device memory and streams only. There is no fallback: if the library is
 missing, importing this module raises.
 
 Entry points mirror include/tree_ssd.h: ``verify``, ``commit``,
-``commit_layers``, ``accept_greedy``, ``tree_info``.
+``commit_layers``, ``accept_greedy``, ``tree_info``, and for the gated delta
+rule ``gdn_verify`` and ``gdn_commit``.
 """
 from __future__ import annotations
 
@@ -29,7 +30,8 @@ ST_BAD_ROOT, ST_BAD_PARENT, ST_BAD_PATH = 1, 2, 4
 STATUS_NAMES = {0: "TSV_OK", 1: "TSV_E_NULL", 2: "TSV_E_SHAPE", 3: "TSV_E_DTYPE",
                 4: "TSV_E_UNSUPPORTED", 5: "TSV_E_LAUNCH"}
 EXPORTS = ("tree_ssd_verify", "tree_ssd_commit", "tree_ssd_commit_layers", "tree_ssd_accept_greedy",
-           "tree_ssd_tree_info", "tree_ssd_status_string", "tree_ssd_abi_version")
+           "tree_ssd_tree_info", "tree_ssd_status_string", "tree_ssd_abi_version", "tree_gdn_verify",
+           "tree_gdn_commit")
 
 
 class Shape(ctypes.Structure):
@@ -71,6 +73,10 @@ def _load():
     L.tree_ssd_accept_greedy.argtypes = [ctypes.c_int32, ctypes.c_int32] + [_VP] * 3 + \
         [ctypes.c_int32] + [_VP] * 5
     L.tree_ssd_accept_greedy.restype = ctypes.c_int
+    L.tree_gdn_verify.argtypes = [ctypes.POINTER(Shape)] + [_VP] * 11
+    L.tree_gdn_verify.restype = ctypes.c_int
+    L.tree_gdn_commit.argtypes = [ctypes.POINTER(Shape)] + [_VP] * 7 + [ctypes.c_int32, _VP, _VP]
+    L.tree_gdn_commit.restype = ctypes.c_int
     L.tree_ssd_tree_info.argtypes = [ctypes.c_int32, ctypes.c_int32] + [_VP] * 5
     L.tree_ssd_tree_info.restype = ctypes.c_int
     L.tree_ssd_status_string.argtypes = [ctypes.c_int32]
@@ -272,6 +278,56 @@ def accept_greedy(parent, draft_tokens, target_tokens, max_path_len: int, accept
     if rc != 0:
         raise TreeSSDError(rc, "tree_ssd_accept_greedy")
     return accepted, accepted_len, next_token, tree_status
+
+
+def _gdn_shape(k, v) -> Shape:
+    Bt, T, H, dk = k.shape
+    return Shape(Bt, T, H, v.shape[-1], dk, 1, TSV_F32, 0, 0)
+
+
+def gdn_verify(q, k, v, g, beta, S0, parent, o=None, e=None, tree_status=None, stream=None):
+    """(o, e) of one gated-delta-rule layer over packed trees (tree_gdn_verify)."""
+    Bt, T, H, dk = k.shape
+    dv = v.shape[-1]
+    dev = k.device
+    f32 = torch.float32
+    for t, name, shp in ((q, "q", (Bt, T, H, dk)), (k, "k", (Bt, T, H, dk)), (v, "v", (Bt, T, H, dv)),
+                         (g, "g", (Bt, T, H)), (beta, "beta", (Bt, T, H)), (S0, "S0", (Bt, H, dv, dk))):
+        _check(t, name, shp, f32, dev)
+    _check(parent, "parent", (Bt, T), torch.int32, dev)
+    o = torch.empty_like(v) if o is None else o
+    e = torch.empty_like(v) if e is None else e
+    _check(o, "o", (Bt, T, H, dv), f32, dev)
+    _check(e, "e", (Bt, T, H, dv), f32, dev)
+    shape = _gdn_shape(k, v)
+    rc = lib.tree_gdn_verify(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                             _ptr(S0), _ptr(parent), _ptr(o), _ptr(e), _ptr(tree_status),
+                             _stream(stream))
+    if rc != 0:
+        raise TreeSSDError(rc, "tree_gdn_verify")
+    return o, e
+
+
+def gdn_commit(k, g, e, S0, parent, accepted, accepted_len, tree_status=None, stream=None):
+    """Overwrite S0 [Bt,H,dv,dk] with the state after each item's accepted path."""
+    Bt, T, H, dk = k.shape
+    dv = e.shape[-1]
+    dev = k.device
+    Lmax = accepted.shape[1] if accepted.dim() == 2 else 0
+    f32 = torch.float32
+    for t, name, shp in ((k, "k", (Bt, T, H, dk)), (g, "g", (Bt, T, H)), (e, "e", (Bt, T, H, dv)),
+                         (S0, "S0", (Bt, H, dv, dk))):
+        _check(t, name, shp, f32, dev)
+    _check(parent, "parent", (Bt, T), torch.int32, dev)
+    _check(accepted, "accepted", (Bt, Lmax), torch.int32, dev)
+    _check(accepted_len, "accepted_len", (Bt,), torch.int32, dev)
+    shape = _gdn_shape(k, e)
+    rc = lib.tree_gdn_commit(ctypes.byref(shape), _ptr(k), _ptr(g), _ptr(e), _ptr(S0), _ptr(parent),
+                             _ptr(accepted), _ptr(accepted_len), int(Lmax), _ptr(tree_status),
+                             _stream(stream))
+    if rc != 0:
+        raise TreeSSDError(rc, "tree_gdn_commit")
+    return S0
 
 
 def tree_info(parent: torch.Tensor, depth=None, anc=None, tree_status=None, stream=None):

@@ -115,6 +115,49 @@ tsv_status tree_ssd_commit_layers(const tsv_shape* s, int32_t n_layers,
     return e == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
 }
 
+namespace {
+// gated-delta-rule shapes: fp32, one group, T <= 64, dk = d_state and
+// dv = head_dim up to 128
+tsv_status check_gdn_shape(const tsv_shape* s) {
+    tsv_status st = check_shape(s);
+    if (st != TSV_OK) return st;
+    if (s->in_dtype != TSV_F32 || s->n_groups != 1) return TSV_E_UNSUPPORTED;
+    if (s->n_nodes > 64 || s->head_dim > 128 || s->d_state > 128) return TSV_E_UNSUPPORTED;
+    return TSV_OK;
+}
+}  // namespace
+
+tsv_status tree_gdn_verify(const tsv_shape* s, const float* q, const float* k, const float* v,
+                           const float* g, const float* beta, const float* S0,
+                           const int32_t* parent, float* o, float* e, int32_t* tree_status,
+                           void* stream) {
+    tsv_status st = check_gdn_shape(s);
+    if (st != TSV_OK) return st;
+    if (s->batch == 0 || s->n_nodes == 0) return TSV_OK;
+    if (!q || !k || !v || !g || !beta || !S0 || !parent || !o) return TSV_E_NULL;
+    hipError_t err = tsv::launch_gdn_verify(s->batch, s->n_nodes, s->n_heads, s->d_state,
+                                            s->head_dim, q, k, v, g, beta, S0, parent, o, e,
+                                            tree_status, (hipStream_t)stream);
+    return err == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
+}
+
+tsv_status tree_gdn_commit(const tsv_shape* s, const float* k, const float* g, const float* e,
+                           float* S0_inout, const int32_t* parent, const int32_t* accepted,
+                           const int32_t* accepted_len, int32_t max_path_len, int32_t* tree_status,
+                           void* stream) {
+    tsv_status st = check_gdn_shape(s);
+    if (st != TSV_OK) return st;
+    if (max_path_len < 0 || max_path_len > kMaxNodes) return TSV_E_SHAPE;
+    if (s->batch == 0 || s->n_nodes == 0) return TSV_OK;
+    if (!k || !g || !e || !S0_inout || !parent || !accepted_len) return TSV_E_NULL;
+    if (max_path_len > 0 && !accepted) return TSV_E_NULL;
+    hipError_t err = tsv::launch_gdn_commit(s->batch, s->n_nodes, s->n_heads, s->d_state,
+                                            s->head_dim, k, g, e, S0_inout, parent, accepted,
+                                            accepted_len, max_path_len, tree_status,
+                                            (hipStream_t)stream);
+    return err == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
+}
+
 tsv_status tree_ssd_accept_greedy(int32_t batch, int32_t n_nodes, const int32_t* parent,
                                   const int32_t* draft_tokens, const int32_t* target_tokens,
                                   int32_t max_path_len, int32_t* accepted, int32_t* accepted_len,

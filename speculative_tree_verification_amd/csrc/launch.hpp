@@ -53,6 +53,16 @@ hipError_t launch_verify_wide(const VerifyArgs& a, int heads_per_block, hipStrea
 
 hipError_t launch_commit(const CommitArgs& a, bool bf16, hipStream_t stream);
 
+// gated delta rule over packed trees (fp32, T <= 64, dk and dv <= 128)
+hipError_t launch_gdn_verify(int batch, int T, int H, int dk, int dv, const float* q,
+                             const float* k, const float* v, const float* g, const float* beta,
+                             const float* S0, const int32_t* parent, float* o, float* e,
+                             int32_t* tree_status, hipStream_t stream);
+hipError_t launch_gdn_commit(int batch, int T, int H, int dk, int dv, const float* k,
+                             const float* g, const float* e, float* S, const int32_t* parent,
+                             const int32_t* accepted, const int32_t* accepted_len, int Lmax,
+                             int32_t* tree_status, hipStream_t stream);
+
 // greedy acceptance of a verified tree (one work-group per item)
 hipError_t launch_accept_greedy(int batch, int T, const int32_t* parent, const int32_t* draft,
                                 const int32_t* target, int Lmax, int32_t* accepted,
