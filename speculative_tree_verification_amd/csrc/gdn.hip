@@ -19,7 +19,9 @@
 // depth and ancestor-pair lists in LDS, decays along each list. Then dk is
 // walked in chunks of 32 columns staged in LDS (S0 columns, k and q rows): the
 // pair scores k_i . k_j and q_i . k_j accumulate per pair, the dense products
-// S0 k_i and S0 q_i per (node, value-row) unit in registers. The solve runs
+// K S0^T and Q S0^T (nodes x value rows) on fp32 MFMA (16x16x4), each wave
+// owning whole 16 x 16 output tiles; a lane's (node, value-row) units are the
+// MFMA output elements it holds, so they stay in registers for the solve. The solve runs
 // depth level by depth level (a barrier per level): every unit of the level
 // sums over its node's strict ancestors' pseudo-values in LDS. The outputs sum
 // over the whole path.
@@ -36,7 +38,8 @@ constexpr int kGdnDim = 128;
 constexpr int kGdnThreads = 512;
 constexpr int kGdnChunk = 32;                          // dk columns staged at a time
 constexpr int kGdnPairs = kGdnNodes * (kGdnNodes + 1) / 2;
-constexpr int kGdnUnits = kGdnNodes * kGdnDim / kGdnThreads;  // (node, row) units per thread
+constexpr int kGdnTilesPW = (kGdnNodes / 16) * (kGdnDim / 16) / (kGdnThreads / kWave);  // 16x16 output tiles per wave
+constexpr int kGdnUnits = 4 * kGdnTilesPW;  // (node, value-row) units per lane
 constexpr int kGdnPairsPT = (kGdnPairs + kGdnThreads - 1) / kGdnThreads;
 
 __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(
@@ -67,13 +70,25 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(
     const int h = blockIdx.x % H;
     const int tid = threadIdx.x;
     const size_t row0 = (size_t)b * T * H + h;  // (b, node 0, h) in units of a node's row
+    const int lane = tid & (kWave - 1);
+    const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int l16 = lane & 15, q4 = lane >> 4;
+    const int NTI = (T + 15) / 16, NTP = (dv + 15) / 16;  // node tiles, value-row tiles
+    // unit m of this lane: output tile tt = w + 8 (m / 4), element row 4 q4 + m % 4,
+    // column l16; node i = 16 (tt / NTP) + 4 q4 + m % 4, value row p = 16 (tt % NTP) + l16
+    auto unit = [&](int m, int& i, int& p) {
+        const int tt = w + (kGdnThreads / kWave) * (m >> 2);
+        i = 16 * (tt / NTP) + 4 * q4 + (m & 3);
+        p = 16 * (tt % NTP) + l16;
+        return tt < NTI * NTP && i < T && p < dv;
+    };
     const int par_i = load_parent(parent + (size_t)b * T, T);
     float vr[kGdnUnits];
 #pragma unroll
     for (int m = 0; m < kGdnUnits; ++m) {
-        const int u = tid + kGdnThreads * m;
-        const int i = min(u / dv, T - 1), p = u % dv;
-        vr[m] = v[(row0 + (size_t)i * H) * dv + p];
+        int i, p;
+        unit(m, i, p);
+        vr[m] = v[(row0 + (size_t)min(i, T - 1) * H) * dv + min(p, dv - 1)];
     }
     const int st = check_tree(par_i, T, s_par);
     if (h == 0 && tid == 0 && tree_status) tree_status[b] = st;
@@ -99,24 +114,25 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(
         atomicMax(&s_maxdep, cnt - 1);
     }
     // dk in chunks: pair scores per pair, S0 k_i and S0 q_i per (node, row) unit
-    float kk_acc[kGdnPairsPT], qk_acc[kGdnPairsPT], R[kGdnUnits], Q0[kGdnUnits];
+    float kk_acc[kGdnPairsPT], qk_acc[kGdnPairsPT];
+    f32x4 R4[kGdnTilesPW], Q4[kGdnTilesPW];
 #pragma unroll
     for (int m = 0; m < kGdnPairsPT; ++m) kk_acc[m] = qk_acc[m] = 0.f;
 #pragma unroll
-    for (int m = 0; m < kGdnUnits; ++m) R[m] = Q0[m] = 0.f;
+    for (int t = 0; t < kGdnTilesPW; ++t) R4[t] = Q4[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     const float* S0h = S0 + ((size_t)b * H + h) * dv * dk;
     for (int c0 = 0; c0 < dk; c0 += KC) {
-        const int w = min(KC, dk - c0);
+        const int wc = min(KC, dk - c0);
         __syncthreads();  // previous chunk consumed (and, the first time, the set-up done)
-        for (int x = tid; x < dv * KC; x += kGdnThreads) {
+        for (int x = tid; x < 16 * NTP * KC; x += kGdnThreads) {
             const int p = x / KC, n = x % KC;
-            s_S0c[p][n] = n < w ? S0h[(size_t)p * dk + c0 + n] : 0.f;
+            s_S0c[p][n] = n < wc && p < dv ? S0h[(size_t)p * dk + c0 + n] : 0.f;
         }
-        for (int x = tid; x < T * KC; x += kGdnThreads) {
+        for (int x = tid; x < 16 * NTI * KC; x += kGdnThreads) {
             const int i = x / KC, n = x % KC;
             const size_t src = (row0 + (size_t)i * H) * dk + c0 + n;
-            s_kc[i][n] = n < w ? k[src] : 0.f;
-            s_qc[i][n] = n < w ? q[src] : 0.f;
+            s_kc[i][n] = n < wc && i < T ? k[src] : 0.f;
+            s_qc[i][n] = n < wc && i < T ? q[src] : 0.f;
         }
         __syncthreads();
         const int npairs = s_off[T - 1] + s_dep[T - 1] + 1;
@@ -136,21 +152,27 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(
                 qk_acc[m] += c;
             }
         }
+        // D[node][row] += sum_n K[node][n] S0[row][n]: A = K (lane l16 = node,
+        // q4 = k), B = S0^T (q4 = k, l16 = row); same for Q
 #pragma unroll
-        for (int m = 0; m < kGdnUnits; ++m) {
-            const int u = tid + kGdnThreads * m;
-            if (u < T * dv) {
-                const int i = u / dv, p = u % dv;
-                float a = 0.f, c = 0.f;
-#pragma unroll 8
-                for (int n = 0; n < KC; ++n) {
-                    a += s_S0c[p][n] * s_kc[i][n];
-                    c += s_S0c[p][n] * s_qc[i][n];
+        for (int t = 0; t < kGdnTilesPW; ++t) {
+            const int tt = w + (kGdnThreads / kWave) * t;
+            if (tt < NTI * NTP) {
+                const int ni = 16 * (tt / NTP) + l16, pr = 16 * (tt % NTP) + l16;
+#pragma unroll
+                for (int ks = 0; ks < KC / 4; ++ks) {
+                    const float bs = s_S0c[pr][4 * ks + q4];
+                    R4[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(s_kc[ni][4 * ks + q4], bs, R4[t], 0, 0, 0);
+                    Q4[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(s_qc[ni][4 * ks + q4], bs, Q4[t], 0, 0, 0);
                 }
-                R[m] += a;
-                Q0[m] += c;
             }
         }
+    }
+    float R[kGdnUnits], Q0[kGdnUnits];
+#pragma unroll
+    for (int m = 0; m < kGdnUnits; ++m) {
+        R[m] = R4[m >> 2][m & 3];
+        Q0[m] = Q4[m >> 2][m & 3];
     }
     {
         const int npairs = s_off[T - 1] + s_dep[T - 1] + 1;
@@ -169,9 +191,8 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(
     for (int d = 0; d <= maxdep; ++d) {
 #pragma unroll
         for (int m = 0; m < kGdnUnits; ++m) {
-            const int u = tid + kGdnThreads * m;
-            if (u < T * dv) {
-                const int i = u / dv, p = u % dv;
+            int i, p;
+            if (unit(m, i, p)) {
                 if (s_dep[i] == d) {
                     const int base = s_off[i];
                     float acc = 0.f;
@@ -189,9 +210,8 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(
     // outputs over the whole path, and the pseudo-values for commit
 #pragma unroll
     for (int m = 0; m < kGdnUnits; ++m) {
-        const int u = tid + kGdnThreads * m;
-        if (u < T * dv) {
-            const int i = u / dv, p = u % dv;
+        int i, p;
+        if (unit(m, i, p)) {
             const int base = s_off[i], cnt = s_dep[i] + 1;
             float acc = s_gam[i] * Q0[m];
             for (int kk = 0; kk < cnt; ++kk) {
