@@ -15,16 +15,22 @@
 //   S'  = exp(G_l) S0 + sum_{j on path(l)} D_lj e_j k_j^T   (commit, path to l).
 //
 // fp32 throughout; trees of up to 64 nodes, dk and dv up to 128.
-// Verify: one work-group of 512 threads per (item, head). Set-up: tree check,
-// depth and ancestor-pair lists in LDS, decays along each list. Then dk is
-// walked in chunks of 32 columns staged in LDS (S0 columns, k and q rows): the
-// pair scores k_i . k_j and q_i . k_j accumulate per pair, the dense products
-// K S0^T and Q S0^T (nodes x value rows) on fp32 MFMA (16x16x4), each wave
-// owning whole 16 x 16 output tiles; a lane's (node, value-row) units are the
-// MFMA output elements it holds, so they stay in registers for the solve. The solve runs
-// depth level by depth level (a barrier per level): every unit of the level
-// sums over its node's strict ancestors' pseudo-values in LDS. The outputs sum
-// over the whole path.
+// Verify: one work-group of 512 threads (8 waves) per (item, head); wave w owns
+// value rows [16 w, 16 w + 16) from the dense products to the outputs.
+//  1. Every load is issued on entry: each wave's S0 rows straight into
+//     registers (the B operand of its products), k and q for LDS, v in the
+//     layout of the product accumulators. Meanwhile wave 0 alone (one lane per
+//     node, no block barrier) checks the tree and finds by pointer jumping each
+//     node's ancestor set (a 64-bit mask) and G_i, then lists the nodes by depth.
+//  2. fp32 MFMA (16x16x4): K S0^T and Q S0^T per wave (nodes x its value rows);
+//     the pair scores K K^T and Q K^T on the lower-triangle 16x16 tiles.
+//  3. The pair-score tiles become two dense node x node matrices in LDS:
+//     A_ij = beta_i D_ij (k_i . k_j) on strict ancestors and W_ij = D_ij (q_i . k_j)
+//     on the path, D_ij = exp(G_i - G_j); each wave writes its right-hand sides
+//     beta_i (v_i - exp(G_i) S0 k_i) into e.
+//  4. The solve runs level by level inside each wave (the unknowns of a value
+//     row depend only on the same row), four nodes of a level at a time.
+//  5. o = exp(G) * (Q S0^T) + W e on MFMA, again per wave.
 // Commit: one work-group per (item, head, 4,096-element chunk of the state),
 // as for the SSD commit, reading the pseudo-values the verify call wrote.
 #include "common.hpp"
@@ -36,191 +42,293 @@ namespace tsv {
 constexpr int kGdnNodes = 64;
 constexpr int kGdnDim = 128;
 constexpr int kGdnThreads = 512;
-constexpr int kGdnChunk = 32;                          // dk columns staged at a time
-constexpr int kGdnPairs = kGdnNodes * (kGdnNodes + 1) / 2;
-constexpr int kGdnTilesPW = (kGdnNodes / 16) * (kGdnDim / 16) / (kGdnThreads / kWave);  // 16x16 output tiles per wave
-constexpr int kGdnUnits = 4 * kGdnTilesPW;  // (node, value-row) units per lane
-constexpr int kGdnPairsPT = (kGdnPairs + kGdnThreads - 1) / kGdnThreads;
+constexpr int kGdnKS = kGdnDim + 4;    // row stride (floats) of staged k and q, and of e
+constexpr int kGdnCS = kGdnNodes + 4;  // row stride of the coefficient matrices A and W
+constexpr int kGdnStage = 2 * kGdnNodes * kGdnKS;                     // k, q
+constexpr int kGdnPost = 2 * kGdnNodes * kGdnCS + kGdnNodes * kGdnKS;  // A, W, e
+constexpr int kGdnUnion = kGdnStage > kGdnPost ? kGdnStage : kGdnPost;
 
+// four consecutive floats of a row with `rem` >= 1 valid elements left (VEC: a
+// 16-byte aligned row of a multiple of four elements)
+template <bool VEC>
+__device__ __forceinline__ float4 ld4(const float* __restrict__ p, int rem) {
+    if (VEC) return *(const float4*)p;
+    float4 r;
+    r.x = p[0];
+    r.y = rem > 1 ? p[1] : 0.f;
+    r.z = rem > 2 ? p[2] : 0.f;
+    r.w = rem > 3 ? p[3] : 0.f;
+    return r;
+}
+
+__device__ __forceinline__ f32x4 mfma4(const float4& a, const float4& b, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, c, 0, 0, 0);
+}
+
+template <bool VEC>
 __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* __restrict__ S0,
     const int32_t* __restrict__ parent, float* __restrict__ o, float* __restrict__ e_out,
     int32_t* __restrict__ tree_status, int T, int H, int dk, int dv) {
-    constexpr int KC = kGdnChunk;
-    __shared__ int s_par[kMaxNodes];
-    __shared__ int s_dep[kMaxNodes];
-    __shared__ int s_off[kMaxNodes];
-    __shared__ int s_scratch[kMaxNodes];
-    __shared__ int s_scan[kGdnThreads / kWave];
-    __shared__ uint16_t s_pair[kGdnPairs];
-    __shared__ float s_KK[kGdnPairs];  // k_i . k_j
-    __shared__ float s_QK[kGdnPairs];  // q_i . k_j
-    __shared__ float s_D[kGdnPairs];   // exp(G_i - G_j)
+    constexpr int KS = kGdnKS, CS = kGdnCS;
+    __shared__ __align__(16) float s_u[kGdnUnion];
+    __shared__ unsigned long long s_mask[kGdnNodes];  // ancestors of i, i included
+    __shared__ float s_G[kGdnNodes];
     __shared__ float s_gam[kGdnNodes];  // exp(G_i)
-    __shared__ float s_g[kGdnNodes];
     __shared__ float s_beta[kGdnNodes];
-    __shared__ float s_S0c[kGdnDim][KC + 1];
-    __shared__ float s_kc[kGdnNodes][KC + 1];
-    __shared__ float s_qc[kGdnNodes][KC + 1];
-    __shared__ float s_e[kGdnNodes][kGdnDim];
-    __shared__ int s_maxdep;
+    __shared__ int s_lvl[kGdnNodes];      // nodes by depth
+    __shared__ int s_lvs[kGdnNodes + 1];  // start of each depth in s_lvl
+    __shared__ int s_info[2];             // tree status, maximum depth
+    float* const s_k = s_u;
+    float* const s_q = s_u + kGdnNodes * KS;
+    float* const s_A = s_u;  // after the products
+    float* const s_W = s_u + kGdnNodes * CS;
+    float* const s_e = s_u + 2 * kGdnNodes * CS;
 
     const int b = blockIdx.x / H;
     const int h = blockIdx.x % H;
     const int tid = threadIdx.x;
-    const size_t row0 = (size_t)b * T * H + h;  // (b, node 0, h) in units of a node's row
     const int lane = tid & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int l16 = lane & 15, q4 = lane >> 4;
-    const int NTI = (T + 15) / 16, NTP = (dv + 15) / 16;  // node tiles, value-row tiles
-    // unit m of this lane: output tile tt = w + 8 (m / 4), element row 4 q4 + m % 4,
-    // column l16; node i = 16 (tt / NTP) + 4 q4 + m % 4, value row p = 16 (tt % NTP) + l16
-    auto unit = [&](int m, int& i, int& p) {
-        const int tt = w + (kGdnThreads / kWave) * (m >> 2);
-        i = 16 * (tt / NTP) + 4 * q4 + (m & 3);
-        p = 16 * (tt % NTP) + l16;
-        return tt < NTI * NTP && i < T && p < dv;
-    };
-    const int par_i = load_parent(parent + (size_t)b * T, T);
-    float vr[kGdnUnits];
-#pragma unroll
-    for (int m = 0; m < kGdnUnits; ++m) {
-        int i, p;
-        unit(m, i, p);
-        vr[m] = v[(row0 + (size_t)min(i, T - 1) * H) * dv + min(p, dv - 1)];
+    const int NTI = (T + 15) >> 4;  // 16-node tiles
+    const int nkk = (dk + 15) >> 4;  // 16-column steps over dk
+    const size_t row0 = (size_t)b * T * H + h;  // (b, node 0, h) in units of a node's row
+    const int p = 16 * w + l16;                  // value row of this lane
+    const bool wave_rows = 16 * w < dv;          // wave-uniform
+
+    // ---- 1. loads
+    int par = 0;
+    float gl = 0.f, bl = 0.f;
+    if (w == 0) {
+        const int i = min(lane, T - 1);
+        par = parent[(size_t)b * T + i];
+        gl = g[row0 + (size_t)i * H];
+        bl = beta[row0 + (size_t)i * H];
     }
-    const int st = check_tree(par_i, T, s_par);
-    if (h == 0 && tid == 0 && tree_status) tree_status[b] = st;
-    if (st) return;
-    if (tid < T) {
-        s_g[tid] = g[row0 + (size_t)tid * H];
-        s_beta[tid] = beta[row0 + (size_t)tid * H];
+    float4 kst[4], qst[4];  // (node, 4 columns) slots of k and q, 32 slots per row
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int slot = tid + kGdnThreads * m, r = slot >> 5, c = 4 * (slot & 31);
+        kst[m] = qst[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (r < T && c < dk) {
+            const size_t src = (row0 + (size_t)r * H) * dk + c;
+            kst[m] = ld4<VEC>(k + src, dk - c);
+            qst[m] = ld4<VEC>(q + src, dk - c);
+        }
     }
-    if (tid == 0) s_maxdep = 0;
-    const int total = build_pairs<kGdnThreads>(s_par, T, s_dep, s_off, s_scratch, s_scan, s_pair,
-                                               kGdnPairs);
-    (void)total;  // every tree of up to 64 nodes fits
-    // decays along each node's list (entry 0 is the node itself)
-    if (tid < T) {
-        const int base = s_off[tid], cnt = s_dep[tid] + 1;
-        float s = 0.f;
-        for (int kk = 0; kk < cnt; ++kk) {
-            const int j = s_pair[base + kk] >> 8;
-            s_D[base + kk] = __expf(s);
-            s += s_g[j];
-        }
-        s_gam[tid] = __expf(s);
-        atomicMax(&s_maxdep, cnt - 1);
+    // S0[p][16 kk + 4 q4 .. + 3]: lane (l16, q4) supplies columns 16 kk + 4 q4 + c
+    // of the contraction over dk at step (kk, c)
+    float4 s0r[kGdnDim / 16];
+    const float* S0p = S0 + (((size_t)b * H + h) * dv + min(p, dv - 1)) * dk;
+#pragma unroll
+    for (int kk = 0; kk < kGdnDim / 16; ++kk) {
+        const int col = 16 * kk + 4 * q4;
+        s0r[kk] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (wave_rows && p < dv && col < dk) s0r[kk] = ld4<VEC>(S0p + col, dk - col);
     }
-    // dk in chunks: pair scores per pair, S0 k_i and S0 q_i per (node, row) unit
-    float kk_acc[kGdnPairsPT], qk_acc[kGdnPairsPT];
-    f32x4 R4[kGdnTilesPW], Q4[kGdnTilesPW];
+    // v at the accumulator positions: node 16 ti + 4 q4 + r, value row p
+    float vr[kGdnNodes / 4];
 #pragma unroll
-    for (int m = 0; m < kGdnPairsPT; ++m) kk_acc[m] = qk_acc[m] = 0.f;
+    for (int ti = 0; ti < kGdnNodes / 16; ++ti)
 #pragma unroll
-    for (int t = 0; t < kGdnTilesPW; ++t) R4[t] = Q4[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const float* S0h = S0 + ((size_t)b * H + h) * dv * dk;
-    for (int c0 = 0; c0 < dk; c0 += KC) {
-        const int wc = min(KC, dk - c0);
-        __syncthreads();  // previous chunk consumed (and, the first time, the set-up done)
-        for (int x = tid; x < 16 * NTP * KC; x += kGdnThreads) {
-            const int p = x / KC, n = x % KC;
-            s_S0c[p][n] = n < wc && p < dv ? S0h[(size_t)p * dk + c0 + n] : 0.f;
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * ti + 4 * q4 + r;
+            vr[4 * ti + r] =
+                wave_rows && i < T && p < dv ? v[(row0 + (size_t)i * H) * dv + p] : 0.f;
         }
-        for (int x = tid; x < 16 * NTI * KC; x += kGdnThreads) {
-            const int i = x / KC, n = x % KC;
-            const size_t src = (row0 + (size_t)i * H) * dk + c0 + n;
-            s_kc[i][n] = n < wc && i < T ? k[src] : 0.f;
-            s_qc[i][n] = n < wc && i < T ? q[src] : 0.f;
+
+    // ---- tree set-up by wave 0, one lane per node
+    if (w == 0) {
+        const bool live = lane < T;
+        const bool br = __ballot(lane == 0 && par != -1) != 0;
+        const bool bp = __ballot(live && lane > 0 && (par < 0 || par >= lane)) != 0;
+        const int st = (br ? kStBadRoot : 0) | (bp ? kStBadParent : 0);
+        if (lane == 0) {
+            s_info[0] = st;
+            if (h == 0 && tree_status) tree_status[b] = st;
         }
-        __syncthreads();
-        const int npairs = s_off[T - 1] + s_dep[T - 1] + 1;
-#pragma unroll
-        for (int m = 0; m < kGdnPairsPT; ++m) {
-            const int pq = tid + kGdnThreads * m;
-            if (pq < npairs) {
-                const int pr = s_pair[pq];
-                const int i = pr & 255, j = pr >> 8;
-                float a = 0.f, c = 0.f;
-#pragma unroll 8
-                for (int n = 0; n < KC; ++n) {
-                    a += s_kc[i][n] * s_kc[j][n];
-                    c += s_qc[i][n] * s_kc[j][n];
-                }
-                kk_acc[m] += a;
-                qk_acc[m] += c;
-            }
-        }
-        // D[node][row] += sum_n K[node][n] S0[row][n]: A = K (lane l16 = node,
-        // q4 = k), B = S0^T (q4 = k, l16 = row); same for Q
-#pragma unroll
-        for (int t = 0; t < kGdnTilesPW; ++t) {
-            const int tt = w + (kGdnThreads / kWave) * t;
-            if (tt < NTI * NTP) {
-                const int ni = 16 * (tt / NTP) + l16, pr = 16 * (tt % NTP) + l16;
-#pragma unroll
-                for (int ks = 0; ks < KC / 4; ++ks) {
-                    const float bs = s_S0c[pr][4 * ks + q4];
-                    R4[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(s_kc[ni][4 * ks + q4], bs, R4[t], 0, 0, 0);
-                    Q4[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(s_qc[ni][4 * ks + q4], bs, Q4[t], 0, 0, 0);
+        if (!st) {
+            // pointer jumping: lane i covers the path from i up to (not including)
+            // n, its mask and its sum of g; merging with n's segment doubles it
+            unsigned long long msk = live ? 1ull << lane : 0ull;
+            int n = live && lane > 0 ? par : -1;
+            float G = live ? gl : 0.f;
+            while (__ballot(n >= 0)) {
+                const int src = n >= 0 ? n : lane;
+                const uint32_t mlo = __shfl((uint32_t)msk, src, kWave);
+                const uint32_t mhi = __shfl((uint32_t)(msk >> 32), src, kWave);
+                const int n2 = __shfl(n, src, kWave);
+                const float G2 = __shfl(G, src, kWave);
+                if (n >= 0) {
+                    msk |= ((unsigned long long)mhi << 32) | mlo;
+                    G += G2;
+                    n = n2;
                 }
             }
-        }
-    }
-    float R[kGdnUnits], Q0[kGdnUnits];
+            const int dep = live ? __popcll(msk) - 1 : -1;
+            int maxdep = dep;
 #pragma unroll
-    for (int m = 0; m < kGdnUnits; ++m) {
-        R[m] = R4[m >> 2][m & 3];
-        Q0[m] = Q4[m >> 2][m & 3];
-    }
-    {
-        const int npairs = s_off[T - 1] + s_dep[T - 1] + 1;
-#pragma unroll
-        for (int m = 0; m < kGdnPairsPT; ++m) {
-            const int pq = tid + kGdnThreads * m;
-            if (pq < npairs) {
-                s_KK[pq] = kk_acc[m];
-                s_QK[pq] = qk_acc[m];
+            for (int off = 32; off > 0; off >>= 1) maxdep = max(maxdep, __shfl_xor(maxdep, off, kWave));
+            int start = 0;
+            for (int d = 0; d <= maxdep; ++d) {
+                const unsigned long long bm = __ballot(dep == d);
+                if (dep == d) s_lvl[start + __popcll(bm & ((1ull << lane) - 1))] = lane;
+                if (lane == 0) s_lvs[d] = start;
+                start += __popcll(bm);
             }
+            if (lane == 0) {
+                s_lvs[maxdep + 1] = start;
+                s_info[1] = maxdep;
+            }
+            s_mask[lane] = msk;
+            s_G[lane] = G;
+            s_gam[lane] = live ? __expf(G) : 0.f;
+            s_beta[lane] = live ? bl : 0.f;
         }
     }
-    __syncthreads();
-    // triangular solve, one depth level at a time
-    const int maxdep = s_maxdep;
-    for (int d = 0; d <= maxdep; ++d) {
 #pragma unroll
-        for (int m = 0; m < kGdnUnits; ++m) {
-            int i, p;
-            if (unit(m, i, p)) {
-                if (s_dep[i] == d) {
-                    const int base = s_off[i];
-                    float acc = 0.f;
-                    for (int kk = 1; kk <= d; ++kk) {
-                        const int j = s_pair[base + kk] >> 8;
-                        acc += s_D[base + kk] * s_KK[base + kk] * s_e[j][p];
+    for (int m = 0; m < 4; ++m) {
+        const int slot = tid + kGdnThreads * m, r = slot >> 5, c = 4 * (slot & 31);
+        *(float4*)&s_k[r * KS + c] = kst[m];
+        *(float4*)&s_q[r * KS + c] = qst[m];
+    }
+    lds_barrier();
+    if (s_info[0]) return;
+
+    // ---- 2. products
+    f32x4 R4[kGdnNodes / 16], Q4[kGdnNodes / 16];
+#pragma unroll
+    for (int ti = 0; ti < kGdnNodes / 16; ++ti) R4[ti] = Q4[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (wave_rows) {
+#pragma unroll
+        for (int ti = 0; ti < kGdnNodes / 16; ++ti) {
+            if (ti < NTI) {
+                const float* ka = s_k + (16 * ti + l16) * KS + 4 * q4;
+                const float* qa = s_q + (16 * ti + l16) * KS + 4 * q4;
+#pragma unroll
+                for (int kk = 0; kk < kGdnDim / 16; ++kk) {
+                    if (kk < nkk) {
+                        R4[ti] = mfma4(*(const float4*)(ka + 16 * kk), s0r[kk], R4[ti]);
+                        Q4[ti] = mfma4(*(const float4*)(qa + 16 * kk), s0r[kk], Q4[ti]);
                     }
-                    const float bi = s_beta[i];
-                    s_e[i][p] = bi * (vr[m] - s_gam[i] * R[m]) - bi * acc;
                 }
             }
         }
-        __syncthreads();
     }
-    // outputs over the whole path, and the pseudo-values for commit
+    // pair scores on the lower-triangle tiles: tile t < ntri of K K^T, then of Q K^T
+    const int ntri = NTI * (NTI + 1) / 2;
+    constexpr int kPT = 3;  // tiles per wave: 2 * 10 lower-triangle tiles over 8 waves
+    f32x4 P4[kPT];
+    int pti[kPT], ptj[kPT];
 #pragma unroll
-    for (int m = 0; m < kGdnUnits; ++m) {
-        int i, p;
-        if (unit(m, i, p)) {
-            const int base = s_off[i], cnt = s_dep[i] + 1;
-            float acc = s_gam[i] * Q0[m];
-            for (int kk = 0; kk < cnt; ++kk) {
-                const int j = s_pair[base + kk] >> 8;
-                acc += s_D[base + kk] * s_QK[base + kk] * s_e[j][p];
+    for (int u = 0; u < kPT; ++u) {
+        P4[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int t = w + (kGdnThreads / kWave) * u;
+        int ti = 0, tj = t < 2 * ntri ? t % ntri : -1;
+        while (tj > ti) tj -= ++ti;
+        pti[u] = ti;
+        ptj[u] = tj;
+        if (tj >= 0) {
+            const float* xa = (t < ntri ? s_k : s_q) + (16 * ti + l16) * KS + 4 * q4;
+            const float* kb = s_k + (16 * tj + l16) * KS + 4 * q4;
+#pragma unroll
+            for (int kk = 0; kk < kGdnDim / 16; ++kk)
+                if (kk < nkk)
+                    P4[u] = mfma4(*(const float4*)(xa + 16 * kk), *(const float4*)(kb + 16 * kk), P4[u]);
+        }
+    }
+    lds_barrier();  // k and q consumed: the region now holds A, W and e
+
+    // ---- 3. coefficients and right-hand sides
+#pragma unroll
+    for (int u = 0; u < kPT; ++u) {
+        const int t = w + (kGdnThreads / kWave) * u;
+        if (ptj[u] >= 0) {
+            const int j = 16 * ptj[u] + l16;
+            const float Gj = s_G[j];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * pti[u] + 4 * q4 + r;
+                const bool anc = (s_mask[i] >> j) & 1ull;  // j on the root path of i
+                const float D = __expf(s_G[i] - Gj);
+                if (t < ntri)
+                    s_A[i * CS + j] = anc && j != i ? s_beta[i] * D * P4[u][r] : 0.f;
+                else
+                    s_W[i * CS + j] = anc ? D * P4[u][r] : 0.f;
             }
-            const size_t dst = (row0 + (size_t)i * H) * dv + p;
-            o[dst] = acc;
-            if (e_out) e_out[dst] = s_e[i][p];
+        }
+    }
+    if (wave_rows) {
+#pragma unroll
+        for (int ti = 0; ti < kGdnNodes / 16; ++ti) {
+            if (ti < NTI) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * ti + 4 * q4 + r;
+                    s_e[i * KS + p] =
+                        i < T ? s_beta[i] * (vr[4 * ti + r] - s_gam[i] * R4[ti][r]) : 0.f;
+                }
+            }
+        }
+    }
+    lds_barrier();
+    if (!wave_rows) return;
+
+    // ---- 4. solve, level by level within the wave
+    const int maxdep = s_info[1];
+    for (int d = 0; d <= maxdep; ++d) {
+        const int hi = s_lvs[d + 1];
+        for (int pos = s_lvs[d] + q4; pos < hi; pos += 4) {
+            const int i = s_lvl[pos];
+            unsigned long long m = s_mask[i] & ~(1ull << i);
+            float acc = s_e[i * KS + p];
+            while (m) {
+                int j[4];
+                bool ok[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    ok[u] = m != 0ull;
+                    j[u] = ok[u] ? (int)__builtin_ctzll(m) : 0;
+                    m &= m - 1ull;
+                }
+                float a[4], x[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    a[u] = s_A[i * CS + j[u]];
+                    x[u] = s_e[j[u] * KS + p];
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc = ok[u] ? acc - a[u] * x[u] : acc;
+            }
+            s_e[i * KS + p] = acc;
+            if (e_out && p < dv) e_out[(row0 + (size_t)i * H) * dv + p] = acc;
+        }
+        wave_sync();
+    }
+
+    // ---- 5. outputs: o = exp(G) (Q S0^T) + W e, tiles below the diagonal only
+#pragma unroll
+    for (int ti = 0; ti < kGdnNodes / 16; ++ti) {
+        if (ti < NTI) {
+            f32x4 acc;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = s_gam[16 * ti + 4 * q4 + r] * Q4[ti][r];
+            for (int tj = 0; tj <= ti; ++tj) {
+                const float4 wv = *(const float4*)&s_W[(16 * ti + l16) * CS + 16 * tj + 4 * q4];
+                const float* ep = s_e + (16 * tj + 4 * q4) * KS + p;
+                const float4 ev = make_float4(ep[0], ep[KS], ep[2 * KS], ep[3 * KS]);
+                acc = mfma4(wv, ev, acc);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * ti + 4 * q4 + r;
+                if (i < T && p < dv) o[(row0 + (size_t)i * H) * dv + p] = acc[r];
+            }
         }
     }
 }
@@ -321,8 +429,13 @@ hipError_t launch_gdn_verify(int batch, int T, int H, int dk, int dv, const floa
                              const float* k, const float* v, const float* g, const float* beta,
                              const float* S0, const int32_t* parent, float* o, float* e,
                              int32_t* tree_status, hipStream_t stream) {
-    hipLaunchKernelGGL(gdn_verify_kernel, dim3(batch * H), dim3(kGdnThreads), 0, stream, q, k, v,
-                       g, beta, S0, parent, o, e, tree_status, T, H, dk, dv);
+    const bool vec = dk % 4 == 0 && (((uintptr_t)q | (uintptr_t)k | (uintptr_t)S0) & 15) == 0;
+    if (vec)
+        hipLaunchKernelGGL(gdn_verify_kernel<true>, dim3(batch * H), dim3(kGdnThreads), 0, stream,
+                           q, k, v, g, beta, S0, parent, o, e, tree_status, T, H, dk, dv);
+    else
+        hipLaunchKernelGGL(gdn_verify_kernel<false>, dim3(batch * H), dim3(kGdnThreads), 0, stream,
+                           q, k, v, g, beta, S0, parent, o, e, tree_status, T, H, dk, dv);
     return hipGetLastError();
 }
 
