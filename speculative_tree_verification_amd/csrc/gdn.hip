@@ -14,23 +14,27 @@
 //   o_i = exp(G_i) S0 q_i + sum_{j on path(i)} D_ij (q_i . k_j) e_j,
 //   S'  = exp(G_l) S0 + sum_{j on path(l)} D_lj e_j k_j^T   (commit, path to l).
 //
-// fp32 throughout; trees of up to 64 nodes, dk and dv up to 128.
-// Verify: one work-group of 512 threads (8 waves) per (item, head); wave w owns
-// value rows [16 w, 16 w + 16) from the dense products to the outputs.
-//  1. Every load is issued on entry: each wave's S0 rows straight into
-//     registers (the B operand of its products), k and q for LDS, v in the
-//     layout of the product accumulators. Meanwhile wave 0 alone (one lane per
-//     node, no block barrier) checks the tree and finds by pointer jumping each
-//     node's ancestor set (a 64-bit mask) and G_i, then lists the nodes by depth.
-//  2. fp32 MFMA (16x16x4): K S0^T and Q S0^T per wave (nodes x its value rows);
-//     the pair scores K K^T and Q K^T on the lower-triangle 16x16 tiles.
-//  3. The pair-score tiles become two dense node x node matrices in LDS:
-//     A_ij = beta_i D_ij (k_i . k_j) on strict ancestors and W_ij = D_ij (q_i . k_j)
-//     on the path, D_ij = exp(G_i - G_j); each wave writes its right-hand sides
-//     beta_i (v_i - exp(G_i) S0 k_i) into e.
-//  4. The solve runs level by level inside each wave (the unknowns of a value
-//     row depend only on the same row), four nodes of a level at a time.
-//  5. o = exp(G) * (Q S0^T) + W e on MFMA, again per wave.
+// Inputs and outputs fp32; trees of up to 64 nodes, dk and dv up to 128.
+// Verify: one work-group of 9 waves per (item, head). Row wave w < 8 owns value
+// rows [16 w, 16 w + 16); the tree wave handles everything node x node.
+//  1. Every load is issued on entry: each row wave's S0 rows straight into
+//     registers (the B operand of its products), k and q for LDS (split into
+//     bf16 high and low parts), v in the layout of the product accumulators.
+//     Meanwhile the tree wave (one lane per node) checks the tree and finds by
+//     pointer jumping each node's ancestor set (a 64-bit mask) and G_i, lists
+//     the nodes by depth and each node's strict ancestors by depth.
+//  2. Row waves: K S0^T and Q S0^T (nodes x its value rows) on MFMA with
+//     three-term bf16 splits (hi*hi + hi*lo + lo*hi, fp32 accumulation), then the
+//     right-hand sides r_i = beta_i (v_i - exp(G_i) S0 k_i) in registers.
+//     Tree wave, at the same time: the pair scores K K^T and Q K^T on the
+//     lower-triangle 16x16 tiles (same splits), A_ij = beta_i D_ij (k_i . k_j) on
+//     strict ancestors, W_ij = D_ij (q_i . k_j) on the path (D_ij = exp(G_i - G_j)),
+//     and M = (I + A)^{-1} by substitution one depth level at a time, one
+//     (node, ancestor) entry per lane: M is ancestor-masked like A, and it is
+//     shared by every value row.
+//  3. Row waves: e = M r and o = exp(G) * (Q S0^T) + W e on fp32 MFMA; the
+//     accumulators of r and e are laid out as the B operand of the next product,
+//     so they never leave registers.
 // Commit: one work-group per (item, head, 4,096-element chunk of the state),
 // as for the SSD commit, reading the pseudo-values the verify call wrote.
 #include "common.hpp"
@@ -41,12 +45,11 @@ namespace tsv {
 
 constexpr int kGdnNodes = 64;
 constexpr int kGdnDim = 128;
-constexpr int kGdnThreads = 512;
-constexpr int kGdnKS = kGdnDim + 4;    // row stride (floats) of staged k and q, and of e
-constexpr int kGdnCS = kGdnNodes + 4;  // row stride of the coefficient matrices A and W
-constexpr int kGdnStage = 2 * kGdnNodes * kGdnKS;                     // k, q
-constexpr int kGdnPost = 2 * kGdnNodes * kGdnCS + kGdnNodes * kGdnKS;  // A, W, e
-constexpr int kGdnUnion = kGdnStage > kGdnPost ? kGdnStage : kGdnPost;
+constexpr int kGdnRowWaves = 8;  // row wave w owns value rows [16 w, 16 w + 16)
+constexpr int kGdnRowThreads = kGdnRowWaves * kWave;
+constexpr int kGdnThreads = kGdnRowThreads + kWave;  // and the tree wave
+constexpr int kGdnRS = kGdnDim + 8;    // row stride (bf16) of the staged halves of k and q
+constexpr int kGdnCS = kGdnNodes + 4;  // row stride of the dense node x node matrices
 
 // four consecutive floats of a row with `rem` >= 1 valid elements left (VEC: a
 // 16-byte aligned row of a multiple of four elements)
@@ -59,6 +62,23 @@ __device__ __forceinline__ float4 ld4(const float* __restrict__ p, int rem) {
     r.z = rem > 2 ? p[2] : 0.f;
     r.w = rem > 3 ? p[3] : 0.f;
     return r;
+}
+
+// x = hi + lo for four floats: bf16 high parts and bf16 residuals, packed in pairs
+__device__ __forceinline__ void split4(const float4& x, uint2& hi, uint2& lo) {
+    const uint32_t h01 = pack_bf16x2(x.x, x.y), h23 = pack_bf16x2(x.z, x.w);
+    hi = make_uint2(h01, h23);
+    lo = make_uint2(pack_bf16x2(x.x - lo_bf16(h01), x.y - hi_bf16(h01)),
+                    pack_bf16x2(x.z - lo_bf16(h23), x.w - hi_bf16(h23)));
+}
+
+// a b with both operands split into bf16 high and low parts: the three products
+// hi*hi + hi*lo + lo*hi accumulate in fp32 (about 16 significant bits per operand)
+__device__ __forceinline__ f32x4 mfma_x3(const bf16x8& ah, const bf16x8& al, const bf16x8& bh,
+                                         const bf16x8& bl, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x4 mfma4(const float4& a, const float4& b, f32x4 c) {
@@ -74,20 +94,24 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(
     const float* __restrict__ g, const float* __restrict__ beta, const float* __restrict__ S0,
     const int32_t* __restrict__ parent, float* __restrict__ o, float* __restrict__ e_out,
     int32_t* __restrict__ tree_status, int T, int H, int dk, int dv) {
-    constexpr int KS = kGdnKS, CS = kGdnCS;
-    __shared__ __align__(16) float s_u[kGdnUnion];
-    __shared__ unsigned long long s_mask[kGdnNodes];  // ancestors of i, i included
-    __shared__ float s_G[kGdnNodes];
-    __shared__ float s_gam[kGdnNodes];  // exp(G_i)
-    __shared__ float s_beta[kGdnNodes];
-    __shared__ int s_lvl[kGdnNodes];      // nodes by depth
-    __shared__ int s_lvs[kGdnNodes + 1];  // start of each depth in s_lvl
-    __shared__ int s_info[2];             // tree status, maximum depth
-    float* const s_k = s_u;
-    float* const s_q = s_u + kGdnNodes * KS;
-    float* const s_A = s_u;  // after the products
-    float* const s_W = s_u + kGdnNodes * CS;
-    float* const s_e = s_u + 2 * kGdnNodes * CS;
+    constexpr int NN = kGdnNodes, RS = kGdnRS, CS = kGdnCS;
+    __shared__ __align__(16) uint16_t s_stage[4 * NN * RS];  // k hi, k lo, q hi, q lo
+    __shared__ __align__(16) float s_A[NN * NN];  // A_ij at [i][depth of j]
+    __shared__ __align__(16) float s_W[NN * CS];
+    __shared__ __align__(16) float s_M[NN * CS];
+    __shared__ __align__(16) uint8_t s_anc[NN * NN];  // strict ancestors of i, root first
+    __shared__ unsigned long long s_mask[NN];          // ancestors of i, i included
+    __shared__ float s_G[NN];
+    __shared__ float s_gam[NN];  // exp(G_i)
+    __shared__ float s_beta[NN];
+    __shared__ int s_dep[NN];
+    __shared__ int s_lvl[NN];      // nodes by depth
+    __shared__ int s_lvs[NN + 1];  // start of each depth in s_lvl
+    __shared__ int s_info[2];      // tree status, maximum depth
+    uint16_t* const s_kh = s_stage;
+    uint16_t* const s_kl = s_kh + NN * RS;
+    uint16_t* const s_qh = s_kl + NN * RS;
+    uint16_t* const s_ql = s_qh + NN * RS;
 
     const int b = blockIdx.x / H;
     const int h = blockIdx.x % H;
@@ -95,16 +119,17 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(
     const int lane = tid & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int l16 = lane & 15, q4 = lane >> 4;
-    const int NTI = (T + 15) >> 4;  // 16-node tiles
-    const int nkk = (dk + 15) >> 4;  // 16-column steps over dk
+    const int NTI = (T + 15) >> 4;   // 16-node tiles
+    const int nks = (dk + 31) >> 5;  // 32-column steps over dk
     const size_t row0 = (size_t)b * T * H + h;  // (b, node 0, h) in units of a node's row
-    const int p = 16 * w + l16;                  // value row of this lane
-    const bool wave_rows = 16 * w < dv;          // wave-uniform
+    const bool tree_wave = w == kGdnRowWaves;
+    const int p = 16 * w + l16;                    // value row of this lane (row waves)
+    const bool wave_rows = !tree_wave && 16 * w < dv;  // wave-uniform
 
     // ---- 1. loads
     int par = 0;
     float gl = 0.f, bl = 0.f;
-    if (w == 0) {
+    if (tree_wave) {
         const int i = min(lane, T - 1);
         par = parent[(size_t)b * T + i];
         gl = g[row0 + (size_t)i * H];
@@ -113,37 +138,16 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(
     float4 kst[4], qst[4];  // (node, 4 columns) slots of k and q, 32 slots per row
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        const int slot = tid + kGdnThreads * m, r = slot >> 5, c = 4 * (slot & 31);
+        const int slot = tid + kGdnRowThreads * m, r = slot >> 5, c = 4 * (slot & 31);
         kst[m] = qst[m] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (r < T && c < dk) {
+        if (!tree_wave && r < T && c < dk) {
             const size_t src = (row0 + (size_t)r * H) * dk + c;
             kst[m] = ld4<VEC>(k + src, dk - c);
             qst[m] = ld4<VEC>(q + src, dk - c);
         }
     }
-    // S0[p][16 kk + 4 q4 .. + 3]: lane (l16, q4) supplies columns 16 kk + 4 q4 + c
-    // of the contraction over dk at step (kk, c)
-    float4 s0r[kGdnDim / 16];
-    const float* S0p = S0 + (((size_t)b * H + h) * dv + min(p, dv - 1)) * dk;
-#pragma unroll
-    for (int kk = 0; kk < kGdnDim / 16; ++kk) {
-        const int col = 16 * kk + 4 * q4;
-        s0r[kk] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (wave_rows && p < dv && col < dk) s0r[kk] = ld4<VEC>(S0p + col, dk - col);
-    }
-    // v at the accumulator positions: node 16 ti + 4 q4 + r, value row p
-    float vr[kGdnNodes / 4];
-#pragma unroll
-    for (int ti = 0; ti < kGdnNodes / 16; ++ti)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = 16 * ti + 4 * q4 + r;
-            vr[4 * ti + r] =
-                wave_rows && i < T && p < dv ? v[(row0 + (size_t)i * H) * dv + p] : 0.f;
-        }
-
-    // ---- tree set-up by wave 0, one lane per node
-    if (w == 0) {
+    if (tree_wave) {
+        // ---- tree set-up, one lane per node
         const bool live = lane < T;
         const bool br = __ballot(lane == 0 && par != -1) != 0;
         const bool bp = __ballot(live && lane > 0 && (par < 0 || par >= lane)) != 0;
@@ -185,149 +189,197 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(
                 s_lvs[maxdep + 1] = start;
                 s_info[1] = maxdep;
             }
+            // the strict ancestors of each node by depth: climb one step a round
+            const int up = live && lane > 0 ? par : 0;
+            int cur = lane;
+            for (int t = 0; t < maxdep; ++t) {
+                cur = __shfl(up, cur, kWave);
+                if (t < dep) s_anc[lane * NN + dep - 1 - t] = (uint8_t)cur;
+            }
+            s_dep[lane] = live ? dep : 0;
             s_mask[lane] = msk;
             s_G[lane] = G;
             s_gam[lane] = live ? __expf(G) : 0.f;
             s_beta[lane] = live ? bl : 0.f;
         }
-    }
+    } else {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int slot = tid + kGdnThreads * m, r = slot >> 5, c = 4 * (slot & 31);
-        *(float4*)&s_k[r * KS + c] = kst[m];
-        *(float4*)&s_q[r * KS + c] = qst[m];
+        for (int m = 0; m < 4; ++m) {
+            const int slot = tid + kGdnRowThreads * m, r = slot >> 5, c = 4 * (slot & 31);
+            uint2 hi, lo;
+            split4(kst[m], hi, lo);
+            *(uint2*)&s_kh[r * RS + c] = hi;
+            *(uint2*)&s_kl[r * RS + c] = lo;
+            split4(qst[m], hi, lo);
+            *(uint2*)&s_qh[r * RS + c] = hi;
+            *(uint2*)&s_ql[r * RS + c] = lo;
+        }
     }
+    // S0 and v are requested only now, so that k and q (needed first) do not
+    // share the memory system with them
+    // S0[p][32 ks + 8 q4 .. + 7]: lane (l16, q4) supplies columns 32 ks + 8 q4 + c
+    // of the contraction over dk at step ks
+    float4 s0r[kGdnDim / 16];
+    const float* S0p = S0 + (((size_t)b * H + h) * dv + min(p, dv - 1)) * dk;
+#pragma unroll
+    for (int kk = 0; kk < kGdnDim / 16; ++kk) {
+        const int col = 32 * (kk >> 1) + 8 * q4 + 4 * (kk & 1);
+        s0r[kk] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (wave_rows && p < dv && col < dk) s0r[kk] = ld4<VEC>(S0p + col, dk - col);
+    }
+    // v at the accumulator positions: node 16 ti + 4 q4 + r, value row p
+    float vr[NN / 4];
+#pragma unroll
+    for (int ti = 0; ti < NN / 16; ++ti)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * ti + 4 * q4 + r;
+            vr[4 * ti + r] =
+                wave_rows && i < T && p < dv ? v[(row0 + (size_t)i * H) * dv + p] : 0.f;
+        }
+
     lds_barrier();
     if (s_info[0]) return;
 
-    // ---- 2. products
-    f32x4 R4[kGdnNodes / 16], Q4[kGdnNodes / 16];
+    // ---- 2. pair scores on the lower-triangle tiles (tile t < ntri of K K^T,
+    // then of Q K^T; three-term bf16 splits), coefficients A and W, M = I there
+    const int ntri = NTI * (NTI + 1) / 2;
+    if (!tree_wave) {
 #pragma unroll
-    for (int ti = 0; ti < kGdnNodes / 16; ++ti) R4[ti] = Q4[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (wave_rows) {
+        for (int u = 0; u < 3; ++u) {  // 2 * 10 tiles at most over 8 waves
+            const int t = w + kGdnRowWaves * u;
+            if (t < 2 * ntri) {
+                const bool kk = t < ntri;
+                int ti = 0, tj = kk ? t : t - ntri;
+                while (tj > ti) tj -= ++ti;
+                const int oa = (16 * ti + l16) * RS + 8 * q4, ob = (16 * tj + l16) * RS + 8 * q4;
+                const uint16_t* xh = kk ? s_kh : s_qh;
+                const uint16_t* xl = kk ? s_kl : s_ql;
+                f32x4 P = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ti = 0; ti < kGdnNodes / 16; ++ti) {
-            if (ti < NTI) {
-                const float* ka = s_k + (16 * ti + l16) * KS + 4 * q4;
-                const float* qa = s_q + (16 * ti + l16) * KS + 4 * q4;
+                for (int ks = 0; ks < kGdnDim / 32; ++ks)
+                    if (ks < nks)
+                        P = mfma_x3(*(const bf16x8*)(xh + oa + 32 * ks), *(const bf16x8*)(xl + oa + 32 * ks),
+                                    *(const bf16x8*)(s_kh + ob + 32 * ks), *(const bf16x8*)(s_kl + ob + 32 * ks), P);
+                const int j = 16 * tj + l16;
+                const float Gj = s_G[j];
+                const int dj = s_dep[j];
 #pragma unroll
-                for (int kk = 0; kk < kGdnDim / 16; ++kk) {
-                    if (kk < nkk) {
-                        R4[ti] = mfma4(*(const float4*)(ka + 16 * kk), s0r[kk], R4[ti]);
-                        Q4[ti] = mfma4(*(const float4*)(qa + 16 * kk), s0r[kk], Q4[ti]);
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * ti + 4 * q4 + r;
+                    const bool anc = (s_mask[i] >> j) & 1ull;  // j on the root path of i
+                    const float D = __expf(s_G[i] - Gj);
+                    if (kk) {
+                        if (anc && j != i) s_A[i * NN + dj] = s_beta[i] * D * P[r];
+                        s_M[i * CS + j] = i == j ? 1.f : 0.f;
+                    } else {
+                        s_W[i * CS + j] = anc ? D * P[r] : 0.f;
                     }
                 }
             }
         }
     }
-    // pair scores on the lower-triangle tiles: tile t < ntri of K K^T, then of Q K^T
-    const int ntri = NTI * (NTI + 1) / 2;
-    constexpr int kPT = 3;  // tiles per wave: 2 * 10 lower-triangle tiles over 8 waves
-    f32x4 P4[kPT];
-    int pti[kPT], ptj[kPT];
-#pragma unroll
-    for (int u = 0; u < kPT; ++u) {
-        P4[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int t = w + (kGdnThreads / kWave) * u;
-        int ti = 0, tj = t < 2 * ntri ? t % ntri : -1;
-        while (tj > ti) tj -= ++ti;
-        pti[u] = ti;
-        ptj[u] = tj;
-        if (tj >= 0) {
-            const float* xa = (t < ntri ? s_k : s_q) + (16 * ti + l16) * KS + 4 * q4;
-            const float* kb = s_k + (16 * tj + l16) * KS + 4 * q4;
-#pragma unroll
-            for (int kk = 0; kk < kGdnDim / 16; ++kk)
-                if (kk < nkk)
-                    P4[u] = mfma4(*(const float4*)(xa + 16 * kk), *(const float4*)(kb + 16 * kk), P4[u]);
-        }
-    }
-    lds_barrier();  // k and q consumed: the region now holds A, W and e
+    lds_barrier();
 
-    // ---- 3. coefficients and right-hand sides
+    f32x4 Q4[NN / 16], R4[NN / 16];  // Q S0^T, then the right-hand sides r
 #pragma unroll
-    for (int u = 0; u < kPT; ++u) {
-        const int t = w + (kGdnThreads / kWave) * u;
-        if (ptj[u] >= 0) {
-            const int j = 16 * ptj[u] + l16;
-            const float Gj = s_G[j];
+    for (int ti = 0; ti < NN / 16; ++ti) R4[ti] = Q4[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (tree_wave) {
+        // ---- 3b. M, by the tree wave while the row waves form their products
+        // (I + A) M = I: for c a strict ancestor of i at depth m,
+        // M_ic = -A_ic - sum over the path nodes x strictly between c and i of A_ix M_xc
+        const int maxdep = s_info[1];
+        for (int d = 1; d <= maxdep; ++d) {
+            const int lo = s_lvs[d], entries = (s_lvs[d + 1] - lo) * d;
+            for (int L = lane; L < entries; L += kWave) {
+                const int ni = L / d, m = L - ni * d;
+                const int i = s_lvl[lo + ni];
+                const uint8_t* an = s_anc + i * NN;
+                const float* ac = s_A + i * NN;
+                const int c = an[m];
+                float acc = -ac[m];
+                for (int t0 = m + 1; t0 < d; t0 += 4) {
+                    float a[4], x[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * pti[u] + 4 * q4 + r;
-                const bool anc = (s_mask[i] >> j) & 1ull;  // j on the root path of i
-                const float D = __expf(s_G[i] - Gj);
-                if (t < ntri)
-                    s_A[i * CS + j] = anc && j != i ? s_beta[i] * D * P4[u][r] : 0.f;
-                else
-                    s_W[i * CS + j] = anc ? D * P4[u][r] : 0.f;
+                    for (int u = 0; u < 4; ++u) {
+                        const int t = min(t0 + u, d - 1);
+                        a[u] = ac[t];
+                        x[u] = s_M[an[t] * CS + c];
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) acc = t0 + u < d ? acc - a[u] * x[u] : acc;
+                }
+                s_M[i * CS + c] = acc;
             }
+            wave_sync();
         }
-    }
-    if (wave_rows) {
+    } else if (wave_rows) {
+        // ---- 3a. products (three-term bf16 splits, fp32 accumulation)
+        bf16x8 s0h[kGdnDim / 32], s0l[kGdnDim / 32];
 #pragma unroll
-        for (int ti = 0; ti < kGdnNodes / 16; ++ti) {
+        for (int ks = 0; ks < kGdnDim / 32; ++ks) split_hi_lo(s0r[2 * ks], s0r[2 * ks + 1], s0h[ks], s0l[ks]);
+#pragma unroll
+        for (int ti = 0; ti < NN / 16; ++ti) {
             if (ti < NTI) {
+                const int oa = (16 * ti + l16) * RS + 8 * q4;
+#pragma unroll
+                for (int ks = 0; ks < kGdnDim / 32; ++ks) {
+                    if (ks < nks) {
+                        const int c = oa + 32 * ks;
+                        R4[ti] = mfma_x3(*(const bf16x8*)(s_kh + c), *(const bf16x8*)(s_kl + c),
+                                         s0h[ks], s0l[ks], R4[ti]);
+                        Q4[ti] = mfma_x3(*(const bf16x8*)(s_qh + c), *(const bf16x8*)(s_ql + c),
+                                         s0h[ks], s0l[ks], Q4[ti]);
+                    }
+                }
+                // right-hand sides r_i = beta_i (v_i - exp(G_i) S0 k_i), 0 past the tree
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = 16 * ti + 4 * q4 + r;
-                    s_e[i * KS + p] =
-                        i < T ? s_beta[i] * (vr[4 * ti + r] - s_gam[i] * R4[ti][r]) : 0.f;
+                    R4[ti][r] = i < T ? s_beta[i] * (vr[4 * ti + r] - s_gam[i] * R4[ti][r]) : 0.f;
                 }
             }
         }
     }
-    lds_barrier();
+    lds_barrier();  // M and W complete
     if (!wave_rows) return;
 
-    // ---- 4. solve, level by level within the wave
-    const int maxdep = s_info[1];
-    for (int d = 0; d <= maxdep; ++d) {
-        const int hi = s_lvs[d + 1];
-        for (int pos = s_lvs[d] + q4; pos < hi; pos += 4) {
-            const int i = s_lvl[pos];
-            unsigned long long m = s_mask[i] & ~(1ull << i);
-            float acc = s_e[i * KS + p];
-            while (m) {
-                int j[4];
-                bool ok[4];
+    // ---- 4. e = M r, o = exp(G) (Q S0^T) + W e over the tiles below the diagonal.
+    // The accumulator of a 16x16 tile holds (node 16 t + 4 q4 + c, row p) in
+    // element c, which is the B operand of node 16 t + 4 q4 + c at k step c.
+    f32x4 E4[NN / 16];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    ok[u] = m != 0ull;
-                    j[u] = ok[u] ? (int)__builtin_ctzll(m) : 0;
-                    m &= m - 1ull;
-                }
-                float a[4], x[4];
+    for (int ti = 0; ti < NN / 16; ++ti) {
+        E4[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (ti < NTI) {
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    a[u] = s_A[i * CS + j[u]];
-                    x[u] = s_e[j[u] * KS + p];
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) acc = ok[u] ? acc - a[u] * x[u] : acc;
+            for (int tj = 0; tj <= ti; ++tj) {
+                const float4 mv = *(const float4*)&s_M[(16 * ti + l16) * CS + 16 * tj + 4 * q4];
+                E4[ti] = mfma4(mv, make_float4(R4[tj][0], R4[tj][1], R4[tj][2], R4[tj][3]), E4[ti]);
             }
-            s_e[i * KS + p] = acc;
-            if (e_out && p < dv) e_out[(row0 + (size_t)i * H) * dv + p] = acc;
         }
-        wave_sync();
     }
-
-    // ---- 5. outputs: o = exp(G) (Q S0^T) + W e, tiles below the diagonal only
+    float* const o_p = o + row0 * dv + p;
+    float* const e_p = e_out ? e_out + row0 * dv + p : nullptr;
+    const size_t step = (size_t)H * dv;  // next node
 #pragma unroll
-    for (int ti = 0; ti < kGdnNodes / 16; ++ti) {
+    for (int ti = 0; ti < NN / 16; ++ti) {
         if (ti < NTI) {
             f32x4 acc;
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[r] = s_gam[16 * ti + 4 * q4 + r] * Q4[ti][r];
+#pragma unroll
             for (int tj = 0; tj <= ti; ++tj) {
                 const float4 wv = *(const float4*)&s_W[(16 * ti + l16) * CS + 16 * tj + 4 * q4];
-                const float* ep = s_e + (16 * tj + 4 * q4) * KS + p;
-                const float4 ev = make_float4(ep[0], ep[KS], ep[2 * KS], ep[3 * KS]);
-                acc = mfma4(wv, ev, acc);
+                acc = mfma4(wv, make_float4(E4[tj][0], E4[tj][1], E4[tj][2], E4[tj][3]), acc);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * ti + 4 * q4 + r;
-                if (i < T && p < dv) o[(row0 + (size_t)i * H) * dv + p] = acc[r];
+                if (i < T && p < dv) {
+                    o_p[(size_t)i * step] = acc[r];
+                    if (e_p) e_p[(size_t)i * step] = E4[ti][r];
+                }
             }
         }
     }
