@@ -37,6 +37,8 @@
 //     so they never leave registers.
 // Commit: one work-group per (item, head, 4,096-element chunk of the state),
 // as for the SSD commit, reading the pseudo-values the verify call wrote.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "verify_common.hpp"
@@ -385,22 +387,39 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(
     }
 }
 
-constexpr int kGdnPathChunk = 16;
+constexpr int kGdnCommitEl = kBlock * 16;                       // state elements per chunk
+// State chunks per work-group. One is the fastest measured: 2 and 4 (the later
+// chunks streamed behind the path rows, their stores overlapping the loads
+// still in flight) leave fewer waves per CU and took 9% and 16% longer at
+// batch 16, 16 heads, dk = dv = 128.
+constexpr int kGdnCommitCPW = 1;
 
+// Commit: S' = w0 S0 + sum_t w_t e_{j_t} k_{j_t}^T over the accepted path
+// j_0 = 0, ..., j_{L-1}, with w_t = exp(sum of g after entry t) and w0 = exp(sum
+// of all g on the path). One work-group per (item, head, CPW chunks of the
+// state). The path indices, the parents and the first state chunk leave first; the tree and the path are
+// validated with barriers that wait for LDS only, so that the next round trip
+// (g of the path, the e and k rows) leaves at once, followed by the other state
+// chunks; each chunk is then updated and written back as it arrives, its
+// stores overlapping the loads still in flight. The weights come from a suffix
+// scan across one wave.
+template <bool VEC, int CPW>
 __global__ __launch_bounds__(kBlock) void gdn_commit_kernel(
     const float* __restrict__ k, const float* __restrict__ g, const float* __restrict__ e,
     float* __restrict__ S, const int32_t* __restrict__ parent, const int32_t* __restrict__ accepted,
     const int32_t* __restrict__ accepted_len, int32_t* __restrict__ tree_status, int T, int H,
-    int dk, int dv, int Lmax, int chunks) {
-    __shared__ int s_par[kMaxNodes];
-    __shared__ int s_path[kMaxNodes];
-    __shared__ float s_w[kMaxNodes];
+    int dk, int dv, int Lmax, int EW, int KW, int groups) {
+    __shared__ int s_par[kGdnNodes];
+    __shared__ int s_path[kGdnNodes];
+    __shared__ int s_bad[kBlock / kWave];
+    __shared__ float s_w[kGdnNodes];
     __shared__ float s_w0;
-    __shared__ float s_e[kGdnPathChunk][kGdnDim];
-    __shared__ float s_k[kGdnPathChunk][kGdnDim];
-    const int chunk = blockIdx.x % chunks;
-    const int bh = blockIdx.x / chunks;
-    const int b = bh / H, h = bh % H;
+    // [min(Lmax, T)][EW] e rows of the path, then [min(Lmax, T)][KW] k rows
+    extern __shared__ __attribute__((aligned(16))) float s_dyn[];
+    float* const s_e = s_dyn;
+    float* const s_k = s_dyn + min(Lmax, T) * EW;
+    const int grp = blockIdx.x % groups;
+    const int b = blockIdx.x / groups / H, h = blockIdx.x / groups % H;
     const int tid = threadIdx.x;
     const int PN = dv * dk;
     const size_t row0 = (size_t)b * T * H + h;
@@ -408,72 +427,169 @@ __global__ __launch_bounds__(kBlock) void gdn_commit_kernel(
     const int acc_i = Lmax > 0 ? accepted[(size_t)b * Lmax + min(tid, Lmax - 1)] : 0;
     const int par_i = load_parent(parent + (size_t)b * T, T);
     float* Sh = S + ((size_t)b * H + h) * PN;
-    constexpr int kEl = 16;  // state elements per thread
-    float acc[kEl];
-    const int e0 = chunk * kBlock * kEl;
+    const int c0 = grp * CPW;  // first chunk of this work-group
+    float4 acc[CPW][4];  // [chunk][piece]: elements (c0 + c) * 4096 + (v * 256 + tid) * 4 ..
+    auto load_chunk = [&](int c) {
 #pragma unroll
-    for (int m = 0; m < kEl; ++m) {
-        const int x = e0 + m * kBlock + tid;
-        acc[m] = x < PN ? Sh[x] : 0.f;
-    }
-    const bool len_ok = len >= 0 && len <= Lmax;
+        for (int v = 0; v < 4; ++v) {
+            const int pe = (c0 + c) * kGdnCommitEl + (v * kBlock + tid) * 4;
+            if (VEC) {
+                acc[c][v] = pe < PN ? *(const float4*)(Sh + pe) : make_float4(0.f, 0.f, 0.f, 0.f);
+            } else {
+                acc[c][v].x = pe < PN ? Sh[pe] : 0.f;
+                acc[c][v].y = pe + 1 < PN ? Sh[pe + 1] : 0.f;
+                acc[c][v].z = pe + 2 < PN ? Sh[pe + 2] : 0.f;
+                acc[c][v].w = pe + 3 < PN ? Sh[pe + 3] : 0.f;
+            }
+        }
+    };
+    load_chunk(0);
+
+    // tree and path checks (a valid path starts at the root and steps from
+    // parent to child, so its indices increase and len <= T)
+    const bool len_ok = len >= 0 && len <= Lmax && len <= T;
+    if (tid < T) s_par[tid] = par_i;
     if (len_ok && tid < len) s_path[tid] = acc_i;
-    int st = check_tree(par_i, T, s_par);
-    int bad = 0;
-    if (!st) {
-        if (!len_ok) {
-            bad = 1;
-        } else if (tid < len) {
-            const int node = s_path[tid];
-            bad = tid == 0 ? node != 0 : (node < 0 || node >= T || s_par[node] != s_path[tid - 1]);
-        }
+    lds_barrier();
+    int bits = 0;
+    if (tid == 0 && par_i != -1) bits |= kStBadRoot;
+    if (tid > 0 && tid < T && (par_i < 0 || par_i >= tid)) bits |= kStBadParent;
+    if (!len_ok) {
+        if (tid == 0) bits |= kStBadPath;
+    } else if (tid < len) {
+        const int node = s_path[tid];
+        if (tid == 0 ? node != 0 : (node < 0 || node >= T || s_par[node] != s_path[tid - 1]))
+            bits |= kStBadPath;
     }
-    if (__syncthreads_or(bad)) st |= kStBadPath;
-    if (h == 0 && chunk == 0 && tid == 0 && tree_status) tree_status[b] = st;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) bits |= __shfl_xor(bits, off, kWave);
+    if ((tid & (kWave - 1)) == 0) s_bad[tid / kWave] = bits;
+    lds_barrier();
+    int st = 0;
+#pragma unroll
+    for (int w = 0; w < kBlock / kWave; ++w) st |= s_bad[w];
+    if (st & (kStBadRoot | kStBadParent)) st &= ~kStBadPath;  // a path is judged on a valid tree only
+    if (h == 0 && grp == 0 && tid == 0 && tree_status) tree_status[b] = st;
     if (st || len == 0) return;
-    // decay weights along the path: w_t = exp(sum of g after entry t), w0 = exp(sum of all)
-    if (tid < len) s_w[tid] = g[row0 + (size_t)s_path[tid] * H];
-    __syncthreads();
-    if (tid == 0) {
-        float c = 0.f;
-        for (int t = len - 1; t >= 0; --t) {
-            const float gt = s_w[t];
-            s_w[t] = __expf(c);
-            c += gt;
-        }
-        s_w0 = __expf(c);
-    }
-    __syncthreads();
-    const float w0 = s_w0;
+
+    // one round trip: g of the path, the e and k rows; then the other chunks
+    const float gt = tid < len ? g[row0 + (size_t)s_path[tid] * H] : 0.f;
+    const int kq = VEC ? dk / 4 : dk;  // k pieces per row
+    const int ne = len * dv, nk = len * kq;
+    for (int base = 0; base < max(ne, nk); base += 4 * kBlock) {
+        float ev[4];
+        float4 kv[4];
 #pragma unroll
-    for (int m = 0; m < kEl; ++m) acc[m] *= w0;
-    for (int t0 = 0; t0 < len; t0 += kGdnPathChunk) {
-        const int tn = min(kGdnPathChunk, len - t0);
-        if (t0 > 0) __syncthreads();
-        for (int x = tid; x < tn * dv; x += kBlock) {
-            const int t = x / dv, p = x % dv;
-            s_e[t][p] = s_w[t0 + t] * e[(row0 + (size_t)s_path[t0 + t] * H) * dv + p];
+        for (int u = 0; u < 4; ++u) {
+            const int x = base + u * kBlock + tid;
+            ev[u] = 0.f;
+            kv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (x < ne) {
+                const int t = x / dv, r = x - t * dv;
+                ev[u] = e[(row0 + (size_t)s_path[t] * H) * dv + r];
+            }
+            if (x < nk) {
+                const int t = x / kq, c = x - t * kq;
+                const float* src = k + (row0 + (size_t)s_path[t] * H) * dk;
+                if (VEC)
+                    kv[u] = *(const float4*)(src + 4 * c);
+                else
+                    kv[u].x = src[c];
+            }
         }
-        for (int x = tid; x < tn * dk; x += kBlock) {
-            const int t = x / dk, n = x % dk;
-            s_k[t][n] = k[(row0 + (size_t)s_path[t0 + t] * H) * dk + n];
-        }
-        __syncthreads();
+        if (base == 0) {
 #pragma unroll
-        for (int m = 0; m < kEl; ++m) {
-            const int x = e0 + m * kBlock + tid;
-            if (x < PN) {
-                const int p = x / dk, n = x % dk;
-                float a = acc[m];
-                for (int t = 0; t < tn; ++t) a += s_e[t][p] * s_k[t][n];
-                acc[m] = a;
+            for (int c = 1; c < CPW; ++c) load_chunk(c);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int x = base + u * kBlock + tid;
+            if (x < ne) {
+                const int t = x / dv;
+                s_e[t * EW + x - t * dv] = ev[u];
+            }
+            if (x < nk) {
+                const int t = x / kq, c = x - t * kq;
+                if (VEC)
+                    *(float4*)&s_k[t * KW + 4 * c] = kv[u];
+                else
+                    s_k[t * KW + c] = kv[u].x;
             }
         }
     }
+    if (tid < kWave) {
+        // w_t = exp(sum of g over entries after t): inclusive suffix scan of the
+        // sequence shifted by one entry (len <= T <= 64 lanes)
+        float x = __shfl_down(gt, 1, kWave);
+        if (tid == kWave - 1) x = 0.f;
 #pragma unroll
-    for (int m = 0; m < kEl; ++m) {
-        const int x = e0 + m * kBlock + tid;
-        if (x < PN) Sh[x] = acc[m];
+        for (int off = 1; off < kWave; off <<= 1) {
+            const float y = __shfl_down(x, off, kWave);
+            if (tid + off < kWave) x += y;
+        }
+        if (tid < len) s_w[tid] = __expf(x);
+        if (tid == 0) s_w0 = __expf(x + gt);
+    }
+    lds_barrier();
+    const float w0 = s_w0;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+        if ((c0 + c) * kGdnCommitEl >= PN) break;
+        float4* a = acc[c];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            a[v].x *= w0;
+            a[v].y *= w0;
+            a[v].z *= w0;
+            a[v].w *= w0;
+        }
+        const int pe0 = (c0 + c) * kGdnCommitEl + tid * 4;
+        if (VEC && (kBlock * 4) % dk == 0) {
+            // the four pieces of this thread cover the same columns n .. n+3 of
+            // four rows: one k read per path entry serves all of them
+            const int n = pe0 % dk;
+            int pr[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) pr[v] = min((pe0 + v * kBlock * 4) / dk, dv - 1);
+            for (int t = 0; t < len; ++t) {
+                const float4 kk = *(const float4*)&s_k[t * KW + n];
+                const float wt = s_w[t];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float ew = wt * s_e[t * EW + pr[v]];
+                    a[v].x += ew * kk.x;
+                    a[v].y += ew * kk.y;
+                    a[v].z += ew * kk.z;
+                    a[v].w += ew * kk.w;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                float f[4] = {a[v].x, a[v].y, a[v].z, a[v].w};
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) {
+                    const int x = pe0 + v * kBlock * 4 + cc;
+                    if (x < PN) {
+                        const int pr = x / dk, n = x - pr * dk;
+                        for (int t = 0; t < len; ++t) f[cc] += s_w[t] * s_e[t * EW + pr] * s_k[t * KW + n];
+                    }
+                }
+                a[v] = make_float4(f[0], f[1], f[2], f[3]);
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int pe = pe0 + v * kBlock * 4;
+            if (VEC) {
+                if (pe < PN) *(float4*)(Sh + pe) = a[v];
+            } else {
+                if (pe < PN) Sh[pe] = a[v].x;
+                if (pe + 1 < PN) Sh[pe + 1] = a[v].y;
+                if (pe + 2 < PN) Sh[pe + 2] = a[v].z;
+                if (pe + 3 < PN) Sh[pe + 3] = a[v].w;
+            }
+        }
     }
 }
 
@@ -495,11 +611,24 @@ hipError_t launch_gdn_commit(int batch, int T, int H, int dk, int dv, const floa
                              const float* g, const float* e, float* S, const int32_t* parent,
                              const int32_t* accepted, const int32_t* accepted_len, int Lmax,
                              int32_t* tree_status, hipStream_t stream) {
-    const int per_wg = kBlock * 16;
-    const int chunks = (dv * dk + per_wg - 1) / per_wg;
-    hipLaunchKernelGGL(gdn_commit_kernel, dim3(batch * H * chunks), dim3(kBlock), 0, stream, k, g,
-                       e, S, parent, accepted, accepted_len, tree_status, T, H, dk, dv, Lmax,
-                       chunks);
+    // row strides of the staged e and k rows, in multiples of 4 floats
+    const int EW = (dv + 3) / 4 * 4;
+    const int KW = (dk + 3) / 4 * 4;
+    const size_t shmem = (size_t)std::min(Lmax, T) * (EW + KW) * sizeof(float);
+    const bool vec = dk % 4 == 0 && (((uintptr_t)S | (uintptr_t)k) & 15) == 0;
+    constexpr int CPW = kGdnCommitCPW;
+    const int groups = ((dv * dk + kGdnCommitEl - 1) / kGdnCommitEl + CPW - 1) / CPW;
+    auto kern = vec ? gdn_commit_kernel<true, CPW> : gdn_commit_kernel<false, CPW>;
+    if (shmem > 48 * 1024) {
+        // paths of up to 64 entries with 128-wide rows take up to 64 KiB
+        const hipError_t err = hipFuncSetAttribute((const void*)kern,
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                   (int)shmem);
+        if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL(kern, dim3(batch * H * groups), dim3(kBlock), shmem, stream, k, g, e, S,
+                       parent, accepted, accepted_len, tree_status, T, H, dk, dv, Lmax, EW, KW,
+                       groups);
     return hipGetLastError();
 }
 
