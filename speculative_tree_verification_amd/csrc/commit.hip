@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
     const int tid = threadIdx.x;
     const int PN = P * N;
 
-    const float Ah = A[hd];  // issued with the first loads, off the dependency chain
+    const float Ah = gload(A + hd);  // issued with the first loads, off the dependency chain
     // the path indices and the parents head the only dependent chain (indices,
     // then the path's rows), so they leave first, the accepted row without
     // waiting for its length
@@ -78,14 +78,17 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
     for (int v = 0; v < kVec; ++v) {
         pe[v] = e0 + (v * kBlock + tid) * 4;
         if (VEC) {
-            const float4 t = pe[v] < PN ? *(const float4*)(hb + pe[v]) : make_float4(0.f, 0.f, 0.f, 0.f);
+            // unconditional (clamped) loads, so that waits for the earlier
+            // index loads can leave these in flight
+            float4 t = gload((const float4*)(hb + min(pe[v], PN - 4)));
+            if (pe[v] >= PN) t = make_float4(0.f, 0.f, 0.f, 0.f);
             acc[v][0] = t.x;
             acc[v][1] = t.y;
             acc[v][2] = t.z;
             acc[v][3] = t.w;
         } else {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) acc[v][c] = (pe[v] + c < PN) ? hb[pe[v] + c] : 0.f;
+            for (int c = 0; c < 4; ++c) acc[v][c] = (pe[v] + c < PN) ? gload(hb + pe[v] + c) : 0.f;
         }
     }
 
@@ -128,11 +131,11 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
                 uint4 vx = make_uint4(0, 0, 0, 0), vb = vx;
                 if (e < nx) {
                     const int k = e / px, c = e - k * px;
-                    vx = *(const uint4*)(x + (((size_t)b * T + s_path[k0 + k]) * H + hd) * P + 8 * c);
+                    vx = gload((const uint4*)(x + (((size_t)b * T + s_path[k0 + k]) * H + hd) * P + 8 * c));
                 }
                 if (e < nb) {
                     const int k = e / pb, c = e - k * pb;
-                    vb = *(const uint4*)(Bm + (((size_t)b * T + s_path[k0 + k]) * G + g) * N + 8 * c);
+                    vb = gload((const uint4*)(Bm + (((size_t)b * T + s_path[k0 + k]) * G + g) * N + 8 * c));
                 }
                 if (e < nx) put8(s_wx + 8 * e, vx);  // piece e: row e / px, columns 8 (e % px) ..
                 if (e < nb) put8(s_B + 8 * e, vb);
@@ -234,11 +237,11 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
     for (int v = 0; v < kVec; ++v) {
         if (VEC) {
             if (pe[v] < PN)
-                *(float4*)(hb + pe[v]) = make_float4(acc[v][0], acc[v][1], acc[v][2], acc[v][3]);
+                gstore((float4*)(hb + pe[v]), make_float4(acc[v][0], acc[v][1], acc[v][2], acc[v][3]));
         } else {
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                if (pe[v] + c < PN) hb[pe[v] + c] = acc[v][c];
+                if (pe[v] + c < PN) gstore(hb + pe[v] + c, acc[v][c]);
         }
     }
 }

@@ -41,23 +41,54 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
+// Loads and stores through the global address space. A pointer read from
+// memory (a caller's table) is generic to the compiler, and its generic (flat)
+// accesses count against both memory counters, so every later LDS wait would
+// also wait for them; these casts keep them plain global accesses.
+template <typename T>
+__device__ __forceinline__ T gload(const T* p) {
+    return *(const T __attribute__((address_space(1)))*)p;
+}
+template <typename T>
+__device__ __forceinline__ void gstore(T* p, const T& v) {
+    *(T __attribute__((address_space(1)))*)p = v;
+}
+// 16-byte vector types go through native vectors: the copy of a HIP vector
+// class takes a generic reference, which would make the access flat again
+typedef float gf32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t gu32x4 __attribute__((ext_vector_type(4)));
+template <>
+__device__ __forceinline__ float4 gload(const float4* p) {
+    const gf32x4 v = *(const gf32x4 __attribute__((address_space(1)))*)p;
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+template <>
+__device__ __forceinline__ uint4 gload(const uint4* p) {
+    const gu32x4 v = *(const gu32x4 __attribute__((address_space(1)))*)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <>
+__device__ __forceinline__ void gstore(float4* p, const float4& v) {
+    *(gf32x4 __attribute__((address_space(1)))*)p = gf32x4{v.x, v.y, v.z, v.w};
+}
+
 // element access for the two input dtypes (float, or bf16 stored as uint16_t)
 template <typename TIO>
 struct Elem;
 
 template <>
 struct Elem<float> {
-    static __device__ __forceinline__ float ld(const float* p, size_t i) { return p[i]; }
-    static __device__ __forceinline__ void st(float* p, size_t i, float v) { p[i] = v; }
+    static __device__ __forceinline__ float ld(const float* p, size_t i) { return gload(p + i); }
+    static __device__ __forceinline__ void st(float* p, size_t i, float v) { gstore(p + i, v); }
 };
 
 template <>
 struct Elem<uint16_t> {
     static __device__ __forceinline__ float ld(const uint16_t* p, size_t i) {
-        return bf16_bits_to_f32(p[i]);
+        return bf16_bits_to_f32(gload(p + i));
     }
     static __device__ __forceinline__ void st(uint16_t* p, size_t i, float v) {
-        p[i] = f32_to_bf16_bits(v);
+        gstore(p + i, f32_to_bf16_bits(v));
     }
 };
 
