@@ -70,9 +70,10 @@ static int path_to(const int32_t* parent, int i, int* path) {
     return len;
 }
 
-/* Depth (edges from the root) and ancestor-or-self bit set (4 x 64 bits) of
- * every node, by walking each node's parent chain. */
-void oracle_tree_info(int n_items, int T, const int32_t* parent, int32_t* depth,
+/* Depth (edges from the root) and ancestor-or-self bit set of every node, by
+ * walking each node's parent chain. Node j is bit j % 64 of word j / 64 of a
+ * row of W words (W >= ceil(T / 64); the library uses max(4, ceil(T / 64))). */
+void oracle_tree_info(int n_items, int T, int W, const int32_t* parent, int32_t* depth,
                       uint64_t* anc, int32_t* status) {
     for (int s = 0; s < n_items; ++s) {
         const int32_t* par = parent + (size_t)s * T;
@@ -80,8 +81,8 @@ void oracle_tree_info(int n_items, int T, const int32_t* parent, int32_t* depth,
         status[s] = st;
         if (st) continue;
         for (int i = 0; i < T; ++i) {
-            uint64_t* a = anc + ((size_t)s * T + i) * 4;
-            a[0] = a[1] = a[2] = a[3] = 0;
+            uint64_t* a = anc + ((size_t)s * T + i) * W;
+            for (int w = 0; w < W; ++w) a[w] = 0;
             int d = -1;
             for (int j = i; j >= 0; j = par[j]) {
                 a[j >> 6] |= (uint64_t)1 << (j & 63);

@@ -38,7 +38,7 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         L.oracle_tree_check.argtypes = [ctypes.c_int, _ip]
         L.oracle_tree_check.restype = ctypes.c_int
-        L.oracle_tree_info.argtypes = [ctypes.c_int, ctypes.c_int, _ip, _ip, _up, _ip]
+        L.oracle_tree_info.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _ip, _ip, _up, _ip]
         L.oracle_tree_info.restype = None
         vargs = [ctypes.c_int] * 4 + [_dp] * 7 + [_ip, _dp, _ip]
         L.oracle_verify.argtypes = vargs
@@ -108,14 +108,22 @@ def commit_slices(x, dt, A, Bm, h0, parent, accepted, accepted_len, Lmax: Option
     return h, st
 
 
+def anc_words(T: int) -> int:
+    """64-bit words per node of an ancestor bit set: 4 up to 256 nodes, then
+    one word per 64 nodes."""
+    return max(4, -(-T // 64))
+
+
 def tree_info(parent: np.ndarray):
-    """(depth [n,T], anc [n,T,4] uint64, status [n]) for parent [n, T]."""
+    """(depth [n,T], anc [n,T,W] uint64 with W = anc_words(T), status [n]) for
+    parent [n, T]."""
     parent = np.ascontiguousarray(parent, np.int32)
     n, T = parent.shape
+    W = anc_words(T)
     depth = np.zeros((n, T), np.int32)
-    anc = np.zeros((n, T, 4), np.uint64)
+    anc = np.zeros((n, T, W), np.uint64)
     st = np.zeros(n, np.int32)
-    lib().oracle_tree_info(n, T, _i(parent), _i(depth), anc.ctypes.data_as(_up), _i(st))
+    lib().oracle_tree_info(n, T, W, _i(parent), _i(depth), anc.ctypes.data_as(_up), _i(st))
     return depth, anc, st
 
 

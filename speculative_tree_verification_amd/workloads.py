@@ -271,8 +271,9 @@ def make_custom(seed: int, batch: int, n_nodes: int, n_heads: int, head_dim: int
     """Inputs of an arbitrary shape with the configurations' distributions.
 
     ``tree`` selects the shape when ``parents`` is not given: "recursive"
-    (uniform earlier parent, depth <= max_depth), "chain", "star", "level"
-    (the 255-node level layout) or "geometric".
+    (uniform earlier parent, depth <= max_depth), "chain", "star", "binary"
+    (complete binary tree in breadth-first order), "level" (the 255-node level
+    layout) or "geometric".
     """
     rng = np.random.default_rng([7000, seed])
     B, T, H, P, N, G = batch, n_nodes, n_heads, head_dim, d_state, n_groups
@@ -287,6 +288,9 @@ def make_custom(seed: int, batch: int, n_nodes: int, n_heads: int, head_dim: int
                 parents[b] = np.arange(-1, T - 1, dtype=np.int32)
             elif tree == "star":
                 parents[b] = np.array([-1] + [0] * (T - 1), dtype=np.int32)
+            elif tree == "binary":
+                parents[b] = (np.arange(T, dtype=np.int32) - 1) // 2
+                parents[b, 0] = -1
             elif tree == "level":
                 parents[b] = level_tree(rng)
             elif tree == "geometric":

@@ -473,3 +473,41 @@ def test_invalid_items_untouched(oracle_mod):
     assert list(st) == [0, 2, 4, 4]  # item 3: len 5 > Lmax 4
     for k in (1, 2, 3):
         assert np.array_equal(h[k], s["h0"][k])
+
+
+def _words(bits: int, W: int):
+    return [(bits >> (64 * w)) & ((1 << 64) - 1) for w in range(W)]
+
+
+def test_tree_info_large_trees(oracle_mod):
+    """Trees past 256 nodes: ancestor bit sets take max(4, ceil(T/64)) words,
+    node j in bit j % 64 of word j // 64. Chain (every node below i), star
+    (root and self), and random recursive trees against ancestor sets built as
+    Python integers from the parent's set."""
+    o = oracle_mod
+    assert [o.anc_words(T) for T in (1, 64, 256, 257, 320, 321, 1024)] == [4, 4, 4, 5, 5, 6, 16]
+    T = 1000
+    chain = np.arange(-1, T - 1, dtype=np.int32)[None]
+    depth, anc, st = o.tree_info(chain)
+    assert not st.any() and anc.shape == (1, T, 16)
+    assert list(depth[0]) == list(range(T))
+    for i in (0, 1, 63, 64, 65, 500, 999):
+        assert [int(v) for v in anc[0, i]] == _words((1 << (i + 1)) - 1, 16)
+    T = 700
+    star = np.zeros((1, T), np.int32)
+    star[0, 0] = -1
+    depth, anc, st = o.tree_info(star)
+    assert list(depth[0]) == [0] + [1] * (T - 1)
+    for i in (0, 5, 255, 256, 699):
+        assert [int(v) for v in anc[0, i]] == _words(1 | (1 << i), 11)
+    rng = np.random.default_rng(31)
+    for T in (257, 600, 1024):
+        par = np.array([[-1] + [int(rng.integers(0, i)) for i in range(1, T)]], np.int32)
+        depth, anc, st = o.tree_info(par)
+        W = o.anc_words(T)
+        sets, dep = [0] * T, [0] * T
+        for i in range(T):
+            sets[i] = (sets[par[0, i]] if i else 0) | (1 << i)
+            dep[i] = dep[par[0, i]] + 1 if i else 0
+        assert list(depth[0]) == dep
+        assert all([int(v) for v in anc[0, i]] == _words(sets[i], W) for i in range(T))
