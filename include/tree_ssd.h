@@ -32,7 +32,9 @@
  *     tree_status[b] (a bit set, see TSV_ST_*). The outputs of an item with any
  *     bit set are left bitwise untouched. tree_status may be NULL (no report;
  *     invalid items are still skipped).
- *   - Nodes are limited to T <= 256 (four 64-bit ancestor words per node).
+ *   - Nodes are limited to T <= 1024. Trees of up to 256 nodes take the MFMA
+ *     kernels where the shape allows; larger trees take plain fp32 kernels
+ *     (same results, lower throughput).
  *   - The launch runs on the device current to the calling thread.
  */
 #ifndef TREE_SSD_H
@@ -51,7 +53,7 @@ typedef enum { TSV_F32 = 0, TSV_BF16 = 1 } tsv_dtype;
 typedef enum {
     TSV_OK = 0,
     TSV_E_NULL = 1,        /* a required pointer is NULL */
-    TSV_E_SHAPE = 2,       /* a size is out of range, H % G != 0, or T > 256 */
+    TSV_E_SHAPE = 2,       /* a size is out of range, H % G != 0, or T > 1024 */
     TSV_E_DTYPE = 3,       /* in_dtype is not a tsv_dtype */
     TSV_E_UNSUPPORTED = 4, /* the size combination has no kernel */
     TSV_E_LAUNCH = 5       /* the HIP launch failed (see hipGetLastError) */
@@ -60,9 +62,10 @@ typedef enum {
 /* Per-item status bits written to tree_status[b] */
 #define TSV_ST_BAD_ROOT 1   /* parent[b][0] != -1 */
 #define TSV_ST_BAD_PARENT 2 /* some parent[b][i] (i >= 1) is not in [0, i) */
-#define TSV_ST_BAD_PATH 4   /* accepted path: len not in [0, max_path_len],
-                               first node not 0, an index not in [0, T), or a
-                               node whose parent is not the previous entry */
+#define TSV_ST_BAD_PATH 4   /* accepted path: len not in [0, max_path_len]
+                               or above T, first node not 0, an index not in
+                               [0, T), or a node whose parent is not the
+                               previous entry */
 
 /* Flags (tsv_shape.flags) */
 #define TSV_FLAG_FORCE_GENERIC 1 /* use the plain VALU verify kernel even where
@@ -72,7 +75,7 @@ typedef enum {
 
 typedef struct {
     int32_t batch;           /* Bt >= 0 (0: nothing to do) */
-    int32_t n_nodes;         /* T in [0, 256] (0: nothing to do) */
+    int32_t n_nodes;         /* T in [0, 1024] (0: nothing to do) */
     int32_t n_heads;         /* H >= 1 */
     int32_t head_dim;        /* P >= 1 */
     int32_t d_state;         /* N >= 1 */
@@ -126,7 +129,7 @@ tsv_status tree_ssd_verify(const tsv_shape* s, const void* x, const void* dt, co
  *   h0_inout [Bt][H][P][N] float   read, then overwritten in place
  *   accepted [Bt][max_path_len] int32  root-path node list of each item
  *   accepted_len [Bt]      int32   number of valid entries of each row
- *   max_path_len           >= 0    row length of `accepted` (1 <= ... <= 256
+ *   max_path_len           >= 0    row length of `accepted` (1 <= ... <= 1024
  *                                  when Bt > 0; 0 allowed with all len == 0)
  *   tree_status [Bt]       int32   optional; bits 1|2|4 of the item
  *
@@ -235,7 +238,7 @@ tsv_status tree_gdn_commit(const tsv_shape* s, const float* k, const float* g, c
  *   parent        [Bt][T] int32   as for tree_ssd_verify
  *   draft_tokens  [Bt][T] int32   token of each node (node 0: the root token)
  *   target_tokens [Bt][T] int32   target model's greedy next token after each node
- *   max_path_len  in [1, 256]     row length of `accepted`
+ *   max_path_len  in [1, 1024]    row length of `accepted`
  *   accepted      [Bt][max_path_len] int32  output: node indices of the path,
  *                                 root first, cut after max_path_len entries;
  *                                 entries past the length are -1
@@ -252,12 +255,13 @@ tsv_status tree_ssd_accept_greedy(int32_t batch, int32_t n_nodes, const int32_t*
 
 /*
  * tree_ssd_tree_info -- the tree mask of each item (the summary's L): depth of
- * every node (edges from the root) and its ancestor-or-self set as four 64-bit
- * words (bit j of word j/64 set iff node j is on the root path of node i).
+ * every node (edges from the root) and its ancestor-or-self set as W 64-bit
+ * words, W = max(4, ceil(n_nodes / 64)) (bit j % 64 of word j / 64 set iff
+ * node j is on the root path of node i); four words up to 256 nodes.
  *
  *   parent   [batch][n_nodes] int32
  *   depth    [batch][n_nodes] int32     output
- *   anc_bits [batch][n_nodes][4] uint64 output (unused words are zero)
+ *   anc_bits [batch][n_nodes][W] uint64 output (unused words are zero)
  *   tree_status [batch] int32           optional; bits 1|2
  * Invalid items leave depth and anc_bits untouched.
  */

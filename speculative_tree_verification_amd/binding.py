@@ -330,14 +330,20 @@ def gdn_commit(k, g, e, S0, parent, accepted, accepted_len, tree_status=None, st
     return S0
 
 
+def anc_words(T: int) -> int:
+    """64-bit words of one node's ancestor set: 4 up to 256 nodes, then one per 64."""
+    return max(4, -(-T // 64))
+
+
 def tree_info(parent: torch.Tensor, depth=None, anc=None, tree_status=None, stream=None):
-    """(depth [Bt,T] int32, anc [Bt,T,4] int64 bit patterns, status [Bt] int32)."""
+    """(depth [Bt,T] int32, anc [Bt,T,W] int64 bit patterns with W = anc_words(T),
+    status [Bt] int32)."""
     Bt, T = parent.shape
     dev = parent.device
     if depth is None:
         depth = torch.zeros((Bt, T), dtype=torch.int32, device=dev)
     if anc is None:
-        anc = torch.zeros((Bt, T, 4), dtype=torch.int64, device=dev)
+        anc = torch.zeros((Bt, T, anc_words(T)), dtype=torch.int64, device=dev)
     if tree_status is None:
         tree_status = torch.zeros((Bt,), dtype=torch.int32, device=dev)
     rc = lib.tree_ssd_tree_info(int(Bt), int(T), _ptr(parent), _ptr(depth), _ptr(anc),

@@ -12,7 +12,8 @@
 // one path matches, with repeats the deepest matching node of smallest index
 // is taken.
 //
-// One work-group per item, one thread per node. After validation every node
+// One work-group per item, one thread per node (256 threads, or 1024 for trees
+// past 256 nodes). After validation every node
 // tests its own match against its parent's target token; pointer jumping over
 // the tree (log2 depth rounds in LDS) gives each node its depth and whether
 // its whole root path matches; an LDS max over (depth, -index) picks the last
@@ -22,17 +23,18 @@
 
 namespace tsv {
 
-__global__ __launch_bounds__(kBlock) void accept_greedy_kernel(
+template <int NT>
+__global__ __launch_bounds__(NT) void accept_greedy_kernel(
     const int32_t* __restrict__ parent, const int32_t* __restrict__ draft,
     const int32_t* __restrict__ target, int T, int Lmax, int32_t* __restrict__ accepted,
     int32_t* __restrict__ accepted_len, int32_t* __restrict__ next_token,
     int32_t* __restrict__ tree_status) {
-    __shared__ int s_par[kMaxNodes];
-    __shared__ int s_tgt[kMaxNodes];
-    __shared__ int s_nxt[kMaxNodes];
-    __shared__ int s_dep[kMaxNodes];
-    __shared__ int s_ok[kMaxNodes];
-    __shared__ int s_path[kMaxNodes];
+    __shared__ int s_par[NT];
+    __shared__ int s_tgt[NT];
+    __shared__ int s_nxt[NT];
+    __shared__ int s_dep[NT];
+    __shared__ int s_ok[NT];
+    __shared__ int s_path[NT];
     __shared__ int s_best;
     const int b = blockIdx.x;
     const int i = threadIdx.x;
@@ -72,12 +74,13 @@ __global__ __launch_bounds__(kBlock) void accept_greedy_kernel(
         dep = d2;
         ok = o2;
     }
-    // deepest fully matching node, smallest index among equals
-    if (ok) atomicMax(&s_best, (dep << 9) | (511 - i));
+    // deepest fully matching node, smallest index among equals: key (depth,
+    // 1023 - index), 10 bits of index
+    if (ok) atomicMax(&s_best, (dep << 10) | (1023 - i));
     __syncthreads();
     const int best = s_best;  // the root always matches, so best >= 0
-    const int last = 511 - (best & 511);
-    const int dl = best >> 9;
+    const int last = 1023 - (best & 1023);
+    const int dl = best >> 10;
     if (i == 0) {
         int j = last;
         for (int k = dl; k >= 0; --k) {
@@ -87,7 +90,7 @@ __global__ __launch_bounds__(kBlock) void accept_greedy_kernel(
     }
     __syncthreads();
     const int len = min(dl + 1, Lmax);
-    for (int k = i; k < Lmax; k += kBlock) accepted[(size_t)b * Lmax + k] = k < len ? s_path[k] : -1;
+    for (int k = i; k < Lmax; k += NT) accepted[(size_t)b * Lmax + k] = k < len ? s_path[k] : -1;
     if (i == 0) {
         accepted_len[b] = len;
         if (next_token) next_token[b] = s_tgt[s_path[len - 1]];
@@ -98,8 +101,14 @@ hipError_t launch_accept_greedy(int batch, int T, const int32_t* parent, const i
                                 const int32_t* target, int Lmax, int32_t* accepted,
                                 int32_t* accepted_len, int32_t* next_token, int32_t* tree_status,
                                 hipStream_t stream) {
-    hipLaunchKernelGGL(accept_greedy_kernel, dim3(batch), dim3(kBlock), 0, stream, parent, draft,
-                       target, T, Lmax, accepted, accepted_len, next_token, tree_status);
+    if (T <= kMaxNodes)
+        hipLaunchKernelGGL(accept_greedy_kernel<kMaxNodes>, dim3(batch), dim3(kMaxNodes), 0, stream,
+                           parent, draft, target, T, Lmax, accepted, accepted_len, next_token,
+                           tree_status);
+    else
+        hipLaunchKernelGGL(accept_greedy_kernel<kMaxNodesLarge>, dim3(batch), dim3(kMaxNodesLarge),
+                           0, stream, parent, draft, target, T, Lmax, accepted, accepted_len,
+                           next_token, tree_status);
     return hipGetLastError();
 }
 

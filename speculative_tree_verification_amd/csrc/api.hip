@@ -6,7 +6,8 @@
 
 namespace {
 
-constexpr int kMaxNodes = 256;
+constexpr int kMaxNodes = 1024;  // trees past 256 nodes take the plain kernels
+constexpr int kMaxNodesMfma = 256;
 constexpr int kMaxDim = 256;
 
 tsv_status check_shape(const tsv_shape* s) {
@@ -26,7 +27,7 @@ tsv_status check_shape(const tsv_shape* s) {
 
 bool use_mfma(const tsv_shape* s) {
     return s->in_dtype == TSV_BF16 && !(s->flags & TSV_FLAG_FORCE_GENERIC) &&
-           s->head_dim == 64 && (s->d_state == 64 || s->d_state == 128);
+           s->n_nodes <= kMaxNodesMfma && s->head_dim == 64 && (s->d_state == 64 || s->d_state == 128);
 }
 
 int compute_units() {
@@ -74,8 +75,10 @@ tsv_status tree_ssd_verify(const tsv_shape* s, const void* x, const void* dt, co
                       parent, y, tree_status, s->batch, s->n_nodes, s->n_heads, s->head_dim,
                       s->d_state, s->n_groups};
     hipStream_t hs = (hipStream_t)stream;
-    hipError_t e = use_mfma(s) ? launch_mfma(s, a, hs)
-                               : tsv::launch_verify_generic(a, s->in_dtype == TSV_BF16, hs);
+    const bool bf16 = s->in_dtype == TSV_BF16;
+    hipError_t e = s->n_nodes > kMaxNodesMfma ? tsv::launch_verify_large(a, bf16, hs)
+                   : use_mfma(s)             ? launch_mfma(s, a, hs)
+                                             : tsv::launch_verify_generic(a, bf16, hs);
     return e == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
 }
 
@@ -92,7 +95,9 @@ tsv_status tree_ssd_commit(const tsv_shape* s, const void* x, const void* dt, co
     tsv::CommitArgs a{x,        dt,          A,           B,           h0_inout,   nullptr,
                       1,        parent,      accepted,    accepted_len, tree_status, s->batch,
                       s->n_nodes, s->n_heads, s->head_dim, s->d_state,  s->n_groups, max_path_len};
-    hipError_t e = tsv::launch_commit(a, s->in_dtype == TSV_BF16, (hipStream_t)stream);
+    hipError_t e = s->n_nodes > kMaxNodesMfma
+                       ? tsv::launch_commit_large(a, s->in_dtype == TSV_BF16, (hipStream_t)stream)
+                       : tsv::launch_commit(a, s->in_dtype == TSV_BF16, (hipStream_t)stream);
     return e == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
 }
 
@@ -111,7 +116,9 @@ tsv_status tree_ssd_commit_layers(const tsv_shape* s, int32_t n_layers,
     tsv::CommitArgs a{nullptr,  nullptr,     nullptr,     nullptr,      nullptr,     layers,
                       n_layers, parent,      accepted,    accepted_len, tree_status, s->batch,
                       s->n_nodes, s->n_heads, s->head_dim, s->d_state,  s->n_groups, max_path_len};
-    hipError_t e = tsv::launch_commit(a, s->in_dtype == TSV_BF16, (hipStream_t)stream);
+    hipError_t e = s->n_nodes > kMaxNodesMfma
+                       ? tsv::launch_commit_large(a, s->in_dtype == TSV_BF16, (hipStream_t)stream)
+                       : tsv::launch_commit(a, s->in_dtype == TSV_BF16, (hipStream_t)stream);
     return e == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
 }
 
@@ -187,7 +194,7 @@ const char* tree_ssd_status_string(int32_t status) {
     switch (status) {
         case TSV_OK: return "ok";
         case TSV_E_NULL: return "null pointer argument";
-        case TSV_E_SHAPE: return "size out of range (T > 256, H % G != 0, negative size, bad heads_per_block or max_path_len)";
+        case TSV_E_SHAPE: return "size out of range (T > 1024, H % G != 0, negative size, bad heads_per_block or max_path_len)";
         case TSV_E_DTYPE: return "unknown input dtype";
         case TSV_E_UNSUPPORTED: return "unsupported size combination (head_dim or d_state > 256)";
         case TSV_E_LAUNCH: return "HIP kernel launch failed";

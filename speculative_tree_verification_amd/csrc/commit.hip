@@ -93,7 +93,9 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
     }
 
     // tree and path indices (one round trip, with the state chunk)
-    const bool len_ok = len >= 0 && len <= Lmax;
+    // a valid path steps from parent to child, so its indices increase and
+    // len <= T (this also keeps every path index inside s_path)
+    const bool len_ok = len >= 0 && len <= Lmax && len <= T;
     if (len_ok && tid < len) s_path[tid] = acc_i;
     int st = check_tree(par_i, T, s_par);  // barrier: s_path visible too
     int bad_path = 0;

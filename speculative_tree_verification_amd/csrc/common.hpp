@@ -12,7 +12,11 @@
 
 namespace tsv {
 
-constexpr int kMaxNodes = 256;
+constexpr int kMaxNodes = 256;       // trees the MFMA kernels take
+constexpr int kMaxNodesLarge = 1024;  // trees past 256 nodes: the plain kernels
+
+// 64-bit words of one node's ancestor bit set (node j: bit j % 64 of word j / 64)
+__host__ __device__ constexpr int anc_words(int T) { return T <= 256 ? 4 : (T + 63) / 64; }
 constexpr int kBlock = 256;
 constexpr int kWave = 64;
 

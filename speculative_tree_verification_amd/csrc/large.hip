@@ -1,0 +1,282 @@
+// large.hip -- verify and commit of one SSD layer over packed trees of 257 to
+// 1024 nodes ("STree: Speculative Tree Decoding for Hybrid State Space
+// Models", atlas.scime.ai summary, section "Approach": the accumulated log
+// transitions along ancestor paths give every node its own path's output in
+// one pass; the accepted state is rebuilt by replaying the activations).
+//
+// Same outputs as the kernels for trees of up to 256 nodes; plain fp32 VALU
+// arithmetic, any head_dim and d_state up to 256, both input dtypes.
+//
+// Verify: one work-group of 1024 threads (16 waves) per (item, head), one
+// thread per node for the tree check. Each wave takes every 16th node; its 64
+// lanes hold the node's C row spread over d_state, so each ancestor's score
+// C_i . B_j is one reduction across the wave, and the node's outputs spread
+// over head_dim (lane p and p + 64k). The decay from ancestor j to i is summed
+// along the walk (no difference of prefix sums). The h0 read-out takes h0
+// from LDS (stored transposed, n-major) when a head's block fits in 64 KiB.
+//
+// Commit: one work-group of 256 threads per (layer, item, head, 4,096-element
+// chunk of the state), as for smaller trees; the tree and the path are checked
+// with each thread taking every 256th entry.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace tsv {
+
+constexpr int kLargeThreads = kMaxNodesLarge;  // one thread per node for the tree check
+constexpr int kLargeWaves = kLargeThreads / kWave;
+constexpr int kLargeH0Lds = 16384;  // floats of h0 staged in LDS (64 KiB)
+
+template <typename TIO, bool H0LDS>
+__global__ __launch_bounds__(kLargeThreads) void verify_large_kernel(
+    const TIO* __restrict__ x, const TIO* __restrict__ dt, const float* __restrict__ A,
+    const TIO* __restrict__ Bm, const TIO* __restrict__ Cm, const float* __restrict__ D,
+    const float* __restrict__ h0, const int32_t* __restrict__ parent, TIO* __restrict__ y,
+    int32_t* __restrict__ tree_status, int T, int H, int P, int N, int G) {
+    __shared__ int s_par[kMaxNodesLarge];
+    __shared__ float s_dt[kMaxNodesLarge];
+    __shared__ float s_h0[H0LDS ? kLargeH0Lds : 1];  // [n][p]
+
+    const int b = blockIdx.x / H;
+    const int h = blockIdx.x % H;
+    const int g = h / (H / G);
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int w = tid / kWave;
+    const int st = load_tree(parent + (size_t)b * T, T, s_par);
+    if (h == 0 && tid == 0 && tree_status) tree_status[b] = st;
+    if (st) return;
+
+    const float Ah = A[h];
+    const float Dh = D[h];
+    const float* H0 = h0 + ((size_t)b * H + h) * P * N;
+    for (int i = tid; i < T; i += kLargeThreads) s_dt[i] = Elem<TIO>::ld(dt, ((size_t)b * T + i) * H + h);
+    if (H0LDS)
+        for (int e = tid; e < P * N; e += kLargeThreads) {
+            const int p = e / N, n = e - p * N;
+            s_h0[n * P + p] = H0[e];
+        }
+    __syncthreads();
+
+    const size_t xrow = (size_t)H * P;  // x / y stride between nodes
+    const TIO* xb = x + ((size_t)b * T * H + h) * P;
+    for (int i = w; i < T; i += kLargeWaves) {
+        const TIO* Ci = Cm + (((size_t)b * T + i) * G + g) * N;
+        float c[4];  // C_i[lane + 64 k]
+#pragma unroll
+        for (int k = 0; k < 4; ++k) c[k] = lane + 64 * k < N ? Elem<TIO>::ld(Ci, lane + 64 * k) : 0.f;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};  // output p = lane + 64 k
+        float s = 0.f;  // sum of dt A over the nodes from i up to (excluding) j
+        for (int j = i; j >= 0; j = s_par[j]) {
+            const TIO* Bj = Bm + (((size_t)b * T + j) * G + g) * N;
+            float gp = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (lane + 64 * k < N) gp += c[k] * Elem<TIO>::ld(Bj, lane + 64 * k);
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) gp += __shfl_xor(gp, off, kWave);
+            const float dtj = s_dt[j];
+            const float wgt = gp * expf(s) * dtj;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (lane + 64 * k < P) acc[k] += wgt * Elem<TIO>::ld(xb, j * xrow + lane + 64 * k);
+            s += dtj * Ah;
+        }
+        const float ei = expf(s);
+        // read-out h0 . C_i: C_i[n] from lane n % 64 of register n / 64 (a
+        // wave-uniform index, so a scalar read of one lane)
+        float ch[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) {
+            if (64 * k2 >= N) break;
+            for (int n2 = 0; n2 < 64 && 64 * k2 + n2 < N; ++n2) {
+                const int n = 64 * k2 + n2;
+                const float cn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c[k2]), n2));
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    if (64 * k >= P) break;
+                    const int p = min(lane + 64 * k, P - 1);
+                    ch[k] += cn * (H0LDS ? s_h0[n * P + p] : H0[(size_t)p * N + n]);
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int p = lane + 64 * k;
+            if (p < P) {
+                const size_t o = i * xrow + p;
+                Elem<TIO>::st(y + ((size_t)b * T * H + h) * P, o, ei * ch[k] + acc[k] + Dh * Elem<TIO>::ld(xb, o));
+            }
+        }
+    }
+}
+
+hipError_t launch_verify_large(const VerifyArgs& a, bool bf16, hipStream_t stream) {
+    dim3 grid((unsigned)(a.batch * a.H));
+    const bool lds = a.P * a.N <= kLargeH0Lds;
+#define TSV_LARGE(TIO, L)                                                                        \
+    hipLaunchKernelGGL((verify_large_kernel<TIO, L>), grid, dim3(kLargeThreads), 0, stream,      \
+                       (const TIO*)a.x, (const TIO*)a.dt, a.A, (const TIO*)a.B, (const TIO*)a.C, \
+                       a.D, a.h0, a.parent, (TIO*)a.y, a.tree_status, a.T, a.H, a.P, a.N, a.G)
+    if (bf16) {
+        if (lds) TSV_LARGE(uint16_t, true);
+        else TSV_LARGE(uint16_t, false);
+    } else {
+        if (lds) TSV_LARGE(float, true);
+        else TSV_LARGE(float, false);
+    }
+#undef TSV_LARGE
+    return hipGetLastError();
+}
+
+constexpr int kLargePathChunk = 16;  // path entries staged in LDS at a time
+
+template <typename TIO>
+__global__ __launch_bounds__(kBlock) void commit_large_kernel(
+    const TIO* __restrict__ x_arg, const TIO* __restrict__ dt_arg, const float* __restrict__ A_arg,
+    const TIO* __restrict__ B_arg, float* __restrict__ h_arg, const tsv_commit_layer* __restrict__ layers,
+    const int32_t* __restrict__ parent, const int32_t* __restrict__ accepted,
+    const int32_t* __restrict__ accepted_len, int32_t* __restrict__ tree_status, int BH, int T,
+    int H, int P, int N, int G, int Lmax, int chunks) {
+    __shared__ int s_par[kMaxNodesLarge];
+    __shared__ int s_path[kMaxNodesLarge];
+    __shared__ float s_w[kMaxNodesLarge];
+    __shared__ float s_w0;
+    // [kLargePathChunk][P] weighted x rows, then [kLargePathChunk][N] B rows
+    extern __shared__ __attribute__((aligned(16))) float s_dyn[];
+    float* s_wx = s_dyn;
+    float* s_B = s_dyn + kLargePathChunk * P;
+
+    const int chunk = blockIdx.x % chunks;
+    const int bh = (blockIdx.x / chunks) % BH;
+    const int layer = blockIdx.x / (chunks * BH);
+    const TIO* x = x_arg;
+    const TIO* dt = dt_arg;
+    const float* A = A_arg;
+    const TIO* Bm = B_arg;
+    float* hp = h_arg;
+    if (layers) {  // uniform over the launch
+        const tsv_commit_layer L = layers[layer];
+        x = (const TIO*)L.x;
+        dt = (const TIO*)L.dt;
+        A = L.A;
+        Bm = (const TIO*)L.B;
+        hp = L.h0_inout;
+    }
+    const int b = bh / H;
+    const int hd = bh % H;
+    const int g = hd / (H / G);
+    const int tid = threadIdx.x;
+    const int PN = P * N;
+    const int len = accepted_len[b];
+
+    // tree and path, each thread taking every kBlock-th entry
+    const bool len_ok = len >= 0 && len <= Lmax;
+    int bad_root = 0, bad_par = 0;
+    for (int i = tid; i < T; i += kBlock) {
+        const int p = parent[(size_t)b * T + i];
+        s_par[i] = p;
+        if (i == 0)
+            bad_root = p != -1;
+        else
+            bad_par |= p < 0 || p >= i;
+    }
+    if (len_ok)
+        for (int k = tid; k < min(len, kMaxNodesLarge); k += kBlock) s_path[k] = accepted[(size_t)b * Lmax + k];
+    int st = 0;
+    if (__syncthreads_or(bad_root | bad_par)) {
+        st = __syncthreads_or(bad_root) ? kStBadRoot : 0;
+        st |= __syncthreads_or(bad_par) ? kStBadParent : 0;
+    }
+    int bad_path = 0;
+    if (!st) {
+        if (!len_ok || len > T) {  // a path of more than T entries repeats a node
+            bad_path = tid == 0;
+        } else {
+            for (int k = tid; k < len; k += kBlock) {
+                const int node = s_path[k];
+                bad_path |= k == 0 ? node != 0 : (node < 0 || node >= T || s_par[node] != s_path[k - 1]);
+            }
+        }
+    }
+    if (__syncthreads_or(bad_path)) st |= kStBadPath;
+    if (layer == 0 && hd == 0 && chunk == 0 && tid == 0 && tree_status) tree_status[b] = st;
+    if (st || len == 0) return;
+
+    const float Ah = gload(A + hd);
+    float* hb = hp + ((size_t)b * H + hd) * PN;
+    constexpr int kEl = 16;  // state elements per thread
+    const int e0 = chunk * kBlock * kEl;
+    float acc[kEl];
+#pragma unroll
+    for (int m = 0; m < kEl; ++m) {
+        const int e = e0 + m * kBlock + tid;
+        acc[m] = e < PN ? gload(hb + e) : 0.f;
+    }
+    // decay weights along the path: w_k = exp(sum of dt A after entry k) dt_k,
+    // w0 = exp(sum over the whole path) (suffix sums, so nothing cancels)
+    for (int k = tid; k < len; k += kBlock) s_w[k] = Elem<TIO>::ld(dt, ((size_t)b * T + s_path[k]) * H + hd);
+    __syncthreads();
+    if (tid == 0) {
+        float c = 0.f;
+        for (int k = len - 1; k >= 0; --k) {
+            const float dtk = s_w[k];
+            s_w[k] = expf(c) * dtk;
+            c += dtk * Ah;
+        }
+        s_w0 = expf(c);
+    }
+    __syncthreads();
+    const float w0 = s_w0;
+#pragma unroll
+    for (int m = 0; m < kEl; ++m) acc[m] *= w0;
+    for (int k0 = 0; k0 < len; k0 += kLargePathChunk) {
+        const int kn = min(kLargePathChunk, len - k0);
+        if (k0 > 0) __syncthreads();  // previous chunk consumed
+        for (int e = tid; e < kn * P; e += kBlock) {
+            const int k = e / P, p = e - k * P;
+            s_wx[e] = s_w[k0 + k] * Elem<TIO>::ld(x, (((size_t)b * T + s_path[k0 + k]) * H + hd) * P + p);
+        }
+        for (int e = tid; e < kn * N; e += kBlock) {
+            const int k = e / N, n = e - k * N;
+            s_B[e] = Elem<TIO>::ld(Bm, (((size_t)b * T + s_path[k0 + k]) * G + g) * N + n);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < kEl; ++m) {
+            const int e = e0 + m * kBlock + tid;
+            if (e < PN) {
+                const int p = e / N, n = e - p * N;
+                float a = acc[m];
+                for (int k = 0; k < kn; ++k) a += s_wx[k * P + p] * s_B[k * N + n];
+                acc[m] = a;
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < kEl; ++m) {
+        const int e = e0 + m * kBlock + tid;
+        if (e < PN) gstore(hb + e, acc[m]);
+    }
+}
+
+hipError_t launch_commit_large(const CommitArgs& a, bool bf16, hipStream_t stream) {
+    const int per_wg = kBlock * 16;
+    const int chunks = (a.P * a.N + per_wg - 1) / per_wg;
+    const int BH = a.batch * a.H;
+    dim3 grid((unsigned)((size_t)a.n_layers * BH * chunks));
+    const size_t lds = sizeof(float) * kLargePathChunk * (size_t)(a.P + a.N);
+    if (bf16)
+        hipLaunchKernelGGL(commit_large_kernel<uint16_t>, grid, dim3(kBlock), lds, stream,
+                           (const uint16_t*)a.x, (const uint16_t*)a.dt, a.A, (const uint16_t*)a.B,
+                           a.h, a.layers, a.parent, a.accepted, a.accepted_len, a.tree_status, BH,
+                           a.T, a.H, a.P, a.N, a.G, a.Lmax, chunks);
+    else
+        hipLaunchKernelGGL(commit_large_kernel<float>, grid, dim3(kBlock), lds, stream,
+                           (const float*)a.x, (const float*)a.dt, a.A, (const float*)a.B, a.h,
+                           a.layers, a.parent, a.accepted, a.accepted_len, a.tree_status, BH, a.T,
+                           a.H, a.P, a.N, a.G, a.Lmax, chunks);
+    return hipGetLastError();
+}
+
+}  // namespace tsv

@@ -53,6 +53,10 @@ hipError_t launch_verify_wide(const VerifyArgs& a, int heads_per_block, hipStrea
 
 hipError_t launch_commit(const CommitArgs& a, bool bf16, hipStream_t stream);
 
+// trees of 257 to 1024 nodes: plain fp32 VALU verify and commit (any P, N <= 256)
+hipError_t launch_verify_large(const VerifyArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_commit_large(const CommitArgs& a, bool bf16, hipStream_t stream);
+
 // gated delta rule over packed trees (fp32, T <= 64, dk and dv <= 128)
 hipError_t launch_gdn_verify(int batch, int T, int H, int dk, int dv, const float* q,
                              const float* k, const float* v, const float* g, const float* beta,

@@ -75,7 +75,7 @@ def good():
 
 
 @pytest.mark.parametrize("field,value,code", [
-    ("n_nodes", 257, 2), ("n_nodes", -1, 2), ("batch", -3, 2), ("n_heads", 0, 2),
+    ("n_nodes", 1025, 2), ("n_nodes", -1, 2), ("batch", -3, 2), ("n_heads", 0, 2),
     ("head_dim", 0, 2), ("d_state", 0, 2), ("n_groups", 3, 2), ("in_dtype", 7, 3),
     ("heads_per_block", 3, 2), ("heads_per_block", -1, 2), ("head_dim", 512, 4),
     ("d_state", 300, 4)])
@@ -110,10 +110,10 @@ def test_empty_inputs_are_noops(L):
 def test_commit_checks(L):
     s = good()
     assert call_commit(L, s, lmax=-1) == 2
-    assert call_commit(L, s, lmax=257) == 2
+    assert call_commit(L, s, lmax=1025) == 2
     assert call_commit(L, s, lmax=4) == 1
     L.tree_ssd_tree_info.argtypes = [ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 5
-    assert L.tree_ssd_tree_info(2, 300, None, None, None, None, None) == 2
+    assert L.tree_ssd_tree_info(2, 1025, None, None, None, None, None) == 2
     assert L.tree_ssd_tree_info(2, 10, None, None, None, None, None) == 1
 
 
@@ -135,7 +135,7 @@ def test_commit_layers_checks(L):
     assert call_commit_layers(L, s, 3) == 1                  # NULL table
     assert call_commit_layers(L, s, 3, fake, parent=fake) == 1            # NULL accepted_len
     assert call_commit_layers(L, s, 3, fake, lmax=4, parent=fake, alen=fake) == 1  # NULL accepted
-    assert call_commit_layers(L, s, 3, fake, lmax=300, parent=fake, alen=fake) == 2
+    assert call_commit_layers(L, s, 3, fake, lmax=1025, parent=fake, alen=fake) == 2
     bad = good()
     bad.n_groups = 3
     assert call_commit_layers(L, bad, 3, fake, parent=fake, alen=fake) == 2
@@ -155,10 +155,10 @@ def test_accept_greedy_checks(L):
         return L.tree_ssd_accept_greedy(batch, T, *ptrs[:3], lmax, *ptrs[3:], None, None, None)
 
     full = [fake] * 5
-    assert call(2, 300, 4, full) == 2       # more than 256 nodes
+    assert call(2, 1025, 4, full) == 2      # more than 1024 nodes
     assert call(-1, 5, 4, full) == 2
     assert call(2, 5, 0, full) == 2         # the root is always kept: at least one entry
-    assert call(2, 5, 257, full) == 2
+    assert call(2, 5, 1025, full) == 2
     assert call(0, 5, 4, [None] * 5) == 0   # nothing to do
     assert call(2, 0, 4, [None] * 5) == 0
     for k in range(5):
@@ -175,3 +175,14 @@ def test_product_path_never_reaches_the_oracle():
         if not os.path.isfile(path) or path.endswith((".so", ".o", ".pyc")):
             continue
         assert not pat.search(open(path, errors="ignore").read()), path
+
+
+def test_trees_up_to_1024_nodes_pass_the_shape_check(L):
+    """Past 256 nodes the plain kernels take over: 1024 passes the shape check
+    (the NULL tensors then give TSV_E_NULL), 1025 does not."""
+    s = good()
+    s.n_nodes = 1024
+    assert call_verify(L, s) == 1
+    assert call_commit(L, s, lmax=1024) == 1
+    s.n_nodes = 1025
+    assert call_verify(L, s) == 2
