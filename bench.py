@@ -50,6 +50,7 @@ def parse():
     ap.add_argument("--secondary-steps", type=int, default=20)
     ap.add_argument("--no-oracle", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-gdn", action="store_true", help="skip the gated-delta-rule tree kernels")
+    ap.add_argument("--no-large", action="store_true", help="skip the 1023-node tree measurement")
     ap.add_argument("--oracle-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--heads-per-block", type=int, default=0)
@@ -363,6 +364,52 @@ def gdn_timing(torch, bnd, W, rounds):
     return out
 
 
+LARGE_SHAPE = dict(batch=4, n_nodes=1023, n_heads=80, head_dim=64, d_state=128, n_groups=1)
+
+
+def large_timing(torch, bnd, W, rounds):
+    """Packed trees past 256 nodes: complete binary trees of 1023 nodes (depth
+    9) at batch 4 with the Mamba2-2.7B head shape, bf16, paths of 1-10 nodes;
+    average durations of back-to-back verify and commit launches over rotating
+    input sets."""
+    sh = LARGE_SHAPE
+    base = W.make_custom(23, **sh, dtype=W.BF16, tree="binary", max_path_len=10)
+    B, T, H, P, N, G = W.shape_of(base)
+    one = sum(a.nbytes for a in base.values()) + base["x"].nbytes
+    nsets = max(2, -(-ROTATE_BYTES // one))
+    d0 = bnd.to_device(base)
+    sets = [d0 if i == 0 else {k: v.clone() for k, v in d0.items()} for i in range(nsets)]
+    for d in sets:
+        d["y"] = torch.empty_like(d["x"])
+    pv = [bnd.PreparedVerify(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], d["parent"], d["y"])
+          for d in sets]
+    pc = [bnd.PreparedCommit(d["x"], d["dt"], d["A"], d["B"], d["h0"], d["parent"], d["accepted"],
+                             d["accepted_len"]) for d in sets]
+    out = {"workload": f"mamba2-2.7b-b{B}-tree{T}-binary", "dtype": "bf16"}
+    nbytes = {"verify": verify_bytes(B, T, H, P, N, G, 2),
+              "commit": commit_bytes(B, T, H, P, N, G, 2, [int(v) for v in base["accepted_len"]],
+                                     base["accepted"].shape[1])}
+    for name, fns in (("verify", pv), ("commit", pc)):
+        for f in fns:
+            f()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(sleep_cycles_for(torch, 2.0))
+        start.record()
+        for r in range(rounds):
+            fns[r % nsets]()
+        end.record()
+        torch.cuda.synchronize()
+        us = start.elapsed_time(end) * 1e3 / rounds
+        gbs = nbytes[name] / (us * 1e-6) / 1e9
+        out[name] = {"avg_us": round(us, 3), "algorithmic_bytes": nbytes[name], "achieved": round(gbs, 1),
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    out["nodes_per_s"] = round(B * T * H / ((out["verify"]["avg_us"] + out["commit"]["avg_us"]) * 1e-6), 1)
+    del sets, pv, pc
+    torch.cuda.empty_cache()
+    return out
+
+
 def accept_timing(torch, bnd, W, wl, rounds):
     """Greedy acceptance on the workload's trees with seeded draft and target
     tokens: average duration of back-to-back launches (one per step, outside
@@ -529,6 +576,11 @@ def main():
         out["gdn"] = gdn_timing(torch, bnd, W, args.secondary_steps)
         log(f"[bench] gated delta rule {out['gdn']['workload']}: verify {out['gdn']['verify']['avg_us']:.2f} us, "
             f"commit {out['gdn']['commit']['avg_us']:.2f} us")
+    if not args.no_large:
+        out["large"] = large_timing(torch, bnd, W, args.secondary_steps)
+        log(f"[bench] large trees {out['large']['workload']}: verify {out['large']['verify']['avg_us']:.2f} us "
+            f"({out['large']['verify']['frac']:.1%}), commit {out['large']['commit']['avg_us']:.2f} us "
+            f"({out['large']['commit']['frac']:.1%})")
     if not args.no_oracle:
         log("[bench] timing the CPU oracle on a sample of the workload")
         out["cpu_baseline"] = cpu_baseline(wl, args.oracle_seconds)

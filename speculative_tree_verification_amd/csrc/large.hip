@@ -12,8 +12,10 @@
 // lanes hold the node's C row spread over d_state, so each ancestor's score
 // C_i . B_j is one reduction across the wave, and the node's outputs spread
 // over head_dim (lane p and p + 64k). The decay from ancestor j to i is summed
-// along the walk (no difference of prefix sums). The h0 read-out takes h0
-// from LDS (stored transposed, n-major) when a head's block fits in 64 KiB.
+// along the walk (no difference of prefix sums); the walk requests the rows of
+// kWalk ancestors at a time. The h0 read-out takes h0 from LDS (rows padded
+// by 4 floats, read 4 columns at a time against the node's C row, which the
+// wave keeps in LDS too) when a head's block fits in 64 KiB.
 //
 // Commit: one work-group of 256 threads per (layer, item, head, 4,096-element
 // chunk of the state), as for smaller trees; the tree and the path are checked
@@ -26,8 +28,11 @@ namespace tsv {
 constexpr int kLargeThreads = kMaxNodesLarge;  // one thread per node for the tree check
 constexpr int kLargeWaves = kLargeThreads / kWave;
 constexpr int kLargeH0Lds = 16384;  // floats of h0 staged in LDS (64 KiB)
+constexpr int kWalk = 8;            // ancestors whose rows are requested together
+constexpr int kMaxDimLarge = 256;
 
-template <typename TIO, bool H0LDS>
+// NK, PK: registers per lane for d_state (lane + 64 k, k < NK) and head_dim
+template <typename TIO, bool H0LDS, int NK, int PK>
 __global__ __launch_bounds__(kLargeThreads) void verify_large_kernel(
     const TIO* __restrict__ x, const TIO* __restrict__ dt, const float* __restrict__ A,
     const TIO* __restrict__ Bm, const TIO* __restrict__ Cm, const float* __restrict__ D,
@@ -35,7 +40,8 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_kernel(
     int32_t* __restrict__ tree_status, int T, int H, int P, int N, int G) {
     __shared__ int s_par[kMaxNodesLarge];
     __shared__ float s_dt[kMaxNodesLarge];
-    __shared__ float s_h0[H0LDS ? kLargeH0Lds : 1];  // [n][p]
+    __shared__ __attribute__((aligned(16))) float s_h0[H0LDS ? kLargeH0Lds : 1];  // [p][N + 4]
+    __shared__ __attribute__((aligned(16))) float s_c[kLargeWaves][kMaxDimLarge];  // each wave's C row
 
     const int b = blockIdx.x / H;
     const int h = blockIdx.x % H;
@@ -51,10 +57,11 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_kernel(
     const float Dh = D[h];
     const float* H0 = h0 + ((size_t)b * H + h) * P * N;
     for (int i = tid; i < T; i += kLargeThreads) s_dt[i] = Elem<TIO>::ld(dt, ((size_t)b * T + i) * H + h);
+    const int NS = ((N + 3) & ~3) + 4;  // padded h0 row, a multiple of 4 floats
     if (H0LDS)
         for (int e = tid; e < P * N; e += kLargeThreads) {
             const int p = e / N, n = e - p * N;
-            s_h0[n * P + p] = H0[e];
+            s_h0[p * NS + n] = H0[e];
         }
     __syncthreads();
 
@@ -62,68 +69,100 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_kernel(
     const TIO* xb = x + ((size_t)b * T * H + h) * P;
     for (int i = w; i < T; i += kLargeWaves) {
         const TIO* Ci = Cm + (((size_t)b * T + i) * G + g) * N;
-        float c[4];  // C_i[lane + 64 k]
+        float c[NK];  // C_i[lane + 64 k]
 #pragma unroll
-        for (int k = 0; k < 4; ++k) c[k] = lane + 64 * k < N ? Elem<TIO>::ld(Ci, lane + 64 * k) : 0.f;
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};  // output p = lane + 64 k
+        for (int k = 0; k < NK; ++k) {
+            c[k] = lane + 64 * k < N ? Elem<TIO>::ld(Ci, lane + 64 * k) : 0.f;
+            s_c[w][lane + 64 * k] = c[k];
+        }
+        float acc[PK];  // output p = lane + 64 k
+#pragma unroll
+        for (int k = 0; k < PK; ++k) acc[k] = 0.f;
         float s = 0.f;  // sum of dt A over the nodes from i up to (excluding) j
-        for (int j = i; j >= 0; j = s_par[j]) {
-            const TIO* Bj = Bm + (((size_t)b * T + j) * G + g) * N;
-            float gp = 0.f;
+        // the walk, kWalk ancestors at a time: their indices from the parents in
+        // LDS, then every B and x load of the batch before the first use, so a
+        // batch costs one memory round trip
+        for (int j = i; j >= 0;) {
+            int js[kWalk];
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                if (lane + 64 * k < N) gp += c[k] * Elem<TIO>::ld(Bj, lane + 64 * k);
+            for (int u = 0; u < kWalk; ++u) {
+                js[u] = j;
+                j = j >= 0 ? s_par[j] : -1;
+            }
+            float bv[kWalk][NK], xv[kWalk][PK];
 #pragma unroll
-            for (int off = 32; off > 0; off >>= 1) gp += __shfl_xor(gp, off, kWave);
-            const float dtj = s_dt[j];
-            const float wgt = gp * expf(s) * dtj;
+            for (int u = 0; u < kWalk; ++u) {
+                const int ju = max(js[u], 0);
+                const TIO* Bj = Bm + (((size_t)b * T + ju) * G + g) * N;
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                if (lane + 64 * k < P) acc[k] += wgt * Elem<TIO>::ld(xb, j * xrow + lane + 64 * k);
-            s += dtj * Ah;
+                for (int k = 0; k < NK; ++k)
+                    bv[u][k] = lane + 64 * k < N ? Elem<TIO>::ld(Bj, lane + 64 * k) : 0.f;
+#pragma unroll
+                for (int k = 0; k < PK; ++k)
+                    xv[u][k] = lane + 64 * k < P ? Elem<TIO>::ld(xb, ju * xrow + lane + 64 * k) : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < kWalk; ++u) {
+                if (js[u] < 0) break;  // wave-uniform
+                float gp = 0.f;
+#pragma unroll
+                for (int k = 0; k < NK; ++k) gp += c[k] * bv[u][k];
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) gp += __shfl_xor(gp, off, kWave);
+                const float dtj = s_dt[js[u]];
+                const float wgt = gp * expf(s) * dtj;
+#pragma unroll
+                for (int k = 0; k < PK; ++k) acc[k] += wgt * xv[u][k];
+                s += dtj * Ah;
+            }
         }
         const float ei = expf(s);
-        // read-out h0 . C_i: C_i[n] from lane n % 64 of register n / 64 (a
-        // wave-uniform index, so a scalar read of one lane)
-        float ch[4] = {0.f, 0.f, 0.f, 0.f};
+        wave_sync();  // the wave's C row in LDS
+        // read-out h0 . C_i, four columns at a time
+        const int N4 = N & ~3;
 #pragma unroll
-        for (int k2 = 0; k2 < 4; ++k2) {
-            if (64 * k2 >= N) break;
-            for (int n2 = 0; n2 < 64 && 64 * k2 + n2 < N; ++n2) {
-                const int n = 64 * k2 + n2;
-                const float cn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c[k2]), n2));
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    if (64 * k >= P) break;
-                    const int p = min(lane + 64 * k, P - 1);
-                    ch[k] += cn * (H0LDS ? s_h0[n * P + p] : H0[(size_t)p * N + n]);
+        for (int k = 0; k < PK; ++k) {
+            if (64 * k >= P) break;  // wave-uniform
+            const int p = min(lane + 64 * k, P - 1);
+            float ch = 0.f;
+            if (H0LDS) {
+                const float* hr = s_h0 + p * NS;
+#pragma unroll 8
+                for (int n = 0; n < N4; n += 4) {
+                    const float4 cv = *(const float4*)&s_c[w][n];
+                    const float4 hv = *(const float4*)&hr[n];
+                    ch += cv.x * hv.x + cv.y * hv.y + cv.z * hv.z + cv.w * hv.w;
                 }
+                for (int n = N4; n < N; ++n) ch += s_c[w][n] * hr[n];
+            } else {
+                const float* hr = H0 + (size_t)p * N;
+                for (int n = 0; n < N; ++n) ch += s_c[w][n] * hr[n];
+            }
+            if (lane + 64 * k < P) {
+                const size_t o = i * xrow + lane + 64 * k;
+                Elem<TIO>::st(y + ((size_t)b * T * H + h) * P, o, ei * ch + acc[k] + Dh * Elem<TIO>::ld(xb, o));
             }
         }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int p = lane + 64 * k;
-            if (p < P) {
-                const size_t o = i * xrow + p;
-                Elem<TIO>::st(y + ((size_t)b * T * H + h) * P, o, ei * ch[k] + acc[k] + Dh * Elem<TIO>::ld(xb, o));
-            }
-        }
+        wave_sync();  // C row consumed before the next node writes it
     }
 }
 
 hipError_t launch_verify_large(const VerifyArgs& a, bool bf16, hipStream_t stream) {
     dim3 grid((unsigned)(a.batch * a.H));
-    const bool lds = a.P * a.N <= kLargeH0Lds;
-#define TSV_LARGE(TIO, L)                                                                        \
-    hipLaunchKernelGGL((verify_large_kernel<TIO, L>), grid, dim3(kLargeThreads), 0, stream,      \
-                       (const TIO*)a.x, (const TIO*)a.dt, a.A, (const TIO*)a.B, (const TIO*)a.C, \
+    const bool lds = a.P * (((a.N + 3) & ~3) + 4) <= kLargeH0Lds;
+    const bool small = a.N <= 128 && a.P <= 64;
+#define TSV_LARGE(TIO, L, NK, PK)                                                                  \
+    hipLaunchKernelGGL((verify_large_kernel<TIO, L, NK, PK>), grid, dim3(kLargeThreads), 0, stream, \
+                       (const TIO*)a.x, (const TIO*)a.dt, a.A, (const TIO*)a.B, (const TIO*)a.C,   \
                        a.D, a.h0, a.parent, (TIO*)a.y, a.tree_status, a.T, a.H, a.P, a.N, a.G)
     if (bf16) {
-        if (lds) TSV_LARGE(uint16_t, true);
-        else TSV_LARGE(uint16_t, false);
+        if (small) TSV_LARGE(uint16_t, true, 2, 1);
+        else if (lds) TSV_LARGE(uint16_t, true, 4, 4);
+        else TSV_LARGE(uint16_t, false, 4, 4);
     } else {
-        if (lds) TSV_LARGE(float, true);
-        else TSV_LARGE(float, false);
+        if (small) TSV_LARGE(float, true, 2, 1);
+        else if (lds) TSV_LARGE(float, true, 4, 4);
+        else TSV_LARGE(float, false, 4, 4);
     }
 #undef TSV_LARGE
     return hipGetLastError();
