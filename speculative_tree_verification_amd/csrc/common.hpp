@@ -3,8 +3,8 @@
 // Tree topology of a packed draft tree ("STree: Speculative Tree Decoding for
 // Hybrid State Space Models", atlas.scime.ai summary, section "Approach": the
 // tree mask L over the packed sequence): node 0 is the root, every parent is
-// listed before its children, T <= 256. One work-group of at least 256
-// threads holds one tree in LDS, one node per thread.
+// listed before its children, T <= 1024 (the MFMA kernels take T <= 256).
+// One work-group with at least one thread per node holds one tree in LDS.
 #pragma once
 
 #include <hip/hip_runtime.h>

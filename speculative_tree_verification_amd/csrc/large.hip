@@ -147,8 +147,183 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_kernel(
     }
 }
 
+// ----------------------------------------------------------------------------
+// MFMA form for bf16 inputs, head_dim 64, d_state 32 KS (64 or 128). Each wave
+// takes tiles of 16 consecutive nodes:
+//  - read-out h0 . C_i of the tile on bf16 MFMA (h0 as bf16 high and low
+//    parts in LDS, C rows as the A operand);
+//  - the ancestors of the tile's nodes, 32 steps of each root path at a time:
+//    node lanes walk the parents in LDS, record each ancestor by distance with
+//    its decay exp(sum of dt A from i up to, not including, j) dt_j, and flag
+//    it; the flags are compacted into the column list J (no repeats);
+//  - per block of 16 columns: G^T = B[J] C[tile]^T on bf16 MFMA, masked to the
+//    recorded (node, ancestor) pairs and weighted by their decays (S), then
+//    S X[J] on fp32 MFMA. The accumulator of G^T holds S[i][j] with i = lane % 16
+//    and j = 4 (lane / 16) + c in element c: the A operand of the step that
+//    takes those j, with the matching X rows as its B operand.
+constexpr int kLmDist = 32;  // path steps per pass
+
+template <int KS>
+__global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const float* __restrict__ A,
+    const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm, const float* __restrict__ D,
+    const float* __restrict__ h0, const int32_t* __restrict__ parent, uint16_t* __restrict__ y,
+    int32_t* __restrict__ tree_status, int T, int H, int G) {
+    constexpr int P = 64, N = 32 * KS, NW = kLargeWaves;
+    constexpr int RH = N + 8;  // row stride (bf16) of the h0 planes
+    __shared__ int s_par[kMaxNodesLarge];
+    __shared__ int s_dep[kMaxNodesLarge];
+    __shared__ int s_nxt[kMaxNodesLarge];
+    __shared__ float s_a[kMaxNodesLarge];  // dt of each node
+    __shared__ __attribute__((aligned(16))) uint16_t s_h0h[P * RH];
+    __shared__ __attribute__((aligned(16))) uint16_t s_h0l[P * RH];
+    __shared__ uint16_t s_path[NW][16][kLmDist];  // ancestor at distance 32 k + t of tile node r
+    __shared__ float s_dec[NW][16][kLmDist];      // its decay times its dt
+    __shared__ float s_cum[NW][16];               // cum of tile node r
+    __shared__ uint8_t s_flag[NW][kMaxNodesLarge];
+    __shared__ uint16_t s_J[NW][16 * kLmDist];
+
+    const int b = blockIdx.x / H;
+    const int h = blockIdx.x % H;
+    const int g = h / (H / G);
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int l16 = lane & 15, q4 = lane >> 4;
+    const int st = load_tree(parent + (size_t)b * T, T, s_par);
+    if (h == 0 && tid == 0 && tree_status) tree_status[b] = st;
+    if (st) return;
+    tree_depth(s_par, T, s_nxt, s_dep);
+
+    const float Ah = A[h];
+    const float Dh = D[h];
+    for (int i = tid; i < T; i += kLargeThreads) s_a[i] = bf16_bits_to_f32(dt[((size_t)b * T + i) * H + h]);
+    const float* H0 = h0 + ((size_t)b * H + h) * P * N;
+    for (int e = tid; e < P * N; e += kLargeThreads) {
+        const int p = e / N, n = e - p * N;
+        const float v = H0[e];
+        const __bf16 hb = (__bf16)v;
+        s_h0h[p * RH + n] = __builtin_bit_cast(uint16_t, hb);
+        s_h0l[p * RH + n] = f32_to_bf16_bits(v - (float)hb);
+    }
+    for (int e = tid; e < NW * kMaxNodesLarge / 4; e += kLargeThreads) ((uint32_t*)&s_flag[0][0])[e] = 0u;
+    __syncthreads();
+
+    const size_t xrow = (size_t)H * P;  // x / y stride between nodes
+    const uint16_t* xb = x + ((size_t)b * T * H + h) * P;
+    uint16_t* yb = y + ((size_t)b * T * H + h) * P;
+    for (int ti = w; 16 * ti < T; ti += NW) {
+        const int i0 = 16 * ti;
+        // C rows of the tile: node i0 + l16, columns 32 ks + 8 q4 ..
+        bf16x8 cf[KS];
+        const uint16_t* crow = Cm + (((size_t)b * T + min(i0 + l16, T - 1)) * G + g) * N;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) cf[ks] = __builtin_bit_cast(bf16x8, *(const uint4*)(crow + 32 * ks + 8 * q4));
+        // read-out: rows i0 + 4 q4 + c, columns p = 16 pt + l16
+        f32x4 y0[4], yw[4];
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+            y0[pt] = yw[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int o = (16 * pt + l16) * RH + 32 * ks + 8 * q4;
+                y0[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf[ks], *(const bf16x8*)&s_h0l[o], y0[pt], 0, 0, 0);
+                y0[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf[ks], *(const bf16x8*)&s_h0h[o], y0[pt], 0, 0, 0);
+            }
+        }
+        // the walk, 32 path steps a pass
+        int jw = lane < 16 && i0 + lane < T ? i0 + lane : -1;
+        float sw = 0.f;
+        const int inode = i0 + l16;
+        const int di = s_dep[min(inode, T - 1)];
+        for (int k = 0;; ++k) {
+            if (lane < 16) {
+                for (int t = 0; t < kLmDist; ++t) {
+                    if (jw >= 0) {
+                        const float dtj = s_a[jw];
+                        s_path[w][lane][t] = (uint16_t)jw;
+                        s_dec[w][lane][t] = expf(sw) * dtj;
+                        sw += dtj * Ah;
+                        s_flag[w][jw] = 1;
+                        jw = s_par[jw];
+                    } else {
+                        s_path[w][lane][t] = 0xffff;
+                    }
+                }
+                s_cum[w][lane] = sw;
+            }
+            wave_sync();
+            int nJ = 0;  // wave-uniform
+            for (int c0 = 0; c0 < T; c0 += kWave) {
+                const int j = c0 + lane;
+                const bool f = j < T && s_flag[w][j];
+                const unsigned long long m = __ballot(f);
+                if (f) {
+                    s_J[w][nJ + __popcll(m & ((1ull << lane) - 1))] = (uint16_t)j;
+                    s_flag[w][j] = 0;
+                }
+                nJ += __popcll(m);
+            }
+            wave_sync();
+            for (int c0 = 0; c0 < nJ; c0 += 16) {
+                // G^T block: rows J[c0 + l16] (A operand: B rows), columns the tile (C rows)
+                const int jr = s_J[w][min(c0 + l16, nJ - 1)];
+                const uint16_t* brow = Bm + (((size_t)b * T + jr) * G + g) * N;
+                f32x4 gt = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    gt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, *(const uint4*)(brow + 32 * ks + 8 * q4)), cf[ks], gt, 0, 0, 0);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int jpos = c0 + 4 * q4 + c;
+                    const int j = s_J[w][min(jpos, nJ - 1)];
+                    float wgt = 0.f;
+                    const int t = di - s_dep[j] - kLmDist * k;
+                    if (jpos < nJ && inode < T && t >= 0 && t < kLmDist && s_path[w][l16][t] == j)
+                        wgt = s_dec[w][l16][t];
+                    const float sv = gt[c] * wgt;
+                    const uint16_t* xr = xb + (size_t)j * xrow;
+#pragma unroll
+                    for (int pt = 0; pt < 4; ++pt)
+                        yw[pt] = __builtin_amdgcn_mfma_f32_16x16x4f32(sv, bf16_bits_to_f32(xr[16 * pt + l16]), yw[pt], 0, 0, 0);
+                }
+            }
+            if (!__ballot(lane < 16 && jw >= 0)) break;
+            wave_sync();  // lists and columns of this pass consumed
+        }
+        wave_sync();  // s_cum
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int i = i0 + 4 * q4 + c;
+            if (i < T) {
+                const float ec = expf(s_cum[w][4 * q4 + c]);
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) {
+                    const size_t o = (size_t)i * xrow + 16 * pt + l16;
+                    yb[o] = f32_to_bf16_bits(ec * y0[pt][c] + yw[pt][c] + Dh * bf16_bits_to_f32(xb[o]));
+                }
+            }
+        }
+        wave_sync();  // s_cum, lists of this tile consumed
+    }
+}
+
 hipError_t launch_verify_large(const VerifyArgs& a, bool bf16, hipStream_t stream) {
     dim3 grid((unsigned)(a.batch * a.H));
+    if (bf16 && a.P == 64 && (a.N == 64 || a.N == 128)) {
+        if (a.N == 128)
+            hipLaunchKernelGGL(verify_large_mfma_kernel<4>, grid, dim3(kLargeThreads), 0, stream,
+                               (const uint16_t*)a.x, (const uint16_t*)a.dt, a.A, (const uint16_t*)a.B,
+                               (const uint16_t*)a.C, a.D, a.h0, a.parent, (uint16_t*)a.y,
+                               a.tree_status, a.T, a.H, a.G);
+        else
+            hipLaunchKernelGGL(verify_large_mfma_kernel<2>, grid, dim3(kLargeThreads), 0, stream,
+                               (const uint16_t*)a.x, (const uint16_t*)a.dt, a.A, (const uint16_t*)a.B,
+                               (const uint16_t*)a.C, a.D, a.h0, a.parent, (uint16_t*)a.y,
+                               a.tree_status, a.T, a.H, a.G);
+        return hipGetLastError();
+    }
     const bool lds = a.P * (((a.N + 3) & ~3) + 4) <= kLargeH0Lds;
     const bool small = a.N <= 128 && a.P <= 64;
 #define TSV_LARGE(TIO, L, NK, PK)                                                                  \

@@ -1,6 +1,8 @@
-"""GPU parity for trees of 257 to 1024 nodes (the plain fp32 kernels of
-large.hip, tree_info with more than four ancestor words, acceptance with 1024
-threads) against the fp64 oracle; integer outputs bit for bit."""
+"""GPU parity for trees of 257 to 1024 nodes (the kernels of large.hip: the
+MFMA verify for bf16 head_dim 64 / d_state 64 or 128, including trees deep
+enough for many 32-step passes, and the plain kernels for other shapes;
+tree_info with more than four ancestor words; acceptance with 1024 threads)
+against the fp64 oracle; integer outputs bit for bit."""
 import numpy as np
 import pytest
 
@@ -69,7 +71,10 @@ def check(bnd, oracle_mod, inp, dtype, label):
     (1000, 3, 70, 20, 1, W.F32, "star", 1, 2),
     (1024, 1, 8, 8, 1, W.F32, "chain", 1024, 700),
     (260, 1, 256, 128, 1, W.BF16, "recursive", 8, 9),
-    (600, 2, 100, 36, 2, W.BF16, "geometric", 12, 13)])
+    (600, 2, 100, 36, 2, W.BF16, "geometric", 12, 13),
+    (1024, 1, 64, 64, 1, W.BF16, "chain", 1024, 600),
+    (700, 2, 64, 128, 1, W.BF16, "recursive", 100, 60),
+    (1000, 2, 64, 128, 2, W.BF16, "star", 1, 2)])
 def test_large_tree_parity(bnd, oracle_mod, T, H, P, N, G, dtype, tree, depth, lmax):
     inp = W.make_custom(T + P, batch=2, n_nodes=T, n_heads=H, head_dim=P, d_state=N, n_groups=G,
                         dtype=dtype, tree=tree, max_depth=depth, max_path_len=lmax)
