@@ -219,18 +219,9 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
         const uint16_t* crow = Cm + (((size_t)b * T + min(i0 + l16, T - 1)) * G + g) * N;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) cf[ks] = __builtin_bit_cast(bf16x8, *(const uint4*)(crow + 32 * ks + 8 * q4));
-        // read-out: rows i0 + 4 q4 + c, columns p = 16 pt + l16
-        f32x4 y0[4], yw[4];
+        f32x4 yw[4];  // walk term: rows i0 + 4 q4 + c, columns p = 16 pt + l16
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-            y0[pt] = yw[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int o = (16 * pt + l16) * RH + 32 * ks + 8 * q4;
-                y0[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf[ks], *(const bf16x8*)&s_h0l[o], y0[pt], 0, 0, 0);
-                y0[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf[ks], *(const bf16x8*)&s_h0h[o], y0[pt], 0, 0, 0);
-            }
-        }
+        for (int pt = 0; pt < 4; ++pt) yw[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
         // the walk, 32 path steps a pass
         int jw = lane < 16 && i0 + lane < T ? i0 + lane : -1;
         float sw = 0.f;
@@ -254,9 +245,10 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
             }
             wave_sync();
             int nJ = 0;  // wave-uniform
-            for (int c0 = 0; c0 < T; c0 += kWave) {
+            const int jmax = min(T, i0 + 16);  // ancestors precede their descendants
+            for (int c0 = 0; c0 < jmax; c0 += kWave) {
                 const int j = c0 + lane;
-                const bool f = j < T && s_flag[w][j];
+                const bool f = j < jmax && s_flag[w][j];
                 const unsigned long long m = __ballot(f);
                 if (f) {
                     s_J[w][nJ + __popcll(m & ((1ull << lane) - 1))] = (uint16_t)j;
@@ -265,15 +257,31 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
                 nJ += __popcll(m);
             }
             wave_sync();
+            // per column block of 16: the X values this lane feeds to the S X
+            // steps (row J[c0 + 4 q4 + c], column 16 pt + l16), requested one
+            // block ahead (clamped rows past the list: loaded, unused)
+            auto xvals = [&](int c0, float (&xq)[4][4]) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint16_t* xr = xb + (size_t)s_J[w][min(c0 + 4 * q4 + c, nJ - 1)] * xrow;
+#pragma unroll
+                    for (int pt = 0; pt < 4; ++pt) xq[c][pt] = bf16_bits_to_f32(xr[16 * pt + l16]);
+                }
+            };
+            float xq[4][4];
+            xvals(0, xq);
             for (int c0 = 0; c0 < nJ; c0 += 16) {
                 // G^T block: rows J[c0 + l16] (A operand: B rows), columns the tile (C rows)
-                const int jr = s_J[w][min(c0 + l16, nJ - 1)];
-                const uint16_t* brow = Bm + (((size_t)b * T + jr) * G + g) * N;
+                const uint16_t* brow = Bm + (((size_t)b * T + s_J[w][min(c0 + l16, nJ - 1)]) * G + g) * N;
+                uint4 bq[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) bq[ks] = *(const uint4*)(brow + 32 * ks + 8 * q4);
+                float xn[4][4];
+                xvals(c0 + 16, xn);
                 f32x4 gt = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
-                    gt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, *(const uint4*)(brow + 32 * ks + 8 * q4)), cf[ks], gt, 0, 0, 0);
+                    gt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bq[ks]), cf[ks], gt, 0, 0, 0);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const int jpos = c0 + 4 * q4 + c;
@@ -283,14 +291,37 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
                     if (jpos < nJ && inode < T && t >= 0 && t < kLmDist && s_path[w][l16][t] == j)
                         wgt = s_dec[w][l16][t];
                     const float sv = gt[c] * wgt;
-                    const uint16_t* xr = xb + (size_t)j * xrow;
 #pragma unroll
                     for (int pt = 0; pt < 4; ++pt)
-                        yw[pt] = __builtin_amdgcn_mfma_f32_16x16x4f32(sv, bf16_bits_to_f32(xr[16 * pt + l16]), yw[pt], 0, 0, 0);
+                        yw[pt] = __builtin_amdgcn_mfma_f32_16x16x4f32(sv, xq[c][pt], yw[pt], 0, 0, 0);
                 }
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+#pragma unroll
+                    for (int pt = 0; pt < 4; ++pt) xq[c][pt] = xn[c][pt];
             }
             if (!__ballot(lane < 16 && jw >= 0)) break;
             wave_sync();  // lists and columns of this pass consumed
+        }
+        // own x values for the D term, requested before the read-out
+        float xi[4][4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int i = min(i0 + 4 * q4 + c, T - 1);
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) xi[c][pt] = bf16_bits_to_f32(xb[(size_t)i * xrow + 16 * pt + l16]);
+        }
+        // read-out h0 . C of the tile, same layout as the walk term
+        f32x4 y0[4];
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+            y0[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int o = (16 * pt + l16) * RH + 32 * ks + 8 * q4;
+                y0[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf[ks], *(const bf16x8*)&s_h0l[o], y0[pt], 0, 0, 0);
+                y0[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf[ks], *(const bf16x8*)&s_h0h[o], y0[pt], 0, 0, 0);
+            }
         }
         wave_sync();  // s_cum
 #pragma unroll
@@ -301,7 +332,7 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt) {
                     const size_t o = (size_t)i * xrow + 16 * pt + l16;
-                    yb[o] = f32_to_bf16_bits(ec * y0[pt][c] + yw[pt][c] + Dh * bf16_bits_to_f32(xb[o]));
+                    yb[o] = f32_to_bf16_bits(ec * y0[pt][c] + yw[pt][c] + Dh * xi[c][pt]);
                 }
             }
         }
