@@ -180,7 +180,8 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
     __shared__ uint16_t s_path[NW][16][kLmDist];  // ancestor at distance 32 k + t of tile node r
     __shared__ float s_dec[NW][16][kLmDist];      // its decay times its dt
     __shared__ float s_cum[NW][16];               // cum of tile node r
-    __shared__ uint8_t s_flag[NW][kMaxNodesLarge];
+    __shared__ int s_plen[NW][16];                // entries of this pass for tile node r
+    __shared__ unsigned long long s_bits[NW][kMaxNodesLarge / 64];  // ancestors flagged this pass
     __shared__ uint16_t s_J[NW][16 * kLmDist];
 
     const int b = blockIdx.x / H;
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
         s_h0h[p * RH + n] = __builtin_bit_cast(uint16_t, hb);
         s_h0l[p * RH + n] = f32_to_bf16_bits(v - (float)hb);
     }
-    for (int e = tid; e < NW * kMaxNodesLarge / 4; e += kLargeThreads) ((uint32_t*)&s_flag[0][0])[e] = 0u;
+    for (int e = tid; e < NW * kMaxNodesLarge / 64; e += kLargeThreads) (&s_bits[0][0])[e] = 0ull;
     __syncthreads();
 
     const size_t xrow = (size_t)H * P;  // x / y stride between nodes
@@ -229,32 +230,28 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
         const int di = s_dep[min(inode, T - 1)];
         for (int k = 0;; ++k) {
             if (lane < 16) {
-                for (int t = 0; t < kLmDist; ++t) {
-                    if (jw >= 0) {
-                        const float dtj = s_a[jw];
-                        s_path[w][lane][t] = (uint16_t)jw;
-                        s_dec[w][lane][t] = expf(sw) * dtj;
-                        sw += dtj * Ah;
-                        s_flag[w][jw] = 1;
-                        jw = s_par[jw];
-                    } else {
-                        s_path[w][lane][t] = 0xffff;
-                    }
+                int t = 0;
+                for (; t < kLmDist && jw >= 0; ++t) {
+                    const float dtj = s_a[jw];
+                    s_path[w][lane][t] = (uint16_t)jw;
+                    s_dec[w][lane][t] = __expf(sw) * dtj;
+                    sw += dtj * Ah;
+                    atomicOr(&s_bits[w][jw >> 6], 1ull << (jw & 63));
+                    jw = s_par[jw];
                 }
+                s_plen[w][lane] = t;
                 s_cum[w][lane] = sw;
             }
             wave_sync();
+            // compact the flagged ancestors (they precede the tile's last node)
             int nJ = 0;  // wave-uniform
-            const int jmax = min(T, i0 + 16);  // ancestors precede their descendants
-            for (int c0 = 0; c0 < jmax; c0 += kWave) {
-                const int j = c0 + lane;
-                const bool f = j < jmax && s_flag[w][j];
-                const unsigned long long m = __ballot(f);
-                if (f) {
-                    s_J[w][nJ + __popcll(m & ((1ull << lane) - 1))] = (uint16_t)j;
-                    s_flag[w][j] = 0;
-                }
+            const int nwords = (min(T, i0 + 16) + 63) >> 6;
+            for (int wd = 0; wd < nwords; ++wd) {
+                const unsigned long long m = s_bits[w][wd];
+                if (!m) continue;  // wave-uniform
+                if ((m >> lane) & 1ull) s_J[w][nJ + __popcll(m & ((1ull << lane) - 1))] = (uint16_t)(64 * wd + lane);
                 nJ += __popcll(m);
+                if (lane == 0) s_bits[w][wd] = 0ull;
             }
             wave_sync();
             // per column block of 16: the X values this lane feeds to the S X
@@ -288,7 +285,7 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
                     const int j = s_J[w][min(jpos, nJ - 1)];
                     float wgt = 0.f;
                     const int t = di - s_dep[j] - kLmDist * k;
-                    if (jpos < nJ && inode < T && t >= 0 && t < kLmDist && s_path[w][l16][t] == j)
+                    if (jpos < nJ && inode < T && t >= 0 && t < s_plen[w][l16] && s_path[w][l16][t] == j)
                         wgt = s_dec[w][l16][t];
                     const float sv = gt[c] * wgt;
 #pragma unroll
