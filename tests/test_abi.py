@@ -17,7 +17,7 @@ def declared_functions():
     for hdr in glob.glob(os.path.join(ROOT, "include", "*.h")):
         text = open(hdr).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b(tree_ssd_\w+)\s*\(", text, flags=re.M):
+        for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b(tree_(?:ssd|gdn)_\w+)\s*\(", text, flags=re.M):
             names.add(m.group(1))
     return names
 
@@ -33,7 +33,8 @@ def L():
 def test_header_declares_entry_points():
     names = declared_functions()
     assert {"tree_ssd_verify", "tree_ssd_commit", "tree_ssd_commit_layers", "tree_ssd_accept_greedy",
-            "tree_ssd_tree_info", "tree_ssd_status_string", "tree_ssd_abi_version"} <= names
+            "tree_ssd_tree_info", "tree_ssd_status_string", "tree_ssd_abi_version",
+            "tree_gdn_verify", "tree_gdn_commit"} <= names
 
 
 def test_every_declared_symbol_exported(L):
@@ -186,3 +187,47 @@ def test_trees_up_to_1024_nodes_pass_the_shape_check(L):
     assert call_commit(L, s, lmax=1024) == 1
     s.n_nodes = 1025
     assert call_verify(L, s) == 2
+
+
+def call_gdn_verify(L, shape, ptrs=None):
+    vp = ctypes.c_void_p
+    L.tree_gdn_verify.argtypes = [ctypes.POINTER(Shape)] + [vp] * 11
+    L.tree_gdn_verify.restype = ctypes.c_int
+    ptrs = ptrs if ptrs is not None else [None] * 11
+    return L.tree_gdn_verify(ctypes.byref(shape) if shape is not None else None, *ptrs)
+
+
+def call_gdn_commit(L, shape, lmax=4, ptrs=None):
+    vp = ctypes.c_void_p
+    L.tree_gdn_commit.argtypes = [ctypes.POINTER(Shape)] + [vp] * 7 + [ctypes.c_int32, vp, vp]
+    L.tree_gdn_commit.restype = ctypes.c_int
+    ptrs = ptrs if ptrs is not None else [None] * 7
+    return L.tree_gdn_commit(ctypes.byref(shape) if shape is not None else None, *ptrs, lmax, None, None)
+
+
+def gdn_good():
+    s = good()
+    s.in_dtype, s.n_groups, s.n_nodes, s.head_dim, s.d_state = 0, 1, 31, 128, 128
+    return s
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("in_dtype", 1, 4), ("n_groups", 2, 4), ("n_nodes", 65, 4), ("head_dim", 129, 4),
+    ("d_state", 129, 4), ("n_nodes", 1025, 2), ("batch", -1, 2), ("n_heads", 0, 2)])
+def test_gdn_rejects_bad_shapes(L, field, value, code):
+    """The gated-delta-rule kernels take fp32, one group, T <= 64, dk and dv <= 128."""
+    s = gdn_good()
+    setattr(s, field, value)
+    assert call_gdn_verify(L, s) == code
+    assert call_gdn_commit(L, s) == code
+
+
+def test_gdn_null_and_empty(L):
+    assert call_gdn_verify(L, None) == 1
+    assert call_gdn_verify(L, gdn_good()) == 1     # NULL tensors
+    assert call_gdn_commit(L, gdn_good()) == 1
+    assert call_gdn_commit(L, gdn_good(), lmax=-1) == 2
+    assert call_gdn_commit(L, gdn_good(), lmax=1025) == 2
+    s = gdn_good()
+    s.batch = 0
+    assert call_gdn_verify(L, s) == 0 and call_gdn_commit(L, s) == 0

@@ -44,7 +44,8 @@ def run(bnd, d):
 @pytest.mark.parametrize("B,T,H,dk,dv,tree", [
     (2, 1, 2, 16, 16, "recursive"), (3, 7, 2, 8, 6, "recursive"), (4, 15, 4, 128, 128, "recursive"),
     (2, 31, 3, 64, 128, "recursive"), (2, 64, 2, 128, 64, "chain"), (2, 64, 2, 32, 32, "star"),
-    (2, 63, 2, 48, 40, "geometric"), (1, 40, 1, 100, 70, "recursive")])
+    (2, 63, 2, 48, 40, "geometric"), (1, 40, 1, 100, 70, "recursive"),
+    (2, 64, 2, 128, 128, "recursive")])
 def test_gdn_matches_oracle(bnd, B, T, H, dk, dv, tree):
     d = W.make_gdn(B * 1000 + T + dk, batch=B, n_nodes=T, n_heads=H, dk=dk, dv=dv, tree=tree,
                    max_depth=8 if tree != "chain" else T, max_path_len=min(T, 9))
@@ -88,3 +89,33 @@ def test_gdn_invalid_items_untouched(bnd):
         assert (o[b] == 5.0).all()
     for b in (1, 2, 3):
         assert torch.equal(S[b], dev["S0"][b])
+
+
+def test_gdn_pseudo_values_optional_and_streams(bnd):
+    """o is bitwise the same when e is not requested (NULL through the C ABI)
+    and when verify and commit run on another stream."""
+    import ctypes
+    import torch
+    d = W.make_gdn(5, batch=3, n_nodes=40, n_heads=2, dk=64, dv=96, max_path_len=6)
+    dev = {k: torch.from_numpy(v).cuda() for k, v in d.items()}
+    args = [dev[x] for x in ("q", "k", "v", "g", "beta", "S0", "parent")]
+    o1, e1 = bnd.gdn_verify(*args)
+    S1 = dev["S0"].clone()
+    bnd.gdn_commit(dev["k"], dev["g"], e1, S1, dev["parent"], dev["accepted"], dev["accepted_len"])
+    torch.cuda.synchronize()
+    o2 = torch.full_like(o1, 7.0)
+    shape = bnd._gdn_shape(dev["k"], dev["v"])
+    say("[gdn] verify without pseudo-values")
+    rc = bnd.lib.tree_gdn_verify(ctypes.byref(shape), *[bnd._ptr(t) for t in args], bnd._ptr(o2), None,
+                                 None, bnd._stream(None))
+    torch.cuda.synchronize()
+    assert rc == 0 and torch.equal(o1, o2)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        say("[gdn] verify and commit on another stream")
+        o3, e3 = bnd.gdn_verify(*args, stream=side)
+        S3 = dev["S0"].clone()
+        bnd.gdn_commit(dev["k"], dev["g"], e3, S3, dev["parent"], dev["accepted"], dev["accepted_len"],
+                       stream=side)
+    side.synchronize()
+    assert torch.equal(o1, o3) and torch.equal(e1, e3) and torch.equal(S1, S3)
