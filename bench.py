@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "tree-verify nodes/sec (batch×nodes×heads×layers) at 1 GPU; % peak HBM GB/s"
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA (no sparsity)
-ROTATE_BYTES = 640 << 20   # rotating input sets must exceed the 256 MB Infinity Cache
+ROTATE_BYTES = 1100 << 20  # rotating input sets: more than 1 GB, far past the 256 MB Infinity Cache
 
 
 def log(*a):
@@ -47,7 +47,9 @@ def parse():
                     help="workload configuration id (0-4); default 1, the 64-layer Mamba2-2.7B step")
     ap.add_argument("--secondary", default="2,4",
                     help="comma list of further workloads measured in the same run ('' for none)")
-    ap.add_argument("--secondary-steps", type=int, default=20)
+    ap.add_argument("--secondary-steps", type=int, default=50)
+    ap.add_argument("--rotate-mib", type=int, default=ROTATE_BYTES >> 20,
+                    help="total size of the rotating input sets (MiB)")
     ap.add_argument("--no-oracle", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-gdn", action="store_true", help="skip the gated-delta-rule tree kernels")
     ap.add_argument("--no-large", action="store_true", help="skip the 1023-node tree measurement")
@@ -509,7 +511,9 @@ def copy_calibration(torch):
 
 
 def main():
+    global ROTATE_BYTES
     args = parse()
+    ROTATE_BYTES = args.rotate_mib << 20
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path has no "
               "multi-GPU mode: heads or items would be sharded with no exchange inside it.",
