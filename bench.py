@@ -322,7 +322,55 @@ def time_steps(torch, wl, steps, warmup):
 GDN_SHAPE = dict(batch=16, n_nodes=31, n_heads=16, dk=128, dv=128)
 
 
-def gdn_timing(torch, bnd, W, rounds):
+def gdn_cpu_baseline(base, seconds):
+    """The fp64 gated-delta-rule oracle (numpy, one BLAS thread) on a bounded
+    sample of the same inputs: whole items (all heads), verify + commit as the
+    unrolled recurrence, cycled until about `seconds` of oracle time."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import gdn as OG
+    B, T, H, _ = base["k"].shape
+    f = lambda a: a.astype(np.float64) if a.dtype == np.float32 else a
+    done, used, parts = 0, 0.0, 0
+    with threadpool_limits(1):
+        while used < seconds:
+            b = parts % B
+            sl = {k: f(v[b:b + 1]) for k, v in base.items()}
+            t0 = time.perf_counter()
+            OG.verify_unrolled(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], sl["S0"], sl["parent"])
+            OG.commit_unrolled(sl["k"], sl["v"], sl["g"], sl["beta"], sl["S0"], sl["parent"],
+                               sl["accepted"], sl["accepted_len"])
+            used += time.perf_counter() - t0
+            done += T * H
+            parts += 1
+    return {"value": round(done / used, 1), "unit": "nodes/s", "cores": 1, "kind": "oracle",
+            "sample": f"{parts} items cycled over the workload's {B}, all {H} heads each: verify + commit "
+                      f"(the unrolled recurrence) in fp64 numpy, {used:.1f} s of oracle time",
+            "seconds": round(used, 2)}
+
+
+def large_cpu_baseline(base, seconds):
+    """The fp64 C oracle on a bounded sample of the large-tree inputs: items,
+    all heads each, verify + commit, cycled until about `seconds`."""
+    from oracle import oracle as O
+    B, T, H, _ = base["x"].shape
+    done, used, parts = 0, 0.0, 0
+    while used < seconds:
+        b = parts % B
+        s = O.gather_slices(base, "bf16", [(b, h) for h in range(H)])
+        t0 = time.perf_counter()
+        O.verify_slices(s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"], s["h0"], s["parent"])
+        O.commit_slices(s["x"], s["dt"], s["A"], s["B"], s["h0"], s["parent"], s["accepted"],
+                        s["accepted_len"], Lmax=base["accepted"].shape[-1])
+        used += time.perf_counter() - t0
+        done += T * H
+        parts += 1
+    return {"value": round(done / used, 1), "unit": "nodes/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"{parts} items cycled over the workload's {B}, all {H} heads each: verify + commit "
+                      f"in fp64, {used:.1f} s of oracle time", "seconds": round(used, 2)}
+
+
+def gdn_timing(torch, bnd, W, rounds, oracle_seconds=0.0):
     """Gated-delta-rule tree verify and commit on a batch-16 layer over the
     31-node random trees (16 heads, dk = dv = 128, fp32), rotating input sets;
     average durations of back-to-back launches of each kernel alone."""
@@ -363,13 +411,15 @@ def gdn_timing(torch, bnd, W, rounds):
         out[name] = {"avg_us": round(us, 3), "algorithmic_bytes": nbytes[name], "achieved": round(gbs, 1),
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
     out["nodes_per_s"] = round(B * T * H / ((out["verify"]["avg_us"] + out["commit"]["avg_us"]) * 1e-6), 1)
+    if oracle_seconds > 0:
+        out["cpu_baseline"] = gdn_cpu_baseline(base, oracle_seconds)
     return out
 
 
 LARGE_SHAPE = dict(batch=4, n_nodes=1023, n_heads=80, head_dim=64, d_state=128, n_groups=1)
 
 
-def large_timing(torch, bnd, W, rounds):
+def large_timing(torch, bnd, W, rounds, oracle_seconds=0.0):
     """Packed trees past 256 nodes: complete binary trees of 1023 nodes (depth
     9) at batch 4 with the Mamba2-2.7B head shape, bf16, paths of 1-10 nodes;
     average durations of back-to-back verify and commit launches over rotating
@@ -409,6 +459,8 @@ def large_timing(torch, bnd, W, rounds):
     out["nodes_per_s"] = round(B * T * H / ((out["verify"]["avg_us"] + out["commit"]["avg_us"]) * 1e-6), 1)
     del sets, pv, pc
     torch.cuda.empty_cache()
+    if oracle_seconds > 0:
+        out["cpu_baseline"] = large_cpu_baseline(base, oracle_seconds)
     return out
 
 
@@ -577,11 +629,11 @@ def main():
     if secondary:
         out["secondary"] = secondary
     if not args.no_gdn:
-        out["gdn"] = gdn_timing(torch, bnd, W, args.secondary_steps)
+        out["gdn"] = gdn_timing(torch, bnd, W, args.secondary_steps, 0.0 if args.no_oracle else 3.0)
         log(f"[bench] gated delta rule {out['gdn']['workload']}: verify {out['gdn']['verify']['avg_us']:.2f} us, "
             f"commit {out['gdn']['commit']['avg_us']:.2f} us")
     if not args.no_large:
-        out["large"] = large_timing(torch, bnd, W, args.secondary_steps)
+        out["large"] = large_timing(torch, bnd, W, args.secondary_steps, 0.0 if args.no_oracle else 4.0)
         log(f"[bench] large trees {out['large']['workload']}: verify {out['large']['verify']['avg_us']:.2f} us "
             f"({out['large']['verify']['frac']:.1%}), commit {out['large']['commit']['avg_us']:.2f} us "
             f"({out['large']['commit']['frac']:.1%})")
