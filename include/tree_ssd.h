@@ -72,6 +72,9 @@ typedef enum {
                                     the MFMA kernel applies (testing aid) */
 #define TSV_FLAG_FORCE_WIDE 2    /* use the wide-tree MFMA verify kernel for any
                                     tree size it supports (testing / tuning aid) */
+#define TSV_FLAG_FORCE_SMALL 4   /* trees of at most 16 nodes: use the 64-node
+                                    small-tree MFMA kernel instead of the one-wave
+                                    tiny-tree kernel (testing / tuning aid) */
 
 typedef struct {
     int32_t batch;           /* Bt >= 0 (0: nothing to do) */

@@ -26,6 +26,7 @@ TSV_F32 = 0
 TSV_BF16 = 1
 TSV_FLAG_FORCE_GENERIC = 1
 TSV_FLAG_FORCE_WIDE = 2
+TSV_FLAG_FORCE_SMALL = 4
 ST_BAD_ROOT, ST_BAD_PARENT, ST_BAD_PATH = 1, 2, 4
 STATUS_NAMES = {0: "TSV_OK", 1: "TSV_E_NULL", 2: "TSV_E_SHAPE", 3: "TSV_E_DTYPE",
                 4: "TSV_E_UNSUPPORTED", 5: "TSV_E_LAUNCH"}
@@ -138,13 +139,14 @@ def make_shape(x: torch.Tensor, Bm: torch.Tensor, flags: int = 0, heads_per_bloc
     return Shape(Bt, T, H, P, N, G, _dtype_code(x), flags, heads_per_block)
 
 
-def _flags(force_generic: bool, force_wide: bool) -> int:
-    return (TSV_FLAG_FORCE_GENERIC if force_generic else 0) | (TSV_FLAG_FORCE_WIDE if force_wide else 0)
+def _flags(force_generic: bool, force_wide: bool, force_small: bool = False) -> int:
+    return ((TSV_FLAG_FORCE_GENERIC if force_generic else 0) | (TSV_FLAG_FORCE_WIDE if force_wide else 0)
+            | (TSV_FLAG_FORCE_SMALL if force_small else 0))
 
 
 def verify(x, dt, A, B, C, D, h0, parent, y=None, tree_status=None, stream=None,
            force_generic: bool = False, heads_per_block: int = 0, check: bool = True,
-           force_wide: bool = False):
+           force_wide: bool = False, force_small: bool = False):
     """y [Bt,T,H,P] of one SSD layer over packed trees (tree_ssd_verify)."""
     Bt, T, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
@@ -164,7 +166,7 @@ def verify(x, dt, A, B, C, D, h0, parent, y=None, tree_status=None, stream=None,
         _check(y, "y", (Bt, T, H, P), io, dev)
     if tree_status is not None and check:
         _check(tree_status, "tree_status", (Bt,), torch.int32, dev)
-    shape = make_shape(x, B, _flags(force_generic, force_wide), heads_per_block)
+    shape = make_shape(x, B, _flags(force_generic, force_wide, force_small), heads_per_block)
     rc = lib.tree_ssd_verify(ctypes.byref(shape), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
                              _ptr(D), _ptr(h0), _ptr(parent), _ptr(y), _ptr(tree_status),
                              _stream(stream))
@@ -380,7 +382,8 @@ class PreparedVerify:
     """tree_ssd_verify with fixed buffers; calling it enqueues one launch."""
 
     def __init__(self, x, dt, A, B, C, D, h0, parent, y, tree_status=None, stream=None,
-                 force_generic: bool = False, heads_per_block: int = 0, force_wide: bool = False):
+                 force_generic: bool = False, heads_per_block: int = 0, force_wide: bool = False,
+                 force_small: bool = False):
         Bt, T, H, P = x.shape
         G, N = B.shape[2], B.shape[3]
         io, dev = x.dtype, x.device
@@ -391,7 +394,7 @@ class PreparedVerify:
                                   (parent, "parent", (Bt, T), torch.int32),
                                   (y, "y", (Bt, T, H, P), io)):
             _check(t, name, shp, dty, dev)
-        self.shape = make_shape(x, B, _flags(force_generic, force_wide), heads_per_block)
+        self.shape = make_shape(x, B, _flags(force_generic, force_wide, force_small), heads_per_block)
         self._keep = (x, dt, A, B, C, D, h0, parent, y, tree_status)
         self.args = (ctypes.byref(self.shape), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
                      _ptr(D), _ptr(h0), _ptr(parent), _ptr(y), _ptr(tree_status),

@@ -55,6 +55,8 @@ int default_heads_per_block(const tsv_shape* s, int per_cu) {
     return best;
 }
 hipError_t launch_mfma(const tsv_shape* s, const tsv::VerifyArgs& a, hipStream_t hs) {
+    if (s->n_nodes <= 16 && !(s->flags & (TSV_FLAG_FORCE_WIDE | TSV_FLAG_FORCE_SMALL)))
+        return tsv::launch_verify_tiny(a, hs);
     const bool small = s->n_nodes <= 64 && !(s->flags & TSV_FLAG_FORCE_WIDE);
     int hb = s->heads_per_block;
     if (hb == 0) hb = default_heads_per_block(s, small ? 4 : 1);

@@ -50,6 +50,9 @@ hipError_t launch_verify_generic(const VerifyArgs& a, bool bf16, hipStream_t str
 // the per-wave head_dim-slice kernel, wider trees the LDS-staged kernel
 hipError_t launch_verify_small(const VerifyArgs& a, int heads_per_block, hipStream_t stream);
 hipError_t launch_verify_wide(const VerifyArgs& a, int heads_per_block, hipStream_t stream);
+// bf16 MFMA verify for trees of at most 16 nodes: one wave per (item, head,
+// 16-row slice of head_dim), no LDS, no barrier (heads_per_block does not apply)
+hipError_t launch_verify_tiny(const VerifyArgs& a, hipStream_t stream);
 
 hipError_t launch_commit(const CommitArgs& a, bool bf16, hipStream_t stream);
 

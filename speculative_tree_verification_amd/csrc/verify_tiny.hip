@@ -1,0 +1,180 @@
+// verify_tiny.hip -- packed-tree verification of one Mamba2/SSD layer for
+// trees of at most 16 nodes, bf16 inputs, head_dim 64, d_state 64 or 128.
+//
+// Method: "STree: Speculative Tree Decoding for Hybrid State Space Models"
+// (atlas.scime.ai summary, section "Approach"): per (item b, head h)
+//   y_i = exp(cum_i) (h0 C_i) + sum_{j on path(i)} G_ij exp(cum_i - cum_j) dt_j x_j + D x_i,
+// G = C B^T, cum_i = sum of dt A over the root path of i (node i included),
+// i.e. A_tree = L (dt A) with L the tree's ancestor mask.
+//
+// Small static trees (the 15-node tree of one decoding step) give a launch of
+// a few MB that is bound by latency, not bandwidth. Here every wave is on its
+// own: a one-wave work-group per (item, head, 16-row slice of head_dim), with
+// no LDS and no barrier, so the only wait is one memory round trip.
+//  * loads leave in the order they are needed: parents and step sizes, the
+//    B and C rows (directly in MFMA operand layout), x, then h0.
+//  * tree (one lane per node, replicated over the four lane groups): the
+//    parent check by ballots; pointer jumping with cross-lane reads gives each
+//    node its ancestor set (a 16-bit mask) and cum_i.
+//  * pair scores on one 16x16x32 bf16 MFMA per k-step: the product
+//    B C^T leaves lane (r, q) holding G_ij for i = r and j = 4q + c.
+//  * those four values, masked by the ancestor set and weighted by
+//    exp(cum_i - cum_j) dt_j (plus D on the diagonal), are exactly the B
+//    operand of step c of a 16x16x4 fp32 MFMA whose A operand is x row 4q + c:
+//    the whole masked quadratic term is four fp32 MFMAs.
+//  * the read-out h0 C^T on bf16 MFMA with h0 split into high and low halves
+//    (about 16 significant bits), in the same accumulator layout (row p of the
+//    slice, column i), so y leaves as one 8-byte store per lane.
+#include "launch.hpp"
+#include "verify_common.hpp"
+
+namespace tsv {
+
+constexpr int kTinyNodes = 16;
+
+template <int KS>
+__global__ __launch_bounds__(64) void verify_tiny_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const float* __restrict__ A,
+    const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
+    const float* __restrict__ D, const float* __restrict__ h0, const int32_t* __restrict__ parent,
+    uint16_t* __restrict__ y, int32_t* __restrict__ tree_status, int T, int H, int G) {
+    constexpr int N = 32 * KS;
+    // logical block = ((b H + h) 4 + slice)
+    const int blk = xcd_block(blockIdx.x, gridDim.x);
+    const int wl = blk & 3;
+    const int bh = blk >> 2;
+    const int b = bh / H;
+    const int h = bh - b * H;
+    const int g = h / (H / G);
+    const int lane = threadIdx.x;
+    const int r16 = lane & 15;  // this lane's node i (and its head_dim row in operands)
+    const int q = lane >> 4;
+    const size_t bc_row0 = ((size_t)b * T) * G + g;  // row (b, node 0, g) of B and C
+    const int nl = min(r16, T - 1);                  // clamped node of this lane
+
+    // ---------------------------------------------------------------- loads
+    // (unconditional, from clamped rows, so that the compiler can count the
+    // loads still in flight at each wait; A and D are scalar loads issued
+    // first, so that they are not a round trip of their own after the check)
+    float Ah = A[h];
+    float Dh = D[h];
+    int par;
+    {
+        typedef const int32_t __attribute__((address_space(1))) gint;
+        uint64_t u = (uint64_t)(parent + (size_t)b * T);
+        asm volatile("" : "+v"(u));  // keep the load first, not next to its use
+        par = ((gint*)u)[nl];
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    const uint16_t* dtb = dt + (size_t)b * T * H + h;
+    const uint32_t dti = gload(dtb + (size_t)nl * H);
+    uint32_t dtj[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dtj[c] = gload(dtb + (size_t)min(4 * q + c, T - 1) * H);
+    uint4 breg[KS], creg[KS];
+    {
+        const uint16_t* brow = Bm + (bc_row0 + (size_t)nl * G) * N + 8 * q;
+        const uint16_t* crow = Cm + (bc_row0 + (size_t)nl * G) * N + 8 * q;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            breg[ks] = gload((const uint4*)(brow + 32 * ks));
+            creg[ks] = gload((const uint4*)(crow + 32 * ks));
+        }
+    }
+    // x[j][p] for j = 4q + c, p = 16 wl + r16 (the A operand of walk step c)
+    uint32_t xv[4];
+    {
+        const uint16_t* xcol = x + ((size_t)b * T * H + h) * kHeadDim + 16 * wl + r16;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) xv[c] = gload(xcol + (size_t)min(4 * q + c, T - 1) * H * kHeadDim);
+    }
+    float4 hr[KS][2];
+    {
+        const float* hrow = h0 + (((size_t)b * H + h) * kHeadDim + 16 * wl + r16) * N + 8 * q;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            hr[ks][0] = gload((const float4*)(hrow + 32 * ks));
+            hr[ks][1] = gload((const float4*)(hrow + 32 * ks + 4));
+        }
+    }
+    asm volatile("" : "+s"(Ah), "+s"(Dh));  // A and D arrive while the vector loads are in flight
+
+    // ---------------------------------------------------------------- tree
+    const bool live = r16 < T;
+    const bool bad_root = r16 == 0 && par != -1;
+    const bool bad_par = r16 > 0 && live && (par < 0 || par >= r16);
+    const int st = (__ballot(bad_root) ? kStBadRoot : 0) | (__ballot(bad_par) ? kStBadParent : 0);
+    if (h == 0 && wl == 0 && lane == 0 && tree_status) tree_status[b] = st;
+    if (st) return;
+
+    // pointer jumping: after round k, nxt is the ancestor 2^k steps up (or -1),
+    // cum the sum of dt A over the nodes passed, anc the set of those nodes
+    int nxt = live ? par : -1;
+    float cum = live ? bf16_bits_to_f32(dti) * Ah : 0.f;
+    uint32_t anc = live ? 1u << r16 : 0u;
+    while (__ballot(nxt >= 0)) {
+        const int src = nxt >= 0 ? nxt : r16;
+        const float c2 = __shfl(cum, src, kWave);
+        const uint32_t a2 = (uint32_t)__shfl((int)anc, src, kWave);
+        const int n2 = __shfl(nxt, src, kWave);
+        if (nxt >= 0) {
+            cum += c2;
+            anc |= a2;
+            nxt = n2;
+        }
+    }
+    float cumj[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) cumj[c] = __shfl(cum, 4 * q + c, kWave);
+
+    // ---------------------------------------------------------------- pair scores
+    // gt[c] = G_ij for i = r16, j = 4q + c (A operand: B rows j, B operand: C rows i)
+    f32x4 gt = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        gt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, breg[ks]),
+                                                     __builtin_bit_cast(bf16x8, creg[ks]), gt, 0, 0, 0);
+
+    // ---------------------------------------------------------------- walk term
+    // S_ij = G_ij exp(cum_i - cum_j) dt_j (+ D for j = i) on ancestors j of i,
+    // 0 elsewhere; tw = x^T S^T: row p of the slice, column i
+    f32x4 tw = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int j = 4 * q + c;
+        const float sij = ((anc >> j) & 1u)
+                              ? gt[c] * __expf(cum - cumj[c]) * bf16_bits_to_f32(dtj[c]) + (j == r16 ? Dh : 0.f)
+                              : 0.f;
+        tw = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_bits_to_f32(xv[c]), sij, tw, 0, 0, 0);
+    }
+
+    // ---------------------------------------------------------------- read-out
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        bf16x8 hi, lo;
+        split_hi_lo(hr[ks][0], hr[ks][1], hi, lo);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, __builtin_bit_cast(bf16x8, creg[ks]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, __builtin_bit_cast(bf16x8, creg[ks]), acc, 0, 0, 0);
+    }
+
+    if (live) {
+        const float sc = __expf(cum);
+        const uint32_t o01 = pack_bf16x2(acc[0] * sc + tw[0], acc[1] * sc + tw[1]);
+        const uint32_t o23 = pack_bf16x2(acc[2] * sc + tw[2], acc[3] * sc + tw[3]);
+        *(uint2*)(y + (((size_t)b * T + r16) * H + h) * kHeadDim + 16 * wl + 4 * q) = make_uint2(o01, o23);
+    }
+}
+
+bool verify_tiny_supported(int T) { return T <= kTinyNodes; }
+
+hipError_t launch_verify_tiny(const VerifyArgs& a, hipStream_t stream) {
+    const void* k = a.N == 64 ? (const void*)verify_tiny_kernel<2> : (const void*)verify_tiny_kernel<4>;
+    dim3 grid((unsigned)(a.batch * a.H * 4));
+    void* args[] = {(void*)&a.x, (void*)&a.dt, (void*)&a.A, (void*)&a.B, (void*)&a.C, (void*)&a.D,
+                    (void*)&a.h0, (void*)&a.parent, (void*)&a.y, (void*)&a.tree_status,
+                    (void*)&a.T, (void*)&a.H, (void*)&a.G};
+    return hipLaunchKernel(k, grid, dim3(kWave), args, 0, stream);
+}
+
+}  // namespace tsv

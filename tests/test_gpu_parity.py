@@ -107,6 +107,46 @@ def test_tree_info_invalid_items(bnd, oracle_mod):
     assert (d.cpu().numpy()[1:] == -5).all() and (a.cpu().numpy()[1:] == -5).all()
 
 
+TINY = [(1, 128, 1, "chain"), (2, 64, 1, "chain"), (7, 128, 2, "binary"), (11, 64, 1, "recursive"),
+        (15, 128, 1, "recursive"), (15, 128, 2, "binary"), (16, 64, 2, "chain"), (16, 128, 1, "star")]
+
+
+@pytest.mark.parametrize("T,N,G,tree", TINY)
+def test_tiny_tree_kernel(bnd, oracle_mod, T, N, G, tree):
+    """Trees of at most 16 nodes take the one-wave kernel by default (outputs
+    written into NaN-filled buffers); the 64-node small-tree kernel, forced,
+    meets the same bar on the same inputs."""
+    import torch
+    inp = W.make_custom(900 + 17 * T + N + G, batch=3, n_nodes=T, n_heads=6, head_dim=64, d_state=N,
+                        n_groups=G, dtype=W.BF16, tree=tree, max_depth=min(T, 5), max_path_len=T)
+    dev = bnd.to_device(inp)
+    y_nan = torch.full_like(dev["x"], float("nan"))
+    check_full(bnd, oracle_mod, inp, W.BF16, f"tiny T={T} {tree}", y=y_nan)
+    assert torch.isfinite(y_nan.float()).all()
+    check_full(bnd, oracle_mod, inp, W.BF16, f"tiny T={T} {tree} small kernel", force_small=True)
+
+
+def test_tiny_tree_invalid_items_untouched(bnd, oracle_mod):
+    import torch
+    inp = W.make_custom(77, batch=4, n_nodes=12, n_heads=4, head_dim=64, d_state=128, n_groups=2,
+                        dtype=W.BF16, max_depth=4)
+    inp["parent"][1, 0] = 2        # bad root
+    inp["parent"][2, 9] = 9        # own parent
+    inp["parent"][3, 4] = -3       # negative parent
+    dev = bnd.to_device(inp)
+    sentinel = torch.full_like(dev["x"], 1232.0)
+    st = torch.full((4,), -1, dtype=torch.int32, device="cuda")
+    say("[verify] tiny-tree invalid items")
+    y = run_verify(bnd, dev, y=sentinel, tree_status=st)
+    torch.cuda.synchronize()
+    assert st.cpu().tolist() == [0, 1, 2, 2]
+    yc = y.float().cpu()
+    assert (yc[1:] == 1232.0).all()
+    good = [(0, h) for h in range(4)]
+    ref, _ = oracle_mod.verify(inp, W.BF16, good)
+    assert slice_err(gpu_y_slices(y, good), ref) <= TOL[W.BF16]
+
+
 RAGGED = [(1, 128, 1), (5, 64, 1), (16, 128, 2), (17, 128, 1), (31, 64, 2), (33, 128, 1),
           (64, 64, 1), (65, 128, 2), (100, 64, 1), (129, 128, 1), (200, 64, 2), (256, 128, 1)]
 
@@ -153,7 +193,7 @@ def test_heads_per_block_bitwise_invariant(bnd, T):
         for hb in (1, 2, 4, 5, 10, 20):
             say(f"[verify] T={T} heads_per_block={hb} rep {rep}")
             y = torch.full_like(dev["x"], float("nan"))
-            run_verify(bnd, dev, heads_per_block=hb, y=y)
+            run_verify(bnd, dev, heads_per_block=hb, y=y, force_small=T <= 16)
             y = y.view(torch.int16).cpu()
             ref = y if ref is None else ref
             assert torch.equal(y, ref), (T, hb, rep)
