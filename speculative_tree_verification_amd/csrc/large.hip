@@ -168,7 +168,7 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const float* __restrict__ A,
     const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm, const float* __restrict__ D,
     const float* __restrict__ h0, const int32_t* __restrict__ parent, uint16_t* __restrict__ y,
-    int32_t* __restrict__ tree_status, int T, int H, int G) {
+    int32_t* __restrict__ tree_status, int T, int H, int G, int S) {
     constexpr int P = 64, N = 32 * KS, NW = kLargeWaves;
     constexpr int RH = N + 8;  // row stride (bf16) of the h0 planes
     __shared__ int s_par[kMaxNodesLarge];
@@ -184,28 +184,51 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
     __shared__ unsigned long long s_bits[NW][kMaxNodesLarge / 64];  // ancestors flagged this pass
     __shared__ uint16_t s_J[NW][16 * kLmDist];
 
-    const int b = blockIdx.x / H;
-    const int h = blockIdx.x % H;
+    // logical block = (b H + h) S + part: the S work-groups of one (item, head)
+    // take every S-th node tile (shallow and deep ones alike) and share an XCD,
+    // so that h0 is fetched into one L2
+    const int lb = xcd_block(blockIdx.x, gridDim.x);
+    const int part = lb % S;
+    const int b = lb / S / H;
+    const int h = lb / S % H;
     const int g = h / (H / G);
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int l16 = lane & 15, q4 = lane >> 4;
-    const int st = load_tree(parent + (size_t)b * T, T, s_par);
-    if (h == 0 && tid == 0 && tree_status) tree_status[b] = st;
+    // the parents, this thread's step size and its share of h0 leave together
+    // (one thread per node, T <= 1024 = threads), so the tree check and the
+    // pointer jumping overlap the other two round trips
+    const int par_i = load_parent(parent + (size_t)b * T, T);
+    const uint32_t dt_i = gload(dt + ((size_t)b * T + min(tid, T - 1)) * H + h);
+    constexpr int HF4 = P * N / 4 / kLargeThreads;  // float4 of h0 per thread
+    static_assert(P * N % (4 * kLargeThreads) == 0, "h0 must split evenly over the threads");
+    float4 hv[HF4];
+    const float4* H0 = (const float4*)(h0 + ((size_t)b * H + h) * P * N);
+#pragma unroll
+    for (int m = 0; m < HF4; ++m) hv[m] = gload(H0 + tid + kLargeThreads * m);
+    const int st = check_tree(par_i, T, s_par);
+    if (h == 0 && part == 0 && tid == 0 && tree_status) tree_status[b] = st;
     if (st) return;
     tree_depth(s_par, T, s_nxt, s_dep);
 
     const float Ah = A[h];
     const float Dh = D[h];
-    for (int i = tid; i < T; i += kLargeThreads) s_a[i] = bf16_bits_to_f32(dt[((size_t)b * T + i) * H + h]);
-    const float* H0 = h0 + ((size_t)b * H + h) * P * N;
-    for (int e = tid; e < P * N; e += kLargeThreads) {
+    if (tid < T) s_a[tid] = bf16_bits_to_f32(dt_i);
+#pragma unroll
+    for (int m = 0; m < HF4; ++m) {
+        const int e = 4 * (tid + kLargeThreads * m);  // 4 consecutive n of row p
         const int p = e / N, n = e - p * N;
-        const float v = H0[e];
-        const __bf16 hb = (__bf16)v;
-        s_h0h[p * RH + n] = __builtin_bit_cast(uint16_t, hb);
-        s_h0l[p * RH + n] = f32_to_bf16_bits(v - (float)hb);
+        const float v[4] = {hv[m].x, hv[m].y, hv[m].z, hv[m].w};
+        uint16_t hb[4], lb[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const __bf16 t = (__bf16)v[k];
+            hb[k] = __builtin_bit_cast(uint16_t, t);
+            lb[k] = f32_to_bf16_bits(v[k] - (float)t);
+        }
+        *(uint2*)&s_h0h[p * RH + n] = make_uint2(hb[0] | ((uint32_t)hb[1] << 16), hb[2] | ((uint32_t)hb[3] << 16));
+        *(uint2*)&s_h0l[p * RH + n] = make_uint2(lb[0] | ((uint32_t)lb[1] << 16), lb[2] | ((uint32_t)lb[3] << 16));
     }
     for (int e = tid; e < NW * kMaxNodesLarge / 64; e += kLargeThreads) (&s_bits[0][0])[e] = 0ull;
     __syncthreads();
@@ -213,8 +236,8 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
     const size_t xrow = (size_t)H * P;  // x / y stride between nodes
     const uint16_t* xb = x + ((size_t)b * T * H + h) * P;
     uint16_t* yb = y + ((size_t)b * T * H + h) * P;
-    for (int ti = w; 16 * ti < T; ti += NW) {
-        const int i0 = 16 * ti;
+    for (int tt = w; 16 * (tt * S + part) < T; tt += NW) {
+        const int i0 = 16 * (tt * S + part);
         // C rows of the tile: node i0 + l16, columns 32 ks + 8 q4 ..
         bf16x8 cf[KS];
         const uint16_t* crow = Cm + (((size_t)b * T + min(i0 + l16, T - 1)) * G + g) * N;
@@ -337,19 +360,41 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
     }
 }
 
+// Work-groups per (item, head) of the MFMA kernel: a work-group fills a
+// compute unit, so the launch runs in rounds of one work-group per unit. Each
+// of the S parts takes every S-th 16-node tile (at least one per wave) and
+// repeats the cheap set-up (tree, depth, h0 planes); S is the split that
+// gives the shortest rounds-times-work estimate, ceil(units S / CUs) / S.
+static int large_split(int units, int T) {
+    int cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    const int tiles = (T + 15) / 16;
+    int best = 1;
+    double best_cost = 1e30;
+    for (int S = 1; S <= 8 && S * kLargeWaves <= tiles; S *= 2) {
+        const double cost = (double)((long)units * S + cus - 1) / cus / S + 0.02 * S;
+        if (cost < best_cost) best_cost = cost, best = S;
+    }
+    return best;
+}
+
 hipError_t launch_verify_large(const VerifyArgs& a, bool bf16, hipStream_t stream) {
     dim3 grid((unsigned)(a.batch * a.H));
     if (bf16 && a.P == 64 && (a.N == 64 || a.N == 128)) {
+        const int S = large_split(a.batch * a.H, a.T);
+        dim3 gs((unsigned)(a.batch * a.H * S));
         if (a.N == 128)
-            hipLaunchKernelGGL(verify_large_mfma_kernel<4>, grid, dim3(kLargeThreads), 0, stream,
+            hipLaunchKernelGGL(verify_large_mfma_kernel<4>, gs, dim3(kLargeThreads), 0, stream,
                                (const uint16_t*)a.x, (const uint16_t*)a.dt, a.A, (const uint16_t*)a.B,
                                (const uint16_t*)a.C, a.D, a.h0, a.parent, (uint16_t*)a.y,
-                               a.tree_status, a.T, a.H, a.G);
+                               a.tree_status, a.T, a.H, a.G, S);
         else
-            hipLaunchKernelGGL(verify_large_mfma_kernel<2>, grid, dim3(kLargeThreads), 0, stream,
+            hipLaunchKernelGGL(verify_large_mfma_kernel<2>, gs, dim3(kLargeThreads), 0, stream,
                                (const uint16_t*)a.x, (const uint16_t*)a.dt, a.A, (const uint16_t*)a.B,
                                (const uint16_t*)a.C, a.D, a.h0, a.parent, (uint16_t*)a.y,
-                               a.tree_status, a.T, a.H, a.G);
+                               a.tree_status, a.T, a.H, a.G, S);
         return hipGetLastError();
     }
     const bool lds = a.P * (((a.N + 3) & ~3) + 4) <= kLargeH0Lds;
