@@ -87,7 +87,9 @@ typedef struct {
     int32_t flags;           /* TSV_FLAG_* (0 = automatic choice) */
     int32_t heads_per_block; /* launch hint: heads one work-group handles for the
                                 MFMA verify kernel; 0 = automatic. Must divide
-                                H / G when given. */
+                                H / G when given. The tiny-tree kernel
+                                (T <= 16) takes one head_dim slice per
+                                work-group and ignores it. */
 } tsv_shape;
 
 /*
