@@ -99,8 +99,8 @@ def verify_flops(B, T, H, P, N, G, pairs):
 
 
 KERNEL_SOURCES = {
-    "verify": ("api.hip", "launch.hpp", "common.hpp", "verify_common.hpp", "verify_mfma.hip",
-               "verify_wide.hip", "verify_generic.hip"),
+    "verify": ("api.hip", "launch.hpp", "common.hpp", "verify_common.hpp", "verify_tiny.hip",
+               "verify_mfma.hip", "verify_wide.hip", "verify_generic.hip"),
     "commit": ("api.hip", "launch.hpp", "common.hpp", "commit.hip"),
 }
 
