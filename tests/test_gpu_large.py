@@ -81,6 +81,31 @@ def test_large_tree_parity(bnd, oracle_mod, T, H, P, N, G, dtype, tree, depth, l
     check(bnd, oracle_mod, inp, dtype, tree)
 
 
+def test_large_workload_full_size_sampled(bnd, oracle_mod):
+    """The 1023-node workload the benchmark times (batch 4, 80 heads, complete
+    binary trees, each (item, head) split over four work-groups), on sampled
+    (item, head) slices the oracle computes one by one."""
+    import torch
+    inp = W.make_custom(23, batch=4, n_nodes=1023, n_heads=80, head_dim=64, d_state=128, n_groups=1,
+                        dtype=W.BF16, tree="binary", max_path_len=10)
+    rng = np.random.default_rng(45)
+    sel = sorted({(int(rng.integers(0, 4)), int(rng.integers(0, 80))) for _ in range(10)} | {(0, 0), (3, 79)})
+    dev = bnd.to_device(inp)
+    say("[large] full-size workload B=4 T=1023 H=80")
+    st = torch.full((4,), -7, dtype=torch.int32, device="cuda")
+    y = torch.full_like(dev["x"], float("nan"))
+    run_verify(bnd, dev, y=y, tree_status=st)
+    h = run_commit(bnd, dev, tree_status=st)
+    torch.cuda.synchronize()
+    assert st.cpu().tolist() == [0] * 4
+    assert torch.isfinite(y.float()).all()
+    ref, _ = oracle_mod.verify(inp, W.BF16, sel)
+    href, _ = oracle_mod.commit(inp, W.BF16, sel)
+    err, herr = slice_err(gpu_y_slices(y, sel), ref), slice_err(gpu_h_slices(h, sel), href)
+    say(f"    verify err {err:.3e}  commit err {herr:.3e}")
+    assert err <= TOL[W.BF16] and herr <= COMMIT_TOL, (err, herr)
+
+
 def test_large_invalid_items_untouched(bnd, oracle_mod):
     import torch
     inp = W.make_custom(91, batch=5, n_nodes=400, n_heads=2, head_dim=32, d_state=16, n_groups=1,
