@@ -468,7 +468,7 @@ __global__ __launch_bounds__(kBlock) void gdn_commit_kernel(
     int st = 0;
 #pragma unroll
     for (int w = 0; w < kBlock / kWave; ++w) st |= s_bad[w];
-    if (st & (kStBadRoot | kStBadParent)) st &= ~kStBadPath;  // a path is judged on a valid tree only
+    if (st & (kStBadRoot | kStBadParent)) st &= ~kStBadPath;  // a path is checked on a valid tree only
     if (h == 0 && grp == 0 && tid == 0 && tree_status) tree_status[b] = st;
     if (st || len == 0) return;
 
