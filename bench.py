@@ -98,6 +98,15 @@ def verify_flops(B, T, H, P, N, G, pairs):
     return 2 * B * H * T * N * P + 2 * N * G * npairs + 2 * P * H * npairs
 
 
+def mfma_report(flops, us, nbytes):
+    """A verify launch's algorithmic flops over its average duration, against
+    the dense bf16 MFMA peak."""
+    tf = flops / (us * 1e-6) / 1e12
+    return {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / PEAK_BF16_TFLOPS, 5), "algorithmic_flops": int(flops),
+            "intensity_flop_per_byte": round(flops / nbytes, 2)}
+
+
 KERNEL_SOURCES = {
     "verify": ("api.hip", "launch.hpp", "common.hpp", "verify_common.hpp", "verify_tiny.hip",
                "verify_mfma.hip", "verify_wide.hip", "verify_generic.hip"),
@@ -456,6 +465,8 @@ def large_timing(torch, bnd, W, rounds, oracle_seconds=0.0):
         gbs = nbytes[name] / (us * 1e-6) / 1e9
         out[name] = {"avg_us": round(us, 3), "algorithmic_bytes": nbytes[name], "achieved": round(gbs, 1),
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    out["verify"]["mfma"] = mfma_report(verify_flops(B, T, H, P, N, G, ancestor_pairs(base["parent"])),
+                                        out["verify"]["avg_us"], nbytes["verify"])
     out["nodes_per_s"] = round(B * T * H / ((out["verify"]["avg_us"] + out["commit"]["avg_us"]) * 1e-6), 1)
     del sets, pv, pc
     torch.cuda.empty_cache()
@@ -538,11 +549,7 @@ def run_workload(torch, bnd, W, cid, steps, warmup, hpb, keep_host):
     name = wl.cfg.name
     v = kernel_report("verify", t["verify_us"], vb, name, source_sha("verify"), t["verify_launches"])
     B, T, H, P, N, G = wl.dims
-    fl = verify_flops(B, T, H, P, N, G, wl.pairs)
-    tf = fl / (t["verify_us"] * 1e-6) / 1e12
-    v["mfma"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                 "frac": round(tf / PEAK_BF16_TFLOPS, 5), "algorithmic_flops": int(fl),
-                 "intensity_flop_per_byte": round(fl / vb, 2)}
+    v["mfma"] = mfma_report(verify_flops(B, T, H, P, N, G, wl.pairs), t["verify_us"], vb)
     c = kernel_report("commit", t["commit_us"], cb, name, source_sha("commit"), t["commit_launches"])
     t["accept"] = accept_timing(torch, bnd, W, wl, steps)
     nodes_s = wl.nodes_per_step / (t["ms_per_step"] * 1e-3)
