@@ -363,8 +363,10 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
 // Work-groups per (item, head) of the MFMA kernel: a work-group fills a
 // compute unit, so the launch runs in rounds of one work-group per unit. Each
 // of the S parts takes every S-th 16-node tile (at least one per wave) and
-// repeats the cheap set-up (tree, depth, h0 planes); S is the split that
-// gives the shortest rounds-times-work estimate, ceil(units S / CUs) / S.
+// repeats the set-up (tree, depth, h0 planes), which costs about a fifth of
+// an unsplit work-group's tile work on the 1023-node trees. S minimises
+// rounds x (set-up + tile work / S) = ceil(units S / CUs) (0.2 + 1 / S).
+constexpr double kLargeSetupShare = 0.2;
 static int large_split(int units, int T) {
     int cus = 0, dev = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
@@ -374,7 +376,7 @@ static int large_split(int units, int T) {
     int best = 1;
     double best_cost = 1e30;
     for (int S = 1; S <= 8 && S * kLargeWaves <= tiles; S *= 2) {
-        const double cost = (double)((long)units * S + cus - 1) / cus / S + 0.02 * S;
+        const double cost = (double)(((long)units * S + cus - 1) / cus) * (kLargeSetupShare + 1.0 / S);
         if (cost < best_cost) best_cost = cost, best = S;
     }
     return best;

@@ -83,7 +83,7 @@ def test_large_tree_parity(bnd, oracle_mod, T, H, P, N, G, dtype, tree, depth, l
 
 def test_large_workload_full_size_sampled(bnd, oracle_mod):
     """The 1023-node workload the benchmark times (batch 4, 80 heads, complete
-    binary trees, each (item, head) split over four work-groups), on sampled
+    binary trees, each (item, head) split over two work-groups), on sampled
     (item, head) slices the oracle computes one by one."""
     import torch
     inp = W.make_custom(23, batch=4, n_nodes=1023, n_heads=80, head_dim=64, d_state=128, n_groups=1,
