@@ -242,6 +242,36 @@ def sleep_cycles_for(torch, ms):
     return int(ms / per)
 
 
+WARM_MS = 30.0  # GPU time of the untimed burst ahead of each timed region
+
+
+def timed_region(torch, fn, rounds):
+    """Average ms per call over `rounds` back-to-back calls fn(0), fn(1), ...,
+    timed with one HIP event pair. An untimed burst of the same calls, about
+    WARM_MS of GPU time, goes first: under it the GPU settles into the clock
+    and power state it keeps under this load (a GPU left idle, or spinning in
+    a sleep kernel, starts the region in a transient that runs several percent
+    slower for the first few milliseconds), and the host enqueues the timed
+    calls while the burst still runs, so the region measures GPU execution."""
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(3):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    per_call = max(e0.elapsed_time(e1) / 3, 1e-3)
+    for i in range(max(3, int(WARM_MS / per_call) + 1)):
+        fn(i)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(rounds):
+        fn(i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / rounds
+
+
 def graph_step_timing(torch, bnd, wl, steps):
     """The same step captured once per rotating input set as a HIP graph (the
     launches re-pointed at a side stream for the capture), replayed `steps`
@@ -268,25 +298,16 @@ def graph_step_timing(torch, bnd, wl, steps):
         graphs.append(g)
         keep.append((vc, cc))
     torch.cuda.synchronize()
-    for i in range(2 * len(graphs)):
-        graphs[i % len(graphs)].replay()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(sleep_cycles_for(torch, 2.0))
-    start.record()
-    for i in range(steps):
-        graphs[i % len(graphs)].replay()
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
+    ms = timed_region(torch, lambda i: graphs[i % len(graphs)].replay(), steps)
     del graphs, keep
     return ms
 
 
 def time_steps(torch, wl, steps, warmup):
-    """Warm up, then time exactly `steps` steps with HIP events; the stream is
-    pre-loaded with a spin kernel so the host enqueues ahead of the GPU and the
-    region measures GPU execution of back-to-back launches.
+    """Warm up, then time exactly `steps` steps with HIP events (see
+    timed_region: an untimed burst of the same steps runs first, so the region
+    measures back-to-back launches in the GPU's steady state under this load,
+    with the host enqueueing ahead).
 
     The average launch duration of each kernel comes from two further timed
     regions of the same kind: the step's verify launches alone, then its commit
@@ -302,29 +323,20 @@ def time_steps(torch, wl, steps, warmup):
     host_per_step = min(host_t) if host_t else 5e-3
 
     def region(fn, rounds):
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()  # barrier (one rank) + synchronize before the timed region
-        torch.cuda._sleep(sleep_cycles_for(torch, 1.5e3 * host_per_step * rounds + 20.0))
-        start.record()
-        t_host = time.perf_counter()
-        for i in range(rounds):
-            fn(i % wl.n_sets)
-        end.record()
-        t_host = time.perf_counter() - t_host
-        torch.cuda.synchronize()
-        return start.elapsed_time(end), t_host
+        # barrier (one rank) + synchronize on both sides of the timed region
+        return timed_region(torch, lambda i: fn(i % wl.n_sets), rounds) * rounds
 
-    ms, t_host = region(wl.step, steps)
+    ms = region(wl.step, steps)
     nv, nc = len(wl.verify_calls[0]), len(wl.commit_calls[0])
 
     def run_all(calls):
         for f in calls:
             f()
 
-    v_ms, _ = region(lambda s: run_all(wl.verify_calls[s]), steps)
-    c_ms, _ = region(lambda s: run_all(wl.commit_calls[s]), steps)
+    v_ms = region(lambda s: run_all(wl.verify_calls[s]), steps)
+    c_ms = region(lambda s: run_all(wl.commit_calls[s]), steps)
     return dict(ms_per_step=ms / steps, verify_us=v_ms * 1e3 / (steps * nv),
-                commit_us=c_ms * 1e3 / (steps * nc), host_ms=1e3 * t_host / steps,
+                commit_us=c_ms * 1e3 / (steps * nc), host_ms=1e3 * host_per_step,
                 verify_launches=nv, commit_launches=nc)
 
 
@@ -407,15 +419,7 @@ def gdn_timing(torch, bnd, W, rounds, oracle_seconds=0.0):
     for name, fn in (("verify", ver), ("commit", com)):
         for d in sets:
             fn(d)
-        torch.cuda.synchronize()
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(sleep_cycles_for(torch, 2.0))
-        start.record()
-        for r in range(rounds):
-            fn(sets[r % nsets])
-        end.record()
-        torch.cuda.synchronize()
-        us = start.elapsed_time(end) * 1e3 / rounds
+        us = timed_region(torch, lambda r: fn(sets[r % nsets]), rounds) * 1e3
         gbs = nbytes[name] / (us * 1e-6) / 1e9
         out[name] = {"avg_us": round(us, 3), "algorithmic_bytes": nbytes[name], "achieved": round(gbs, 1),
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
@@ -453,15 +457,7 @@ def large_timing(torch, bnd, W, rounds, oracle_seconds=0.0):
     for name, fns in (("verify", pv), ("commit", pc)):
         for f in fns:
             f()
-        torch.cuda.synchronize()
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(sleep_cycles_for(torch, 2.0))
-        start.record()
-        for r in range(rounds):
-            fns[r % nsets]()
-        end.record()
-        torch.cuda.synchronize()
-        us = start.elapsed_time(end) * 1e3 / rounds
+        us = timed_region(torch, lambda r: fns[r % nsets](), rounds) * 1e3
         gbs = nbytes[name] / (us * 1e-6) / 1e9
         out[name] = {"avg_us": round(us, 3), "algorithmic_bytes": nbytes[name], "achieved": round(gbs, 1),
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
