@@ -252,7 +252,9 @@ def timed_region(torch, fn, rounds):
     and power state it keeps under this load (a GPU left idle, or spinning in
     a sleep kernel, starts the region in a transient that runs several percent
     slower for the first few milliseconds), and the host enqueues the timed
-    calls while the burst still runs, so the region measures GPU execution."""
+    calls while the burst still runs, so the region measures GPU execution.
+    Where one call takes the host about as long to enqueue as the GPU to run,
+    a sleep kernel of the region's enqueue time goes between the two."""
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -261,8 +263,16 @@ def timed_region(torch, fn, rounds):
     e1.record()
     torch.cuda.synchronize()
     per_call = max(e0.elapsed_time(e1) / 3, 1e-3)
-    for i in range(max(3, int(WARM_MS / per_call) + 1)):
+    nwarm = max(3, int(WARM_MS / per_call) + 1)
+    t0 = time.perf_counter()
+    for i in range(nwarm):
         fn(i)
+    host_ms = (time.perf_counter() - t0) * 1e3 / nwarm
+    if host_ms > 0.8 * per_call:
+        # the host enqueues a call about as slowly as the GPU runs it: a short
+        # sleep kernel, sized to the enqueue time of the region, lets it get
+        # ahead (the GPU idles only that long)
+        torch.cuda._sleep(sleep_cycles_for(torch, 1.3 * host_ms * rounds + 0.5))
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(rounds):
