@@ -110,3 +110,40 @@ def test_status_bits():
     assert st.tolist() == [0, 1, 2, 4]
     for b in (1, 2, 3):
         assert np.array_equal(S[b], d["S0"][b])
+
+
+def test_gate_and_step_together_by_hand():
+    """Gate and step both active, values worked out by hand ("TreeWY", fugumt
+    page, abstract, read as the gated delta rule of Gated DeltaNet: the decay
+    multiplies the erased old state, the write beta v k^T is not decayed).
+    Two-node chain, dk = dv = 2:
+      node 0: S0 = [[1, 2], [3, 4]], k = (1, 0), v = (2, 6), q = (1, 1),
+              g = ln(1/2), beta = 1/2.
+              S0 (I - beta k k^T) = [[0.5, 2], [1.5, 4]]; times exp(g) = 1/2 gives
+              [[0.25, 1], [0.75, 2]]; plus beta v k^T = [[1, 0], [3, 0]]:
+              S1 = [[1.25, 1], [3.75, 2]], o_0 = S1 q = (2.25, 5.75).
+      node 1: k = (0, 1), v = (1, 1), q = (1, 0), g = 0, beta = 1 (the write
+              replaces the state's response to k): S1 diag(1, 0) = [[1.25, 0],
+              [3.75, 0]] plus v k^T = [[0, 1], [0, 1]]: S2 = [[1.25, 1], [3.75, 1]],
+              o_1 = S2 q = (1.25, 3.75).
+    Decaying the write as well would give S1 = [[0.75, 1], [2.25, 2]]; erasing
+    with the opposite sign [[1.75, 1], [5.25, 2]]; erasing from the left
+    (I - beta k k^T) S0 [[1.25, 0.5], [4.5, 2]]; each fails here."""
+    q = np.array([[1.0, 1.0], [1.0, 0.0]]).reshape(1, 2, 1, 2)
+    k = np.array([[1.0, 0.0], [0.0, 1.0]]).reshape(1, 2, 1, 2)
+    v = np.array([[2.0, 6.0], [1.0, 1.0]]).reshape(1, 2, 1, 2)
+    g = np.array([np.log(0.5), 0.0]).reshape(1, 2, 1)
+    beta = np.array([0.5, 1.0]).reshape(1, 2, 1)
+    S0 = np.array([[1.0, 2.0], [3.0, 4.0]]).reshape(1, 1, 2, 2)
+    parent = np.array([[-1, 0]], np.int32)
+    o, st = O.verify_unrolled(q, k, v, g, beta, S0, parent)
+    assert not st.any()
+    assert np.allclose(o[0, 0, 0], [2.25, 5.75], rtol=0, atol=1e-14)
+    assert np.allclose(o[0, 1, 0], [1.25, 3.75], rtol=0, atol=1e-14)
+    for n, want in ((1, [[1.25, 1.0], [3.75, 2.0]]), (2, [[1.25, 1.0], [3.75, 1.0]])):
+        acc = np.array([[0, 1]], np.int32)
+        S, st = O.commit_unrolled(k, v, g, beta, S0, parent, acc, np.array([n], np.int32))
+        assert not st.any()
+        assert np.allclose(S[0, 0], want, rtol=0, atol=1e-14), n
+    ow, _ = O.verify_wy(q, k, v, g, beta, S0, parent)
+    assert np.allclose(ow[0, :, 0], [[2.25, 5.75], [1.25, 3.75]], rtol=0, atol=1e-13)
