@@ -12,10 +12,11 @@
 // its layer's operand pointers from the caller's table. The path indices and
 // the parents leave first (the accepted row without waiting for its length),
 // then the state chunk; the tree and the path are validated bit-exactly from
-// LDS; then dt, x and B of the path rows are staged
-// in one more round trip (two in all for paths of up to 16 entries). The state
-// is streamed once: each element is read and written by the same thread
-// (rank-L update in registers). Invalid items leave h0 untouched.
+// LDS behind LDS-only barriers, so dt, x and B of the path rows are requested
+// while the state chunk is still in flight (their round trip overlaps the
+// state's). The state is streamed once: each element is read and written by
+// the same thread (rank-L update in registers). Invalid items leave h0
+// untouched.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -35,6 +36,7 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
     __shared__ int s_path[kMaxNodes];
     __shared__ float s_w[kMaxNodes];
     __shared__ float s_w0;
+    __shared__ int s_red[kBlock / kWave];
     // [kPathChunk][P] x rows, then [kPathChunk][N] B rows, of the path
     extern __shared__ __attribute__((aligned(16))) float s_dyn[];
     float* s_wx = s_dyn;
@@ -97,7 +99,9 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
     // len <= T (this also keeps every path index inside s_path)
     const bool len_ok = len >= 0 && len <= Lmax && len <= T;
     if (len_ok && tid < len) s_path[tid] = acc_i;
-    int st = check_tree(par_i, T, s_par);  // barrier: s_path visible too
+    // LDS-only barriers from here on: the state chunk stays in flight while the
+    // tree and path are checked and the path rows are requested
+    int st = check_tree_lds<kBlock>(par_i, T, s_par, s_red);  // barrier: s_path visible too
     int bad_path = 0;
     if (!st) {
         if (!len_ok) {
@@ -110,7 +114,7 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
                 bad_path = node < 0 || node >= T || s_par[node] != s_path[tid - 1];
         }
     }
-    if (__syncthreads_or(bad_path)) st |= kStBadPath;
+    if (lds_sync_or<kBlock>(bad_path, s_red)) st |= kStBadPath;
     if (layer == 0 && hd == 0 && chunk == 0 && tid == 0 && tree_status) tree_status[b] = st;
     if (st || len == 0) return;
 
@@ -155,10 +159,10 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
     };
     for (int k0 = 0; k0 < len; k0 += kPathChunk) {
         const int kn = min(kPathChunk, len - k0);
-        if (k0 > 0) __syncthreads();  // previous chunk consumed
+        if (k0 > 0) lds_barrier();  // previous chunk consumed
         if (k0 == 0 && tid < len) s_w[tid] = Elem<TIO>::ld(dt, ((size_t)b * T + s_path[tid]) * H + hd);
         stage_rows(k0, kn);
-        __syncthreads();
+        lds_barrier();
         if (k0 == 0) {
             // decay weights along the path: w_k = exp(c_{k+1}) dt_{j_k}, w0 = exp(c_0)
             if (tid == 0) {
@@ -170,7 +174,7 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
                 }
                 s_w0 = expf(c);
             }
-            __syncthreads();
+            lds_barrier();
             const float w0 = s_w0;
 #pragma unroll
             for (int v = 0; v < kVec; ++v)
@@ -179,7 +183,7 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
         }
         // weight the staged x rows in place
         for (int e = tid; e < kn * P; e += kBlock) s_wx[e] *= s_w[k0 + e / P];
-        __syncthreads();
+        lds_barrier();
         if (VEC && (kBlock * 4) % N == 0 && pe[kVec - 1] < PN) {
             // every float4 of this thread covers the same columns n .. n+3 of
             // its own row p_v: one B read per path entry serves all of them,

@@ -75,6 +75,15 @@ template <>
 __device__ __forceinline__ void gstore(float4* p, const float4& v) {
     *(gf32x4 __attribute__((address_space(1)))*)p = gf32x4{v.x, v.y, v.z, v.w};
 }
+typedef uint32_t gu32x2 __attribute__((ext_vector_type(2)));
+template <>
+__device__ __forceinline__ void gstore(uint2* p, const uint2& v) {
+    *(gu32x2 __attribute__((address_space(1)))*)p = gu32x2{v.x, v.y};
+}
+template <>
+__device__ __forceinline__ void gstore(uint4* p, const uint4& v) {
+    *(gu32x4 __attribute__((address_space(1)))*)p = gu32x4{v.x, v.y, v.z, v.w};
+}
 
 // element access for the two input dtypes (float, or bf16 stored as uint16_t)
 template <typename TIO>
@@ -124,9 +133,28 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// OR of p over the NT threads of the block, with LDS-only barriers: global
+// loads still in flight are not waited for (a __syncthreads-based reduction
+// carries a work-group release fence, which on gfx9 waits for every
+// outstanding vector memory operation, loads included). `s_red` holds at least
+// NT/64 ints of LDS.
+template <int NT>
+__device__ __forceinline__ int lds_sync_or(int p, int* s_red) {
+    const int wave = threadIdx.x / kWave;
+    const int any = __ballot(p) != 0ull;
+    if ((threadIdx.x & (kWave - 1)) == 0) s_red[wave] = any;
+    lds_barrier();
+    int r = 0;
+#pragma unroll
+    for (int w = 0; w < NT / kWave; ++w) r |= s_red[w];
+    lds_barrier();  // s_red may be reused
+    return r;
+}
+
 // Exclusive prefix sum over the NT threads of the block. `scratch` holds at
 // least NT/64 ints of LDS. Returns the exclusive prefix; *total gets the sum.
-template <int NT = kBlock>
+// With LDS_ONLY the barriers order LDS traffic only (see lds_sync_or).
+template <int NT = kBlock, bool LDS_ONLY = false>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -137,7 +165,10 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
         if (lane >= off) incl += o;
     }
     if (lane == kWave - 1) scratch[wave] = incl;
-    __syncthreads();
+    if (LDS_ONLY)
+        lds_barrier();
+    else
+        __syncthreads();
     int base = 0, sum = 0;
 #pragma unroll
     for (int w = 0; w < NT / kWave; ++w) {
@@ -146,7 +177,10 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
         sum += t;
     }
     *total = sum;
-    __syncthreads();
+    if (LDS_ONLY)
+        lds_barrier();
+    else
+        __syncthreads();
     return base + incl - v;
 }
 
@@ -186,10 +220,72 @@ __device__ __forceinline__ int check_tree(int p, int T, int* s_par) {
     return r | (__syncthreads_or(bad_par) ? kStBadParent : 0);
 }
 
+// check_tree with LDS-only barriers: loads issued before it stay in flight.
+// `s_red` holds at least NT/64 ints of LDS.
+template <int NT>
+__device__ __forceinline__ int check_tree_lds(int p, int T, int* s_par, int* s_red) {
+    const int i = threadIdx.x;
+    int bad_root = 0, bad_par = 0;
+    if (i < T) {
+        s_par[i] = p;
+        if (i == 0)
+            bad_root = (p != -1);
+        else
+            bad_par = (p < 0 || p >= i);
+    }
+    // one reduction on the common path; a second one tells the two errors apart
+    if (!lds_sync_or<NT>(bad_root | bad_par, s_red)) return 0;
+    int r = lds_sync_or<NT>(bad_root, s_red) ? kStBadRoot : 0;
+    return r | (lds_sync_or<NT>(bad_par, s_red) ? kStBadParent : 0);
+}
+
 // load_parent + check_tree in one step.
 __device__ __forceinline__ int load_tree(const int32_t* __restrict__ parent_b, int T,
                                          int* s_par) {
     return check_tree(load_parent(parent_b, T), T, s_par);
+}
+
+// Depth of node threadIdx.x for shallow trees: each thread walks to the root
+// through the parents in LDS (no barrier per step), at most kWalkDepth steps;
+// if some node is deeper, pointer jumping takes over. All barriers are
+// LDS-only, so global loads issued earlier stay in flight. s_nxt, s_dep: LDS
+// scratch of at least T ints; s_red: NT/64 ints.
+constexpr int kWalkDepth = 16;
+template <int NT>
+__device__ __forceinline__ int tree_depth_shallow(const int* s_par, int T, int* s_nxt, int* s_dep,
+                                                  int* s_red) {
+    const int i = threadIdx.x;
+    int d = 0, j = i < T ? s_par[i] : -1;
+#pragma unroll 1
+    for (int k = 0; k < kWalkDepth && j >= 0; ++k) {
+        ++d;
+        j = s_par[j];
+    }
+    if (!lds_sync_or<NT>(j >= 0, s_red)) return i < T ? d : 0;
+    // pointer jumping: after round r every node knows its distance to the
+    // ancestor 2^r steps up
+    int nxt = -1, dep = 0;
+    if (i < T) {
+        nxt = s_par[i];
+        dep = (nxt >= 0) ? 1 : 0;
+        s_nxt[i] = nxt;
+        s_dep[i] = dep;
+    }
+    while (lds_sync_or<NT>(nxt >= 0, s_red)) {
+        int n2 = nxt, d2 = dep;
+        if (nxt >= 0) {
+            d2 = dep + s_dep[nxt];
+            n2 = s_nxt[nxt];
+        }
+        lds_barrier();
+        if (i < T) {
+            s_dep[i] = d2;
+            s_nxt[i] = n2;
+        }
+        nxt = n2;
+        dep = d2;
+    }
+    return dep;
 }
 
 // Depth (edges from the root) of node threadIdx.x by pointer jumping over the

@@ -110,19 +110,22 @@ __device__ __forceinline__ void split_hi_lo(const float4& a, const float4& b, bf
 }
 
 // Tree set-up shared by the verify kernels, run by all NT threads after the
-// tree has been validated: depth by pointer jumping, the ancestor-pair list of
+// tree has been validated: depth (walks to the root for shallow trees, else
+// pointer jumping), the ancestor-pair list of
 // every node (node i's pairs occupy [s_off[i], s_off[i] + s_dep[i] + 1), from
 // i itself up to the root; entry = i | j << 8), and the total pair count.
 // Pairs are written only when they fit in max_pairs. s_scratch needs
 // kMaxNodes ints and is clobbered.
+// All barriers are LDS-only: global loads issued before the call stay in flight.
+// s_scan holds at least NT/64 ints.
 template <int NT = kBlock>
 __device__ __forceinline__ int build_pairs(const int* s_par, int T, int* s_dep, int* s_off,
                                            int* s_scratch, int* s_scan, uint16_t* s_pair,
                                            int max_pairs) {
     const int tid = threadIdx.x;
-    const int dep = tree_depth(s_par, T, s_scratch, s_dep);
+    const int dep = tree_depth_shallow<NT>(s_par, T, s_scratch, s_dep, s_scan);
     int total;
-    const int off = block_exclusive_scan<NT>(tid < T ? dep + 1 : 0, s_scan, &total);
+    const int off = block_exclusive_scan<NT, true>(tid < T ? dep + 1 : 0, s_scan, &total);
     if (tid < T) {
         s_off[tid] = off;
         s_dep[tid] = dep;

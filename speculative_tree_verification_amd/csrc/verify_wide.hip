@@ -169,14 +169,15 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
     };
 
     // ---------------------------------------------------------------- set-up
-    // No set-up load depends on the tree, so all of them leave at once: the
-    // parents first, then the item's C and B tiles (chunk c = tid + NT m is row
-    // c / CPR, chunk column c % CPR), the step sizes of all HB heads and head 0's
-    // h0. Vector memory operations complete in order, so the tree check waits
-    // for the parents only. Head 0's x goes out right after it: while an
-    // asynchronous LDS load is in flight the compiler waits for every
-    // outstanding load at each register use, so the tree work that needs no
-    // memory comes first and overlaps the rest of the traffic.
+    // The set-up loads leave together: the parents first, then the item's C
+    // and B tiles (chunk c = tid + NT m is row c / CPR, chunk column c % CPR)
+    // and the step sizes of all HB heads, all into registers; head 0 follows
+    // the tree check. Vector memory operations complete in order and every
+    // set-up barrier is LDS-only (a __syncthreads would wait for every load in
+    // flight), so the tree check waits for the parents only, the pair scores
+    // for the B and C tiles only, and the tree work overlaps the rest of the
+    // traffic. (No asynchronous LDS load is in flight during the set-up: with
+    // one outstanding, the compiler waits for every load at each register use.)
     const int par_i = load_parent(parent + (size_t)b * T, T);
     constexpr int BC_PT = TPM * CPR / NT;                       // tile chunks per thread
     constexpr int DT_PT = (kWideMaxHeads * TPM + NT - 1) / NT;  // step sizes per thread
@@ -197,11 +198,20 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
         const int n = e / HB, hh = e - n * HB;  // consecutive threads: consecutive heads of node n
         dtr[m] = dt[((size_t)b * T + n) * H + h_first + hh];
     }
-    prefetch(h_first);
-    const int st = check_tree(par_i, T, s_par);
+    const int st = check_tree_lds<NT>(par_i, T, s_par, s_scan);
     if (h_first == 0 && tid == 0 && tree_status) tree_status[b] = st;
     if (st) return;
-    stage_x(h_first, BufC<0>{});
+    // head 0's h0 and x (16-byte chunk c = tid + NT m is row c / 8, chunk c % 8)
+    // only now: issued with the set-up loads, they queue ahead of the parents
+    // and tiles of other compute units and delay every set-up step
+    prefetch(h_first);
+    constexpr int X0_PT = TPM * 8 / NT;
+    uint4 x0r[X0_PT];
+#pragma unroll
+    for (int m = 0; m < X0_PT; ++m) {
+        const int c = tid + NT * m, r = min(c >> 3, T - 1);
+        x0r[m] = gload((const uint4*)(x + (((size_t)b * T + r) * H + h_first) * kHeadDim + 8 * (c & 7)));
+    }
     const int total_pairs = build_pairs<NT>(s_par, T, s_dep, s_off, s_scratch, s_scan, s_pair, MAXP);
     const bool cached = total_pairs <= MAXP;
     // C tile (TPM x N bf16, rows swizzled) in the h0 buffers, which are still free
@@ -231,7 +241,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
             const int c = tid + NT * m, r = c / CPR, ch = c % CPR;
             if ((ch >> 3) == pass) *(uint4*)(s_x1 + swz_off(r, ch & 7, 8, r)) = bt[m];
         }
-        __syncthreads();  // pass columns of B (and, first time, the C tile and pair lists) visible
+        lds_barrier();  // pass columns of B (and, first time, the C tile and pair lists) visible
         if (cached) {
 #pragma unroll
             for (int k = 0; k < PPT; ++k) {
@@ -251,7 +261,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
                 }
             }
         }
-        __syncthreads();  // B columns consumed
+        lds_barrier();  // B columns consumed
     }
     if (cached) {
 #pragma unroll
@@ -263,10 +273,14 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
     for (int ks = 0; ks < KS; ++ks) creg[ks] = *(const bf16x8*)(cbase + swz_off(i, 4 * ks + q, CPR, i));
     const int my_base = (i < T) ? s_off[i] : 0;
     const int my_cnt = (i < T) ? s_dep[i] + 1 : 0;
-    __syncthreads();  // C tile consumed: the h0 buffers are free
+    lds_barrier();  // C tile consumed: the h0 buffers are free
     stage_h0(0);
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's x chunks of head 0 have landed
-    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < X0_PT; ++m) {
+        const int c = tid + NT * m, r = c >> 3;
+        if (r < T) *(uint4*)(s_x0 + swz_off(r, c & 7, 8, x_key(r))) = x0r[m];
+    }
+    lds_barrier();
 
     // ---------------------------------------------------------------- heads
     const bool tile_live = 16 * tile < T;
@@ -345,20 +359,33 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_wide_kernel(
                     // entries k and k+1 of the list; entry 0 is the node itself with
                     // weight G_ii dt_i + D. The first two rows take the weights to
                     // about 16 bits, the older ancestors to bf16.
+                    // The list entries of the next pair are read while the
+                    // current pair's rows are in flight, so each step waits for
+                    // one LDS round trip rather than two.
+                    const int last = my_cnt - 1;
+                    int pr0 = s_pair[my_base], pr1 = s_pair[my_base + min(1, last)];
+                    float g0 = s_G[my_base], g1 = s_G[my_base + min(1, last)];
                     auto pair_step = [&](int k, auto loc) {
-                        const int j0 = s_pair[my_base + k] >> 8;
+                        const int kn0 = min(k + 2, last), kn1 = min(k + 3, last);
+                        const int npr0 = s_pair[my_base + kn0], npr1 = s_pair[my_base + kn1];
+                        const float ng0 = s_G[my_base + kn0], ng1 = s_G[my_base + kn1];
+                        const int j0 = pr0 >> 8;
                         const float dj0 = bf16_bits_to_f32(sdt[j0]);
-                        const float w0 = s_G[my_base + k] * __expf(s) * dj0 + (k == 0 ? Dh : 0.f);
+                        const float w0 = g0 * __expf(s) * dj0 + (k == 0 ? Dh : 0.f);
                         s += dj0 * Ah;
                         int j1 = j0;
                         float w1 = 0.f;
                         if (k + 1 < my_cnt) {
-                            j1 = s_pair[my_base + k + 1] >> 8;
+                            j1 = pr1 >> 8;
                             const float dj1 = bf16_bits_to_f32(sdt[j1]);
-                            w1 = s_G[my_base + k + 1] * __expf(s) * dj1;
+                            w1 = g1 * __expf(s) * dj1;
                             s += dj1 * Ah;
                         }
                         add_rows(j0, w0, j1, w1, loc);
+                        pr0 = npr0;
+                        pr1 = npr1;
+                        g0 = ng0;
+                        g1 = ng1;
                     };
                     pair_step(0, BufC<1>{});
                     for (int k = 2; k < my_cnt; k += 2) pair_step(k, BufC<0>{});
