@@ -274,6 +274,96 @@ tsv_status tree_ssd_tree_info(int32_t batch, int32_t n_nodes, const int32_t* par
                               int32_t* depth, uint64_t* anc_bits, int32_t* tree_status,
                               void* stream);
 
+/* ------------------------------------------------------------------------
+ * The two forms a packed tree replaces, on the same inputs, for measuring it
+ * against them ("STree: Speculative Tree Decoding for Hybrid State Space
+ * Models", atlas.scime.ai summary: without a packed-tree scan an SSM unrolls
+ * the draft tree into repeated sequences with extra states and memory, section
+ * "Problem"; the paper's baseline is a fused selective scan over the unrolled
+ * tree, section "Experimental setup", times in "Key results". The Bole and
+ * TreeWY abstracts, mlsanity and fugumt pages, describe the other form: a full
+ * recurrent state materialised for every draft node).
+ * ------------------------------------------------------------------------ */
+
+/* Per-item status bit of tree_ssd_unroll_plan: more leaves than max_leaves, or
+ * a root path longer than max_len */
+#define TSV_ST_OVER_CAPACITY 8
+
+/*
+ * tree_ssd_unroll_plan -- the unrolled form of each item's tree: one sequence
+ * per leaf (a node that is no node's parent, leaves taken by increasing
+ * index), holding the leaf's root path from node 0.
+ *
+ *   parent     [Bt][T] int32
+ *   max_leaves in [1, 1024]   sequence slots per item (Lcap)
+ *   max_len    in [1, 1024]   positions per sequence (S)
+ *   seq_nodes  [Bt][Lcap][S] int32  output: node at each position, -1 past the end
+ *   seq_len    [Bt][Lcap] int32     output: path length, 0 for unused slots
+ *   n_leaves   [Bt] int32           output: sequences of the item
+ *   tree_status [Bt] int32          optional; bits 1|2, or TSV_ST_OVER_CAPACITY
+ * Every output is written for every item: an invalid or over-capacity item
+ * gets n_leaves 0 and empty slots.
+ */
+tsv_status tree_ssd_unroll_plan(int32_t batch, int32_t n_nodes, const int32_t* parent, int32_t max_leaves,
+                                int32_t max_len, int32_t* seq_nodes, int32_t* seq_len, int32_t* n_leaves,
+                                int32_t* tree_status, void* stream);
+
+/*
+ * tree_ssd_unroll_gather -- materialise the unrolled sequences: for sequence
+ * q = b * max_leaves + l and position s < seq_len[q], copy node
+ * n = seq_nodes[q][s]'s rows, and give every sequence its own copy of h0[b].
+ * Layouts follow the packed ones with (item, leaf) as the batch index:
+ *   x_u [Bt*Lcap][S][H][P], dt_u [Bt*Lcap][S][H], B_u, C_u [Bt*Lcap][S][G][N]
+ *   (in_dtype), h0_u [Bt*Lcap][H][P][N] float.
+ * s gives the packed shape (x, dt, B, C, h0 as for tree_ssd_verify). Positions
+ * past a sequence's length and sequences of length 0 are not written; a
+ * length outside [0, S] or a node index outside [0, T) skips the slot.
+ */
+tsv_status tree_ssd_unroll_gather(const tsv_shape* s, int32_t max_leaves, int32_t max_len, const void* x,
+                                  const void* dt, const void* B, const void* C, const float* h0,
+                                  const int32_t* seq_nodes, const int32_t* seq_len, void* x_u, void* dt_u,
+                                  void* B_u, void* C_u, float* h0_u, void* stream);
+
+/*
+ * tree_ssd_seq_scan -- an ordinary Mamba2 scan over sequences (no tree): for
+ * each sequence q and head h, from the state h_inout[q][h],
+ *   H <- exp(dt_t A_h) H + dt_t x_t (outer) B_t,   y_t = H C_t + D_h x_t
+ * for t < seq_len[q]; the final state is written back to h_inout. The shape's
+ * batch is the number of sequences and n_nodes their row count S; layouts as
+ * written by tree_ssd_unroll_gather, y_u like x_u. head_dim, d_state <= 256
+ * and head_dim * d_state <= 16384 (TSV_E_UNSUPPORTED otherwise). Sequences
+ * whose length is outside [1, S] are skipped. fp32 arithmetic.
+ */
+tsv_status tree_ssd_seq_scan(const tsv_shape* s, const void* x_u, const void* dt_u, const float* A,
+                             const void* B_u, const void* C_u, const float* D, float* h_inout,
+                             const int32_t* seq_len, void* y_u, void* stream);
+
+/*
+ * tree_ssd_snapshot_verify -- every node's state materialised: states[b][h][i]
+ * is the state after node i's root path (formed from the parent's stored
+ * state), and y_i = states_i C_i + D x_i. Arguments as for tree_ssd_verify,
+ * plus
+ *   states [Bt][H][T][P][N] float  output (T * P * N * 4 bytes per item and head)
+ * head_dim, d_state <= 256, head_dim * d_state <= 16384. An invalid item
+ * leaves y and states untouched. fp32 arithmetic.
+ */
+tsv_status tree_ssd_snapshot_verify(const tsv_shape* s, const void* x, const void* dt, const float* A,
+                                    const void* B, const void* C, const float* D, const float* h0,
+                                    const int32_t* parent, void* y, float* states, int32_t* tree_status,
+                                    void* stream);
+
+/*
+ * tree_ssd_snapshot_commit -- the snapshot form's commit: copy the stored state
+ * of each item's last accepted node into h0_inout [Bt][H][P][N]. states as
+ * written by tree_ssd_snapshot_verify; parent, accepted, accepted_len,
+ * max_path_len and tree_status (bits 1|2|4) as for tree_ssd_commit. len == 0
+ * leaves h0 unchanged; an invalid item leaves it untouched.
+ */
+tsv_status tree_ssd_snapshot_commit(const tsv_shape* s, const float* states, float* h0_inout,
+                                    const int32_t* parent, const int32_t* accepted,
+                                    const int32_t* accepted_len, int32_t max_path_len, int32_t* tree_status,
+                                    void* stream);
+
 /* Static, human-readable name of a tsv_status value. */
 const char* tree_ssd_status_string(int32_t status);
 

@@ -12,6 +12,7 @@ rule ``gdn_verify`` and ``gdn_commit``.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Dict, Optional
@@ -32,7 +33,9 @@ STATUS_NAMES = {0: "TSV_OK", 1: "TSV_E_NULL", 2: "TSV_E_SHAPE", 3: "TSV_E_DTYPE"
                 4: "TSV_E_UNSUPPORTED", 5: "TSV_E_LAUNCH"}
 EXPORTS = ("tree_ssd_verify", "tree_ssd_commit", "tree_ssd_commit_layers", "tree_ssd_accept_greedy",
            "tree_ssd_tree_info", "tree_ssd_status_string", "tree_ssd_abi_version", "tree_gdn_verify",
-           "tree_gdn_commit")
+           "tree_gdn_commit", "tree_ssd_unroll_plan", "tree_ssd_unroll_gather", "tree_ssd_seq_scan",
+           "tree_ssd_snapshot_verify", "tree_ssd_snapshot_commit")
+ST_OVER_CAPACITY = 8
 
 
 class Shape(ctypes.Structure):
@@ -84,6 +87,17 @@ def _load():
     L.tree_ssd_status_string.restype = ctypes.c_char_p
     L.tree_ssd_abi_version.argtypes = []
     L.tree_ssd_abi_version.restype = ctypes.c_int32
+    L.tree_ssd_unroll_plan.argtypes = [ctypes.c_int32, ctypes.c_int32, _VP, ctypes.c_int32, ctypes.c_int32] + \
+        [_VP] * 5
+    L.tree_ssd_unroll_plan.restype = ctypes.c_int
+    L.tree_ssd_unroll_gather.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int32] + [_VP] * 13
+    L.tree_ssd_unroll_gather.restype = ctypes.c_int
+    L.tree_ssd_seq_scan.argtypes = [ctypes.POINTER(Shape)] + [_VP] * 10
+    L.tree_ssd_seq_scan.restype = ctypes.c_int
+    L.tree_ssd_snapshot_verify.argtypes = [ctypes.POINTER(Shape)] + [_VP] * 12
+    L.tree_ssd_snapshot_verify.restype = ctypes.c_int
+    L.tree_ssd_snapshot_commit.argtypes = [ctypes.POINTER(Shape)] + [_VP] * 5 + [ctypes.c_int32, _VP, _VP]
+    L.tree_ssd_snapshot_commit.restype = ctypes.c_int
     return L
 
 
@@ -110,6 +124,19 @@ def _stream(stream) -> ctypes.c_void_p:
     if isinstance(stream, torch.cuda.Stream):
         return ctypes.c_void_p(stream.cuda_stream)
     return ctypes.c_void_p(int(stream))
+
+
+def _on_stream(stream):
+    """Context under which the binding allocates and fills default outputs and
+    temporary tables: the stream the kernel is launched on, so that the fill is
+    ordered before the kernel and a freed temporary is reused only by later
+    work on that stream (torch's caching allocator ties a block to the stream
+    it was allocated on)."""
+    if stream is None:
+        return contextlib.nullcontext()
+    if isinstance(stream, torch.cuda.Stream):
+        return torch.cuda.stream(stream)
+    return torch.cuda.stream(torch.cuda.ExternalStream(int(stream)))
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -139,15 +166,16 @@ def make_shape(x: torch.Tensor, Bm: torch.Tensor, flags: int = 0, heads_per_bloc
     return Shape(Bt, T, H, P, N, G, _dtype_code(x), flags, heads_per_block)
 
 
-def _flags(force_generic: bool, force_wide: bool, force_small: bool = False) -> int:
+def _flags(force_generic: bool, force_wide: bool, force_small: bool = False, extra: int = 0) -> int:
     return ((TSV_FLAG_FORCE_GENERIC if force_generic else 0) | (TSV_FLAG_FORCE_WIDE if force_wide else 0)
-            | (TSV_FLAG_FORCE_SMALL if force_small else 0))
+            | (TSV_FLAG_FORCE_SMALL if force_small else 0) | int(extra))
 
 
 def verify(x, dt, A, B, C, D, h0, parent, y=None, tree_status=None, stream=None,
            force_generic: bool = False, heads_per_block: int = 0, check: bool = True,
-           force_wide: bool = False, force_small: bool = False):
-    """y [Bt,T,H,P] of one SSD layer over packed trees (tree_ssd_verify)."""
+           force_wide: bool = False, force_small: bool = False, flags: int = 0):
+    """y [Bt,T,H,P] of one SSD layer over packed trees (tree_ssd_verify).
+    ``flags`` adds further TSV_FLAG_* kernel choices (testing aids)."""
     Bt, T, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     dev, io = x.device, x.dtype
@@ -161,12 +189,13 @@ def verify(x, dt, A, B, C, D, h0, parent, y=None, tree_status=None, stream=None,
         _check(parent, "parent", (Bt, T), torch.int32, dev)
         _check(x, "x", (Bt, T, H, P), io, dev)
     if y is None:
-        y = torch.empty_like(x)
+        with _on_stream(stream):
+            y = torch.empty_like(x)
     elif check:
         _check(y, "y", (Bt, T, H, P), io, dev)
     if tree_status is not None and check:
         _check(tree_status, "tree_status", (Bt,), torch.int32, dev)
-    shape = make_shape(x, B, _flags(force_generic, force_wide, force_small), heads_per_block)
+    shape = make_shape(x, B, _flags(force_generic, force_wide, force_small, flags), heads_per_block)
     rc = lib.tree_ssd_verify(ctypes.byref(shape), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
                              _ptr(D), _ptr(h0), _ptr(parent), _ptr(y), _ptr(tree_status),
                              _stream(stream))
@@ -241,12 +270,13 @@ def commit_layers(layers, parent, accepted, accepted_len, tree_status=None, stre
     _check(accepted_len, "accepted_len", (Bt,), torch.int32, dev)
     if tree_status is not None:
         _check(tree_status, "tree_status", (Bt,), torch.int32, dev)
-    if table is None:
-        table = layer_table(layers, dev)
-    shape = make_shape(x0, B0)
-    rc = lib.tree_ssd_commit_layers(ctypes.byref(shape), int(n), _ptr(table), _ptr(parent),
-                                    _ptr(accepted), _ptr(accepted_len), int(Lmax),
-                                    _ptr(tree_status), _stream(stream))
+    with _on_stream(stream):
+        if table is None:
+            table = layer_table(layers, dev)
+        shape = make_shape(x0, B0)
+        rc = lib.tree_ssd_commit_layers(ctypes.byref(shape), int(n), _ptr(table), _ptr(parent),
+                                        _ptr(accepted), _ptr(accepted_len), int(Lmax),
+                                        _ptr(tree_status), _stream(stream))
     if rc != 0:
         raise TreeSSDError(rc, "tree_ssd_commit_layers")
 
@@ -261,14 +291,15 @@ def accept_greedy(parent, draft_tokens, target_tokens, max_path_len: int, accept
     _check(parent, "parent", (Bt, T), torch.int32, dev)
     _check(draft_tokens, "draft_tokens", (Bt, T), torch.int32, dev)
     _check(target_tokens, "target_tokens", (Bt, T), torch.int32, dev)
-    if accepted is None:
-        accepted = torch.full((Bt, max_path_len), -1, dtype=torch.int32, device=dev)
-    if accepted_len is None:
-        accepted_len = torch.zeros((Bt,), dtype=torch.int32, device=dev)
-    if next_token is None:
-        next_token = torch.full((Bt,), -1, dtype=torch.int32, device=dev)
-    if tree_status is None:
-        tree_status = torch.zeros((Bt,), dtype=torch.int32, device=dev)
+    with _on_stream(stream):
+        if accepted is None:
+            accepted = torch.full((Bt, max_path_len), -1, dtype=torch.int32, device=dev)
+        if accepted_len is None:
+            accepted_len = torch.zeros((Bt,), dtype=torch.int32, device=dev)
+        if next_token is None:
+            next_token = torch.full((Bt,), -1, dtype=torch.int32, device=dev)
+        if tree_status is None:
+            tree_status = torch.zeros((Bt,), dtype=torch.int32, device=dev)
     _check(accepted, "accepted", (Bt, max_path_len), torch.int32, dev)
     _check(accepted_len, "accepted_len", (Bt,), torch.int32, dev)
     _check(next_token, "next_token", (Bt,), torch.int32, dev)
@@ -297,8 +328,9 @@ def gdn_verify(q, k, v, g, beta, S0, parent, o=None, e=None, tree_status=None, s
                          (g, "g", (Bt, T, H)), (beta, "beta", (Bt, T, H)), (S0, "S0", (Bt, H, dv, dk))):
         _check(t, name, shp, f32, dev)
     _check(parent, "parent", (Bt, T), torch.int32, dev)
-    o = torch.empty_like(v) if o is None else o
-    e = torch.empty_like(v) if e is None else e
+    with _on_stream(stream):
+        o = torch.empty_like(v) if o is None else o
+        e = torch.empty_like(v) if e is None else e
     _check(o, "o", (Bt, T, H, dv), f32, dev)
     _check(e, "e", (Bt, T, H, dv), f32, dev)
     shape = _gdn_shape(k, v)
@@ -342,12 +374,13 @@ def tree_info(parent: torch.Tensor, depth=None, anc=None, tree_status=None, stre
     status [Bt] int32)."""
     Bt, T = parent.shape
     dev = parent.device
-    if depth is None:
-        depth = torch.zeros((Bt, T), dtype=torch.int32, device=dev)
-    if anc is None:
-        anc = torch.zeros((Bt, T, anc_words(T)), dtype=torch.int64, device=dev)
-    if tree_status is None:
-        tree_status = torch.zeros((Bt,), dtype=torch.int32, device=dev)
+    with _on_stream(stream):
+        if depth is None:
+            depth = torch.zeros((Bt, T), dtype=torch.int32, device=dev)
+        if anc is None:
+            anc = torch.zeros((Bt, T, anc_words(T)), dtype=torch.int64, device=dev)
+        if tree_status is None:
+            tree_status = torch.zeros((Bt,), dtype=torch.int32, device=dev)
     rc = lib.tree_ssd_tree_info(int(Bt), int(T), _ptr(parent), _ptr(depth), _ptr(anc),
                                 _ptr(tree_status), _stream(stream))
     if rc != 0:
@@ -383,7 +416,7 @@ class PreparedVerify:
 
     def __init__(self, x, dt, A, B, C, D, h0, parent, y, tree_status=None, stream=None,
                  force_generic: bool = False, heads_per_block: int = 0, force_wide: bool = False,
-                 force_small: bool = False):
+                 force_small: bool = False, flags: int = 0):
         Bt, T, H, P = x.shape
         G, N = B.shape[2], B.shape[3]
         io, dev = x.dtype, x.device
@@ -394,7 +427,7 @@ class PreparedVerify:
                                   (parent, "parent", (Bt, T), torch.int32),
                                   (y, "y", (Bt, T, H, P), io)):
             _check(t, name, shp, dty, dev)
-        self.shape = make_shape(x, B, _flags(force_generic, force_wide, force_small), heads_per_block)
+        self.shape = make_shape(x, B, _flags(force_generic, force_wide, force_small, flags), heads_per_block)
         self._keep = (x, dt, A, B, C, D, h0, parent, y, tree_status)
         self.args = (ctypes.byref(self.shape), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
                      _ptr(D), _ptr(h0), _ptr(parent), _ptr(y), _ptr(tree_status),
@@ -451,7 +484,8 @@ class PreparedCommitLayers:
         _check(parent, "parent", (Bt, x0.shape[1]), torch.int32, dev)
         _check(accepted, "accepted", (Bt, Lmax), torch.int32, dev)
         _check(accepted_len, "accepted_len", (Bt,), torch.int32, dev)
-        self.table = layer_table(layers, dev)
+        with _on_stream(stream):
+            self.table = layer_table(layers, dev)
         self.shape = make_shape(x0, B0)
         self._keep = (list(layers), parent, accepted, accepted_len, tree_status)
         self.args = (ctypes.byref(self.shape), int(n), _ptr(self.table), _ptr(parent),
@@ -473,10 +507,11 @@ class PreparedAccept:
         for t, name in ((parent, "parent"), (draft_tokens, "draft_tokens"),
                         (target_tokens, "target_tokens")):
             _check(t, name, (Bt, T), torch.int32, dev)
-        self.accepted = torch.full((Bt, max_path_len), -1, dtype=torch.int32, device=dev)
-        self.accepted_len = torch.zeros((Bt,), dtype=torch.int32, device=dev)
-        self.next_token = torch.full((Bt,), -1, dtype=torch.int32, device=dev)
-        self.tree_status = torch.zeros((Bt,), dtype=torch.int32, device=dev)
+        with _on_stream(stream):
+            self.accepted = torch.full((Bt, max_path_len), -1, dtype=torch.int32, device=dev)
+            self.accepted_len = torch.zeros((Bt,), dtype=torch.int32, device=dev)
+            self.next_token = torch.full((Bt,), -1, dtype=torch.int32, device=dev)
+            self.tree_status = torch.zeros((Bt,), dtype=torch.int32, device=dev)
         self._keep = (parent, draft_tokens, target_tokens)
         self.args = (int(Bt), int(T), _ptr(parent), _ptr(draft_tokens), _ptr(target_tokens),
                      int(max_path_len), _ptr(self.accepted), _ptr(self.accepted_len),
@@ -486,3 +521,140 @@ class PreparedAccept:
         rc = lib.tree_ssd_accept_greedy(*self.args)
         if rc != 0:
             raise TreeSSDError(rc, "tree_ssd_accept_greedy")
+
+
+# ---------------------------------------------------------------------------
+# the forms a packed tree replaces: unrolled sequences and per-node snapshots
+# ---------------------------------------------------------------------------
+def unroll_capacity(parent) -> tuple:
+    """(max_leaves, max_len) that hold the unrolled form of every item of a
+    host copy of ``parent`` [Bt, T]: the most leaves of any item and the
+    longest root path. Buffer sizing only."""
+    par = np.asarray(parent)
+    Bt, T = par.shape
+    most, longest = 1, 1
+    for row in par:
+        has_child = np.zeros(T, bool)
+        has_child[row[1:][row[1:] >= 0]] = True
+        depth = np.zeros(T, np.int64)
+        for i in range(1, T):
+            depth[i] = depth[row[i]] + 1 if 0 <= row[i] < i else 0
+        most = max(most, int((~has_child).sum()))
+        longest = max(longest, int(depth.max()) + 1)
+    return most, longest
+
+
+def unroll_plan(parent, max_leaves: int, max_len: int, stream=None):
+    """(seq_nodes [Bt, max_leaves, max_len], seq_len [Bt, max_leaves],
+    n_leaves [Bt], tree_status [Bt]) of tree_ssd_unroll_plan."""
+    Bt, T = parent.shape
+    dev = parent.device
+    _check(parent, "parent", (Bt, T), torch.int32, dev)
+    with _on_stream(stream):
+        nodes = torch.empty((Bt, max_leaves, max_len), dtype=torch.int32, device=dev)
+        lens = torch.empty((Bt, max_leaves), dtype=torch.int32, device=dev)
+        nl = torch.empty((Bt,), dtype=torch.int32, device=dev)
+        st = torch.empty((Bt,), dtype=torch.int32, device=dev)
+    rc = lib.tree_ssd_unroll_plan(int(Bt), int(T), _ptr(parent), int(max_leaves), int(max_len), _ptr(nodes),
+                                  _ptr(lens), _ptr(nl), _ptr(st), _stream(stream))
+    if rc != 0:
+        raise TreeSSDError(rc, "tree_ssd_unroll_plan")
+    return nodes, lens, nl, st
+
+
+def unroll_gather(x, dt, B, C, h0, seq_nodes, seq_len, out: Optional[Dict[str, torch.Tensor]] = None,
+                  stream=None) -> Dict[str, torch.Tensor]:
+    """The unrolled sequences of tree_ssd_unroll_gather: x_u [Bt*Lcap, S, H, P],
+    dt_u [Bt*Lcap, S, H], B_u / C_u [Bt*Lcap, S, G, N], h0_u [Bt*Lcap, H, P, N]."""
+    Bt, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    Lcap, S = seq_nodes.shape[1], seq_nodes.shape[2]
+    dev, io = x.device, x.dtype
+    for t, name, shp, dty in ((dt, "dt", (Bt, T, H), io), (B, "B", (Bt, T, G, N), io),
+                              (C, "C", (Bt, T, G, N), io), (h0, "h0", (Bt, H, P, N), torch.float32),
+                              (seq_nodes, "seq_nodes", (Bt, Lcap, S), torch.int32),
+                              (seq_len, "seq_len", (Bt, Lcap), torch.int32), (x, "x", (Bt, T, H, P), io)):
+        _check(t, name, shp, dty, dev)
+    ns = Bt * Lcap
+    shapes = {"x_u": ((ns, S, H, P), io), "dt_u": ((ns, S, H), io), "B_u": ((ns, S, G, N), io),
+              "C_u": ((ns, S, G, N), io), "h0_u": ((ns, H, P, N), torch.float32)}
+    if out is None:
+        with _on_stream(stream):
+            out = {k: torch.zeros(shp, dtype=dty, device=dev) for k, (shp, dty) in shapes.items()}
+    for k, (shp, dty) in shapes.items():
+        _check(out[k], k, shp, dty, dev)
+    shape = make_shape(x, B)
+    rc = lib.tree_ssd_unroll_gather(ctypes.byref(shape), int(Lcap), int(S), _ptr(x), _ptr(dt), _ptr(B), _ptr(C),
+                                    _ptr(h0), _ptr(seq_nodes), _ptr(seq_len), _ptr(out["x_u"]),
+                                    _ptr(out["dt_u"]), _ptr(out["B_u"]), _ptr(out["C_u"]), _ptr(out["h0_u"]),
+                                    _stream(stream))
+    if rc != 0:
+        raise TreeSSDError(rc, "tree_ssd_unroll_gather")
+    return out
+
+
+def seq_scan(x_u, dt_u, A, B_u, C_u, D, h_u, seq_len, y_u=None, stream=None):
+    """Plain Mamba2 scan over sequences (tree_ssd_seq_scan): returns y_u; the
+    final state of each sequence overwrites h_u."""
+    ns, S, H, P = x_u.shape
+    G, N = B_u.shape[2], B_u.shape[3]
+    dev, io = x_u.device, x_u.dtype
+    for t, name, shp, dty in ((dt_u, "dt_u", (ns, S, H), io), (B_u, "B_u", (ns, S, G, N), io),
+                              (C_u, "C_u", (ns, S, G, N), io), (A, "A", (H,), torch.float32),
+                              (D, "D", (H,), torch.float32), (h_u, "h_u", (ns, H, P, N), torch.float32),
+                              (seq_len, "seq_len", (ns,), torch.int32)):
+        _check(t, name, shp, dty, dev)
+    if y_u is None:
+        with _on_stream(stream):
+            y_u = torch.zeros_like(x_u)
+    _check(y_u, "y_u", (ns, S, H, P), io, dev)
+    shape = Shape(ns, S, H, P, N, G, _dtype_code(x_u), 0, 0)
+    rc = lib.tree_ssd_seq_scan(ctypes.byref(shape), _ptr(x_u), _ptr(dt_u), _ptr(A), _ptr(B_u), _ptr(C_u),
+                               _ptr(D), _ptr(h_u), _ptr(seq_len), _ptr(y_u), _stream(stream))
+    if rc != 0:
+        raise TreeSSDError(rc, "tree_ssd_seq_scan")
+    return y_u
+
+
+def snapshot_verify(x, dt, A, B, C, D, h0, parent, y=None, states=None, tree_status=None, stream=None):
+    """(y, states [Bt, H, T, P, N]) of tree_ssd_snapshot_verify."""
+    Bt, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev, io = x.device, x.dtype
+    for t, name, shp, dty in ((dt, "dt", (Bt, T, H), io), (B, "B", (Bt, T, G, N), io),
+                              (C, "C", (Bt, T, G, N), io), (A, "A", (H,), torch.float32),
+                              (D, "D", (H,), torch.float32), (h0, "h0", (Bt, H, P, N), torch.float32),
+                              (parent, "parent", (Bt, T), torch.int32), (x, "x", (Bt, T, H, P), io)):
+        _check(t, name, shp, dty, dev)
+    with _on_stream(stream):
+        if y is None:
+            y = torch.empty_like(x)
+        if states is None:
+            states = torch.empty((Bt, H, T, P, N), dtype=torch.float32, device=dev)
+    _check(y, "y", (Bt, T, H, P), io, dev)
+    _check(states, "states", (Bt, H, T, P, N), torch.float32, dev)
+    shape = make_shape(x, B)
+    rc = lib.tree_ssd_snapshot_verify(ctypes.byref(shape), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                                      _ptr(D), _ptr(h0), _ptr(parent), _ptr(y), _ptr(states),
+                                      _ptr(tree_status), _stream(stream))
+    if rc != 0:
+        raise TreeSSDError(rc, "tree_ssd_snapshot_verify")
+    return y, states
+
+
+def snapshot_commit(states, h0, parent, accepted, accepted_len, tree_status=None, stream=None):
+    """Copy each item's last accepted node's stored state into h0 (tree_ssd_snapshot_commit)."""
+    Bt, H, T, P, N = states.shape
+    dev = states.device
+    Lmax = accepted.shape[1] if accepted.dim() == 2 else 0
+    _check(states, "states", (Bt, H, T, P, N), torch.float32, dev)
+    _check(h0, "h0", (Bt, H, P, N), torch.float32, dev)
+    _check(parent, "parent", (Bt, T), torch.int32, dev)
+    _check(accepted, "accepted", (Bt, Lmax), torch.int32, dev)
+    _check(accepted_len, "accepted_len", (Bt,), torch.int32, dev)
+    shape = Shape(Bt, T, H, P, N, 1, TSV_F32, 0, 0)
+    rc = lib.tree_ssd_snapshot_commit(ctypes.byref(shape), _ptr(states), _ptr(h0), _ptr(parent), _ptr(accepted),
+                                      _ptr(accepted_len), int(Lmax), _ptr(tree_status), _stream(stream))
+    if rc != 0:
+        raise TreeSSDError(rc, "tree_ssd_snapshot_commit")
+    return h0

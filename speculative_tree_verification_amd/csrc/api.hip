@@ -192,6 +192,94 @@ tsv_status tree_ssd_tree_info(int32_t batch, int32_t n_nodes, const int32_t* par
     return e == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
 }
 
+// ---- the forms a packed tree replaces
+namespace {
+constexpr int kBaseMaxDim = 256;     // head_dim, d_state of the baseline kernels
+constexpr int kBaseMaxState = 16384; // head_dim * d_state: 64 state elements per thread
+}  // namespace
+
+tsv_status tree_ssd_unroll_plan(int32_t batch, int32_t n_nodes, const int32_t* parent, int32_t max_leaves,
+                                int32_t max_len, int32_t* seq_nodes, int32_t* seq_len, int32_t* n_leaves,
+                                int32_t* tree_status, void* stream) {
+    if (batch < 0 || n_nodes < 0 || n_nodes > kMaxNodes) return TSV_E_SHAPE;
+    if (max_leaves < 1 || max_leaves > kMaxNodes || max_len < 1 || max_len > kMaxNodes) return TSV_E_SHAPE;
+    if (batch == 0 || n_nodes == 0) return TSV_OK;
+    if (!parent || !seq_nodes || !seq_len || !n_leaves) return TSV_E_NULL;
+    hipError_t e = tsv::launch_unroll_plan(batch, n_nodes, parent, max_leaves, max_len, seq_nodes, seq_len,
+                                           n_leaves, tree_status, (hipStream_t)stream);
+    return e == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
+}
+
+tsv_status tree_ssd_unroll_gather(const tsv_shape* s, int32_t max_leaves, int32_t max_len, const void* x,
+                                  const void* dt, const void* B, const void* C, const float* h0,
+                                  const int32_t* seq_nodes, const int32_t* seq_len, void* x_u, void* dt_u,
+                                  void* B_u, void* C_u, float* h0_u, void* stream) {
+    tsv_status st = check_shape(s);
+    if (st != TSV_OK) return st;
+    if (max_leaves < 1 || max_leaves > kMaxNodes || max_len < 1 || max_len > kMaxNodes) return TSV_E_SHAPE;
+    if (s->batch == 0 || s->n_nodes == 0) return TSV_OK;
+    if (!x || !dt || !B || !C || !h0 || !seq_nodes || !seq_len || !x_u || !dt_u || !B_u || !C_u || !h0_u)
+        return TSV_E_NULL;
+    const long long nseq = (long long)s->batch * max_leaves;
+    if (nseq * (max_len + s->n_heads) > 0x7fffffffLL) return TSV_E_UNSUPPORTED;
+    tsv::UnrollArgs u{x,  dt,   B,    C,        h0,       seq_nodes,   seq_len,    x_u,
+                      dt_u, B_u, C_u, h0_u, s->batch, s->n_nodes, s->n_heads, s->head_dim,
+                      s->d_state, s->n_groups, max_leaves, max_len};
+    hipError_t e = tsv::launch_unroll_gather(u, s->in_dtype == TSV_BF16, (hipStream_t)stream);
+    return e == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
+}
+
+tsv_status tree_ssd_seq_scan(const tsv_shape* s, const void* x_u, const void* dt_u, const float* A,
+                             const void* B_u, const void* C_u, const float* D, float* h_inout,
+                             const int32_t* seq_len, void* y_u, void* stream) {
+    tsv_status st = check_shape(s);
+    if (st != TSV_OK) return st;
+    if (s->batch == 0 || s->n_nodes == 0) return TSV_OK;
+    if (s->head_dim > kBaseMaxDim || s->d_state > kBaseMaxDim ||
+        s->head_dim * s->d_state > kBaseMaxState)
+        return TSV_E_UNSUPPORTED;
+    if ((long long)s->batch * s->n_heads > 0x7fffffffLL) return TSV_E_UNSUPPORTED;
+    if (!x_u || !dt_u || !A || !B_u || !C_u || !D || !h_inout || !seq_len || !y_u) return TSV_E_NULL;
+    tsv::SeqScanArgs a{x_u, dt_u, A, B_u, C_u, D, h_inout, seq_len, y_u,
+                       s->batch, s->n_nodes, s->n_heads, s->head_dim, s->d_state, s->n_groups};
+    hipError_t e = tsv::launch_seq_scan(a, s->in_dtype == TSV_BF16, (hipStream_t)stream);
+    return e == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
+}
+
+tsv_status tree_ssd_snapshot_verify(const tsv_shape* s, const void* x, const void* dt, const float* A,
+                                    const void* B, const void* C, const float* D, const float* h0,
+                                    const int32_t* parent, void* y, float* states, int32_t* tree_status,
+                                    void* stream) {
+    tsv_status st = check_shape(s);
+    if (st != TSV_OK) return st;
+    if (s->batch == 0 || s->n_nodes == 0) return TSV_OK;
+    if (s->head_dim > kBaseMaxDim || s->d_state > kBaseMaxDim ||
+        s->head_dim * s->d_state > kBaseMaxState)
+        return TSV_E_UNSUPPORTED;
+    if (!x || !dt || !A || !B || !C || !D || !h0 || !parent || !y || !states) return TSV_E_NULL;
+    tsv::VerifyArgs a{x,  dt, A,           B,        C,          D,          h0,
+                      parent, y, tree_status, s->batch, s->n_nodes, s->n_heads, s->head_dim,
+                      s->d_state, s->n_groups};
+    hipError_t e = tsv::launch_snapshot_verify(a, states, s->in_dtype == TSV_BF16, (hipStream_t)stream);
+    return e == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
+}
+
+tsv_status tree_ssd_snapshot_commit(const tsv_shape* s, const float* states, float* h0_inout,
+                                    const int32_t* parent, const int32_t* accepted,
+                                    const int32_t* accepted_len, int32_t max_path_len, int32_t* tree_status,
+                                    void* stream) {
+    tsv_status st = check_shape(s);
+    if (st != TSV_OK) return st;
+    if (max_path_len < 0 || max_path_len > kMaxNodes) return TSV_E_SHAPE;
+    if (s->batch == 0 || s->n_nodes == 0) return TSV_OK;
+    if (!states || !h0_inout || !parent || !accepted_len) return TSV_E_NULL;
+    if (max_path_len > 0 && !accepted) return TSV_E_NULL;
+    hipError_t e = tsv::launch_snapshot_commit(s->batch, s->n_nodes, s->n_heads, s->head_dim * s->d_state,
+                                               states, h0_inout, parent, accepted, accepted_len,
+                                               max_path_len, tree_status, (hipStream_t)stream);
+    return e == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
+}
+
 const char* tree_ssd_status_string(int32_t status) {
     switch (status) {
         case TSV_OK: return "ok";

@@ -70,6 +70,44 @@ hipError_t launch_gdn_commit(int batch, int T, int H, int dk, int dv, const floa
                              const int32_t* accepted, const int32_t* accepted_len, int Lmax,
                              int32_t* tree_status, hipStream_t stream);
 
+// ---- the forms a packed tree replaces (measured beside it)
+struct UnrollArgs {
+    const void* x;
+    const void* dt;
+    const void* B;
+    const void* C;
+    const float* h0;
+    const int32_t* seq_nodes;
+    const int32_t* seq_len;
+    void* x_u;
+    void* dt_u;
+    void* B_u;
+    void* C_u;
+    float* h0_u;
+    int batch, T, H, P, N, G, Lcap, S;
+};
+struct SeqScanArgs {
+    const void* x_u;
+    const void* dt_u;
+    const float* A;
+    const void* B_u;
+    const void* C_u;
+    const float* D;
+    float* h_io;
+    const int32_t* seq_len;
+    void* y_u;
+    int nseq, S, H, P, N, G;
+};
+hipError_t launch_unroll_plan(int batch, int T, const int32_t* parent, int Lcap, int S, int32_t* seq_nodes,
+                              int32_t* seq_len, int32_t* n_leaves, int32_t* tree_status, hipStream_t stream);
+hipError_t launch_unroll_gather(const UnrollArgs& u, bool bf16, hipStream_t stream);
+hipError_t launch_seq_scan(const SeqScanArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_snapshot_verify(const VerifyArgs& a, float* states, bool bf16, hipStream_t stream);
+hipError_t launch_snapshot_commit(int batch, int T, int H, int PN, const float* states, float* h0,
+                                  const int32_t* parent, const int32_t* accepted,
+                                  const int32_t* accepted_len, int Lmax, int32_t* tree_status,
+                                  hipStream_t stream);
+
 // greedy acceptance of a verified tree (one work-group per item)
 hipError_t launch_accept_greedy(int batch, int T, const int32_t* parent, const int32_t* draft,
                                 const int32_t* target, int Lmax, int32_t* accepted,
