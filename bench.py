@@ -45,14 +45,19 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=1,
                     help="workload configuration id (0-4); default 1, the 64-layer Mamba2-2.7B step")
-    ap.add_argument("--secondary", default="2,4",
+    ap.add_argument("--secondary", default="2,3,4",
                     help="comma list of further workloads measured in the same run ('' for none)")
     ap.add_argument("--secondary-steps", type=int, default=50)
+    ap.add_argument("--reps", type=int, default=50,
+                    help="timed regions per kernel (median and minimum are taken over them)")
     ap.add_argument("--rotate-mib", type=int, default=ROTATE_BYTES >> 20,
                     help="total size of the rotating input sets (MiB)")
     ap.add_argument("--no-oracle", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-gdn", action="store_true", help="skip the gated-delta-rule tree kernels")
     ap.add_argument("--no-large", action="store_true", help="skip the 1023-node tree measurement")
+    ap.add_argument("--baselines", default="1,2,3,4",
+                    help="workloads on which the unrolled and snapshot forms are timed beside the packed "
+                         "form ('' for none)")
     ap.add_argument("--oracle-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--heads-per-block", type=int, default=0)
@@ -282,6 +287,41 @@ def timed_region(torch, fn, rounds):
     return start.elapsed_time(end) / rounds
 
 
+def timed_stats(torch, fn, reps, rounds):
+    """Per-call duration statistics over `reps` timed regions of `rounds`
+    back-to-back calls each (one HIP event pair per region, the regions back to
+    back after one untimed burst as in timed_region). Returns mean, median and
+    minimum of the per-region averages, in ms per call."""
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(3):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    per_call = max(e0.elapsed_time(e1) / 3, 1e-3)
+    nwarm = max(3, int(WARM_MS / per_call) + 1)
+    t0 = time.perf_counter()
+    for i in range(nwarm):
+        fn(i)
+    host_ms = (time.perf_counter() - t0) * 1e3 / nwarm
+    if host_ms > 0.8 * per_call:
+        torch.cuda._sleep(sleep_cycles_for(torch, 1.3 * host_ms * rounds * reps + 0.5))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    k = 0
+    ev[0].record()
+    for r in range(reps):
+        for _ in range(rounds):
+            fn(k)
+            k += 1
+        ev[r + 1].record()
+    torch.cuda.synchronize()
+    per = sorted(ev[r].elapsed_time(ev[r + 1]) / rounds for r in range(reps))
+    mean = ev[0].elapsed_time(ev[reps]) / (rounds * reps)
+    return {"mean": mean, "median": per[len(per) // 2], "min": per[0], "reps": reps,
+            "calls_per_rep": rounds}
+
+
 def graph_step_timing(torch, bnd, wl, steps):
     """The same step captured once per rotating input set as a HIP graph (the
     launches re-pointed at a side stream for the capture), replayed `steps`
@@ -313,7 +353,7 @@ def graph_step_timing(torch, bnd, wl, steps):
     return ms
 
 
-def time_steps(torch, wl, steps, warmup):
+def time_steps(torch, wl, steps, warmup, reps=50):
     """Warm up, then time exactly `steps` steps with HIP events (see
     timed_region: an untimed burst of the same steps runs first, so the region
     measures back-to-back launches in the GPU's steady state under this load,
@@ -343,41 +383,55 @@ def time_steps(torch, wl, steps, warmup):
         for f in calls:
             f()
 
-    v_ms = region(lambda s: run_all(wl.verify_calls[s]), steps)
-    c_ms = region(lambda s: run_all(wl.commit_calls[s]), steps)
-    return dict(ms_per_step=ms / steps, verify_us=v_ms * 1e3 / (steps * nv),
-                commit_us=c_ms * 1e3 / (steps * nc), host_ms=1e3 * host_per_step,
-                verify_launches=nv, commit_launches=nc)
+    # per-launch statistics: `reps` regions, each of `rounds` steps' launches of
+    # one kernel (about a millisecond of GPU time or more per region)
+    step_stats = timed_stats(torch, lambda i: wl.step(i % wl.n_sets), reps, 1)
+    rounds = max(1, min(steps, 20))
+    vs = timed_stats(torch, lambda i: run_all(wl.verify_calls[i % wl.n_sets]), reps, rounds)
+    cs = timed_stats(torch, lambda i: run_all(wl.commit_calls[i % wl.n_sets]), reps, rounds)
+    scale = lambda st, n: {k: (v * 1e3 / n if k in ("mean", "median", "min") else v) for k, v in st.items()}
+    vs, cs = scale(vs, nv), scale(cs, nc)
+    return dict(ms_per_step=ms / steps, verify_us=vs["median"], commit_us=cs["median"],
+                verify_stats=vs, commit_stats=cs, step_stats=step_stats,
+                host_ms=1e3 * host_per_step, verify_launches=nv, commit_launches=nc)
 
 
 GDN_SHAPE = dict(batch=16, n_nodes=31, n_heads=16, dk=128, dv=128)
 
 
 def gdn_cpu_baseline(base, seconds):
-    """The fp64 gated-delta-rule oracle (numpy, one BLAS thread) on a bounded
-    sample of the same inputs: whole items (all heads), verify + commit as the
-    unrolled recurrence, cycled until about `seconds` of oracle time."""
+    """The fp64 gated-delta-rule oracle (numpy) on a bounded sample of the same
+    inputs: whole items (all heads), verify + commit as the unrolled
+    recurrence, one item per worker thread (one BLAS thread each) on the
+    host's OpenMP thread count, cycled until about `seconds` of wall time."""
+    import concurrent.futures
     import numpy as np
     from threadpoolctl import threadpool_limits
     from oracle import gdn as OG
+    from oracle import oracle as O
     B, T, H, _ = base["k"].shape
     f = lambda a: a.astype(np.float64) if a.dtype == np.float32 else a
-    done, used, parts = 0, 0.0, 0
-    with threadpool_limits(1):
-        while used < seconds:
-            b = parts % B
-            sl = {k: f(v[b:b + 1]) for k, v in base.items()}
-            t0 = time.perf_counter()
-            OG.verify_unrolled(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], sl["S0"], sl["parent"])
-            OG.commit_unrolled(sl["k"], sl["v"], sl["g"], sl["beta"], sl["S0"], sl["parent"],
-                               sl["accepted"], sl["accepted_len"])
-            used += time.perf_counter() - t0
-            done += T * H
-            parts += 1
-    return {"value": round(done / used, 1), "unit": "nodes/s", "cores": 1, "kind": "oracle",
+    items = [{k: f(v[b:b + 1]) for k, v in base.items()} for b in range(B)]
+    nthr = max(1, O.num_threads())
+
+    def one(sl):
+        OG.verify_unrolled(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], sl["S0"], sl["parent"])
+        OG.commit_unrolled(sl["k"], sl["v"], sl["g"], sl["beta"], sl["S0"], sl["parent"],
+                           sl["accepted"], sl["accepted_len"])
+        return T * H
+
+    done, parts = 0, 0
+    t0 = time.perf_counter()
+    with threadpool_limits(1), concurrent.futures.ThreadPoolExecutor(nthr) as ex:
+        while time.perf_counter() - t0 < seconds:
+            batch = [items[(parts + i) % B] for i in range(nthr)]
+            done += sum(ex.map(one, batch))
+            parts += nthr
+    used = time.perf_counter() - t0
+    return {"value": round(done / used, 1), "unit": "nodes/s", "cores": nthr, "kind": "oracle",
             "sample": f"{parts} items cycled over the workload's {B}, all {H} heads each: verify + commit "
-                      f"(the unrolled recurrence) in fp64 numpy, {used:.1f} s of oracle time",
-            "seconds": round(used, 2)}
+                      f"(the unrolled recurrence) in fp64 numpy, {nthr} worker threads (Python loops "
+                      f"share one interpreter lock), {used:.1f} s", "seconds": round(used, 2), **host_cpus()}
 
 
 def large_cpu_baseline(base, seconds):
@@ -398,7 +452,7 @@ def large_cpu_baseline(base, seconds):
         parts += 1
     return {"value": round(done / used, 1), "unit": "nodes/s", "cores": O.num_threads(), "kind": "oracle",
             "sample": f"{parts} items cycled over the workload's {B}, all {H} heads each: verify + commit "
-                      f"in fp64, {used:.1f} s of oracle time", "seconds": round(used, 2)}
+                      f"in fp64, {used:.1f} s of oracle time", "seconds": round(used, 2), **host_cpus()}
 
 
 def gdn_timing(torch, bnd, W, rounds, oracle_seconds=0.0):
@@ -510,17 +564,99 @@ def accept_timing(torch, bnd, W, wl, rounds):
             "bound": "latency (a few KB per launch)"}
 
 
-def kernel_report(name, us, nbytes, workload, sha, launches):
+def _adaptive_stats(torch, fn, reps, min_region_ms=2.0):
+    """timed_stats with enough calls per region for about min_region_ms of GPU time."""
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    fn(0)
+    e1.record()
+    torch.cuda.synchronize()
+    rounds = max(1, int(min_region_ms / max(e0.elapsed_time(e1), 1e-3)))
+    st = timed_stats(torch, fn, reps, rounds)
+    return {k: (round(v * 1e3, 3) if k in ("mean", "median", "min") else v) for k, v in st.items()}
+
+
+def baseline_forms(torch, bnd, W, cid, reps=20):
+    """The packed path against the two forms it replaces, on layer 0 of the
+    workload (one input set, the same for all three): the tree unrolled into
+    per-leaf sequences (plan, gather of the sequences with one h0 copy each,
+    plain sequence scan) and per-node state snapshots (every node's state
+    written to HBM; commit copies the accepted node's state). Durations are
+    per call (us); transient bytes are what each form writes beyond the packed
+    inputs and outputs."""
+    inp = W.make_inputs(cid, 0)
+    d = bnd.to_device(inp)
+    B, T, H, P, N, G = W.shape_of(inp)
+    cfg = W.CONFIGS[cid]
+    out = {"workload": cfg.name, "layer_calls_per_step": cfg.layers}
+    y = torch.empty_like(d["x"])
+    pv = bnd.PreparedVerify(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], d["parent"], y)
+    h = d["h0"].clone()
+    pc = bnd.PreparedCommit(d["x"], d["dt"], d["A"], d["B"], h, d["parent"], d["accepted"], d["accepted_len"])
+    h_rst = lambda: h.copy_(d["h0"])
+    packed_v = _adaptive_stats(torch, lambda i: pv(), reps)
+    packed_c = _adaptive_stats(torch, lambda i: pc(), reps)
+    h_rst()
+    out["packed"] = {"verify_us": packed_v["median"], "commit_us": packed_c["median"], "transient_bytes": 0,
+                     "verify_stats_us": packed_v}
+    Lcap, S = bnd.unroll_capacity(inp["parent"])
+    pu = bnd.PreparedUnrolled(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], d["parent"], Lcap, S)
+    unrolled_v = _adaptive_stats(torch, lambda i: pu(), reps)
+    nl = pu.n_leaves.cpu()
+    out["unrolled"] = {"verify_us": unrolled_v["median"], "transient_bytes": pu.materialised_bytes(),
+                       "sequences": int(nl.sum()), "sequence_slots": B * Lcap, "positions_per_sequence": S,
+                       "verify_stats_us": unrolled_v,
+                       "what": "tree_ssd_unroll_plan + tree_ssd_unroll_gather (per-leaf copies of x, dt, B, "
+                               "C and of h0) + tree_ssd_seq_scan; commit would replay as in the packed form"}
+    del pu
+    torch.cuda.empty_cache()
+    ps = bnd.PreparedSnapshot(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], d["parent"],
+                              d["accepted"], d["accepted_len"])
+    snap_v = _adaptive_stats(torch, lambda i: ps.verify(), reps)
+    hs = d["h0"].clone()
+    snap_c = _adaptive_stats(torch, lambda i: ps.commit(hs), reps)
+    out["snapshot"] = {"verify_us": snap_v["median"], "commit_us": snap_c["median"],
+                       "transient_bytes": ps.materialised_bytes(), "verify_stats_us": snap_v,
+                       "what": "tree_ssd_snapshot_verify (every node's state written to HBM) + "
+                               "tree_ssd_snapshot_commit (copy of the accepted node's state)"}
+    del ps
+    torch.cuda.empty_cache()
+    pk = out["packed"]["verify_us"]
+    out["unrolled_over_packed_verify"] = round(out["unrolled"]["verify_us"] / pk, 2)
+    out["snapshot_over_packed_verify"] = round(out["snapshot"]["verify_us"] / pk, 2)
+    out["timing"] = "HIP events, median over timed regions of back-to-back calls on one input set"
+    return out
+
+
+def kernel_report(name, us, nbytes, workload, sha, launches, stats=None):
+    """Roofline record of one kernel: algorithmic bytes over the median launch
+    duration (`us`), with the mean and minimum beside it when `stats` is given."""
     gbs = nbytes / (us * 1e-6) / 1e9
     rec = traffic_record(name, workload, sha)
     traffic = None
     if rec is not None:
         traffic = int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
-    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
-            "kernel": name, "avg_us": round(us, 3), "algorithmic_bytes": int(nbytes),
-            "launches_per_step": launches,
-            "timing": "HIP events around back-to-back launches of this kernel alone"}
+    out = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+           "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+           "kernel": name, "avg_us": round(us, 3), "algorithmic_bytes": int(nbytes),
+           "launches_per_step": launches,
+           "timing": "HIP events around back-to-back launches of this kernel alone"}
+    if stats is not None:
+        out["avg_us_is"] = "median over timed regions"
+        out["stats_us"] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in stats.items()}
+    return out
+
+
+def host_cpus():
+    """The host's CPU counts beside the OpenMP threads the oracle used (the
+    box's OMP_NUM_THREADS, if set, bounds the latter)."""
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        aff = None
+    return {"host_cpus": os.cpu_count(), "affinity_cpus": aff,
+            "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS")}
 
 
 def cpu_baseline(wl, seconds):
@@ -545,18 +681,20 @@ def cpu_baseline(wl, seconds):
     what = (f"{parts} (layer, item) units cycled over the workload's {len(units)}, all {H} heads "
             f"each: verify + commit in fp64, {used:.1f} s of oracle time")
     return {"value": round(done_nodes / used, 1), "unit": "nodes/s", "cores": O.num_threads(),
-            "kind": "oracle", "sample": what, "seconds": round(used, 2)}
+            "kind": "oracle", "sample": what, "seconds": round(used, 2), **host_cpus()}
 
 
-def run_workload(torch, bnd, W, cid, steps, warmup, hpb, keep_host):
+def run_workload(torch, bnd, W, cid, steps, warmup, hpb, keep_host, reps=50):
     wl = Workload(cid, torch, bnd, W, heads_per_block=hpb, keep_host=keep_host)
-    t = time_steps(torch, wl, steps, warmup)
+    t = time_steps(torch, wl, steps, warmup, reps)
     vb, cb = wl.algorithmic_bytes()
     name = wl.cfg.name
-    v = kernel_report("verify", t["verify_us"], vb, name, source_sha("verify"), t["verify_launches"])
+    v = kernel_report("verify", t["verify_us"], vb, name, source_sha("verify"), t["verify_launches"],
+                      t["verify_stats"])
     B, T, H, P, N, G = wl.dims
     v["mfma"] = mfma_report(verify_flops(B, T, H, P, N, G, wl.pairs), t["verify_us"], vb)
-    c = kernel_report("commit", t["commit_us"], cb, name, source_sha("commit"), t["commit_launches"])
+    c = kernel_report("commit", t["commit_us"], cb, name, source_sha("commit"), t["commit_launches"],
+                      t["commit_stats"])
     t["accept"] = accept_timing(torch, bnd, W, wl, steps)
     nodes_s = wl.nodes_per_step / (t["ms_per_step"] * 1e-3)
     log(f"[bench] workload {cid}: {t['ms_per_step']:.4f} ms/step, {nodes_s:.4g} nodes/s; "
@@ -594,7 +732,8 @@ def main():
         return
 
     wl, t, v, c, nodes_s = run_workload(torch, bnd, W, args.workload, args.steps, args.warmup,
-                                        args.heads_per_block, keep_host=not args.no_oracle)
+                                        args.heads_per_block, keep_host=not args.no_oracle,
+                                        reps=args.reps)
     B, T, H, P, N, G = wl.dims
     layers = wl.cfg.layers
     # the kernel that takes most of the step's time
@@ -620,6 +759,8 @@ def main():
                             + (f" ({layers} layers)" if layers > 1 else "")),
                    "rotating_sets": wl.n_sets},
         "roofline": roofline,
+        "step_stats_ms": {k: (round(vv, 5) if isinstance(vv, float) else vv)
+                          for k, vv in t["step_stats"].items()},
         "kernels": {"verify": v, "commit": c},
         "accept": t["accept"],
     }
@@ -633,7 +774,7 @@ def main():
         if sid == args.workload:
             continue
         wl2, t2, v2, c2, ns2 = run_workload(torch, bnd, W, sid, args.secondary_steps, 3,
-                                            0, keep_host=False)
+                                            0, keep_host=False, reps=args.reps)
         secondary.append({"workload": wl2.cfg.name, "nodes_per_s": round(ns2, 1),
                           "ms_per_step": round(t2["ms_per_step"], 5),
                           "verify": v2, "commit": c2, "accept": t2["accept"]})
@@ -641,6 +782,16 @@ def main():
         torch.cuda.empty_cache()
     if secondary:
         out["secondary"] = secondary
+    bl = [int(c) for c in args.baselines.split(",") if c.strip()]
+    if bl:
+        out["baselines"] = []
+        for cid in bl:
+            r = baseline_forms(torch, bnd, W, cid)
+            log(f"[bench] forms on {r['workload']}: packed {r['packed']['verify_us']:.1f} us, unrolled "
+                f"{r['unrolled']['verify_us']:.1f} us ({r['unrolled']['transient_bytes'] / 2**20:.0f} MiB), "
+                f"snapshot {r['snapshot']['verify_us']:.1f} us ({r['snapshot']['transient_bytes'] / 2**20:.0f} MiB)")
+            out["baselines"].append(r)
+            torch.cuda.empty_cache()
     if not args.no_gdn:
         out["gdn"] = gdn_timing(torch, bnd, W, args.secondary_steps, 0.0 if args.no_oracle else 3.0)
         log(f"[bench] gated delta rule {out['gdn']['workload']}: verify {out['gdn']['verify']['avg_us']:.2f} us, "

@@ -658,3 +658,100 @@ def snapshot_commit(states, h0, parent, accepted, accepted_len, tree_status=None
     if rc != 0:
         raise TreeSSDError(rc, "tree_ssd_snapshot_commit")
     return h0
+
+
+class PreparedUnrolled:
+    """The unrolled form of one verify call with fixed buffers: calling it
+    enqueues tree_ssd_unroll_plan, tree_ssd_unroll_gather and
+    tree_ssd_seq_scan (outputs y_u per sequence position; h0_u ends holding
+    each sequence's final state). ``max_leaves`` / ``max_len`` size the
+    sequence buffers (unroll_capacity gives exact ones)."""
+
+    def __init__(self, x, dt, A, B, C, D, h0, parent, max_leaves: int, max_len: int, stream=None):
+        Bt, T, H, P = x.shape
+        G, N = B.shape[2], B.shape[3]
+        dev, io = x.device, x.dtype
+        for t, name, shp, dty in ((dt, "dt", (Bt, T, H), io), (B, "B", (Bt, T, G, N), io),
+                                  (C, "C", (Bt, T, G, N), io), (A, "A", (H,), torch.float32),
+                                  (D, "D", (H,), torch.float32), (h0, "h0", (Bt, H, P, N), torch.float32),
+                                  (parent, "parent", (Bt, T), torch.int32)):
+            _check(t, name, shp, dty, dev)
+        Lc, S = int(max_leaves), int(max_len)
+        ns = Bt * Lc
+        with _on_stream(stream):
+            self.seq_nodes = torch.empty((Bt, Lc, S), dtype=torch.int32, device=dev)
+            self.seq_len = torch.empty((Bt, Lc), dtype=torch.int32, device=dev)
+            self.n_leaves = torch.empty((Bt,), dtype=torch.int32, device=dev)
+            self.tree_status = torch.empty((Bt,), dtype=torch.int32, device=dev)
+            self.x_u = torch.zeros((ns, S, H, P), dtype=io, device=dev)
+            self.dt_u = torch.zeros((ns, S, H), dtype=io, device=dev)
+            self.B_u = torch.zeros((ns, S, G, N), dtype=io, device=dev)
+            self.C_u = torch.zeros((ns, S, G, N), dtype=io, device=dev)
+            self.h0_u = torch.zeros((ns, H, P, N), dtype=torch.float32, device=dev)
+            self.y_u = torch.zeros((ns, S, H, P), dtype=io, device=dev)
+        self.shape = make_shape(x, B)
+        self.seq_shape = Shape(ns, S, H, P, N, G, _dtype_code(x), 0, 0)
+        self._keep = (x, dt, A, B, C, D, h0, parent)
+        st = _stream(stream)
+        self.plan_args = (int(Bt), int(T), _ptr(parent), Lc, S, _ptr(self.seq_nodes), _ptr(self.seq_len),
+                          _ptr(self.n_leaves), _ptr(self.tree_status), st)
+        self.gather_args = (ctypes.byref(self.shape), Lc, S, _ptr(x), _ptr(dt), _ptr(B), _ptr(C), _ptr(h0),
+                            _ptr(self.seq_nodes), _ptr(self.seq_len), _ptr(self.x_u), _ptr(self.dt_u),
+                            _ptr(self.B_u), _ptr(self.C_u), _ptr(self.h0_u), st)
+        self.scan_args = (ctypes.byref(self.seq_shape), _ptr(self.x_u), _ptr(self.dt_u), _ptr(A), _ptr(self.B_u),
+                          _ptr(self.C_u), _ptr(D), _ptr(self.h0_u), _ptr(self.seq_len), _ptr(self.y_u), st)
+
+    def materialised_bytes(self) -> int:
+        """Bytes of the unrolled copies this form writes (inputs, states, outputs)."""
+        return sum(t.numel() * t.element_size() for t in (self.x_u, self.dt_u, self.B_u, self.C_u,
+                                                          self.h0_u, self.y_u))
+
+    def __call__(self):
+        for fn, args, name in ((lib.tree_ssd_unroll_plan, self.plan_args, "tree_ssd_unroll_plan"),
+                               (lib.tree_ssd_unroll_gather, self.gather_args, "tree_ssd_unroll_gather"),
+                               (lib.tree_ssd_seq_scan, self.scan_args, "tree_ssd_seq_scan")):
+            rc = fn(*args)
+            if rc != 0:
+                raise TreeSSDError(rc, name)
+
+
+class PreparedSnapshot:
+    """The snapshot form with fixed buffers: ``verify()`` enqueues
+    tree_ssd_snapshot_verify (every node's state into ``states``),
+    ``commit(h)`` tree_ssd_snapshot_commit into h."""
+
+    def __init__(self, x, dt, A, B, C, D, h0, parent, accepted, accepted_len, stream=None):
+        Bt, T, H, P = x.shape
+        G, N = B.shape[2], B.shape[3]
+        dev, io = x.device, x.dtype
+        for t, name, shp, dty in ((dt, "dt", (Bt, T, H), io), (B, "B", (Bt, T, G, N), io),
+                                  (C, "C", (Bt, T, G, N), io), (A, "A", (H,), torch.float32),
+                                  (D, "D", (H,), torch.float32), (h0, "h0", (Bt, H, P, N), torch.float32),
+                                  (parent, "parent", (Bt, T), torch.int32)):
+            _check(t, name, shp, dty, dev)
+        Lmax = accepted.shape[1]
+        _check(accepted, "accepted", (Bt, Lmax), torch.int32, dev)
+        _check(accepted_len, "accepted_len", (Bt,), torch.int32, dev)
+        with _on_stream(stream):
+            self.y = torch.empty_like(x)
+            self.states = torch.empty((Bt, H, T, P, N), dtype=torch.float32, device=dev)
+        self.shape = make_shape(x, B)
+        self.cshape = Shape(Bt, T, H, P, N, 1, TSV_F32, 0, 0)
+        self._keep = (x, dt, A, B, C, D, h0, parent, accepted, accepted_len)
+        self.st = _stream(stream)
+        self.verify_args = (ctypes.byref(self.shape), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                            _ptr(h0), _ptr(parent), _ptr(self.y), _ptr(self.states), None, self.st)
+        self.commit_tail = (_ptr(parent), _ptr(accepted), _ptr(accepted_len), int(Lmax), None, self.st)
+
+    def materialised_bytes(self) -> int:
+        return self.states.numel() * 4
+
+    def verify(self):
+        rc = lib.tree_ssd_snapshot_verify(*self.verify_args)
+        if rc != 0:
+            raise TreeSSDError(rc, "tree_ssd_snapshot_verify")
+
+    def commit(self, h):
+        rc = lib.tree_ssd_snapshot_commit(ctypes.byref(self.cshape), _ptr(self.states), _ptr(h), *self.commit_tail)
+        if rc != 0:
+            raise TreeSSDError(rc, "tree_ssd_snapshot_commit")

@@ -87,8 +87,15 @@ __device__ __forceinline__ void copy_elems(E* __restrict__ dst, const E* __restr
     const bool vec = ((((uintptr_t)dst) | ((uintptr_t)src)) & 15) == 0 && (n * (int)sizeof(E)) % 16 == 0;
     if (vec) {
         const int nv = n * (int)sizeof(E) / 16;
-        for (int i = threadIdx.x; i < nv; i += kBaseThreads)
-            gstore((uint4*)dst + i, gload((const uint4*)src + i));
+        int i = threadIdx.x;
+        for (; i + 3 * kBaseThreads < nv; i += 4 * kBaseThreads) {  // four loads in flight per thread
+            uint4 t[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) t[u] = gload((const uint4*)src + i + u * kBaseThreads);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) gstore((uint4*)dst + i + u * kBaseThreads, t[u]);
+        }
+        for (; i < nv; i += kBaseThreads) gstore((uint4*)dst + i, gload((const uint4*)src + i));
     } else {
         for (int i = threadIdx.x; i < n; i += kBaseThreads) gstore(dst + i, gload(src + i));
     }
@@ -129,26 +136,103 @@ __global__ __launch_bounds__(kBaseThreads) void unroll_gather_kernel(
 }
 
 // ---------------------------------------------------------------- rows staged in LDS
-template <typename TIO>
+// kTimeChunk rows of x, y (head_dim each), B, C (d_state each) and dt, in the
+// launch's dynamic LDS, sized to the shape so that several work-groups share a
+// compute unit.
 struct RowStage {
-    float x[kTimeChunk][kBaseMaxDim];
-    float B[kTimeChunk][kBaseMaxDim];
-    float C[kTimeChunk][kBaseMaxDim];
-    float y[kTimeChunk][kBaseMaxDim];
-    float dt[kTimeChunk];
+    float* xs;
+    float* ys;
+    float* Bs;
+    float* Cs;
+    float* dts;
+    int P, N;
+    __device__ __forceinline__ RowStage(float* base, int P_, int N_) : P(P_), N(N_) {
+        xs = base;
+        ys = xs + kTimeChunk * P;
+        Bs = ys + kTimeChunk * P;
+        Cs = Bs + kTimeChunk * N;
+        dts = Cs + kTimeChunk * N;
+    }
+    __device__ __forceinline__ float* x(int t) { return xs + t * P; }
+    __device__ __forceinline__ float* y(int t) { return ys + t * P; }
+    __device__ __forceinline__ float* B(int t) { return Bs + t * N; }
+    __device__ __forceinline__ float* C(int t) { return Cs + t * N; }
+};
+static size_t row_stage_bytes(int P, int N) { return sizeof(float) * ((size_t)kTimeChunk * (2 * P + 2 * N) + kTimeChunk); }
+
+// ---------------------------------------------------------------- state slices
+// Thread tid owns the KE consecutive state elements tid*KE .. tid*KE+KE-1 of
+// the P x N state (row-major, n fastest), so its elements sit in one or a few
+// rows and its part of y_t[p] = sum_n H[p][n] C_t[n] is summed in registers
+// and added to the row's LDS total once per row it touches.
+template <int KE>
+struct StateSlice {
+    float v[KE];
+    int e0, p0, n0;  // first element, its row and column
+    __device__ __forceinline__ void init(int PN, int N) {
+        e0 = threadIdx.x * KE;
+        p0 = e0 / N;
+        n0 = e0 - p0 * N;
+    }
+    __device__ __forceinline__ void load(const float* __restrict__ src, int PN) {
+        if ((KE % 4) == 0 && e0 + KE <= PN && (PN % 4) == 0) {
+#pragma unroll
+            for (int k = 0; k < KE; k += 4) {
+                const float4 t = gload((const float4*)(src + e0 + k));
+                v[k] = t.x;
+                v[k + 1] = t.y;
+                v[k + 2] = t.z;
+                v[k + 3] = t.w;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < KE; ++k) v[k] = e0 + k < PN ? gload(src + e0 + k) : 0.f;
+        }
+    }
+    __device__ __forceinline__ void store(float* __restrict__ dst, int PN) const {
+        if ((KE % 4) == 0 && e0 + KE <= PN && (PN % 4) == 0) {
+#pragma unroll
+            for (int k = 0; k < KE; k += 4) gstore((float4*)(dst + e0 + k), make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]));
+        } else {
+#pragma unroll
+            for (int k = 0; k < KE; ++k)
+                if (e0 + k < PN) gstore(dst + e0 + k, v[k]);
+        }
+    }
+    // one step of the recurrence from `src` (this thread's elements of the
+    // previous state), adding this thread's part of y = H C to yrow
+    __device__ __forceinline__ void step(const float (&src)[KE], float a, float d, const float* xr,
+                                         const float* Br, const float* Cr, float* yrow, int PN, int N) {
+        int p = p0, n = n0;
+        float part = 0.f;
+#pragma unroll
+        for (int k = 0; k < KE; ++k) {
+            if (e0 + k < PN) {
+                v[k] = a * src[k] + d * xr[p] * Br[n];
+                part += v[k] * Cr[n];
+            }
+            if (++n == N || k == KE - 1) {
+                if (e0 + k < PN) atomicAdd(&yrow[p], part);
+                part = 0.f;
+                n = 0;
+                ++p;
+            }
+        }
+    }
 };
 
 // ---------------------------------------------------------------- sequence scan
 // One work-group per (sequence, head): h <- exp(dt A) h + dt x (outer) B,
 // y = h C + D x over the sequence's positions, h read from and written back to
-// h_io. Thread tid owns state elements tid + 256 k.
+// h_io.
 template <typename TIO, int KE>
 __global__ __launch_bounds__(kBaseThreads) void seq_scan_kernel(
     const TIO* __restrict__ x_u, const TIO* __restrict__ dt_u, const float* __restrict__ A,
     const TIO* __restrict__ B_u, const TIO* __restrict__ C_u, const float* __restrict__ D,
     float* __restrict__ h_io, const int32_t* __restrict__ seq_len, TIO* __restrict__ y_u, int S,
     int H, int P, int N, int G) {
-    __shared__ RowStage<TIO> rs;
+    extern __shared__ float s_stage[];
+    RowStage rs(s_stage, P, N);
     const int seq = blockIdx.x / H, h = blockIdx.x % H;
     const int g = h / (H / G);
     const int tid = threadIdx.x;
@@ -156,55 +240,38 @@ __global__ __launch_bounds__(kBaseThreads) void seq_scan_kernel(
     if (len <= 0 || len > S) return;
     const int PN = P * N;
     float* hs = h_io + ((size_t)seq * H + h) * PN;
-    float st[KE];
-    int pk[KE], nk[KE];
-#pragma unroll
-    for (int k = 0; k < KE; ++k) {
-        const int e = tid + kBaseThreads * k;
-        pk[k] = e < PN ? e / N : 0;
-        nk[k] = e < PN ? e - pk[k] * N : 0;
-        st[k] = e < PN ? gload(hs + e) : 0.f;
-    }
+    StateSlice<KE> st;
+    st.init(PN, N);
+    st.load(hs, PN);
     const float Ah = A[h], Dh = D[h];
     for (int t0 = 0; t0 < len; t0 += kTimeChunk) {
         const int tc = min(kTimeChunk, len - t0);
         for (int i = tid; i < tc * P; i += kBaseThreads) {
             const int t = i / P, p = i - t * P;
-            rs.x[t][p] = Elem<TIO>::ld(x_u, (((size_t)seq * S + t0 + t) * H + h) * P + p);
-            rs.y[t][p] = 0.f;
+            rs.x(t)[p] = Elem<TIO>::ld(x_u, (((size_t)seq * S + t0 + t) * H + h) * P + p);
+            rs.y(t)[p] = 0.f;
         }
         for (int i = tid; i < tc * N; i += kBaseThreads) {
             const int t = i / N, n = i - t * N;
             const size_t row = (((size_t)seq * S + t0 + t) * G + g) * N + n;
-            rs.B[t][n] = Elem<TIO>::ld(B_u, row);
-            rs.C[t][n] = Elem<TIO>::ld(C_u, row);
+            rs.B(t)[n] = Elem<TIO>::ld(B_u, row);
+            rs.C(t)[n] = Elem<TIO>::ld(C_u, row);
         }
         for (int t = tid; t < tc; t += kBaseThreads)
-            rs.dt[t] = Elem<TIO>::ld(dt_u, ((size_t)seq * S + t0 + t) * H + h);
+            rs.dts[t] = Elem<TIO>::ld(dt_u, ((size_t)seq * S + t0 + t) * H + h);
         __syncthreads();
         for (int t = 0; t < tc; ++t) {
-            const float d = rs.dt[t];
-            const float a = __expf(d * Ah);
-#pragma unroll
-            for (int k = 0; k < KE; ++k) {
-                if (tid + kBaseThreads * k < PN) {
-                    st[k] = a * st[k] + d * rs.x[t][pk[k]] * rs.B[t][nk[k]];
-                    atomicAdd(&rs.y[t][pk[k]], st[k] * rs.C[t][nk[k]]);
-                }
-            }
+            const float d = rs.dts[t];
+            st.step(st.v, __expf(d * Ah), d, rs.x(t), rs.B(t), rs.C(t), rs.y(t), PN, N);
         }
         __syncthreads();
         for (int i = tid; i < tc * P; i += kBaseThreads) {
             const int t = i / P, p = i - t * P;
-            Elem<TIO>::st(y_u, (((size_t)seq * S + t0 + t) * H + h) * P + p, rs.y[t][p] + Dh * rs.x[t][p]);
+            Elem<TIO>::st(y_u, (((size_t)seq * S + t0 + t) * H + h) * P + p, rs.y(t)[p] + Dh * rs.x(t)[p]);
         }
         __syncthreads();
     }
-#pragma unroll
-    for (int k = 0; k < KE; ++k) {
-        const int e = tid + kBaseThreads * k;
-        if (e < PN) gstore(hs + e, st[k]);
-    }
+    st.store(hs, PN);
 }
 
 // ---------------------------------------------------------------- tree checks (any T <= 1024)
@@ -231,7 +298,8 @@ __global__ __launch_bounds__(kBaseThreads) void snapshot_verify_kernel(
     const TIO* __restrict__ Bm, const TIO* __restrict__ Cm, const float* __restrict__ D,
     const float* __restrict__ h0, const int32_t* __restrict__ parent, TIO* __restrict__ y,
     float* __restrict__ states, int32_t* __restrict__ tree_status, int T, int H, int P, int N, int G) {
-    __shared__ RowStage<TIO> rs;
+    extern __shared__ float s_stage[];
+    RowStage rs(s_stage, P, N);
     __shared__ int s_par[kTimeChunk];
     const int b = blockIdx.x / H, h = blockIdx.x % H;
     const int g = h / (H / G);
@@ -242,56 +310,45 @@ __global__ __launch_bounds__(kBaseThreads) void snapshot_verify_kernel(
     if (st) return;
     const int PN = P * N;
     float* sb = states + ((size_t)b * H + h) * T * PN;
-    float cur[KE];
-    int pk[KE], nk[KE];
-#pragma unroll
-    for (int k = 0; k < KE; ++k) {
-        const int e = tid + kBaseThreads * k;
-        pk[k] = e < PN ? e / N : 0;
-        nk[k] = e < PN ? e - pk[k] * N : 0;
-        cur[k] = e < PN ? gload(h0 + ((size_t)b * H + h) * PN + e) : 0.f;
-    }
+    StateSlice<KE> cur, par;
+    cur.init(PN, N);
+    par.init(PN, N);
+    cur.load(h0 + ((size_t)b * H + h) * PN, PN);
     const float Ah = A[h], Dh = D[h];
     for (int t0 = 0; t0 < T; t0 += kTimeChunk) {
         const int tc = min(kTimeChunk, T - t0);
         for (int i = tid; i < tc * P; i += kBaseThreads) {
             const int t = i / P, p = i - t * P;
-            rs.x[t][p] = Elem<TIO>::ld(x, (((size_t)b * T + t0 + t) * H + h) * P + p);
-            rs.y[t][p] = 0.f;
+            rs.x(t)[p] = Elem<TIO>::ld(x, (((size_t)b * T + t0 + t) * H + h) * P + p);
+            rs.y(t)[p] = 0.f;
         }
         for (int i = tid; i < tc * N; i += kBaseThreads) {
             const int t = i / N, n = i - t * N;
             const size_t row = (((size_t)b * T + t0 + t) * G + g) * N + n;
-            rs.B[t][n] = Elem<TIO>::ld(Bm, row);
-            rs.C[t][n] = Elem<TIO>::ld(Cm, row);
+            rs.B(t)[n] = Elem<TIO>::ld(Bm, row);
+            rs.C(t)[n] = Elem<TIO>::ld(Cm, row);
         }
         for (int t = tid; t < tc; t += kBaseThreads) {
-            rs.dt[t] = Elem<TIO>::ld(dt, ((size_t)b * T + t0 + t) * H + h);
+            rs.dts[t] = Elem<TIO>::ld(dt, ((size_t)b * T + t0 + t) * H + h);
             s_par[t] = gload(par_b + t0 + t);
         }
         __syncthreads();
         for (int t = 0; t < tc; ++t) {
             const int node = t0 + t;
             const int pn = s_par[t];
-            const float d = rs.dt[t];
-            const float a = __expf(d * Ah);
-            const bool from_regs = node == 0 || pn == node - 1;
-            const float* ps = sb + (size_t)(from_regs ? 0 : pn) * PN;
-#pragma unroll
-            for (int k = 0; k < KE; ++k) {
-                const int e = tid + kBaseThreads * k;
-                if (e < PN) {
-                    const float src = from_regs ? cur[k] : gload(ps + e);
-                    cur[k] = a * src + d * rs.x[t][pk[k]] * rs.B[t][nk[k]];
-                    gstore(sb + (size_t)node * PN + e, cur[k]);
-                    atomicAdd(&rs.y[t][pk[k]], cur[k] * rs.C[t][nk[k]]);
-                }
+            const float d = rs.dts[t];
+            if (node == 0 || pn == node - 1) {
+                cur.step(cur.v, __expf(d * Ah), d, rs.x(t), rs.B(t), rs.C(t), rs.y(t), PN, N);
+            } else {
+                par.load(sb + (size_t)pn * PN, PN);
+                cur.step(par.v, __expf(d * Ah), d, rs.x(t), rs.B(t), rs.C(t), rs.y(t), PN, N);
             }
+            cur.store(sb + (size_t)node * PN, PN);
         }
         __syncthreads();
         for (int i = tid; i < tc * P; i += kBaseThreads) {
             const int t = i / P, p = i - t * P;
-            Elem<TIO>::st(y, (((size_t)b * T + t0 + t) * H + h) * P + p, rs.y[t][p] + Dh * rs.x[t][p]);
+            Elem<TIO>::st(y, (((size_t)b * T + t0 + t) * H + h) * P + p, rs.y(t)[p] + Dh * rs.x(t)[p]);
         }
         __syncthreads();
     }
@@ -366,7 +423,7 @@ static hipError_t launch_ke(int PN, dim3 grid, hipStream_t stream, Args... args)
 
 template <typename TIO, int KE>
 static void seq_scan_launch(int nblk, hipStream_t stream, const SeqScanArgs& a) {
-    seq_scan_kernel<TIO, KE><<<nblk, kBaseThreads, 0, stream>>>(
+    seq_scan_kernel<TIO, KE><<<nblk, kBaseThreads, row_stage_bytes(a.P, a.N), stream>>>(
         (const TIO*)a.x_u, (const TIO*)a.dt_u, a.A, (const TIO*)a.B_u, (const TIO*)a.C_u, a.D, a.h_io,
         a.seq_len, (TIO*)a.y_u, a.S, a.H, a.P, a.N, a.G);
 }
@@ -395,7 +452,7 @@ hipError_t launch_seq_scan(const SeqScanArgs& a, bool bf16, hipStream_t stream) 
 
 template <typename TIO, int KE>
 static void snapshot_launch(const VerifyArgs& a, float* states, hipStream_t stream) {
-    snapshot_verify_kernel<TIO, KE><<<a.batch * a.H, kBaseThreads, 0, stream>>>(
+    snapshot_verify_kernel<TIO, KE><<<a.batch * a.H, kBaseThreads, row_stage_bytes(a.P, a.N), stream>>>(
         (const TIO*)a.x, (const TIO*)a.dt, a.A, (const TIO*)a.B, (const TIO*)a.C, a.D, a.h0, a.parent,
         (TIO*)a.y, states, a.tree_status, a.T, a.H, a.P, a.N, a.G);
 }
