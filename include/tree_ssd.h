@@ -55,7 +55,9 @@ typedef enum {
     TSV_E_NULL = 1,        /* a required pointer is NULL */
     TSV_E_SHAPE = 2,       /* a size is out of range, H % G != 0, or T > 1024 */
     TSV_E_DTYPE = 3,       /* in_dtype is not a tsv_dtype */
-    TSV_E_UNSUPPORTED = 4, /* the size combination has no kernel */
+    TSV_E_UNSUPPORTED = 4, /* the size combination has no kernel (this includes
+                              head_dim or d_state above 256 and more than
+                              65535 heads) */
     TSV_E_LAUNCH = 5       /* the HIP launch failed (see hipGetLastError) */
 } tsv_status;
 

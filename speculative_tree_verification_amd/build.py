@@ -34,9 +34,19 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-file additions: in verify_tiny.hip the first kernel arguments (up to 14
+# dwords) are preloaded into scalar registers, so that its latency-bound
+# one-wave work-groups issue their first loads without reading the kernel
+# arguments first (the kernel orders its arguments for it). Measured against
+# the same build without it, in one process: 3.82 -> 3.58 us per launch of the
+# 15-node, 80-head layer; the commit kernel ran slower with it (69.3 -> 73.4 us
+# for the 64-layer commit), so it is not preloaded.
+FILE_FLAGS = {"verify_tiny.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON_FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

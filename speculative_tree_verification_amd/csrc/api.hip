@@ -20,6 +20,7 @@ tsv_status check_shape(const tsv_shape* s) {
     if (s->heads_per_block > 0 && (s->n_heads / s->n_groups) % s->heads_per_block != 0)
         return TSV_E_SHAPE;
     if (s->head_dim > kMaxDim || s->d_state > kMaxDim) return TSV_E_UNSUPPORTED;
+    if (s->n_heads > 0xffff) return TSV_E_UNSUPPORTED;  // sizes are packed into 16-bit fields
     // the per-launch grid stays well inside 2^31 work-groups
     if ((long long)s->batch * s->n_heads * 64 > 0x7fffffffLL) return TSV_E_UNSUPPORTED;
     return TSV_OK;

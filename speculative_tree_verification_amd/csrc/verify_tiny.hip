@@ -15,7 +15,8 @@
 //    B and C rows (directly in MFMA operand layout), x, then h0.
 //  * tree (one lane per node, replicated over the four lane groups): the
 //    parent check by ballots; pointer jumping with cross-lane reads gives each
-//    node its ancestor set (a 16-bit mask) and cum_i.
+//    node its ancestor set (a 16-bit mask) and the root-path sum of dt
+//    (cum_i is A times it).
 //  * pair scores on one 16x16x32 bf16 MFMA per k-step: the product
 //    B C^T leaves lane (r, q) holding G_ij for i = r and j = 4q + c.
 //  * those four values, masked by the ancestor set and weighted by
@@ -32,15 +33,22 @@ namespace tsv {
 
 constexpr int kTinyNodes = 16;
 
+// The arguments are ordered so that everything the first loads need (the
+// sizes, then the parents, step sizes, B, C, x and h0) sits in the first 14
+// dwords, which this file's build preloads into scalar registers: the wave
+// issues its loads without waiting for a kernel-argument read.
 template <int KS>
 __global__ __launch_bounds__(64) void verify_tiny_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const float* __restrict__ A,
-    const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
-    const float* __restrict__ D, const float* __restrict__ h0, const int32_t* __restrict__ parent,
-    uint16_t* __restrict__ y, int32_t* __restrict__ tree_status, int T, int H, int G) {
+    int TG, int H, const int32_t* __restrict__ parent, const uint16_t* __restrict__ dt,
+    const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm, const uint16_t* __restrict__ x,
+    const float* __restrict__ h0, const float* __restrict__ A, const float* __restrict__ D,
+    uint16_t* __restrict__ y, int32_t* __restrict__ tree_status) {
     constexpr int N = 32 * KS;
-    // logical block = ((b H + h) 4 + slice)
-    const int blk = xcd_block(blockIdx.x, gridDim.x);
+    const int T = TG & 0xffff, G = TG >> 16;  // T <= 16, G <= H
+    // block = ((b H + h) 4 + slice), in launch order: with every head of an
+    // item reading the same B and C rows, grouping an item on one XCD saves
+    // little, and the grid size would cost a kernel-argument read
+    const int blk = blockIdx.x;
     const int wl = blk & 3;
     const int bh = blk >> 2;
     const int b = bh / H;
@@ -54,10 +62,10 @@ __global__ __launch_bounds__(64) void verify_tiny_kernel(
 
     // ---------------------------------------------------------------- loads
     // (unconditional, from clamped rows, so that the compiler can count the
-    // loads still in flight at each wait; A and D are scalar loads issued
-    // first, so that they are not a round trip of their own after the check)
-    float Ah = A[h];
-    float Dh = D[h];
+    // loads still in flight at each wait). Every vector load's address comes
+    // from preloaded arguments, so they all leave at once; A and D (pointers
+    // read from the kernel arguments) follow as scalar loads and arrive while
+    // the vector loads are in flight.
     int par;
     {
         typedef const int32_t __attribute__((address_space(1))) gint;
@@ -97,6 +105,8 @@ __global__ __launch_bounds__(64) void verify_tiny_kernel(
             hr[ks][1] = gload((const float4*)(hrow + 32 * ks + 4));
         }
     }
+    float Ah = A[h];
+    float Dh = D[h];
     asm volatile("" : "+s"(Ah), "+s"(Dh));  // A and D arrive while the vector loads are in flight
 
     // ---------------------------------------------------------------- tree
@@ -108,24 +118,26 @@ __global__ __launch_bounds__(64) void verify_tiny_kernel(
     if (st) return;
 
     // pointer jumping: after round k, nxt is the ancestor 2^k steps up (or -1),
-    // cum the sum of dt A over the nodes passed, anc the set of those nodes
+    // dsum the sum of dt over the nodes passed (cum = A dsum: A is only needed
+    // once the decays are formed, so its load is off this chain), anc the set
+    // of those nodes
     int nxt = live ? par : -1;
-    float cum = live ? bf16_bits_to_f32(dti) * Ah : 0.f;
+    float dsum = live ? bf16_bits_to_f32(dti) : 0.f;
     uint32_t anc = live ? 1u << r16 : 0u;
     while (__ballot(nxt >= 0)) {
         const int src = nxt >= 0 ? nxt : r16;
-        const float c2 = __shfl(cum, src, kWave);
+        const float c2 = __shfl(dsum, src, kWave);
         const uint32_t a2 = (uint32_t)__shfl((int)anc, src, kWave);
         const int n2 = __shfl(nxt, src, kWave);
         if (nxt >= 0) {
-            cum += c2;
+            dsum += c2;
             anc |= a2;
             nxt = n2;
         }
     }
-    float cumj[4];
+    float dsumj[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) cumj[c] = __shfl(cum, 4 * q + c, kWave);
+    for (int c = 0; c < 4; ++c) dsumj[c] = __shfl(dsum, 4 * q + c, kWave);
 
     // ---------------------------------------------------------------- pair scores
     // gt[c] = G_ij for i = r16, j = 4q + c (A operand: B rows j, B operand: C rows i)
@@ -136,14 +148,14 @@ __global__ __launch_bounds__(64) void verify_tiny_kernel(
                                                      __builtin_bit_cast(bf16x8, creg[ks]), gt, 0, 0, 0);
 
     // ---------------------------------------------------------------- walk term
-    // S_ij = G_ij exp(cum_i - cum_j) dt_j (+ D for j = i) on ancestors j of i,
+    // S_ij = G_ij exp(A (dsum_i - dsum_j)) dt_j (+ D for j = i) on ancestors j of i,
     // 0 elsewhere; tw = x^T S^T: row p of the slice, column i
     f32x4 tw = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const int j = 4 * q + c;
         const float sij = ((anc >> j) & 1u)
-                              ? gt[c] * __expf(cum - cumj[c]) * bf16_bits_to_f32(dtj[c]) + (j == r16 ? Dh : 0.f)
+                              ? gt[c] * __expf(Ah * (dsum - dsumj[c])) * bf16_bits_to_f32(dtj[c]) + (j == r16 ? Dh : 0.f)
                               : 0.f;
         tw = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_bits_to_f32(xv[c]), sij, tw, 0, 0, 0);
     }
@@ -159,7 +171,7 @@ __global__ __launch_bounds__(64) void verify_tiny_kernel(
     }
 
     if (live) {
-        const float sc = __expf(cum);
+        const float sc = __expf(Ah * dsum);
         const uint32_t o01 = pack_bf16x2(acc[0] * sc + tw[0], acc[1] * sc + tw[1]);
         const uint32_t o23 = pack_bf16x2(acc[2] * sc + tw[2], acc[3] * sc + tw[3]);
         *(uint2*)(y + (((size_t)b * T + r16) * H + h) * kHeadDim + 16 * wl + 4 * q) = make_uint2(o01, o23);
@@ -171,9 +183,10 @@ bool verify_tiny_supported(int T) { return T <= kTinyNodes; }
 hipError_t launch_verify_tiny(const VerifyArgs& a, hipStream_t stream) {
     const void* k = a.N == 64 ? (const void*)verify_tiny_kernel<2> : (const void*)verify_tiny_kernel<4>;
     dim3 grid((unsigned)(a.batch * a.H * 4));
-    void* args[] = {(void*)&a.x, (void*)&a.dt, (void*)&a.A, (void*)&a.B, (void*)&a.C, (void*)&a.D,
-                    (void*)&a.h0, (void*)&a.parent, (void*)&a.y, (void*)&a.tree_status,
-                    (void*)&a.T, (void*)&a.H, (void*)&a.G};
+    int TG = a.T | (a.G << 16);  // T <= 16; the shape check bounds G by H
+    void* args[] = {(void*)&TG,  (void*)&a.H,  (void*)&a.parent, (void*)&a.dt,
+                    (void*)&a.B, (void*)&a.C,  (void*)&a.x,      (void*)&a.h0,
+                    (void*)&a.A, (void*)&a.D,  (void*)&a.y,      (void*)&a.tree_status};
     return hipLaunchKernel(k, grid, dim3(kWave), args, 0, stream);
 }
 
