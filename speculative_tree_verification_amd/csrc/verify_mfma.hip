@@ -22,18 +22,15 @@
 //    node's root path through the parents in LDS, and the next parent, the
 //    step size, the x row and the score of an ancestor are read in one round.
 //  * every load leaves at the start, the parents first: no load depends on
-//    the tree, vector memory operations complete in order and every barrier
-//    is LDS-only (a __syncthreads would wait for every load in flight), so the
-//    tree check waits for the parents only, the pair scores for the B and C
-//    tiles, the walk for the x rows, and only the read-out waits for the
-//    wave's 16 x N slice of h0, which is requested last.
+//    the tree, and vector memory operations complete in order, so the tree
+//    check waits for the parents only while the rest (B and C tiles, step
+//    sizes, each wave's 16 x N slice of h0 and its x rows) streams in.
 //  * the read-out C h0^T runs on MFMA with h0 split into bf16 high + low
 //    halves (about 16 significant bits), one k-step at a time; C is an exact
 //    bf16 operand kept in registers.
 //  * the intra-tree term is sparse (depth+1 terms per node), so it is summed
 //    along each node's root path in fp32 VALU, with exp evaluated only on
-//    ancestor pairs and the decay summed along the path (no cancellation). It
-//    runs before the read-out, while h0 is still arriving.
+//    ancestor pairs and the decay summed along the path (no cancellation).
 #include "launch.hpp"
 #include "verify_common.hpp"
 
@@ -69,7 +66,6 @@ void verify_mfma_kernel(
     __shared__ float s_G[TP * TP];
     __shared__ __attribute__((aligned(16))) uint16_t s_x[4 * HW][TP * kXStride];
     __shared__ uint16_t s_dth[HW * TP];  // dt of the work-group's heads, bf16 [slot][node]
-    __shared__ int s_red[NT / kWave];
     // B and C rows of the item's group, padded by 16 bytes per row
     constexpr int BCS = N + 8;
     __shared__ __attribute__((aligned(16))) uint16_t s_Bt[TP * BCS];
@@ -102,37 +98,36 @@ void verify_mfma_kernel(
     for (int m = 0; m < BC_PT; ++m) {
         const int c = tid + NT * m;
         const int r = min(c / CPR, T - 1), ch = c % CPR;
-        breg[m] = gload((const uint4*)(Bm + (bc_row0 + (size_t)r * G) * N + 8 * ch));
-        cregt[m] = gload((const uint4*)(Cm + (bc_row0 + (size_t)r * G) * N + 8 * ch));
+        breg[m] = *(const uint4*)(Bm + (bc_row0 + (size_t)r * G) * N + 8 * ch);
+        cregt[m] = *(const uint4*)(Cm + (bc_row0 + (size_t)r * G) * N + 8 * ch);
     }
     uint32_t dtr[DT_PT];
 #pragma unroll
     for (int m = 0; m < DT_PT; ++m) {
         const int e = min(tid + NT * m, T * HW - 1);
         const int n = e / HW, hh = e - n * HW;  // consecutive threads: consecutive heads of node n
-        dtr[m] = gload(dt + ((size_t)b * T + n) * H + h_first + hh);
+        dtr[m] = dt[((size_t)b * T + n) * H + h_first + hh];
     }
-    // this wave's 16 columns of x (needed by the walk, so requested first) and
-    // its 16 x N slice of h0 (rows 16 wl + r16, needed by the read-out only)
-    uint4 xr[Cfg::kXChunks];
-#pragma unroll
-    for (int m = 0; m < Cfg::kXChunks; ++m) {
-        const int c = lane + kWave * m;
-        const int row = min(c >> 1, T - 1), half = c & 1;  // rows past T are not staged
-        xr[m] = gload((const uint4*)(x + (((size_t)b * T + row) * H + h) * kP + 16 * wl + 8 * half));
-    }
+    // this wave's 16 x N slice of h0 (rows 16 wl + r16) and its 16 columns of x
     float4 hr[KS][2];
     {
         const float* hrow = h0 + (((size_t)b * H + h) * kP + 16 * wl + r16) * N + 8 * q;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            hr[ks][0] = gload((const float4*)(hrow + 32 * ks));
-            hr[ks][1] = gload((const float4*)(hrow + 32 * ks + 4));
+            hr[ks][0] = *(const float4*)(hrow + 32 * ks);
+            hr[ks][1] = *(const float4*)(hrow + 32 * ks + 4);
         }
+    }
+    uint4 xr[Cfg::kXChunks];
+#pragma unroll
+    for (int m = 0; m < Cfg::kXChunks; ++m) {
+        const int c = lane + kWave * m;
+        const int row = min(c >> 1, T - 1), half = c & 1;  // rows past T are not staged
+        xr[m] = *(const uint4*)(x + (((size_t)b * T + row) * H + h) * kP + 16 * wl + 8 * half);
     }
 
     // ---------------------------------------------------------------- set-up
-    const int st = check_tree_lds<NT>(par_i, T, s_par, s_red);
+    const int st = check_tree(par_i, T, s_par);
     if (h_first == 0 && tid == 0 && tree_status) tree_status[b] = st;
     if (st) return;
 #pragma unroll
@@ -151,19 +146,7 @@ void verify_mfma_kernel(
         const int n = e / HW, hh = e - n * HW;
         if (e < T * HW) s_dth[hh * TP + n] = (uint16_t)dtr[m];
     }
-    // this wave's x slice in its own LDS region
-    uint16_t* sx = s_x[w];
-#pragma unroll
-    for (int m = 0; m < Cfg::kXChunks; ++m) {
-        const int c = lane + kWave * m;
-        const int row = c >> 1, half = c & 1;
-        if (row < T) {
-            uint2* dst = (uint2*)(sx + row * kXStride + 8 * half);
-            dst[0] = make_uint2(xr[m].x, xr[m].y);
-            dst[1] = make_uint2(xr[m].z, xr[m].w);
-        }
-    }
-    lds_barrier();
+    __syncthreads();
     // C operands of the read-out MFMA
     bf16x8 creg[TI][KS];
 #pragma unroll
@@ -190,50 +173,21 @@ void verify_mfma_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) s_G[(16 * ti + 4 * q + r) * TP + 16 * tj + r16] = g4[r];
     }
-    lds_barrier();
+    // this wave's x slice in its own LDS region
+    uint16_t* sx = s_x[w];
+#pragma unroll
+    for (int m = 0; m < Cfg::kXChunks; ++m) {
+        const int c = lane + kWave * m;
+        const int row = c >> 1, half = c & 1;
+        if (row < T) {
+            uint2* dst = (uint2*)(sx + row * kXStride + 8 * half);
+            dst[0] = make_uint2(xr[m].x, xr[m].y);
+            dst[1] = make_uint2(xr[m].z, xr[m].w);
+        }
+    }
+    __syncthreads();
 
     // ---------------------------------------------------------------- head
-    // The walk needs the tree, the pair scores and x only, so it runs while the
-    // wave's h0 slice is still in flight; the read-out comes last.
-    const uint16_t* sdt = s_dth + slot * TP;
-    const float Ah = A[h];
-    const float Dh = D[h];
-    float tw[TI][4];  // intra-tree term + D x_i, columns 4q .. 4q+3 of the slice
-    float sc[TI];     // exp(cum_i)
-#pragma unroll
-    for (int it = 0; it < TI; ++it) {
-        const int i = 16 * it + r16;
-        float t0 = 0.f, t1 = 0.f, t2 = 0.f, t3 = 0.f;
-        float s = 0.f;  // sum of dt*A over the path nodes from i up to (excluding) j
-        if (i < T) {
-            // walk up the root path of node i: the next ancestor, its step size,
-            // its x row and its pair score are read in the same round
-            const float* Gi = s_G + i * TP;
-            for (int j = i; j >= 0;) {
-                const int pj = s_par[j];
-                const float dtj = bf16_bits_to_f32(sdt[j]);
-                const float wt = Gi[j] * __expf(s) * dtj;
-                const uint2 xv = *(const uint2*)(sx + j * kXStride + 4 * q);
-                t0 += wt * lo_bf16(xv.x);
-                t1 += wt * hi_bf16(xv.x);
-                t2 += wt * lo_bf16(xv.y);
-                t3 += wt * hi_bf16(xv.y);
-                s += dtj * Ah;
-                j = pj;
-            }
-            const uint2 xi = *(const uint2*)(sx + i * kXStride + 4 * q);
-            t0 += Dh * lo_bf16(xi.x);
-            t1 += Dh * hi_bf16(xi.x);
-            t2 += Dh * lo_bf16(xi.y);
-            t3 += Dh * hi_bf16(xi.y);
-        }
-        tw[it][0] = t0;
-        tw[it][1] = t1;
-        tw[it][2] = t2;
-        tw[it][3] = t3;
-        sc[it] = __expf(s);
-    }
-
     // state read-out: acc[it] = (h0 C^T) tile, rows p = 16 wl + 4q + r, column
     // i; h0 is split into bf16 high and low halves one k-step at a time
     f32x4 acc[TI];
@@ -249,17 +203,39 @@ void verify_mfma_kernel(
             acc[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, creg[it][ks], acc[it], 0, 0, 0);
         }
     }
+
+    const uint16_t* sdt = s_dth + slot * TP;
+    const float Ah = A[h];
+    const float Dh = D[h];
 #pragma unroll
     for (int it = 0; it < TI; ++it) {
         const int i = 16 * it + r16;
-        if (i < T) {
-            const float o0 = acc[it][0] * sc[it] + tw[it][0];
-            const float o1 = acc[it][1] * sc[it] + tw[it][1];
-            const float o2 = acc[it][2] * sc[it] + tw[it][2];
-            const float o3 = acc[it][3] * sc[it] + tw[it][3];
-            gstore((uint2*)(y + (((size_t)b * T + i) * H + h) * kP + 16 * wl + 4 * q),
-                   make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)));
+        if (i >= T) continue;
+        // walk up the root path of node i: the next ancestor, its step size, its
+        // x row and its pair score are read in the same round
+        float t0 = 0.f, t1 = 0.f, t2 = 0.f, t3 = 0.f;
+        float s = 0.f;  // sum of dt*A over the path nodes from i up to (excluding) j
+        const float* Gi = s_G + i * TP;
+        for (int j = i; j >= 0;) {
+            const int pj = s_par[j];
+            const float dtj = bf16_bits_to_f32(sdt[j]);
+            const float wt = Gi[j] * __expf(s) * dtj;
+            const uint2 xv = *(const uint2*)(sx + j * kXStride + 4 * q);
+            t0 += wt * lo_bf16(xv.x);
+            t1 += wt * hi_bf16(xv.x);
+            t2 += wt * lo_bf16(xv.y);
+            t3 += wt * hi_bf16(xv.y);
+            s += dtj * Ah;
+            j = pj;
         }
+        const float sc = __expf(s);
+        const uint2 xi = *(const uint2*)(sx + i * kXStride + 4 * q);
+        const float o0 = acc[it][0] * sc + t0 + Dh * lo_bf16(xi.x);
+        const float o1 = acc[it][1] * sc + t1 + Dh * hi_bf16(xi.x);
+        const float o2 = acc[it][2] * sc + t2 + Dh * lo_bf16(xi.y);
+        const float o3 = acc[it][3] * sc + t3 + Dh * hi_bf16(xi.y);
+        *(uint2*)(y + (((size_t)b * T + i) * H + h) * kP + 16 * wl + 4 * q) =
+            make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
     }
 }
 
