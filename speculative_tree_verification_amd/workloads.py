@@ -364,6 +364,64 @@ def make_tokens(seed: int, parent: np.ndarray, vocab: int = 32000, p_hit: float 
     return draft, target
 
 
+# Vocabulary sizes of the model families the configurations are shaped on
+# (GPT-NeoX tokenizer of Mamba2-2.7B, Llama-3 tokenizer of the 8B hybrid).
+VOCAB = {0: 64, 1: 50280, 2: 50280, 3: 128256, 4: 50280}
+
+
+def make_sampling(seed: int, parent: np.ndarray, vocab: int, temperature: float = 1.0,
+                  draft_noise: float = 2.0, logit_scale: float = 2.0) -> Dict[str, np.ndarray]:
+    """Seeded inputs of stochastic tree acceptance for trees ``parent`` [B][T].
+
+    Synthetic logits per node: the target's are logit_scale times standard
+    Gumbel noise (a peaked, heavy-tailed distribution over the vocabulary),
+    the drafter's the same plus draft_noise times standard normal noise (a
+    drafter that roughly tracks the target; with the defaults the 15-node
+    tree accepts about 2.4 nodes per step at temperature 1, the range of
+    acceptance lengths the STree pages report). Both are turned into fp32
+    distributions by a softmax at ``temperature``. The children of each node
+    draw their tokens from the node's draft distribution one after another
+    without replacement, in increasing node index (Gumbel top-k on the log
+    probabilities). Uniforms are fp32 in [0, 1).
+
+    Returns parent, draft [B][T] int32, p_target and q_draft [B][T][V] fp32,
+    u_node [B][T] fp32 and u_final [B] fp32.
+    """
+    rng = np.random.default_rng([8200, seed])
+    parent = np.asarray(parent, np.int32)
+    B, T = parent.shape
+    V = int(vocab)
+    zt = logit_scale * rng.gumbel(size=(B, T, V))
+    zd = zt + draft_noise * rng.standard_normal((B, T, V))
+
+    def softmax(z):
+        z = z / temperature
+        z = z - z.max(axis=-1, keepdims=True)
+        e = np.exp(z)
+        return (e / e.sum(axis=-1, keepdims=True)).astype(np.float32)
+
+    p = softmax(zt)
+    del zt
+    q = softmax(zd)
+    del zd
+    draft = np.zeros((B, T), np.int32)
+    for b in range(B):
+        kids = [[] for _ in range(T)]
+        for c in range(1, T):
+            kids[parent[b, c]].append(c)
+        draft[b, 0] = rng.integers(0, V)
+        for u in range(T):
+            if not kids[u]:
+                continue
+            with np.errstate(divide="ignore"):
+                keys = np.log(q[b, u].astype(np.float64)) + rng.gumbel(size=V)
+            order = np.argsort(-keys, kind="stable")[:len(kids[u])]
+            draft[b, kids[u]] = order
+    return {"parent": parent, "draft": draft, "p_target": p, "q_draft": q,
+            "u_node": rng.random((B, T), dtype=np.float32),
+            "u_final": rng.random(B, dtype=np.float32)}
+
+
 def make_gdn(seed: int, batch: int, n_nodes: int, n_heads: int, dk: int, dv: int,
              tree: str = "recursive", max_depth: int = 8, max_path_len: int = 9,
              parents: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
