@@ -564,6 +564,38 @@ def accept_timing(torch, bnd, W, wl, rounds):
             "bound": "latency (a few KB per launch)"}
 
 
+def accept_stochastic_timing(torch, bnd, W, wl, reps):
+    """Stochastic acceptance (multi-step speculative sampling) on the
+    workload's trees with synthetic target and draft distributions over the
+    model family's vocabulary, drawn on the GPU. Median and minimum over
+    timed regions of back-to-back launches. Algorithmic bytes: the p and q
+    rows of every visited node read once, plus the small per-node inputs;
+    the kernel re-reads a row once per rejected child (from L2)."""
+    import numpy as np
+    par = wl.sets[0][0]["parent"].cpu().numpy()
+    B, T = par.shape
+    V = W.VOCAB[wl.cfg.cid]
+    d = W.make_sampling_device(31, par, V, "cuda")
+    L = wl.cfg.max_path_len
+    pa = bnd.PreparedAcceptStochastic(d["parent"], d["draft"], d["p_target"], d["q_draft"], d["u_node"],
+                                      d["u_final"], L)
+    for _ in range(3):
+        pa()
+    torch.cuda.synchronize()
+    st = _adaptive_stats(torch, lambda i: pa(), reps)
+    lens = pa.accepted_len.cpu().numpy().astype(np.int64)
+    nbytes = int(lens.sum()) * 8 * V + 4 * (5 * B * T + B * L + 4 * B)
+    us = st["median"]
+    del d, pa
+    torch.cuda.empty_cache()
+    return {"kernel": "accept_stochastic", "vocab": V, "avg_us": round(us, 3), "stats_us": st,
+            "algorithmic_bytes": nbytes, "achieved_GBps": round(nbytes / (us * 1e-6) / 1e9, 2),
+            "mean_accepted_len": round(float(lens.mean()), 3),
+            "timing": "HIP events around back-to-back launches of this kernel alone",
+            "bound": "latency: one work-group per item walks the tree; a rejection is one pass over "
+                     "the node's p and q rows"}
+
+
 def _adaptive_stats(torch, fn, reps, min_region_ms=2.0):
     """timed_stats with enough calls per region for about min_region_ms of GPU time."""
     torch.cuda.synchronize()
@@ -696,6 +728,7 @@ def run_workload(torch, bnd, W, cid, steps, warmup, hpb, keep_host, reps=50):
     c = kernel_report("commit", t["commit_us"], cb, name, source_sha("commit"), t["commit_launches"],
                       t["commit_stats"])
     t["accept"] = accept_timing(torch, bnd, W, wl, steps)
+    t["accept_stochastic"] = accept_stochastic_timing(torch, bnd, W, wl, reps)
     nodes_s = wl.nodes_per_step / (t["ms_per_step"] * 1e-3)
     log(f"[bench] workload {cid}: {t['ms_per_step']:.4f} ms/step, {nodes_s:.4g} nodes/s; "
         f"verify {t['verify_us']:.2f} us ({v['achieved']:.0f} GB/s), "
@@ -763,6 +796,7 @@ def main():
                           for k, vv in t["step_stats"].items()},
         "kernels": {"verify": v, "commit": c},
         "accept": t["accept"],
+        "accept_stochastic": t["accept_stochastic"],
     }
     if layers > 1:
         gms = graph_step_timing(torch, bnd, wl, args.steps)
@@ -777,7 +811,8 @@ def main():
                                             0, keep_host=False, reps=args.reps)
         secondary.append({"workload": wl2.cfg.name, "nodes_per_s": round(ns2, 1),
                           "ms_per_step": round(t2["ms_per_step"], 5),
-                          "verify": v2, "commit": c2, "accept": t2["accept"]})
+                          "verify": v2, "commit": c2, "accept": t2["accept"],
+                          "accept_stochastic": t2["accept_stochastic"]})
         del wl2
         torch.cuda.empty_cache()
     if secondary:

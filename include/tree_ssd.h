@@ -260,6 +260,64 @@ tsv_status tree_ssd_accept_greedy(int32_t batch, int32_t n_nodes, const int32_t*
                                   int32_t max_path_len, int32_t* accepted, int32_t* accepted_len,
                                   int32_t* next_token, int32_t* tree_status, void* stream);
 
+#define TSV_ST_BAD_TOKEN 16 /* a non-root draft token is outside [0, vocab) */
+
+/*
+ * tree_ssd_accept_stochastic -- the accepted root path of each verified tree
+ * at temperature > 0: multi-step speculative sampling over the tree with
+ * siblings drawn without replacement ("STree: Speculative Tree Decoding for
+ * Hybrid State-Space Models", atlas.scime.ai summary, measured-effects table:
+ * multi-step speculative sampling; "TreeSpark: Adaptive Draft Trees
+ * Accelerate Speculative Decoding by 8-14%", section on the lossless
+ * guarantee: siblings sampled without replacement and rejected tokens
+ * resampled from the residual, recursively). The produced tokens follow the
+ * target's distribution whatever the draft's.
+ *
+ * Starting at the root with residual r = p_target[root], the children of the
+ * current node u are tested in increasing index. The k-th child's token t was
+ * drawn from d = q_draft[u] without the earlier children's tokens, divided by
+ * m = 1 - (their draft mass) (d = 0 when m <= 0 or t repeats an earlier
+ * sibling's token). It is accepted when u_node[c] * d[t] < r[t]; an accepted
+ * child becomes u. A rejection replaces r by max(r - d, 0) divided by its mass
+ * (r is kept when that mass is 0). When no child is accepted, next_token is
+ * the first token whose running sum of r exceeds u_final times r's total
+ * (-1 if r has no mass). The path is cut after max_path_len nodes; a child
+ * accepted below the cut gives next_token instead (its token is a draw from
+ * the cut node's target). Decisions are taken in fp64; sums over the
+ * vocabulary are taken in an order of the kernel's own, so a decision can
+ * differ from a left-to-right evaluation only within fp64 rounding of its
+ * threshold.
+ *
+ *   n_nodes       in [1, 1024]; vocab >= 1
+ *   parent        [Bt][T] int32   as for tree_ssd_verify
+ *   draft_tokens  [Bt][T] int32   token of each node (node 0's is not used)
+ *   p_target      [Bt][T][vocab] float32  target distribution of the token
+ *                                 after each node (rows sum to 1)
+ *   q_draft       [Bt][T][vocab] float32  draft distribution the children of
+ *                                 each node drew their tokens from, one after
+ *                                 another without replacement, in index order
+ *   u_node        [Bt][T] float32 uniforms in [0, 1): each non-root node's test
+ *   u_final       [Bt] float32    uniform in [0, 1) of each item's final draw
+ *   max_path_len  in [1, 1024]    row length of `accepted`
+ *   accepted      [Bt][max_path_len] int32  output: node indices of the path,
+ *                                 root first; entries past the length are -1
+ *   accepted_len  [Bt] int32      output: entries of the path (>= 1)
+ *   next_token    [Bt] int32      optional output: the token after the path
+ *   tree_status   [Bt] int32      optional; bits 1|2 of the item's tree, and
+ *                                 TSV_ST_BAD_TOKEN
+ * Only the rows of visited nodes are read (one pass over p_target and q_draft
+ * of a node per rejected child, one more for the final draw). No workspace:
+ * the residual is never stored. Invalid items leave accepted, accepted_len and
+ * next_token untouched. Returns TSV_E_SHAPE for sizes out of range and
+ * TSV_E_NULL for a NULL required pointer.
+ */
+tsv_status tree_ssd_accept_stochastic(int32_t batch, int32_t n_nodes, int32_t vocab,
+                                      const int32_t* parent, const int32_t* draft_tokens,
+                                      const float* p_target, const float* q_draft, const float* u_node,
+                                      const float* u_final, int32_t max_path_len, int32_t* accepted,
+                                      int32_t* accepted_len, int32_t* next_token, int32_t* tree_status,
+                                      void* stream);
+
 /*
  * tree_ssd_tree_info -- the tree mask of each item (the summary's L): depth of
  * every node (edges from the root) and its ancestor-or-self set as W 64-bit

@@ -34,8 +34,9 @@ STATUS_NAMES = {0: "TSV_OK", 1: "TSV_E_NULL", 2: "TSV_E_SHAPE", 3: "TSV_E_DTYPE"
 EXPORTS = ("tree_ssd_verify", "tree_ssd_commit", "tree_ssd_commit_layers", "tree_ssd_accept_greedy",
            "tree_ssd_tree_info", "tree_ssd_status_string", "tree_ssd_abi_version", "tree_gdn_verify",
            "tree_gdn_commit", "tree_ssd_unroll_plan", "tree_ssd_unroll_gather", "tree_ssd_seq_scan",
-           "tree_ssd_snapshot_verify", "tree_ssd_snapshot_commit")
+           "tree_ssd_snapshot_verify", "tree_ssd_snapshot_commit", "tree_ssd_accept_stochastic")
 ST_OVER_CAPACITY = 8
+ST_BAD_TOKEN = 16
 
 
 class Shape(ctypes.Structure):
@@ -77,6 +78,8 @@ def _load():
     L.tree_ssd_accept_greedy.argtypes = [ctypes.c_int32, ctypes.c_int32] + [_VP] * 3 + \
         [ctypes.c_int32] + [_VP] * 5
     L.tree_ssd_accept_greedy.restype = ctypes.c_int
+    L.tree_ssd_accept_stochastic.argtypes = [ctypes.c_int32] * 3 + [_VP] * 6 + [ctypes.c_int32] + [_VP] * 5
+    L.tree_ssd_accept_stochastic.restype = ctypes.c_int
     L.tree_gdn_verify.argtypes = [ctypes.POINTER(Shape)] + [_VP] * 11
     L.tree_gdn_verify.restype = ctypes.c_int
     L.tree_gdn_commit.argtypes = [ctypes.POINTER(Shape)] + [_VP] * 7 + [ctypes.c_int32, _VP, _VP]
@@ -313,6 +316,52 @@ def accept_greedy(parent, draft_tokens, target_tokens, max_path_len: int, accept
     return accepted, accepted_len, next_token, tree_status
 
 
+def _sampling_args(parent, draft_tokens, p_target, q_draft, u_node, u_final):
+    Bt, T = parent.shape
+    V = p_target.shape[-1]
+    dev = parent.device
+    _check(parent, "parent", (Bt, T), torch.int32, dev)
+    _check(draft_tokens, "draft_tokens", (Bt, T), torch.int32, dev)
+    _check(p_target, "p_target", (Bt, T, V), torch.float32, dev)
+    _check(q_draft, "q_draft", (Bt, T, V), torch.float32, dev)
+    _check(u_node, "u_node", (Bt, T), torch.float32, dev)
+    _check(u_final, "u_final", (Bt,), torch.float32, dev)
+    return Bt, T, V, dev
+
+
+def _accept_outputs(Bt, max_path_len, dev, stream):
+    with _on_stream(stream):
+        return (torch.full((Bt, max_path_len), -1, dtype=torch.int32, device=dev),
+                torch.zeros((Bt,), dtype=torch.int32, device=dev),
+                torch.full((Bt,), -1, dtype=torch.int32, device=dev),
+                torch.zeros((Bt,), dtype=torch.int32, device=dev))
+
+
+def accept_stochastic(parent, draft_tokens, p_target, q_draft, u_node, u_final, max_path_len: int,
+                      accepted=None, accepted_len=None, next_token=None, tree_status=None, stream=None):
+    """Stochastic acceptance (multi-step speculative sampling, siblings drawn
+    without replacement) of each item's verified tree: (accepted [Bt,
+    max_path_len] int32, accepted_len [Bt], next_token [Bt], tree_status
+    [Bt]). Outputs of invalid items are left as passed in."""
+    Bt, T, V, dev = _sampling_args(parent, draft_tokens, p_target, q_draft, u_node, u_final)
+    outs = _accept_outputs(Bt, max_path_len, dev, stream)
+    accepted = outs[0] if accepted is None else accepted
+    accepted_len = outs[1] if accepted_len is None else accepted_len
+    next_token = outs[2] if next_token is None else next_token
+    tree_status = outs[3] if tree_status is None else tree_status
+    _check(accepted, "accepted", (Bt, max_path_len), torch.int32, dev)
+    _check(accepted_len, "accepted_len", (Bt,), torch.int32, dev)
+    _check(next_token, "next_token", (Bt,), torch.int32, dev)
+    _check(tree_status, "tree_status", (Bt,), torch.int32, dev)
+    rc = lib.tree_ssd_accept_stochastic(int(Bt), int(T), int(V), _ptr(parent), _ptr(draft_tokens),
+                                        _ptr(p_target), _ptr(q_draft), _ptr(u_node), _ptr(u_final),
+                                        int(max_path_len), _ptr(accepted), _ptr(accepted_len),
+                                        _ptr(next_token), _ptr(tree_status), _stream(stream))
+    if rc != 0:
+        raise TreeSSDError(rc, "tree_ssd_accept_stochastic")
+    return accepted, accepted_len, next_token, tree_status
+
+
 def _gdn_shape(k, v) -> Shape:
     Bt, T, H, dk = k.shape
     return Shape(Bt, T, H, v.shape[-1], dk, 1, TSV_F32, 0, 0)
@@ -521,6 +570,26 @@ class PreparedAccept:
         rc = lib.tree_ssd_accept_greedy(*self.args)
         if rc != 0:
             raise TreeSSDError(rc, "tree_ssd_accept_greedy")
+
+
+class PreparedAcceptStochastic:
+    """tree_ssd_accept_stochastic with fixed buffers; calling it enqueues one launch."""
+
+    def __init__(self, parent, draft_tokens, p_target, q_draft, u_node, u_final, max_path_len: int,
+                 stream=None):
+        Bt, T, V, dev = _sampling_args(parent, draft_tokens, p_target, q_draft, u_node, u_final)
+        self.accepted, self.accepted_len, self.next_token, self.tree_status = \
+            _accept_outputs(Bt, max_path_len, dev, stream)
+        self._keep = (parent, draft_tokens, p_target, q_draft, u_node, u_final)
+        self.args = (int(Bt), int(T), int(V), _ptr(parent), _ptr(draft_tokens), _ptr(p_target),
+                     _ptr(q_draft), _ptr(u_node), _ptr(u_final), int(max_path_len), _ptr(self.accepted),
+                     _ptr(self.accepted_len), _ptr(self.next_token), _ptr(self.tree_status),
+                     _stream(stream))
+
+    def __call__(self):
+        rc = lib.tree_ssd_accept_stochastic(*self.args)
+        if rc != 0:
+            raise TreeSSDError(rc, "tree_ssd_accept_stochastic")
 
 
 # ---------------------------------------------------------------------------

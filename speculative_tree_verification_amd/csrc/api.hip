@@ -182,6 +182,24 @@ tsv_status tree_ssd_accept_greedy(int32_t batch, int32_t n_nodes, const int32_t*
     return e == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
 }
 
+tsv_status tree_ssd_accept_stochastic(int32_t batch, int32_t n_nodes, int32_t vocab,
+                                      const int32_t* parent, const int32_t* draft_tokens,
+                                      const float* p_target, const float* q_draft, const float* u_node,
+                                      const float* u_final, int32_t max_path_len, int32_t* accepted,
+                                      int32_t* accepted_len, int32_t* next_token, int32_t* tree_status,
+                                      void* stream) {
+    if (batch < 0 || n_nodes < 0 || n_nodes > kMaxNodes || vocab < 1) return TSV_E_SHAPE;
+    if (max_path_len < 1 || max_path_len > kMaxNodes) return TSV_E_SHAPE;
+    if (batch == 0 || n_nodes == 0) return TSV_OK;
+    if (!parent || !draft_tokens || !p_target || !q_draft || !u_node || !u_final || !accepted ||
+        !accepted_len)
+        return TSV_E_NULL;
+    hipError_t e = tsv::launch_accept_stochastic(batch, n_nodes, vocab, parent, draft_tokens, p_target,
+                                                 q_draft, u_node, u_final, max_path_len, accepted,
+                                                 accepted_len, next_token, tree_status, (hipStream_t)stream);
+    return e == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
+}
+
 tsv_status tree_ssd_tree_info(int32_t batch, int32_t n_nodes, const int32_t* parent,
                               int32_t* depth, uint64_t* anc_bits, int32_t* tree_status,
                               void* stream) {

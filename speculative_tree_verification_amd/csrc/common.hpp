@@ -23,6 +23,7 @@ constexpr int kWave = 64;
 constexpr int kStBadRoot = 1;
 constexpr int kStBadParent = 2;
 constexpr int kStBadPath = 4;
+constexpr int kStBadToken = 16;  // a draft token outside the vocabulary
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

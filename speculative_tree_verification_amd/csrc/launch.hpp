@@ -113,5 +113,9 @@ hipError_t launch_accept_greedy(int batch, int T, const int32_t* parent, const i
                                 const int32_t* target, int Lmax, int32_t* accepted,
                                 int32_t* accepted_len, int32_t* next_token, int32_t* tree_status,
                                 hipStream_t stream);
+hipError_t launch_accept_stochastic(int batch, int T, int V, const int32_t* parent, const int32_t* draft,
+                                    const float* p_target, const float* q_draft, const float* u_node,
+                                    const float* u_final, int Lmax, int32_t* accepted, int32_t* accepted_len,
+                                    int32_t* next_token, int32_t* tree_status, hipStream_t stream);
 
 }  // namespace tsv

@@ -422,6 +422,50 @@ def make_sampling(seed: int, parent: np.ndarray, vocab: int, temperature: float 
             "u_final": rng.random(B, dtype=np.float32)}
 
 
+def make_sampling_device(seed: int, parent: np.ndarray, vocab: int, device, temperature: float = 1.0,
+                         draft_noise: float = 2.0, logit_scale: float = 2.0) -> Dict[str, object]:
+    """make_sampling's recipe drawn with torch on ``device`` (for vocabulary
+    rows too large to build on the host): the same distributions, not the
+    same numbers. Returns torch tensors under make_sampling's keys."""
+    import torch
+    parent = np.asarray(parent, np.int32)
+    B, T = parent.shape
+    V = int(vocab)
+    g = torch.Generator(device=device)
+    g.manual_seed(8300 + seed)
+
+    def gumbel(shape):
+        u = torch.rand(shape, generator=g, device=device, dtype=torch.float32).clamp_(1e-30, 1.0)
+        return -torch.log(-torch.log(u).clamp_(max=-1e-30))
+
+    zt = logit_scale * gumbel((B, T, V))
+    zd = zt + draft_noise * torch.randn((B, T, V), generator=g, device=device)
+    p = torch.softmax(zt / temperature, dim=-1)
+    del zt
+    q = torch.softmax(zd / temperature, dim=-1)
+    del zd
+    rank = np.zeros((B, T), np.int64)
+    kmax = 1
+    for b in range(B):
+        seen = np.zeros(T, np.int64)
+        for c in range(1, T):
+            rank[b, c] = seen[parent[b, c]]
+            seen[parent[b, c]] += 1
+        kmax = max(kmax, int(seen.max()))
+    keys = torch.log(q) + gumbel((B, T, V))
+    top = torch.topk(keys, kmax, dim=-1).indices          # draw order, best first
+    del keys
+    par_t = torch.from_numpy(np.maximum(parent, 0).astype(np.int64)).to(device)
+    rank_t = torch.from_numpy(rank).to(device)
+    bidx = torch.arange(B, device=device)[:, None].expand(B, T)
+    draft = top[bidx, par_t, rank_t].to(torch.int32)
+    draft[:, 0] = torch.randint(0, V, (B,), generator=g, device=device, dtype=torch.int32)
+    return {"parent": torch.from_numpy(parent).to(device), "draft": draft.contiguous(),
+            "p_target": p.contiguous(), "q_draft": q.contiguous(),
+            "u_node": torch.rand((B, T), generator=g, device=device),
+            "u_final": torch.rand((B,), generator=g, device=device)}
+
+
 def make_gdn(seed: int, batch: int, n_nodes: int, n_heads: int, dk: int, dv: int,
              tree: str = "recursive", max_depth: int = 8, max_path_len: int = 9,
              parents: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
