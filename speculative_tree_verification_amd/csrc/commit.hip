@@ -15,8 +15,19 @@
 // LDS behind LDS-only barriers, so dt, x and B of the path rows are requested
 // while the state chunk is still in flight (their round trip overlaps the
 // state's). The state is streamed once: each element is read and written by
-// the same thread (rank-L update in registers). Invalid items leave h0
-// untouched.
+// the same thread (rank-L update in registers), with nontemporal loads and
+// stores, so that it does not displace the rows and indices that every
+// work-group of a layer re-reads (the 64-layer commit of the 15-node tree
+// went from 62.9 to 56.6 us with them, batch 16 x 31 nodes from 22.4 to 17.9,
+// batch 32 x 63 nodes from 20.8 to 16.8, batch 64 x 255 nodes from 66.3 to
+// 60.0, each measured in one process against the same build without). Invalid items leave h0
+// untouched. For small trees (one 16-byte piece of x and B rows per thread
+// covers every node) the rows of all nodes are requested in the first round
+// trip instead, and the path's rows are picked from registers after
+// validation: no second round trip (the 64-layer commit of the 15-node tree:
+// 69.4 -> 62.9 us). The x rows of the other nodes cost a few percent of the
+// state's traffic there (T <= N / 4); two pieces per thread (the 31- and
+// 63-node trees) needed 118 registers and ran no faster.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -25,7 +36,15 @@ namespace tsv {
 constexpr int kPathChunk = 16;  // path entries staged in LDS at a time
 constexpr int kVec = 4;         // float4 per thread per work-group
 
-template <typename TIO, bool VEC>
+// eight bf16 values (one 16-byte piece of a row) to fp32 in LDS
+__device__ __forceinline__ void put8(float* dst, uint4 v) {
+    *(float4*)dst = make_float4(bf16_bits_to_f32(v.x & 0xffff), bf16_bits_to_f32(v.x >> 16),
+                                bf16_bits_to_f32(v.y & 0xffff), bf16_bits_to_f32(v.y >> 16));
+    *(float4*)(dst + 4) = make_float4(bf16_bits_to_f32(v.z & 0xffff), bf16_bits_to_f32(v.z >> 16),
+                                      bf16_bits_to_f32(v.w & 0xffff), bf16_bits_to_f32(v.w >> 16));
+}
+
+template <typename TIO, bool VEC, bool PRE>
 __global__ __launch_bounds__(kBlock) void commit_kernel(
     const TIO* __restrict__ x_arg, const TIO* __restrict__ dt_arg, const float* __restrict__ A_arg,
     const TIO* __restrict__ B_arg, float* __restrict__ h_arg, const tsv_commit_layer* __restrict__ layers,
@@ -34,6 +53,7 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
     int H, int P, int N, int G, int Lmax, int chunks) {
     __shared__ int s_par[kMaxNodes];
     __shared__ int s_path[kMaxNodes];
+    __shared__ int s_pos[kMaxNodes];  // path position of each node, or -1 (PRE)
     __shared__ float s_w[kMaxNodes];
     __shared__ float s_w0;
     __shared__ int s_red[kBlock / kWave];
@@ -71,6 +91,19 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
     const int len = accepted_len[b];
     const int acc_i = Lmax > 0 ? accepted[(size_t)b * Lmax + min(tid, Lmax - 1)] : 0;
     const int par_i = load_parent(parent + (size_t)b * T, T);
+    // PRE: piece tid of every node's x rows and of every node's B rows, and
+    // node tid's dt, ahead of the state (waiting for them leaves the state in
+    // flight); clamped, so every thread issues the same loads
+    constexpr bool pre = PRE && sizeof(TIO) == 2 && VEC;  // the launch checks the sizes
+    const int px = P / 8, pb = N / 8;
+    uint4 rx = make_uint4(0, 0, 0, 0), rb = rx;
+    uint32_t rdt = 0;
+    if (pre) {
+        const int ex = min(tid, T * px - 1), eb = min(tid, T * pb - 1);
+        rx = gload((const uint4*)(x + (((size_t)b * T + ex / px) * H + hd) * P + 8 * (ex % px)));
+        rb = gload((const uint4*)(Bm + (((size_t)b * T + eb / pb) * G + g) * N + 8 * (eb % pb)));
+        rdt = gload((const uint16_t*)dt + ((size_t)b * T + min(tid, T - 1)) * H + hd);
+    }
     // state chunk (written back only for a valid item)
     float* hb = h + ((size_t)b * H + hd) * PN;
     const int e0 = chunk * (kBlock * kVec * 4);
@@ -82,7 +115,7 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
         if (VEC) {
             // unconditional (clamped) loads, so that waits for the earlier
             // index loads can leave these in flight
-            float4 t = gload((const float4*)(hb + min(pe[v], PN - 4)));
+            float4 t = gload_nt((const float4*)(hb + min(pe[v], PN - 4)));
             if (pe[v] >= PN) t = make_float4(0.f, 0.f, 0.f, 0.f);
             acc[v][0] = t.x;
             acc[v][1] = t.y;
@@ -99,6 +132,7 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
     // len <= T (this also keeps every path index inside s_path)
     const bool len_ok = len >= 0 && len <= Lmax && len <= T;
     if (len_ok && tid < len) s_path[tid] = acc_i;
+    if (pre && tid < T) s_pos[tid] = -1;
     // LDS-only barriers from here on: the state chunk stays in flight while the
     // tree and path are checked and the path rows are requested
     int st = check_tree_lds<kBlock>(par_i, T, s_par, s_red);  // barrier: s_path visible too
@@ -112,6 +146,7 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
                 bad_path = node != 0;
             else
                 bad_path = node < 0 || node >= T || s_par[node] != s_path[tid - 1];
+            if (pre && node >= 0 && node < T) s_pos[node] = tid;  // used only for a valid path
         }
     }
     if (lds_sync_or<kBlock>(bad_path, s_red)) st |= kStBadPath;
@@ -127,12 +162,6 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
             // head_dim 64 and d_state 128)
             const int px = P / 8, pb = N / 8;
             const int nx = kn * px, nb = kn * pb;
-            auto put8 = [](float* dst, uint4 v) {
-                *(float4*)dst = make_float4(bf16_bits_to_f32(v.x & 0xffff), bf16_bits_to_f32(v.x >> 16),
-                                            bf16_bits_to_f32(v.y & 0xffff), bf16_bits_to_f32(v.y >> 16));
-                *(float4*)(dst + 4) = make_float4(bf16_bits_to_f32(v.z & 0xffff), bf16_bits_to_f32(v.z >> 16),
-                                                  bf16_bits_to_f32(v.w & 0xffff), bf16_bits_to_f32(v.w >> 16));
-            };
             for (int e = tid; e < max(nx, nb); e += kBlock) {
                 uint4 vx = make_uint4(0, 0, 0, 0), vb = vx;
                 if (e < nx) {
@@ -160,8 +189,16 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
     for (int k0 = 0; k0 < len; k0 += kPathChunk) {
         const int kn = min(kPathChunk, len - k0);
         if (k0 > 0) lds_barrier();  // previous chunk consumed
-        if (k0 == 0 && tid < len) s_w[tid] = Elem<TIO>::ld(dt, ((size_t)b * T + s_path[tid]) * H + hd);
-        stage_rows(k0, kn);
+        if (pre) {
+            // len <= Lmax <= kPathChunk: one chunk; the path's rows out of the
+            // preloaded pieces, at their path positions
+            if (tid < T && s_pos[tid] >= 0) s_w[s_pos[tid]] = bf16_bits_to_f32(rdt);
+            if (tid < T * px && s_pos[tid / px] >= 0) put8(s_wx + 8 * (s_pos[tid / px] * px + tid % px), rx);
+            if (tid < T * pb && s_pos[tid / pb] >= 0) put8(s_B + 8 * (s_pos[tid / pb] * pb + tid % pb), rb);
+        } else {
+            if (k0 == 0 && tid < len) s_w[tid] = Elem<TIO>::ld(dt, ((size_t)b * T + s_path[tid]) * H + hd);
+            stage_rows(k0, kn);
+        }
         lds_barrier();
         if (k0 == 0) {
             // decay weights along the path: w_k = exp(c_{k+1}) dt_{j_k}, w0 = exp(c_0)
@@ -243,7 +280,7 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
     for (int v = 0; v < kVec; ++v) {
         if (VEC) {
             if (pe[v] < PN)
-                gstore((float4*)(hb + pe[v]), make_float4(acc[v][0], acc[v][1], acc[v][2], acc[v][3]));
+                gstore_nt((float4*)(hb + pe[v]), make_float4(acc[v][0], acc[v][1], acc[v][2], acc[v][3]));
         } else {
 #pragma unroll
             for (int c = 0; c < 4; ++c)
@@ -259,17 +296,21 @@ hipError_t launch_commit(const CommitArgs& a, bool bf16, hipStream_t stream) {
     dim3 grid((unsigned)((size_t)a.n_layers * BH * chunks));
     const size_t lds = sizeof(float) * kPathChunk * (size_t)(a.P + a.N);
     const bool vec = (a.N % 4) == 0;
-#define TSV_COMMIT(TIO, V)                                                                   \
-    hipLaunchKernelGGL((commit_kernel<TIO, V>), grid, dim3(kBlock), lds, stream,             \
+    // one piece of every node's x and B rows per thread, the path in one chunk
+    const bool pre = bf16 && vec && a.P % 8 == 0 && a.N % 8 == 0 && a.T * (a.P / 8) <= kBlock &&
+                     a.T * (a.N / 8) <= kBlock && 4 * a.T <= a.N && a.Lmax <= kPathChunk;
+#define TSV_COMMIT(TIO, V, PR)                                                               \
+    hipLaunchKernelGGL((commit_kernel<TIO, V, PR>), grid, dim3(kBlock), lds, stream,         \
                        (const TIO*)a.x, (const TIO*)a.dt, a.A, (const TIO*)a.B, a.h, a.layers, \
                        a.parent, a.accepted, a.accepted_len, a.tree_status, BH, a.T, a.H, a.P, \
                        a.N, a.G, a.Lmax, chunks)
     if (bf16) {
-        if (vec) TSV_COMMIT(uint16_t, true);
-        else TSV_COMMIT(uint16_t, false);
+        if (pre) TSV_COMMIT(uint16_t, true, true);
+        else if (vec) TSV_COMMIT(uint16_t, true, false);
+        else TSV_COMMIT(uint16_t, false, false);
     } else {
-        if (vec) TSV_COMMIT(float, true);
-        else TSV_COMMIT(float, false);
+        if (vec) TSV_COMMIT(float, true, false);
+        else TSV_COMMIT(float, false, false);
     }
 #undef TSV_COMMIT
     return hipGetLastError();

@@ -86,6 +86,23 @@ __device__ __forceinline__ void gstore(uint4* p, const uint4& v) {
     *(gu32x4 __attribute__((address_space(1)))*)p = gu32x4{v.x, v.y, v.z, v.w};
 }
 
+// Nontemporal 16-byte global load and store, for data a launch touches once
+// (a state read once and written once): it is streamed instead of being kept
+// in the caches other work-groups re-read from.
+__device__ __forceinline__ float4 gload_nt(const float4* p) {
+    const gf32x4 v = __builtin_nontemporal_load((const gf32x4 __attribute__((address_space(1)))*)p);
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void gstore_nt(float4* p, const float4& v) {
+    __builtin_nontemporal_store(gf32x4{v.x, v.y, v.z, v.w}, (gf32x4 __attribute__((address_space(1)))*)p);
+}
+__device__ __forceinline__ void gstore_nt(uint2* p, const uint2& v) {
+    __builtin_nontemporal_store(gu32x2{v.x, v.y}, (gu32x2 __attribute__((address_space(1)))*)p);
+}
+__device__ __forceinline__ void gstore_nt(uint4* p, const uint4& v) {
+    __builtin_nontemporal_store(gu32x4{v.x, v.y, v.z, v.w}, (gu32x4 __attribute__((address_space(1)))*)p);
+}
+
 // element access for the two input dtypes (float, or bf16 stored as uint16_t)
 template <typename TIO>
 struct Elem;

@@ -12,7 +12,10 @@
 // own: a one-wave work-group per (item, head, 16-row slice of head_dim), with
 // no LDS and no barrier, so the only wait is one memory round trip.
 //  * loads leave in the order they are needed: parents and step sizes, the
-//    B and C rows (directly in MFMA operand layout), x, then h0.
+//    B and C rows (directly in MFMA operand layout), x, then h0. h0, read
+//    once, and y are streamed with nontemporal accesses (3.57 -> 3.37 us per
+//    launch of the 15-node, 80-head layer, measured in one process against
+//    the same build with plain accesses).
 //  * tree (one lane per node, replicated over the four lane groups): the
 //    parent check by ballots; pointer jumping with cross-lane reads gives each
 //    node its ancestor set (a 16-bit mask) and the root-path sum of dt
@@ -101,8 +104,8 @@ __global__ __launch_bounds__(64) void verify_tiny_kernel(
         const float* hrow = h0 + (((size_t)b * H + h) * kHeadDim + 16 * wl + r16) * N + 8 * q;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            hr[ks][0] = gload((const float4*)(hrow + 32 * ks));
-            hr[ks][1] = gload((const float4*)(hrow + 32 * ks + 4));
+            hr[ks][0] = gload_nt((const float4*)(hrow + 32 * ks));
+            hr[ks][1] = gload_nt((const float4*)(hrow + 32 * ks + 4));
         }
     }
     float Ah = A[h];
@@ -174,7 +177,7 @@ __global__ __launch_bounds__(64) void verify_tiny_kernel(
         const float sc = __expf(Ah * dsum);
         const uint32_t o01 = pack_bf16x2(acc[0] * sc + tw[0], acc[1] * sc + tw[1]);
         const uint32_t o23 = pack_bf16x2(acc[2] * sc + tw[2], acc[3] * sc + tw[3]);
-        *(uint2*)(y + (((size_t)b * T + r16) * H + h) * kHeadDim + 16 * wl + 4 * q) = make_uint2(o01, o23);
+        gstore_nt((uint2*)(y + (((size_t)b * T + r16) * H + h) * kHeadDim + 16 * wl + 4 * q), make_uint2(o01, o23));
     }
 }
 
