@@ -455,19 +455,27 @@ def large_cpu_baseline(base, seconds):
                       f"in fp64, {used:.1f} s of oracle time", "seconds": round(used, 2), **host_cpus()}
 
 
-def gdn_timing(torch, bnd, W, rounds, oracle_seconds=0.0):
+def gdn_timing(torch, bnd, W, rounds, oracle_seconds=0.0, dtype="f32", shape=None, tree="recursive"):
     """Gated-delta-rule tree verify and commit on a batch-16 layer over the
-    31-node random trees (16 heads, dk = dv = 128, fp32), rotating input sets;
-    average durations of back-to-back launches of each kernel alone."""
-    sh = GDN_SHAPE
-    base = W.make_gdn(31, **sh, max_path_len=5)
+    31-node random trees (16 heads, dk = dv = 128; q, k, v and o fp32 or
+    bf16), rotating input sets; average durations of back-to-back launches of
+    each kernel alone."""
+    import numpy as np
+    sh = shape or GDN_SHAPE
+    base = W.make_gdn(31, **sh, max_path_len=5, dtype=dtype, tree=tree)
     B, T, H, dk, dv = sh["batch"], sh["n_nodes"], sh["n_heads"], sh["dk"], sh["dv"]
-    one = sum(a.nbytes for a in base.values()) + 2 * base["v"].nbytes
+    io = 2 if dtype == W.BF16 else 4
+    one = sum(a.nbytes for a in base.values()) + base["v"].nbytes + 4 * base["v"].size
     nsets = max(2, -(-ROTATE_BYTES // one))
+
+    def up(v):
+        t = torch.from_numpy(np.ascontiguousarray(v))
+        return (t.view(torch.int16).view(torch.bfloat16) if v.dtype == np.uint16 else t).cuda()
     sets = []
     for i in range(nsets):
-        d = {k: torch.from_numpy(v).cuda() for k, v in base.items()}
-        d["o"], d["e"] = torch.empty_like(d["v"]), torch.empty_like(d["v"])
+        d = {k: up(v) for k, v in base.items()}
+        d["o"] = torch.empty_like(d["v"])
+        d["e"] = torch.empty(d["v"].shape, dtype=torch.float32, device=d["v"].device)
         sets.append(d)
 
     def ver(d):
@@ -476,10 +484,14 @@ def gdn_timing(torch, bnd, W, rounds, oracle_seconds=0.0):
     def com(d):
         bnd.gdn_commit(d["k"], d["g"], d["e"], d["S0"], d["parent"], d["accepted"], d["accepted_len"])
 
-    out = {"workload": f"gdn-b{B}-tree{T}-h{H}-dk{dk}-dv{dv}", "dtype": "f32"}
+    out = {"workload": f"gdn-b{B}-tree{T}{'-' + tree if tree != 'recursive' else ''}-h{H}-dk{dk}-dv{dv}",
+           "dtype": dtype}
     L = int(base["accepted_len"].sum())
-    nbytes = {"verify": 4 * (B * T * H * (2 * dk + 3 * dv + 2) + B * H * dv * dk) + 4 * B * T,
-              "commit": 4 * (2 * B * H * dv * dk + L * H * (dk + dv + 1)) + 4 * B * (T + 6)}
+    # verify: q, k, v read and o written in the input type; e written, g,
+    # beta, S0 and the parents read in fp32 / int32. commit: S0 read and
+    # written, the path's k rows (input type), e rows and g.
+    nbytes = {"verify": B * T * H * (io * (2 * dk + 2 * dv) + 4 * dv + 8) + 4 * B * H * dv * dk + 4 * B * T,
+              "commit": 8 * B * H * dv * dk + L * H * (io * dk + 4 * dv + 4) + 4 * B * (T + 6)}
     for name, fn in (("verify", ver), ("commit", com)):
         for d in sets:
             fn(d)
@@ -829,6 +841,9 @@ def main():
             torch.cuda.empty_cache()
     if not args.no_gdn:
         out["gdn"] = gdn_timing(torch, bnd, W, args.secondary_steps, 0.0 if args.no_oracle else 3.0)
+        out["gdn_bf16"] = gdn_timing(torch, bnd, W, args.secondary_steps, 0.0, dtype=W.BF16)
+        out["gdn_large"] = gdn_timing(torch, bnd, W, args.secondary_steps, 0.0,
+                                      shape=dict(GDN_SHAPE, n_nodes=255), tree="level")
         log(f"[bench] gated delta rule {out['gdn']['workload']}: verify {out['gdn']['verify']['avg_us']:.2f} us, "
             f"commit {out['gdn']['commit']['avg_us']:.2f} us")
     if not args.no_large:

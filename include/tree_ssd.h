@@ -197,34 +197,41 @@ tsv_status tree_ssd_commit_layers(const tsv_shape* s, int32_t n_layers,
  *       = beta_i (v_i - exp(G_i) S0 k_i)
  * and o_i = exp(G_i) S0 q_i + sum_{j on path(i)} exp(G_i - G_j) (q_i . k_j) e_j.
  *
- * The shape uses tsv_shape with head_dim = dv, d_state = dk, n_groups = 1,
- * in_dtype = TSV_F32 (all tensors fp32); n_nodes <= 64, dk and dv <= 128
- * (TSV_E_UNSUPPORTED otherwise).
+ * The shape uses tsv_shape with head_dim = dv, d_state = dk, n_groups = 1;
+ * in_dtype is the type of q, k, v and o: TSV_F32 or TSV_BF16 (bf16 bit
+ * patterns); g, beta, S0 and e are fp32 either way. n_nodes <= 256, dk and
+ * dv <= 128 (TSV_E_UNSUPPORTED otherwise). Trees of 65 to 256 nodes take a
+ * plain kernel that solves the pseudo-values in place in e, so e is required
+ * there (TSV_E_NULL otherwise), and a tree with more than 4096
+ * ancestor-or-self pairs (the sum over nodes of depth + 1) sets status bit 8
+ * and is left untouched.
  *   q, k   [Bt][T][H][dk]   queries and keys (keys normally of unit length)
  *   v      [Bt][T][H][dv]   values
  *   g      [Bt][T][H]       log gate (<= 0)
  *   beta   [Bt][T][H]       step in [0, 1]
  *   S0     [Bt][H][dv][dk]  state before the root (read only)
  *   parent [Bt][T]          as for tree_ssd_verify
- *   o      [Bt][T][H][dv]   output
- *   e      [Bt][T][H][dv]   optional output: the pseudo-values, input of commit
- *   tree_status [Bt]        optional; bits 1|2
- * fp32 arithmetic throughout.
+ *   o      [Bt][T][H][dv]   output (in_dtype; bf16 rounded to nearest even)
+ *   e      [Bt][T][H][dv]   optional output, fp32: the pseudo-values, input of commit
+ *   tree_status [Bt]        optional; bits 1|2, and 8 as above
+ * fp32 arithmetic throughout (bf16 inputs are exact in it).
  */
-tsv_status tree_gdn_verify(const tsv_shape* s, const float* q, const float* k, const float* v,
+tsv_status tree_gdn_verify(const tsv_shape* s, const void* q, const void* k, const void* v,
                            const float* g, const float* beta, const float* S0,
-                           const int32_t* parent, float* o, float* e, int32_t* tree_status,
+                           const int32_t* parent, void* o, float* e, int32_t* tree_status,
                            void* stream);
 
 /*
  * tree_gdn_commit -- overwrite S0 with the state at the end of each item's
  * accepted root path from the pseudo-values tree_gdn_verify wrote:
  *   S' = exp(G_l) S0 + sum_{j on the path} exp(G_l - G_j) e_j k_j^T.
- * k, g, parent as for tree_gdn_verify; e from it; accepted, accepted_len,
+ * k (in_dtype), g, parent as for tree_gdn_verify; e (fp32) from it; accepted, accepted_len,
  * max_path_len and tree_status (bits 1|2|4) as for tree_ssd_commit. len == 0
- * leaves S0 unchanged; invalid items leave it untouched.
+ * leaves S0 unchanged; invalid items leave it untouched. Past 64 nodes,
+ * max_path_len must be at most 64 (TSV_E_UNSUPPORTED otherwise): the path's
+ * rows are staged whole in LDS.
  */
-tsv_status tree_gdn_commit(const tsv_shape* s, const float* k, const float* g, const float* e,
+tsv_status tree_gdn_commit(const tsv_shape* s, const void* k, const float* g, const float* e,
                            float* S0_inout, const int32_t* parent, const int32_t* accepted,
                            const int32_t* accepted_len, int32_t max_path_len, int32_t* tree_status,
                            void* stream);

@@ -364,23 +364,25 @@ def accept_stochastic(parent, draft_tokens, p_target, q_draft, u_node, u_final, 
 
 def _gdn_shape(k, v) -> Shape:
     Bt, T, H, dk = k.shape
-    return Shape(Bt, T, H, v.shape[-1], dk, 1, TSV_F32, 0, 0)
+    return Shape(Bt, T, H, v.shape[-1], dk, 1, _dtype_code(k), 0, 0)
 
 
 def gdn_verify(q, k, v, g, beta, S0, parent, o=None, e=None, tree_status=None, stream=None):
-    """(o, e) of one gated-delta-rule layer over packed trees (tree_gdn_verify)."""
+    """(o, e) of one gated-delta-rule layer over packed trees (tree_gdn_verify).
+    q, k, v (and o) float32 or bfloat16; g, beta, S0 and e float32."""
     Bt, T, H, dk = k.shape
     dv = v.shape[-1]
-    dev = k.device
+    dev, io = k.device, k.dtype
     f32 = torch.float32
-    for t, name, shp in ((q, "q", (Bt, T, H, dk)), (k, "k", (Bt, T, H, dk)), (v, "v", (Bt, T, H, dv)),
-                         (g, "g", (Bt, T, H)), (beta, "beta", (Bt, T, H)), (S0, "S0", (Bt, H, dv, dk))):
-        _check(t, name, shp, f32, dev)
+    for t, name, shp, dt in ((q, "q", (Bt, T, H, dk), io), (k, "k", (Bt, T, H, dk), io),
+                             (v, "v", (Bt, T, H, dv), io), (g, "g", (Bt, T, H), f32),
+                             (beta, "beta", (Bt, T, H), f32), (S0, "S0", (Bt, H, dv, dk), f32)):
+        _check(t, name, shp, dt, dev)
     _check(parent, "parent", (Bt, T), torch.int32, dev)
     with _on_stream(stream):
         o = torch.empty_like(v) if o is None else o
-        e = torch.empty_like(v) if e is None else e
-    _check(o, "o", (Bt, T, H, dv), f32, dev)
+        e = torch.empty(v.shape, dtype=f32, device=dev) if e is None else e
+    _check(o, "o", (Bt, T, H, dv), io, dev)
     _check(e, "e", (Bt, T, H, dv), f32, dev)
     shape = _gdn_shape(k, v)
     rc = lib.tree_gdn_verify(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
@@ -398,9 +400,9 @@ def gdn_commit(k, g, e, S0, parent, accepted, accepted_len, tree_status=None, st
     dev = k.device
     Lmax = accepted.shape[1] if accepted.dim() == 2 else 0
     f32 = torch.float32
-    for t, name, shp in ((k, "k", (Bt, T, H, dk)), (g, "g", (Bt, T, H)), (e, "e", (Bt, T, H, dv)),
-                         (S0, "S0", (Bt, H, dv, dk))):
-        _check(t, name, shp, f32, dev)
+    for t, name, shp, dt in ((k, "k", (Bt, T, H, dk), k.dtype), (g, "g", (Bt, T, H), f32),
+                             (e, "e", (Bt, T, H, dv), f32), (S0, "S0", (Bt, H, dv, dk), f32)):
+        _check(t, name, shp, dt, dev)
     _check(parent, "parent", (Bt, T), torch.int32, dev)
     _check(accepted, "accepted", (Bt, Lmax), torch.int32, dev)
     _check(accepted_len, "accepted_len", (Bt,), torch.int32, dev)

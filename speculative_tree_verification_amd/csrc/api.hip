@@ -131,38 +131,48 @@ namespace {
 tsv_status check_gdn_shape(const tsv_shape* s) {
     tsv_status st = check_shape(s);
     if (st != TSV_OK) return st;
-    if (s->in_dtype != TSV_F32 || s->n_groups != 1) return TSV_E_UNSUPPORTED;
-    if (s->n_nodes > 64 || s->head_dim > 128 || s->d_state > 128) return TSV_E_UNSUPPORTED;
+    if ((s->in_dtype != TSV_F32 && s->in_dtype != TSV_BF16) || s->n_groups != 1) return TSV_E_UNSUPPORTED;
+    if (s->n_nodes > kMaxNodesMfma || s->head_dim > 128 || s->d_state > 128) return TSV_E_UNSUPPORTED;
     return TSV_OK;
 }
 }  // namespace
 
-tsv_status tree_gdn_verify(const tsv_shape* s, const float* q, const float* k, const float* v,
+tsv_status tree_gdn_verify(const tsv_shape* s, const void* q, const void* k, const void* v,
                            const float* g, const float* beta, const float* S0,
-                           const int32_t* parent, float* o, float* e, int32_t* tree_status,
+                           const int32_t* parent, void* o, float* e, int32_t* tree_status,
                            void* stream) {
     tsv_status st = check_gdn_shape(s);
     if (st != TSV_OK) return st;
     if (s->batch == 0 || s->n_nodes == 0) return TSV_OK;
     if (!q || !k || !v || !g || !beta || !S0 || !parent || !o) return TSV_E_NULL;
+    if (tsv::gdn_large_supported(s->n_nodes)) {
+        if (!e) return TSV_E_NULL;  // the pseudo-values are solved in place in e
+        hipError_t err = tsv::launch_gdn_large(s->batch, s->n_nodes, s->n_heads, s->d_state, s->head_dim,
+                                               s->in_dtype == TSV_BF16, q, k, v, g, beta, S0, parent, o, e,
+                                               tree_status, (hipStream_t)stream);
+        return err == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
+    }
     hipError_t err = tsv::launch_gdn_verify(s->batch, s->n_nodes, s->n_heads, s->d_state,
-                                            s->head_dim, q, k, v, g, beta, S0, parent, o, e,
+                                            s->head_dim, s->in_dtype == TSV_BF16, q, k, v, g, beta,
+                                            S0, parent, o, e,
                                             tree_status, (hipStream_t)stream);
     return err == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
 }
 
-tsv_status tree_gdn_commit(const tsv_shape* s, const float* k, const float* g, const float* e,
+tsv_status tree_gdn_commit(const tsv_shape* s, const void* k, const float* g, const float* e,
                            float* S0_inout, const int32_t* parent, const int32_t* accepted,
                            const int32_t* accepted_len, int32_t max_path_len, int32_t* tree_status,
                            void* stream) {
     tsv_status st = check_gdn_shape(s);
     if (st != TSV_OK) return st;
     if (max_path_len < 0 || max_path_len > kMaxNodes) return TSV_E_SHAPE;
+    if (s->n_nodes > 64 && max_path_len > 64) return TSV_E_UNSUPPORTED;  // paths staged whole in LDS
     if (s->batch == 0 || s->n_nodes == 0) return TSV_OK;
     if (!k || !g || !e || !S0_inout || !parent || !accepted_len) return TSV_E_NULL;
     if (max_path_len > 0 && !accepted) return TSV_E_NULL;
     hipError_t err = tsv::launch_gdn_commit(s->batch, s->n_nodes, s->n_heads, s->d_state,
-                                            s->head_dim, k, g, e, S0_inout, parent, accepted,
+                                            s->head_dim, s->in_dtype == TSV_BF16, k, g, e, S0_inout,
+                                            parent, accepted,
                                             accepted_len, max_path_len, tree_status,
                                             (hipStream_t)stream);
     return err == hipSuccess ? TSV_OK : TSV_E_LAUNCH;

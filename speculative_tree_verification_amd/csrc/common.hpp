@@ -78,6 +78,11 @@ __device__ __forceinline__ void gstore(float4* p, const float4& v) {
 }
 typedef uint32_t gu32x2 __attribute__((ext_vector_type(2)));
 template <>
+__device__ __forceinline__ uint2 gload(const uint2* p) {
+    const gu32x2 v = *(const gu32x2 __attribute__((address_space(1)))*)p;
+    return make_uint2(v.x, v.y);
+}
+template <>
 __device__ __forceinline__ void gstore(uint2* p, const uint2& v) {
     *(gu32x2 __attribute__((address_space(1)))*)p = gu32x2{v.x, v.y};
 }
@@ -200,6 +205,40 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
     else
         __syncthreads();
     return base + incl - v;
+}
+
+// four consecutive floats of a row with `rem` >= 1 valid elements left (VEC: a
+// 16-byte aligned row of a multiple of four elements)
+template <bool VEC>
+__device__ __forceinline__ float4 ld4(const float* __restrict__ p, int rem) {
+    if (VEC) return *(const float4*)p;
+    float4 r;
+    r.x = p[0];
+    r.y = rem > 1 ? p[1] : 0.f;
+    r.z = rem > 2 ? p[2] : 0.f;
+    r.w = rem > 3 ? p[3] : 0.f;
+    return r;
+}
+
+// four consecutive elements of a row of q, k or v as floats (bf16 rows: VEC
+// means an 8-byte aligned row of a multiple of four elements)
+template <typename TIO, bool VEC>
+__device__ __forceinline__ float4 ld4io(const TIO* __restrict__ p, int rem) {
+    if constexpr (sizeof(TIO) == 4) {
+        return ld4<VEC>((const float*)p, rem);
+    } else {
+        if (VEC) {
+            const uint2 u = gload((const uint2*)p);
+            return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                               __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+        }
+        float4 r;
+        r.x = Elem<TIO>::ld(p, 0);
+        r.y = rem > 1 ? Elem<TIO>::ld(p, 1) : 0.f;
+        r.z = rem > 2 ? Elem<TIO>::ld(p, 2) : 0.f;
+        r.w = rem > 3 ? Elem<TIO>::ld(p, 3) : 0.f;
+        return r;
+    }
 }
 
 // ---------------------------------------------------------------- topology

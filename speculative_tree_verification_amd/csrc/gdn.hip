@@ -14,7 +14,9 @@
 //   o_i = exp(G_i) S0 q_i + sum_{j on path(i)} D_ij (q_i . k_j) e_j,
 //   S'  = exp(G_l) S0 + sum_{j on path(l)} D_lj e_j k_j^T   (commit, path to l).
 //
-// Inputs and outputs fp32; trees of up to 64 nodes, dk and dv up to 128.
+// q, k, v and o fp32 or bf16 (bits); g, beta, S0 and the pseudo-values e
+// fp32; trees of up to 64 nodes, dk and dv up to 128. bf16 rows are converted
+// on load: split into bf16 high and low parts they are exact in the high part.
 // Verify: one work-group of 9 waves per (item, head). Row wave w < 8 owns value
 // rows [16 w, 16 w + 16); the tree wave handles everything node x node.
 //  1. Every load is issued on entry: each row wave's S0 rows straight into
@@ -53,19 +55,6 @@ constexpr int kGdnThreads = kGdnRowThreads + kWave;  // and the tree wave
 constexpr int kGdnRS = kGdnDim + 8;    // row stride (bf16) of the staged halves of k and q
 constexpr int kGdnCS = kGdnNodes + 4;  // row stride of the dense node x node matrices
 
-// four consecutive floats of a row with `rem` >= 1 valid elements left (VEC: a
-// 16-byte aligned row of a multiple of four elements)
-template <bool VEC>
-__device__ __forceinline__ float4 ld4(const float* __restrict__ p, int rem) {
-    if (VEC) return *(const float4*)p;
-    float4 r;
-    r.x = p[0];
-    r.y = rem > 1 ? p[1] : 0.f;
-    r.z = rem > 2 ? p[2] : 0.f;
-    r.w = rem > 3 ? p[3] : 0.f;
-    return r;
-}
-
 // x = hi + lo for four floats: bf16 high parts and bf16 residuals, packed in pairs
 __device__ __forceinline__ void split4(const float4& x, uint2& hi, uint2& lo) {
     const uint32_t h01 = pack_bf16x2(x.x, x.y), h23 = pack_bf16x2(x.z, x.w);
@@ -90,13 +79,14 @@ __device__ __forceinline__ f32x4 mfma4(const float4& a, const float4& b, f32x4 c
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, c, 0, 0, 0);
 }
 
-template <bool VEC>
+template <typename TIO, bool VEC>
 __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(
-    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const TIO* __restrict__ q, const TIO* __restrict__ k, const TIO* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* __restrict__ S0,
-    const int32_t* __restrict__ parent, float* __restrict__ o, float* __restrict__ e_out,
+    const int32_t* __restrict__ parent, TIO* __restrict__ o, float* __restrict__ e_out,
     int32_t* __restrict__ tree_status, int T, int H, int dk, int dv) {
     constexpr int NN = kGdnNodes, RS = kGdnRS, CS = kGdnCS;
+    constexpr bool SVEC = VEC;  // the launch checks S0's alignment with the rows'
     __shared__ __align__(16) uint16_t s_stage[4 * NN * RS];  // k hi, k lo, q hi, q lo
     __shared__ __align__(16) float s_A[NN * NN];  // A_ij at [i][depth of j]
     __shared__ __align__(16) float s_W[NN * CS];
@@ -144,8 +134,8 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(
         kst[m] = qst[m] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (!tree_wave && r < T && c < dk) {
             const size_t src = (row0 + (size_t)r * H) * dk + c;
-            kst[m] = ld4<VEC>(k + src, dk - c);
-            qst[m] = ld4<VEC>(q + src, dk - c);
+            kst[m] = ld4io<TIO, VEC>(k + src, dk - c);
+            qst[m] = ld4io<TIO, VEC>(q + src, dk - c);
         }
     }
     if (tree_wave) {
@@ -227,7 +217,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(
     for (int kk = 0; kk < kGdnDim / 16; ++kk) {
         const int col = 32 * (kk >> 1) + 8 * q4 + 4 * (kk & 1);
         s0r[kk] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (wave_rows && p < dv && col < dk) s0r[kk] = ld4<VEC>(S0p + col, dk - col);
+        if (wave_rows && p < dv && col < dk) s0r[kk] = ld4<SVEC>(S0p + col, dk - col);
     }
     // v at the accumulator positions: node 16 ti + 4 q4 + r, value row p
     float vr[NN / 4];
@@ -237,7 +227,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(
         for (int r = 0; r < 4; ++r) {
             const int i = 16 * ti + 4 * q4 + r;
             vr[4 * ti + r] =
-                wave_rows && i < T && p < dv ? v[(row0 + (size_t)i * H) * dv + p] : 0.f;
+                wave_rows && i < T && p < dv ? Elem<TIO>::ld(v, (row0 + (size_t)i * H) * dv + p) : 0.f;
         }
 
     lds_barrier();
@@ -361,7 +351,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(
             }
         }
     }
-    float* const o_p = o + row0 * dv + p;
+    TIO* const o_p = o + row0 * dv + p;
     float* const e_p = e_out ? e_out + row0 * dv + p : nullptr;
     const size_t step = (size_t)H * dv;  // next node
 #pragma unroll
@@ -379,7 +369,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * ti + 4 * q4 + r;
                 if (i < T && p < dv) {
-                    o_p[(size_t)i * step] = acc[r];
+                    Elem<TIO>::st(o_p, (size_t)i * step, acc[r]);
                     if (e_p) e_p[(size_t)i * step] = E4[ti][r];
                 }
             }
@@ -403,14 +393,14 @@ constexpr int kGdnCommitCPW = 1;
 // chunks; each chunk is then updated and written back as it arrives, its
 // stores overlapping the loads still in flight. The weights come from a suffix
 // scan across one wave.
-template <bool VEC, int CPW>
+template <typename TIO, bool VEC, int CPW>
 __global__ __launch_bounds__(kBlock) void gdn_commit_kernel(
-    const float* __restrict__ k, const float* __restrict__ g, const float* __restrict__ e,
+    const TIO* __restrict__ k, const float* __restrict__ g, const float* __restrict__ e,
     float* __restrict__ S, const int32_t* __restrict__ parent, const int32_t* __restrict__ accepted,
     const int32_t* __restrict__ accepted_len, int32_t* __restrict__ tree_status, int T, int H,
     int dk, int dv, int Lmax, int EW, int KW, int groups) {
-    __shared__ int s_par[kGdnNodes];
-    __shared__ int s_path[kGdnNodes];
+    __shared__ int s_par[kMaxNodes];   // trees of up to 256 nodes
+    __shared__ int s_path[kGdnNodes];  // paths of up to 64 nodes
     __shared__ int s_bad[kBlock / kWave];
     __shared__ float s_w[kGdnNodes];
     __shared__ float s_w0;
@@ -490,11 +480,11 @@ __global__ __launch_bounds__(kBlock) void gdn_commit_kernel(
             }
             if (x < nk) {
                 const int t = x / kq, c = x - t * kq;
-                const float* src = k + (row0 + (size_t)s_path[t] * H) * dk;
+                const TIO* src = k + (row0 + (size_t)s_path[t] * H) * dk;
                 if (VEC)
-                    kv[u] = *(const float4*)(src + 4 * c);
+                    kv[u] = ld4io<TIO, true>(src + 4 * c, 4);
                 else
-                    kv[u].x = src[c];
+                    kv[u].x = Elem<TIO>::ld(src, c);
             }
         }
         if (base == 0) {
@@ -593,21 +583,30 @@ __global__ __launch_bounds__(kBlock) void gdn_commit_kernel(
     }
 }
 
-hipError_t launch_gdn_verify(int batch, int T, int H, int dk, int dv, const float* q,
-                             const float* k, const float* v, const float* g, const float* beta,
-                             const float* S0, const int32_t* parent, float* o, float* e,
+hipError_t launch_gdn_verify(int batch, int T, int H, int dk, int dv, bool bf16, const void* q,
+                             const void* k, const void* v, const float* g, const float* beta,
+                             const float* S0, const int32_t* parent, void* o, float* e,
                              int32_t* tree_status, hipStream_t stream) {
-    const bool vec = dk % 4 == 0 && (((uintptr_t)q | (uintptr_t)k | (uintptr_t)S0) & 15) == 0;
-    if (vec)
-        hipLaunchKernelGGL(gdn_verify_kernel<true>, dim3(batch * H), dim3(kGdnThreads), 0, stream,
-                           q, k, v, g, beta, S0, parent, o, e, tree_status, T, H, dk, dv);
-    else
-        hipLaunchKernelGGL(gdn_verify_kernel<false>, dim3(batch * H), dim3(kGdnThreads), 0, stream,
-                           q, k, v, g, beta, S0, parent, o, e, tree_status, T, H, dk, dv);
+    // vector loads: rows of a multiple of four elements, q and k 16-byte (fp32)
+    // or 8-byte (bf16) aligned, S0 16-byte aligned
+    const uintptr_t ra = bf16 ? 7 : 15;
+    const bool vec = dk % 4 == 0 && (((uintptr_t)q | (uintptr_t)k) & ra) == 0 && ((uintptr_t)S0 & 15) == 0;
+#define TSV_GDN_V(TIO, V)                                                                              \
+    hipLaunchKernelGGL((gdn_verify_kernel<TIO, V>), dim3(batch * H), dim3(kGdnThreads), 0, stream,     \
+                       (const TIO*)q, (const TIO*)k, (const TIO*)v, g, beta, S0, parent, (TIO*)o, e, \
+                       tree_status, T, H, dk, dv)
+    if (bf16) {
+        if (vec) TSV_GDN_V(uint16_t, true);
+        else TSV_GDN_V(uint16_t, false);
+    } else {
+        if (vec) TSV_GDN_V(float, true);
+        else TSV_GDN_V(float, false);
+    }
+#undef TSV_GDN_V
     return hipGetLastError();
 }
 
-hipError_t launch_gdn_commit(int batch, int T, int H, int dk, int dv, const float* k,
+hipError_t launch_gdn_commit(int batch, int T, int H, int dk, int dv, bool bf16, const void* k,
                              const float* g, const float* e, float* S, const int32_t* parent,
                              const int32_t* accepted, const int32_t* accepted_len, int Lmax,
                              int32_t* tree_status, hipStream_t stream) {
@@ -615,21 +614,23 @@ hipError_t launch_gdn_commit(int batch, int T, int H, int dk, int dv, const floa
     const int EW = (dv + 3) / 4 * 4;
     const int KW = (dk + 3) / 4 * 4;
     const size_t shmem = (size_t)std::min(Lmax, T) * (EW + KW) * sizeof(float);
-    const bool vec = dk % 4 == 0 && (((uintptr_t)S | (uintptr_t)k) & 15) == 0;
+    const uintptr_t ra = bf16 ? 7 : 15;
+    const bool vec = dk % 4 == 0 && ((uintptr_t)S & 15) == 0 && ((uintptr_t)k & ra) == 0;
     constexpr int CPW = kGdnCommitCPW;
     const int groups = ((dv * dk + kGdnCommitEl - 1) / kGdnCommitEl + CPW - 1) / CPW;
-    auto kern = vec ? gdn_commit_kernel<true, CPW> : gdn_commit_kernel<false, CPW>;
+    const void* kern = bf16 ? (vec ? (const void*)gdn_commit_kernel<uint16_t, true, CPW>
+                                   : (const void*)gdn_commit_kernel<uint16_t, false, CPW>)
+                            : (vec ? (const void*)gdn_commit_kernel<float, true, CPW>
+                                   : (const void*)gdn_commit_kernel<float, false, CPW>);
     if (shmem > 48 * 1024) {
         // paths of up to 64 entries with 128-wide rows take up to 64 KiB
-        const hipError_t err = hipFuncSetAttribute((const void*)kern,
-                                                   hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                   (int)shmem);
+        const hipError_t err = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
         if (err != hipSuccess) return err;
     }
-    hipLaunchKernelGGL(kern, dim3(batch * H * groups), dim3(kBlock), shmem, stream, k, g, e, S,
-                       parent, accepted, accepted_len, tree_status, T, H, dk, dv, Lmax, EW, KW,
-                       groups);
-    return hipGetLastError();
+    void* args[] = {(void*)&k, (void*)&g, (void*)&e, (void*)&S, (void*)&parent, (void*)&accepted,
+                    (void*)&accepted_len, (void*)&tree_status, (void*)&T, (void*)&H, (void*)&dk,
+                    (void*)&dv, (void*)&Lmax, (void*)&EW, (void*)&KW, (void*)&groups};
+    return hipLaunchKernel(kern, dim3(batch * H * groups), dim3(kBlock), args, shmem, stream);
 }
 
 }  // namespace tsv

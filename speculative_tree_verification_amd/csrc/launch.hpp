@@ -60,12 +60,17 @@ hipError_t launch_commit(const CommitArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_verify_large(const VerifyArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_commit_large(const CommitArgs& a, bool bf16, hipStream_t stream);
 
-// gated delta rule over packed trees (fp32, T <= 64, dk and dv <= 128)
-hipError_t launch_gdn_verify(int batch, int T, int H, int dk, int dv, const float* q,
-                             const float* k, const float* v, const float* g, const float* beta,
-                             const float* S0, const int32_t* parent, float* o, float* e,
+// gated delta rule over packed trees (q, k, v, o fp32 or bf16; T <= 64, dk and dv <= 128)
+hipError_t launch_gdn_verify(int batch, int T, int H, int dk, int dv, bool bf16, const void* q,
+                             const void* k, const void* v, const float* g, const float* beta,
+                             const float* S0, const int32_t* parent, void* o, float* e,
                              int32_t* tree_status, hipStream_t stream);
-hipError_t launch_gdn_commit(int batch, int T, int H, int dk, int dv, const float* k,
+// trees of 65 to 256 nodes (plain kernel; e is required: it holds the solve)
+bool gdn_large_supported(int T);
+hipError_t launch_gdn_large(int batch, int T, int H, int dk, int dv, bool bf16, const void* q, const void* k,
+                            const void* v, const float* g, const float* beta, const float* S0,
+                            const int32_t* parent, void* o, float* e, int32_t* tree_status, hipStream_t stream);
+hipError_t launch_gdn_commit(int batch, int T, int H, int dk, int dv, bool bf16, const void* k,
                              const float* g, const float* e, float* S, const int32_t* parent,
                              const int32_t* accepted, const int32_t* accepted_len, int Lmax,
                              int32_t* tree_status, hipStream_t stream);

@@ -468,11 +468,13 @@ def make_sampling_device(seed: int, parent: np.ndarray, vocab: int, device, temp
 
 def make_gdn(seed: int, batch: int, n_nodes: int, n_heads: int, dk: int, dv: int,
              tree: str = "recursive", max_depth: int = 8, max_path_len: int = 9,
-             parents: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
-    """Seeded fp32 inputs of a gated-delta-rule layer over packed trees:
+             parents: Optional[np.ndarray] = None, dtype: str = F32) -> Dict[str, np.ndarray]:
+    """Seeded inputs of a gated-delta-rule layer over packed trees:
     q, k [B][T][H][dk] (k scaled to unit length, q by 1/sqrt(dk)), v [B][T][H][dv]
     ~ N(0, 1), log gate g = log U(0.9, 1), step beta = sigmoid(N(0, 1)), state
-    S0 [B][H][dv][dk] ~ 0.1 N(0, 1); trees and accepted paths as make_custom."""
+    S0 [B][H][dv][dk] ~ 0.1 N(0, 1); trees and accepted paths as make_custom.
+    With dtype BF16, q, k and v are rounded to bf16 and returned as bit
+    patterns (uint16); g, beta and S0 stay fp32."""
     rng = np.random.default_rng([9100, seed])
     B, T, H = batch, n_nodes, n_heads
     if parents is None:
@@ -491,5 +493,6 @@ def make_gdn(seed: int, batch: int, n_nodes: int, n_heads: int, dk: int, dv: int
     beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H))))
     S0 = 0.1 * rng.standard_normal((B, H, dv, dk))
     f = lambda a: np.ascontiguousarray(a, dtype=np.float32)
-    return dict(q=f(q), k=f(k), v=f(v), g=f(g), beta=f(beta), S0=f(S0), parent=parents,
+    io = (lambda a: f32_to_bf16_bits(f(a))) if dtype == BF16 else f
+    return dict(q=io(q), k=io(k), v=io(v), g=f(g), beta=f(beta), S0=f(S0), parent=parents,
                 accepted=acc, accepted_len=acc_len)

@@ -212,10 +212,11 @@ def gdn_good():
 
 
 @pytest.mark.parametrize("field,value,code", [
-    ("in_dtype", 1, 4), ("n_groups", 2, 4), ("n_nodes", 65, 4), ("head_dim", 129, 4),
+    ("in_dtype", 2, 3), ("n_groups", 2, 4), ("n_nodes", 257, 4), ("head_dim", 129, 4),
     ("d_state", 129, 4), ("n_nodes", 1025, 2), ("batch", -1, 2), ("n_heads", 0, 2)])
 def test_gdn_rejects_bad_shapes(L, field, value, code):
-    """The gated-delta-rule kernels take fp32, one group, T <= 64, dk and dv <= 128."""
+    """The gated-delta-rule kernels take fp32 or bf16 q, k, v, one group,
+    T <= 256, dk and dv <= 128; an unknown dtype is TSV_E_DTYPE."""
     s = gdn_good()
     setattr(s, field, value)
     assert call_gdn_verify(L, s) == code

@@ -119,3 +119,132 @@ def test_gdn_pseudo_values_optional_and_streams(bnd):
                        stream=side)
     side.synchronize()
     assert torch.equal(o1, o3) and torch.equal(e1, e3) and torch.equal(S1, S3)
+
+
+def _dev_io(d):
+    """Upload: bf16 bit patterns (uint16) become torch.bfloat16 tensors."""
+    import torch
+    out = {}
+    for k, v in d.items():
+        t = torch.from_numpy(np.ascontiguousarray(v))
+        if v.dtype == np.uint16:
+            t = t.view(torch.int16).view(torch.bfloat16)
+        out[k] = t.cuda()
+    return out
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,tree", [
+    (2, 1, 2, 16, 16, "recursive"), (3, 15, 4, 128, 128, "recursive"), (2, 31, 3, 64, 128, "recursive"),
+    (2, 64, 2, 128, 64, "chain"), (2, 63, 2, 48, 40, "geometric"), (1, 40, 1, 100, 70, "recursive"),
+    (2, 17, 2, 6, 10, "star")])
+def test_gdn_bf16_inputs(bnd, B, T, H, dk, dv, tree):
+    """q, k, v (and o) in bf16: o within the bf16 bar of the oracle run on the
+    same (bf16-exact) values, e and S' within the fp32 bar; and the bf16 call
+    equals the fp32 call on those values converted to fp32 (e and S' bit for
+    bit, o as its bf16 rounding)."""
+    import torch
+    d = W.make_gdn(B * 2000 + T + dk, batch=B, n_nodes=T, n_heads=H, dk=dk, dv=dv, tree=tree,
+                   max_depth=8 if tree != "chain" else T, max_path_len=min(T, 9), dtype=W.BF16)
+    say(f"[gdn bf16] B={B} T={T} H={H} dk={dk} dv={dv} {tree}")
+    dev = _dev_io(d)
+    st = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    o, e = bnd.gdn_verify(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], dev["S0"], dev["parent"],
+                          tree_status=st)
+    S = dev["S0"].clone()
+    bnd.gdn_commit(dev["k"], dev["g"], e, S, dev["parent"], dev["accepted"], dev["accepted_len"])
+    # the same values as fp32
+    f32 = {k: (dev[k].float() if k in ("q", "k", "v") else dev[k]) for k in dev}
+    o32, e32 = bnd.gdn_verify(f32["q"], f32["k"], f32["v"], f32["g"], f32["beta"], f32["S0"], f32["parent"])
+    S32 = dev["S0"].clone()
+    bnd.gdn_commit(f32["k"], f32["g"], e32, S32, f32["parent"], f32["accepted"], f32["accepted_len"])
+    torch.cuda.synchronize()
+    assert st.cpu().tolist() == [0] * B
+    assert o.dtype == torch.bfloat16 and e.dtype == torch.float32
+    assert torch.equal(e, e32) and torch.equal(S, S32)
+    assert torch.equal(o, o32.to(torch.bfloat16))
+    x = {k: (W.to_f64(v, W.BF16) if v.dtype == np.uint16 else
+             (v.astype(np.float64) if v.dtype == np.float32 else v)) for k, v in d.items()}
+    ref, _ = O.verify_unrolled(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], x["parent"])
+    _, eref = O.verify_wy(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], x["parent"])
+    Sref, _ = O.commit_unrolled(x["k"], x["v"], x["g"], x["beta"], x["S0"], x["parent"],
+                                x["accepted"], x["accepted_len"])
+    on, en, Sn = (t.float().cpu().double().numpy() for t in (o, e, S))
+    err = lambda a, r, sl: np.max(np.abs(a[sl] - r[sl])) / np.max(np.abs(r[sl]))
+    err_o = max(err(on, ref, (b, slice(None), h)) for b in range(B) for h in range(H))
+    err_e = max(err(en, eref, (b, slice(None), h)) for b in range(B) for h in range(H))
+    err_S = max(err(Sn, Sref, (b, h)) for b in range(B) for h in range(H))
+    say(f"    o err {err_o:.2e}  e err {err_e:.2e}  S' err {err_S:.2e}")
+    assert err_o <= 2e-2 and err_e <= TOL and err_S <= TOL, (err_o, err_e, err_S)
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,tree,dtype", [
+    (2, 65, 2, 64, 64, "recursive", W.F32), (2, 100, 2, 128, 128, "recursive", W.F32),
+    (2, 255, 2, 128, 128, "level", W.F32), (1, 256, 2, 100, 70, "recursive", W.F32),
+    (2, 200, 1, 6, 10, "star", W.F32), (2, 120, 2, 32, 48, "geometric", W.F32),
+    (2, 90, 1, 16, 16, "chain", W.F32),
+    (2, 255, 2, 128, 128, "level", W.BF16), (2, 90, 3, 64, 128, "recursive", W.BF16)])
+def test_gdn_large_trees(bnd, B, T, H, dk, dv, tree, dtype):
+    """Trees of 65 to 256 nodes (the plain kernel): o within the bar of its
+    dtype, e and the committed state within the fp32 bar, against the
+    unrolled recurrence."""
+    import torch
+    d = W.make_gdn(B * 3000 + T + dk, batch=B, n_nodes=T, n_heads=H, dk=dk, dv=dv, tree=tree,
+                   max_depth=8 if tree != "chain" else T, max_path_len=min(T, 9), dtype=dtype)
+    say(f"[gdn large] B={B} T={T} H={H} dk={dk} dv={dv} {tree} {dtype}")
+    dev = _dev_io(d)
+    st = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    o, e = bnd.gdn_verify(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], dev["S0"], dev["parent"],
+                          tree_status=st)
+    S = dev["S0"].clone()
+    st2 = torch.full_like(st, -7)
+    bnd.gdn_commit(dev["k"], dev["g"], e, S, dev["parent"], dev["accepted"], dev["accepted_len"],
+                   tree_status=st2)
+    torch.cuda.synchronize()
+    x = {k: (W.to_f64(v, W.BF16) if v.dtype == np.uint16 else
+             (v.astype(np.float64) if v.dtype == np.float32 else v)) for k, v in d.items()}
+    ref, rst = O.verify_unrolled(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], x["parent"])
+    _, eref = O.verify_wy(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], x["parent"])
+    Sref, cst = O.commit_unrolled(x["k"], x["v"], x["g"], x["beta"], x["S0"], x["parent"],
+                                  x["accepted"], x["accepted_len"])
+    assert st.cpu().tolist() == rst.tolist() == [0] * B and st2.cpu().tolist() == cst.tolist()
+    on, en, Sn = (t.float().cpu().double().numpy() for t in (o, e, S))
+    err = lambda a, r, sl: np.max(np.abs(a[sl] - r[sl])) / np.max(np.abs(r[sl]))
+    err_o = max(err(on, ref, (b, slice(None), h)) for b in range(B) for h in range(H))
+    err_e = max(err(en, eref, (b, slice(None), h)) for b in range(B) for h in range(H))
+    err_S = max(err(Sn, Sref, (b, h)) for b in range(B) for h in range(H))
+    say(f"    o err {err_o:.2e}  e err {err_e:.2e}  S' err {err_S:.2e}")
+    assert err_o <= (2e-2 if dtype == W.BF16 else TOL) and err_e <= TOL and err_S <= TOL, (err_o, err_e, err_S)
+
+
+def test_gdn_large_capacity_invalid_and_null_e(bnd):
+    """A tree with more ancestor pairs than the kernel holds (a 200-node
+    chain) gets status 8 and untouched outputs; invalid trees 1/2; the plain
+    kernel needs e (NULL is TSV_E_NULL); a path row longer than 64 is
+    TSV_E_UNSUPPORTED for trees past 64 nodes."""
+    import ctypes
+    import torch
+    T = 200
+    d = W.make_gdn(91, batch=4, n_nodes=T, n_heads=2, dk=16, dv=16, max_path_len=5)
+    d["parent"][0] = np.array([-1] + list(range(T - 1)), np.int32)  # chain: 20100 pairs
+    d["parent"][1, 0] = 3
+    d["parent"][2, 150] = 170
+    dev = _dev_io(d)
+    o = torch.full_like(dev["v"], 5.0)
+    st = torch.full((4,), -7, dtype=torch.int32, device="cuda")
+    bnd.gdn_verify(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], dev["S0"], dev["parent"], o=o,
+                   tree_status=st)
+    torch.cuda.synchronize()
+    assert st.cpu().tolist() == [8, 1, 2, 0]
+    for b in (0, 1, 2):
+        assert (o[b] == 5.0).all()
+    assert not (o[3] == 5.0).any()
+    shape = bnd._gdn_shape(dev["k"], dev["v"])
+    args = [dev[x] for x in ("q", "k", "v", "g", "beta", "S0", "parent")]
+    rc = bnd.lib.tree_gdn_verify(ctypes.byref(shape), *[bnd._ptr(t) for t in args], bnd._ptr(o), None,
+                                 None, bnd._stream(None))
+    assert rc == 1
+    acc = torch.full((4, 65), -1, dtype=torch.int32, device="cuda")
+    rc = bnd.lib.tree_gdn_commit(ctypes.byref(shape), bnd._ptr(dev["k"]), bnd._ptr(dev["g"]),
+                                 bnd._ptr(o), bnd._ptr(dev["S0"]), bnd._ptr(dev["parent"]), bnd._ptr(acc),
+                                 bnd._ptr(dev["accepted_len"]), 65, None, bnd._stream(None))
+    assert rc == 4
