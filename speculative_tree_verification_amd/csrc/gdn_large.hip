@@ -19,11 +19,13 @@
 //     operand reads it (one linear 1 KB read per wave and step).
 //  2. K S0^T for the wave's 16 nodes on MFMA (three-term bf16 splits, fp32
 //     accumulation; two terms for bf16 inputs, whose low parts are zero), then
-//     r into the caller's e buffer; Q S0^T stays in registers. The column
-//     order of the product tiles gives each lane four consecutive value rows
-//     twice, so v, r, e and o move as 16-byte vectors.
-//  3. pair scores, eight lanes per pair (k_i, k_j and q_i rows from memory);
-//     M by substitution one depth level at a time, one pair entry per thread:
+//     r into the caller's e buffer. The column order of the product tiles
+//     gives each lane four consecutive value rows twice, so v, r, e and o move
+//     as 16-byte vectors.
+//  3. pair scores of the wave's nodes from the k and q columns its lanes hold
+//     as A operands (only the ancestors' k rows are loaded), then Q S0^T,
+//     kept in registers; M by substitution one depth level at a time, one
+//     pair entry per thread:
 //        M_ij = -A_ij - sum_{x strictly between j and i} A_ix M_xj;
 //     then N_ij = sum_{x from i down to j} W_ix M_xj, all entries at once.
 //  4. e_i = sum_j M_ij r_j and o_i = exp(G_i) (S0 q_i) + sum_j N_ij r_j over the
@@ -85,31 +87,93 @@ __device__ __forceinline__ void st4io(TIO* __restrict__ p, const float4& x, int 
     }
 }
 
-// The 16 x 32 A operand of step ks for the wave's nodes: lane (l16, q4) holds
-// columns 32 ks + 8 q4 .. + 7 of node row `row` (zero past dk or past the tree)
+// The lane's share of a node row as the 16 x 32 A operand of the products:
+// lane (l16, q4) holds columns 32 ks + 8 q4 .. + 7 for every step ks (zero
+// past dk or past the tree); fp32 rows as floats, bf16 rows as their bits
+template <typename TIO>
+struct ARow;
+template <>
+struct ARow<float> {
+    float4 v[2 * kLKS];
+};
+template <>
+struct ARow<uint16_t> {
+    uint4 v[kLKS];
+};
+
 template <typename TIO, bool VEC>
-__device__ __forceinline__ void load_a(const TIO* __restrict__ row, bool live, int q4, int dk, float4* a) {
+__device__ __forceinline__ void load_a(const TIO* __restrict__ row, bool live, int q4, int dk, ARow<TIO>& a) {
 #pragma unroll
     for (int ks = 0; ks < kLKS; ++ks) {
         const int c = 32 * ks + 8 * q4;
-        a[2 * ks] = a[2 * ks + 1] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (live && c < dk) a[2 * ks] = ld4io<TIO, VEC>(row + c, dk - c);
-        if (live && c + 4 < dk) a[2 * ks + 1] = ld4io<TIO, VEC>(row + c + 4, dk - c - 4);
+        if constexpr (sizeof(TIO) == 4) {
+            a.v[2 * ks] = a.v[2 * ks + 1] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (live && c < dk) a.v[2 * ks] = ld4<VEC>(row + c, dk - c);
+            if (live && c + 4 < dk) a.v[2 * ks + 1] = ld4<VEC>(row + c + 4, dk - c - 4);
+        } else {
+            a.v[ks] = make_uint4(0u, 0u, 0u, 0u);
+            if (VEC) {
+                if (live && c < dk) {
+                    const uint2 x = gload((const uint2*)(row + c));
+                    a.v[ks].x = x.x;
+                    a.v[ks].y = x.y;
+                }
+                if (live && c + 4 < dk) {
+                    const uint2 x = gload((const uint2*)(row + c + 4));
+                    a.v[ks].z = x.x;
+                    a.v[ks].w = x.y;
+                }
+            } else {
+                uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+                    if (live && c + t < dk) w[t >> 1] |= (uint32_t)gload(row + c + t) << (16 * (t & 1));
+                a.v[ks] = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
     }
+}
+
+// bf16 high and low parts of step ks (bf16 rows: the bits, and no low part)
+template <typename TIO>
+__device__ __forceinline__ void a_parts(const ARow<TIO>& a, int ks, bf16x8& hi, bf16x8& lo) {
+    if constexpr (sizeof(TIO) == 4) {
+        split_hi_lo(a.v[2 * ks], a.v[2 * ks + 1], hi, lo);
+    } else {
+        hi = __builtin_bit_cast(bf16x8, a.v[ks]);
+        lo = hi;  // unused
+    }
+}
+
+// partial dot products of two rows over the lane's columns (fp32 arithmetic;
+// bf16 products are exact in it)
+template <typename TIO>
+__device__ __forceinline__ float a_dot(const ARow<TIO>& a, const ARow<TIO>& b) {
+    float s = 0.f;
+    if constexpr (sizeof(TIO) == 4) {
+#pragma unroll
+        for (int u = 0; u < 2 * kLKS; ++u)
+            s += (a.v[u].x * b.v[u].x + a.v[u].y * b.v[u].y) + (a.v[u].z * b.v[u].z + a.v[u].w * b.v[u].w);
+    } else {
+#pragma unroll
+        for (int u = 0; u < kLKS; ++u) s = dot8_bf16(a.v[u], b.v[u], s);
+    }
+    return s;
 }
 
 // X S0^T for the wave's 16 nodes: acc[nb] holds (node 16 w + 4 q4 + r, value
 // row vrow(nb, l16)) in element r
-template <bool BF>
-__device__ __forceinline__ void s0_product(const float4* a, const bf16x8* __restrict__ s_S0, int lane, int dk,
+template <typename TIO>
+__device__ __forceinline__ void s0_product(const ARow<TIO>& a, const bf16x8* __restrict__ s_S0, int lane, int dk,
                                            int dv, f32x4* acc) {
+    constexpr bool BF = sizeof(TIO) == 2;
 #pragma unroll
     for (int nb = 0; nb < kLNB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < kLKS; ++ks) {
         if (32 * ks >= dk) break;
         bf16x8 ah, al;
-        split_hi_lo(a[2 * ks], a[2 * ks + 1], ah, al);
+        a_parts<TIO>(a, ks, ah, al);
 #pragma unroll
         for (int nb = 0; nb < kLNB; ++nb) {
             if (vrow(nb, 0) >= dv) continue;
@@ -175,8 +239,9 @@ __global__ __launch_bounds__(kGdnLargeNT) void gdn_large_kernel(
     }
     const int ia = 16 * w + l16;  // A-operand row of this lane
     const bool alive = rows && ia < T;
-    float4 ka[2 * kLKS];
+    ARow<TIO> ka;
     load_a<TIO, VEC>(k + (row0 + (size_t)min(ia, T - 1) * H) * dk, alive, q4, dk, ka);
+    const int i4 = 16 * w + 4 * q4;  // nodes i4 .. i4 + 3 of this lane's accumulators
 
     const int st = check_tree_lds<NT>(par_i, T, s_par, s_red);
     if (st) {
@@ -233,10 +298,15 @@ __global__ __launch_bounds__(kGdnLargeNT) void gdn_large_kernel(
     lds_barrier();
     if (tid < T) s_lvl[atomicAdd(&s_cnt[s_dep[tid]], 1)] = tid;
 
-    // ---- 2. K S0^T -> r into e; Q S0^T kept
+    // ---- 2. K S0^T, then r = beta (v - exp(G) K S0^T) into e (all stores
+    // issued together, after the last load they depend on)
     f32x4 qs[kLNB];
+    ARow<TIO> qa;
     if (rows) {
-        const int i4 = 16 * w + 4 * q4;  // nodes i4 .. i4 + 3 of this lane's accumulators
+        f32x4 ks_[kLNB];
+        s0_product<TIO>(ka, s_S0, lane, dk, dv, ks_);
+        __builtin_amdgcn_sched_barrier(0);
+        // v at the accumulator positions: node i4 + r, value rows p0 .. p0 + 3
         float4 vv[8];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -246,71 +316,49 @@ __global__ __launch_bounds__(kGdnLargeNT) void gdn_large_kernel(
                 vv[2 * r + hf] = make_float4(0.f, 0.f, 0.f, 0.f);
                 if (i < T && p0 < dv) vv[2 * r + hf] = ld4io<TIO, VEC>(v + (row0 + (size_t)i * H) * dv + p0, dv - p0);
             }
-        f32x4 ks_[kLNB];
-        s0_product<BF>(ka, s_S0, lane, dk, dv, ks_);
-        float4 qa[2 * kLKS];
-        load_a<TIO, VEC>(q + (row0 + (size_t)min(ia, T - 1) * H) * dk, alive, q4, dk, qa);
+        // every value first, then the stores: no wait between two stores
+        float4 rr[8];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int i = i4 + r;
-            if (i >= T) continue;
+            const int i = min(i4 + r, T - 1);
             const float bt = s_bt[i], gm = s_gam[i];
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
-                const int p0 = 64 * hf + 4 * l16;
-                if (p0 >= dv) continue;
                 const float4 x = vv[2 * r + hf];
-                const float4 rr = make_float4(bt * (x.x - gm * ks_[4 * hf][r]), bt * (x.y - gm * ks_[4 * hf + 1][r]),
-                                              bt * (x.z - gm * ks_[4 * hf + 2][r]),
-                                              bt * (x.w - gm * ks_[4 * hf + 3][r]));
-                st4io<float, VEC>(e + (row0 + (size_t)i * H) * dv + p0, rr, dv - p0);
+                rr[2 * r + hf] = make_float4(bt * (x.x - gm * ks_[4 * hf][r]), bt * (x.y - gm * ks_[4 * hf + 1][r]),
+                                             bt * (x.z - gm * ks_[4 * hf + 2][r]),
+                                             bt * (x.w - gm * ks_[4 * hf + 3][r]));
             }
         }
-        s0_product<BF>(qa, s_S0, lane, dk, dv, qs);
-    }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int i = i4 + r, p0 = 64 * hf + 4 * l16;
+                if (i < T && p0 < dv) st4io<float, VEC>(e + (row0 + (size_t)i * H) * dv + p0, rr[2 * r + hf], dv - p0);
+            }
+        __builtin_amdgcn_sched_barrier(0);  // q is loaded only once v and the products are consumed
+        load_a<TIO, VEC>(q + (row0 + (size_t)min(ia, T - 1) * H) * dk, alive, q4, dk, qa);
 
-    // ---- 3. pair scores, eight lanes per pair (lane part: columns 16 sub .. + 15)
-    {
-        const int sub = lane & 7;
-        const int rounds = (total + NT / 8 - 1) / (NT / 8);
-        for (int rd = 0; rd < rounds; ++rd) {
-            const int idx = rd * (NT / 8) + (tid >> 3);
-            float kk = 0.f, qk = 0.f;
-            int i = 0;
-            if (idx < total) {
-                const int pr = s_pair[idx];
-                i = pr & 255;
-                const int j = pr >> 8, c0 = 16 * sub;
-                const TIO* ki = k + (row0 + (size_t)i * H) * dk + c0;
-                const TIO* kj = k + (row0 + (size_t)j * H) * dk + c0;
-                const TIO* qi = q + (row0 + (size_t)i * H) * dk + c0;
-                float4 a[4], bj[4], qq[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    a[u] = bj[u] = qq[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-                    if (c0 + 4 * u < dk) {
-                        a[u] = ld4io<TIO, VEC>(ki + 4 * u, dk - c0 - 4 * u);
-                        bj[u] = ld4io<TIO, VEC>(kj + 4 * u, dk - c0 - 4 * u);
-                        qq[u] = ld4io<TIO, VEC>(qi + 4 * u, dk - c0 - 4 * u);
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    kk += (a[u].x * bj[u].x + a[u].y * bj[u].y) + (a[u].z * bj[u].z + a[u].w * bj[u].w);
-                    qk += (qq[u].x * bj[u].x + qq[u].y * bj[u].y) + (qq[u].z * bj[u].z + qq[u].w * bj[u].w);
-                }
-            }
-#pragma unroll
-            for (int off = 1; off < 8; off <<= 1) {
-                kk += __shfl_xor(kk, off, kWave);
-                qk += __shfl_xor(qk, off, kWave);
-            }
-            if (idx < total && sub == 0) {
-                const float D = __expf(s_A[idx]);
-                s_A[idx] = idx > s_off[i] ? s_bt[i] * D * kk : 0.f;
-                s_W[idx] = D * qk;
+        // ---- 3. pair scores of the wave's nodes: lane (l16, q4) holds the
+        // product columns of k_i and q_i (i = ia); for each ancestor j it loads
+        // the same columns of k_j, and the four lanes of node i add up
+        const int cnt = alive ? s_dep[ia] + 1 : 0, base = alive ? s_off[ia] : 0;
+        for (int m = 0; m < cnt; ++m) {
+            ARow<TIO> kj = ka;
+            if (m > 0) load_a<TIO, VEC>(k + (row0 + (size_t)(s_pair[base + m] >> 8) * H) * dk, true, q4, dk, kj);
+            float kk = a_dot<TIO>(ka, kj), qk = a_dot<TIO>(qa, kj);
+            kk += __shfl_xor(kk, 16, kWave);
+            qk += __shfl_xor(qk, 16, kWave);
+            kk += __shfl_xor(kk, 32, kWave);
+            qk += __shfl_xor(qk, 32, kWave);
+            if (q4 == 0) {
+                const float D = __expf(s_A[base + m]);
+                s_A[base + m] = m > 0 ? s_bt[ia] * D * kk : 0.f;
+                s_W[base + m] = D * qk;
             }
         }
+        s0_product<TIO>(qa, s_S0, lane, dk, dv, qs);
     }
     lds_barrier();
 
@@ -357,19 +405,23 @@ __global__ __launch_bounds__(kGdnLargeNT) void gdn_large_kernel(
     }
     __syncthreads();  // N complete, and every wave's r is in e
 
-    // ---- 4. e = M r, o = exp(G) (Q S0^T) + N r over each root path
-    float4 ea[8];
+    // ---- 4. e = M r, o = exp(G) (Q S0^T) + N r over each root path; the
+    // stores follow the last load
+    float4 ea[8], oa[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int i = 16 * w + 4 * q4 + r;
-        ea[2 * r] = ea[2 * r + 1] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (!rows || i >= T) continue;
-        const float gm = s_gam[i];
-        float4 oa[2];
+        const float gm = rows ? s_gam[min(i4 + r, T - 1)] : 0.f;
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-            oa[hf] = make_float4(gm * qs[4 * hf][r], gm * qs[4 * hf + 1][r], gm * qs[4 * hf + 2][r],
-                                 gm * qs[4 * hf + 3][r]);
+        for (int hf = 0; hf < 2; ++hf) {
+            ea[2 * r + hf] = make_float4(0.f, 0.f, 0.f, 0.f);
+            oa[2 * r + hf] = make_float4(gm * qs[4 * hf][r], gm * qs[4 * hf + 1][r], gm * qs[4 * hf + 2][r],
+                                         gm * qs[4 * hf + 3][r]);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int i = i4 + r;
+        if (!rows || i >= T) continue;
         const int base = s_off[i], cnt = s_dep[i] + 1;
         for (int m0 = 0; m0 < cnt; m0 += 4) {
             float4 rv[4][2];
@@ -390,34 +442,35 @@ __global__ __launch_bounds__(kGdnLargeNT) void gdn_large_kernel(
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
                     const float4 x = rv[u][hf];
-                    ea[2 * r + hf].x += mv * x.x;
-                    ea[2 * r + hf].y += mv * x.y;
-                    ea[2 * r + hf].z += mv * x.z;
-                    ea[2 * r + hf].w += mv * x.w;
-                    oa[hf].x += nv * x.x;
-                    oa[hf].y += nv * x.y;
-                    oa[hf].z += nv * x.z;
-                    oa[hf].w += nv * x.w;
+                    float4& ev = ea[2 * r + hf];
+                    float4& ov = oa[2 * r + hf];
+                    ev.x += mv * x.x;
+                    ev.y += mv * x.y;
+                    ev.z += mv * x.z;
+                    ev.w += mv * x.w;
+                    ov.x += nv * x.x;
+                    ov.y += nv * x.y;
+                    ov.z += nv * x.z;
+                    ov.w += nv * x.w;
                 }
             }
         }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-            const int p0 = 64 * hf + 4 * l16;
-            if (p0 < dv) st4io<TIO, VEC>(o + (row0 + (size_t)i * H) * dv + p0, oa[hf], dv - p0);
+            const int i = i4 + r, p0 = 64 * hf + 4 * l16;
+            if (rows && i < T && p0 < dv) st4io<TIO, VEC>(o + (row0 + (size_t)i * H) * dv + p0, oa[2 * r + hf], dv - p0);
         }
-    }
     __syncthreads();  // every wave has read r
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int i = 16 * w + 4 * q4 + r;
-        if (!rows || i >= T) continue;
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-            const int p0 = 64 * hf + 4 * l16;
-            if (p0 < dv) st4io<float, VEC>(e + (row0 + (size_t)i * H) * dv + p0, ea[2 * r + hf], dv - p0);
+            const int i = i4 + r, p0 = 64 * hf + 4 * l16;
+            if (rows && i < T && p0 < dv) st4io<float, VEC>(e + (row0 + (size_t)i * H) * dv + p0, ea[2 * r + hf], dv - p0);
         }
-    }
 }
 
 }  // namespace
