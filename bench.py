@@ -844,8 +844,10 @@ def main():
         out["gdn_bf16"] = gdn_timing(torch, bnd, W, args.secondary_steps, 0.0, dtype=W.BF16)
         out["gdn_large"] = gdn_timing(torch, bnd, W, args.secondary_steps, 0.0,
                                       shape=dict(GDN_SHAPE, n_nodes=255), tree="level")
-        log(f"[bench] gated delta rule {out['gdn']['workload']}: verify {out['gdn']['verify']['avg_us']:.2f} us, "
-            f"commit {out['gdn']['commit']['avg_us']:.2f} us")
+        for key in ("gdn", "gdn_bf16", "gdn_large"):
+            r = out[key]
+            log(f"[bench] gated delta rule {r['workload']} {r['dtype']}: verify {r['verify']['avg_us']:.2f} us "
+                f"({r['verify']['frac']:.1%}), commit {r['commit']['avg_us']:.2f} us ({r['commit']['frac']:.1%})")
     if not args.no_large:
         out["large"] = large_timing(torch, bnd, W, args.secondary_steps, 0.0 if args.no_oracle else 4.0)
         log(f"[bench] large trees {out['large']['workload']}: verify {out['large']['verify']['avg_us']:.2f} us "
