@@ -106,6 +106,32 @@ def test_large_workload_full_size_sampled(bnd, oracle_mod):
     assert err <= TOL[W.BF16] and herr <= COMMIT_TOL, (err, herr)
 
 
+def test_large_mfma_units_across_items(bnd, oracle_mod):
+    """The MFMA kernel's persistent launch: 4 items x 95 heads of 300-node trees
+    are more (item, head) units than compute units, so work-groups take two
+    consecutive units, and two of them step from one item to the next (units
+    94-95 and 284-285). Items 1 and 2 have invalid trees: their outputs stay
+    untouched, and the units of items 0 and 3 next to them are computed."""
+    import torch
+    inp = W.make_custom(77, batch=4, n_nodes=300, n_heads=95, head_dim=64, d_state=64, n_groups=1,
+                        dtype=W.BF16, tree="recursive", max_depth=12, max_path_len=9)
+    inp["parent"][1, 200] = 250  # parent after child
+    inp["parent"][2, 0] = 5      # bad root
+    dev = bnd.to_device(inp)
+    say("[large] persistent units B=4 T=300 H=95, items 1 and 2 invalid")
+    y = torch.full_like(dev["x"], 1232.0)
+    st = torch.full((4,), -1, dtype=torch.int32, device="cuda")
+    run_verify(bnd, dev, y=y, tree_status=st)
+    torch.cuda.synchronize()
+    assert st.cpu().tolist() == [0, 2, 1, 0]
+    assert (y[1].float() == 1232.0).all() and (y[2].float() == 1232.0).all()
+    good = [(b, h) for b in (0, 3) for h in range(95)]
+    ref, _ = oracle_mod.verify(inp, W.BF16, good)
+    err = slice_err(gpu_y_slices(y, good), ref)
+    say(f"    verify err {err:.3e}")
+    assert err <= TOL[W.BF16], err
+
+
 def test_large_invalid_items_untouched(bnd, oracle_mod):
     import torch
     inp = W.make_custom(91, batch=5, n_nodes=400, n_heads=2, head_dim=32, d_state=16, n_groups=1,
