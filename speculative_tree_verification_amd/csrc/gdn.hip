@@ -15,8 +15,10 @@
 //   S'  = exp(G_l) S0 + sum_{j on path(l)} D_lj e_j k_j^T   (commit, path to l).
 //
 // q, k, v and o fp32 or bf16 (bits); g, beta, S0 and the pseudo-values e
-// fp32; trees of up to 64 nodes, dk and dv up to 128. bf16 rows are converted
-// on load: split into bf16 high and low parts they are exact in the high part.
+// fp32; trees of up to 64 nodes, dk and dv up to 128. bf16 rows of q and k go
+// to LDS as their bits: they are the exact high part, with no low part to
+// stage or multiply (their products with S0 take two terms, their pair scores
+// one).
 // Verify: one work-group of 9 waves per (item, head). Row wave w < 8 owns value
 // rows [16 w, 16 w + 16); the tree wave handles everything node x node.
 //  1. Every load is issued on entry: each row wave's S0 rows straight into
@@ -70,6 +72,23 @@ __device__ __forceinline__ f32x4 mfma_x3(const bf16x8& ah, const bf16x8& al, con
     c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, c, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, c, 0, 0, 0);
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, c, 0, 0, 0);
+}
+
+// a b with a exact in bf16 (a bf16 input row) and b split: hi*lo + hi*hi
+__device__ __forceinline__ f32x4 mfma_x2(const bf16x8& ah, const bf16x8& bh, const bf16x8& bl, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, c, 0, 0, 0);
+}
+
+// four consecutive bf16 elements of a row as bits (zero past the row's end)
+template <bool VEC>
+__device__ __forceinline__ uint2 ld4bits(const uint16_t* __restrict__ p, int rem) {
+    if (VEC) return gload((const uint2*)p);
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        if (t < rem) w[t >> 1] |= (uint32_t)gload(p + t) << (16 * (t & 1));
+    return make_uint2(w[0], w[1]);
 }
 
 __device__ __forceinline__ f32x4 mfma4(const float4& a, const float4& b, f32x4 c) {
@@ -127,15 +146,26 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(
         gl = g[row0 + (size_t)i * H];
         bl = beta[row0 + (size_t)i * H];
     }
-    float4 kst[4], qst[4];  // (node, 4 columns) slots of k and q, 32 slots per row
+    // (node, 4 columns) slots of k and q, 32 slots per row: fp32 rows as
+    // floats (split into bf16 parts for LDS), bf16 rows as their bits (exact
+    // in the high part; no low part is staged or multiplied)
+    constexpr bool BF = sizeof(TIO) == 2;
+    float4 kst[4], qst[4];
+    uint2 kbits[4], qbits[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         const int slot = tid + kGdnRowThreads * m, r = slot >> 5, c = 4 * (slot & 31);
         kst[m] = qst[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+        kbits[m] = qbits[m] = make_uint2(0u, 0u);
         if (!tree_wave && r < T && c < dk) {
             const size_t src = (row0 + (size_t)r * H) * dk + c;
-            kst[m] = ld4io<TIO, VEC>(k + src, dk - c);
-            qst[m] = ld4io<TIO, VEC>(q + src, dk - c);
+            if constexpr (BF) {
+                kbits[m] = ld4bits<VEC>((const uint16_t*)k + src, dk - c);
+                qbits[m] = ld4bits<VEC>((const uint16_t*)q + src, dk - c);
+            } else {
+                kst[m] = ld4io<TIO, VEC>(k + src, dk - c);
+                qst[m] = ld4io<TIO, VEC>(q + src, dk - c);
+            }
         }
     }
     if (tree_wave) {
@@ -198,13 +228,18 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int slot = tid + kGdnRowThreads * m, r = slot >> 5, c = 4 * (slot & 31);
-            uint2 hi, lo;
-            split4(kst[m], hi, lo);
-            *(uint2*)&s_kh[r * RS + c] = hi;
-            *(uint2*)&s_kl[r * RS + c] = lo;
-            split4(qst[m], hi, lo);
-            *(uint2*)&s_qh[r * RS + c] = hi;
-            *(uint2*)&s_ql[r * RS + c] = lo;
+            if constexpr (BF) {
+                *(uint2*)&s_kh[r * RS + c] = kbits[m];
+                *(uint2*)&s_qh[r * RS + c] = qbits[m];
+            } else {
+                uint2 hi, lo;
+                split4(kst[m], hi, lo);
+                *(uint2*)&s_kh[r * RS + c] = hi;
+                *(uint2*)&s_kl[r * RS + c] = lo;
+                split4(qst[m], hi, lo);
+                *(uint2*)&s_qh[r * RS + c] = hi;
+                *(uint2*)&s_ql[r * RS + c] = lo;
+            }
         }
     }
     // S0 and v are requested only now, so that k and q (needed first) do not
@@ -251,8 +286,12 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(
 #pragma unroll
                 for (int ks = 0; ks < kGdnDim / 32; ++ks)
                     if (ks < nks)
-                        P = mfma_x3(*(const bf16x8*)(xh + oa + 32 * ks), *(const bf16x8*)(xl + oa + 32 * ks),
-                                    *(const bf16x8*)(s_kh + ob + 32 * ks), *(const bf16x8*)(s_kl + ob + 32 * ks), P);
+                        P = BF ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(xh + oa + 32 * ks),
+                                                                         *(const bf16x8*)(s_kh + ob + 32 * ks), P, 0,
+                                                                         0, 0)
+                               : mfma_x3(*(const bf16x8*)(xh + oa + 32 * ks), *(const bf16x8*)(xl + oa + 32 * ks),
+                                         *(const bf16x8*)(s_kh + ob + 32 * ks), *(const bf16x8*)(s_kl + ob + 32 * ks),
+                                         P);
                 const int j = 16 * tj + l16;
                 const float Gj = s_G[j];
                 const int dj = s_dep[j];
@@ -318,10 +357,15 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(
                 for (int ks = 0; ks < kGdnDim / 32; ++ks) {
                     if (ks < nks) {
                         const int c = oa + 32 * ks;
-                        R4[ti] = mfma_x3(*(const bf16x8*)(s_kh + c), *(const bf16x8*)(s_kl + c),
-                                         s0h[ks], s0l[ks], R4[ti]);
-                        Q4[ti] = mfma_x3(*(const bf16x8*)(s_qh + c), *(const bf16x8*)(s_ql + c),
-                                         s0h[ks], s0l[ks], Q4[ti]);
+                        if constexpr (BF) {
+                            R4[ti] = mfma_x2(*(const bf16x8*)(s_kh + c), s0h[ks], s0l[ks], R4[ti]);
+                            Q4[ti] = mfma_x2(*(const bf16x8*)(s_qh + c), s0h[ks], s0l[ks], Q4[ti]);
+                        } else {
+                            R4[ti] = mfma_x3(*(const bf16x8*)(s_kh + c), *(const bf16x8*)(s_kl + c),
+                                             s0h[ks], s0l[ks], R4[ti]);
+                            Q4[ti] = mfma_x3(*(const bf16x8*)(s_qh + c), *(const bf16x8*)(s_ql + c),
+                                             s0h[ks], s0l[ks], Q4[ti]);
+                        }
                     }
                 }
                 // right-hand sides r_i = beta_i (v_i - exp(G_i) S0 k_i), 0 past the tree
