@@ -31,6 +31,14 @@ bool use_mfma(const tsv_shape* s) {
            s->n_nodes <= kMaxNodesMfma && s->head_dim == 64 && (s->d_state == 64 || s->d_state == 128);
 }
 
+int compute_units() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return 256;
+    return n;
+}
+
 // Heads per work-group: the largest divisor of the heads of one group that
 // still gives the GPU `per_cu` work-groups per compute unit. More heads per
 // work-group amortise the tree set-up (validation, pair lists, pair scores);
@@ -40,7 +48,7 @@ bool use_mfma(const tsv_shape* s) {
 // per compute unit, the wide-tree kernel (which fills a compute unit's LDS
 // and takes its heads one after another) at one.
 int default_heads_per_block(const tsv_shape* s, int per_cu) {
-    const long want = (long)tsv::compute_units() * per_cu;
+    const long want = (long)compute_units() * per_cu;
     const int hpg = s->n_heads / s->n_groups;
     int best = 1;
     for (int d = 1; d <= hpg; ++d)
@@ -316,15 +324,3 @@ const char* tree_ssd_status_string(int32_t status) {
 int32_t tree_ssd_abi_version(void) { return TREE_SSD_ABI_VERSION; }
 
 }  // extern "C"
-
-namespace tsv {
-
-int compute_units() {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-        return 256;
-    return n;
-}
-
-}  // namespace tsv

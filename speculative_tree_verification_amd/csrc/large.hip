@@ -161,13 +161,6 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_kernel(
 //    S X[J] on fp32 MFMA. The accumulator of G^T holds S[i][j] with i = lane % 16
 //    and j = 4 (lane / 16) + c in element c: the A operand of the step that
 //    takes those j, with the matching X rows as its B operand.
-// The launch is persistent: at most one work-group per compute unit, each
-// taking a contiguous run of units (item, head, part), where part p of S takes
-// every S-th node tile. The tree set-up (validation, depth) runs once per item
-// a work-group meets, not once per unit; each unit stages its head's step
-// sizes and h0 planes, and the next unit's h0 and step sizes are requested as
-// soon as a wave has finished its tiles, so they arrive while the slower waves
-// of the work-group still walk.
 constexpr int kLmDist = 32;  // path steps per pass
 
 template <int KS>
@@ -175,7 +168,7 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const float* __restrict__ A,
     const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm, const float* __restrict__ D,
     const float* __restrict__ h0, const int32_t* __restrict__ parent, uint16_t* __restrict__ y,
-    int32_t* __restrict__ tree_status, int T, int H, int G, int S, int n_units, int per_wg) {
+    int32_t* __restrict__ tree_status, int T, int H, int G, int S) {
     constexpr int P = 64, N = 32 * KS, NW = kLargeWaves;
     constexpr int RH = N + 8;  // row stride (bf16) of the h0 planes
     __shared__ int s_par[kMaxNodesLarge];
@@ -191,220 +184,199 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
     __shared__ unsigned long long s_bits[NW][kMaxNodesLarge / 64];  // ancestors flagged this pass
     __shared__ uint16_t s_J[NW][16 * kLmDist];
 
-    // logical block lb takes units [lb per_wg, (lb + 1) per_wg); unit = (b H + h) S
-    // + part. Consecutive logical blocks share an XCD, and with it the L2 that
-    // holds their item's rows
+    // logical block = (b H + h) S + part: the S work-groups of one (item, head)
+    // take every S-th node tile (shallow and deep ones alike) and share an XCD,
+    // so that h0 is fetched into one L2
     const int lb = xcd_block(blockIdx.x, gridDim.x);
-    const int u_begin = lb * per_wg, u_end = min(u_begin + per_wg, n_units);
+    const int part = lb % S;
+    const int b = lb / S / H;
+    const int h = lb / S % H;
+    const int g = h / (H / G);
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int l16 = lane & 15, q4 = lane >> 4;
+    // the parents, this thread's step size and its share of h0 leave together
+    // (one thread per node, T <= 1024 = threads), so the tree check and the
+    // pointer jumping overlap the other two round trips
+    const int par_i = load_parent(parent + (size_t)b * T, T);
+    const uint32_t dt_i = gload(dt + ((size_t)b * T + min(tid, T - 1)) * H + h);
     constexpr int HF4 = P * N / 4 / kLargeThreads;  // float4 of h0 per thread
     static_assert(P * N % (4 * kLargeThreads) == 0, "h0 must split evenly over the threads");
-    if (u_begin >= u_end) return;
-    // the first unit's parents, this thread's step size and its share of h0
-    // leave together (one thread per node, T <= 1024 = threads), so the tree
-    // check and the pointer jumping overlap the other two round trips
-    int b = u_begin / S / H, h = u_begin / S % H;
-    int par_i = load_parent(parent + (size_t)b * T, T);
-    uint32_t dt_i = gload(dt + ((size_t)b * T + min(tid, T - 1)) * H + h);
     float4 hv[HF4];
-    {
-        const float4* H0 = (const float4*)(h0 + ((size_t)b * H + h) * P * N);
+    const float4* H0 = (const float4*)(h0 + ((size_t)b * H + h) * P * N);
 #pragma unroll
-        for (int m = 0; m < HF4; ++m) hv[m] = gload(H0 + tid + kLargeThreads * m);
+    for (int m = 0; m < HF4; ++m) hv[m] = gload(H0 + tid + kLargeThreads * m);
+    const int st = check_tree(par_i, T, s_par);
+    if (h == 0 && part == 0 && tid == 0 && tree_status) tree_status[b] = st;
+    if (st) return;
+    tree_depth(s_par, T, s_nxt, s_dep);
+
+    const float Ah = A[h];
+    const float Dh = D[h];
+    if (tid < T) s_a[tid] = bf16_bits_to_f32(dt_i);
+#pragma unroll
+    for (int m = 0; m < HF4; ++m) {
+        const int e = 4 * (tid + kLargeThreads * m);  // 4 consecutive n of row p
+        const int p = e / N, n = e - p * N;
+        const float v[4] = {hv[m].x, hv[m].y, hv[m].z, hv[m].w};
+        uint16_t hb[4], lb[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const __bf16 t = (__bf16)v[k];
+            hb[k] = __builtin_bit_cast(uint16_t, t);
+            lb[k] = f32_to_bf16_bits(v[k] - (float)t);
+        }
+        *(uint2*)&s_h0h[p * RH + n] = make_uint2(hb[0] | ((uint32_t)hb[1] << 16), hb[2] | ((uint32_t)hb[3] << 16));
+        *(uint2*)&s_h0l[p * RH + n] = make_uint2(lb[0] | ((uint32_t)lb[1] << 16), lb[2] | ((uint32_t)lb[3] << 16));
     }
     for (int e = tid; e < NW * kMaxNodesLarge / 64; e += kLargeThreads) (&s_bits[0][0])[e] = 0ull;
-    int cur_b = -1, st = 0;
-    for (int u = u_begin; u < u_end; ++u) {
-        const int part = u % S;
-        b = u / S / H;
-        h = u / S % H;
-        const int g = h / (H / G);
-        if (b != cur_b) {
-            st = check_tree(par_i, T, s_par);
-            if (!st) tree_depth(s_par, T, s_nxt, s_dep);
-            cur_b = b;
-        }
-        if (h == 0 && part == 0 && tid == 0 && tree_status) tree_status[b] = st;
-        if (!st) {
-            const float Ah = A[h];
-            const float Dh = D[h];
-            if (tid < T) s_a[tid] = bf16_bits_to_f32(dt_i);
-#pragma unroll
-            for (int m = 0; m < HF4; ++m) {
-                const int e = 4 * (tid + kLargeThreads * m);  // 4 consecutive n of row p
-                const int p = e / N, n = e - p * N;
-                const float v[4] = {hv[m].x, hv[m].y, hv[m].z, hv[m].w};
-                uint16_t hb[4], lb[4];
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const __bf16 t = (__bf16)v[k];
-                    hb[k] = __builtin_bit_cast(uint16_t, t);
-                    lb[k] = f32_to_bf16_bits(v[k] - (float)t);
-                }
-                *(uint2*)&s_h0h[p * RH + n] = make_uint2(hb[0] | ((uint32_t)hb[1] << 16), hb[2] | ((uint32_t)hb[3] << 16));
-                *(uint2*)&s_h0l[p * RH + n] = make_uint2(lb[0] | ((uint32_t)lb[1] << 16), lb[2] | ((uint32_t)lb[3] << 16));
-            }
-            __syncthreads();
+    __syncthreads();
 
-            const size_t xrow = (size_t)H * P;  // x / y stride between nodes
-            const uint16_t* xb = x + ((size_t)b * T * H + h) * P;
-            uint16_t* yb = y + ((size_t)b * T * H + h) * P;
-            for (int tt = w; 16 * (tt * S + part) < T; tt += NW) {
-                const int i0 = 16 * (tt * S + part);
-                // C rows of the tile: node i0 + l16, columns 32 ks + 8 q4 ..
-                bf16x8 cf[KS];
-                const uint16_t* crow = Cm + (((size_t)b * T + min(i0 + l16, T - 1)) * G + g) * N;
+    const size_t xrow = (size_t)H * P;  // x / y stride between nodes
+    const uint16_t* xb = x + ((size_t)b * T * H + h) * P;
+    uint16_t* yb = y + ((size_t)b * T * H + h) * P;
+    for (int tt = w; 16 * (tt * S + part) < T; tt += NW) {
+        const int i0 = 16 * (tt * S + part);
+        // C rows of the tile: node i0 + l16, columns 32 ks + 8 q4 ..
+        bf16x8 cf[KS];
+        const uint16_t* crow = Cm + (((size_t)b * T + min(i0 + l16, T - 1)) * G + g) * N;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) cf[ks] = __builtin_bit_cast(bf16x8, *(const uint4*)(crow + 32 * ks + 8 * q4));
-                f32x4 yw[4];  // walk term: rows i0 + 4 q4 + c, columns p = 16 pt + l16
+        for (int ks = 0; ks < KS; ++ks) cf[ks] = __builtin_bit_cast(bf16x8, *(const uint4*)(crow + 32 * ks + 8 * q4));
+        f32x4 yw[4];  // walk term: rows i0 + 4 q4 + c, columns p = 16 pt + l16
 #pragma unroll
-                for (int pt = 0; pt < 4; ++pt) yw[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                // the walk, 32 path steps a pass
-                int jw = lane < 16 && i0 + lane < T ? i0 + lane : -1;
-                float sw = 0.f;
-                const int inode = i0 + l16;
-                const int di = s_dep[min(inode, T - 1)];
-                for (int k = 0;; ++k) {
-                    if (lane < 16) {
-                        int t = 0;
-                        for (; t < kLmDist && jw >= 0; ++t) {
-                            const float dtj = s_a[jw];
-                            s_path[w][lane][t] = (uint16_t)jw;
-                            s_dec[w][lane][t] = __expf(sw) * dtj;
-                            sw += dtj * Ah;
-                            atomicOr(&s_bits[w][jw >> 6], 1ull << (jw & 63));
-                            jw = s_par[jw];
-                        }
-                        s_plen[w][lane] = t;
-                        s_cum[w][lane] = sw;
-                    }
-                    wave_sync();
-                    // compact the flagged ancestors (they precede the tile's last node)
-                    int nJ = 0;  // wave-uniform
-                    const int nwords = (min(T, i0 + 16) + 63) >> 6;
-                    for (int wd = 0; wd < nwords; ++wd) {
-                        const unsigned long long m = s_bits[w][wd];
-                        if (!m) continue;  // wave-uniform
-                        if ((m >> lane) & 1ull) s_J[w][nJ + __popcll(m & ((1ull << lane) - 1))] = (uint16_t)(64 * wd + lane);
-                        nJ += __popcll(m);
-                        if (lane == 0) s_bits[w][wd] = 0ull;
-                    }
-                    wave_sync();
-                    // per column block of 16: the X values this lane feeds to the S X
-                    // steps (row J[c0 + 4 q4 + c], column 16 pt + l16), requested one
-                    // block ahead (clamped rows past the list: loaded, unused)
-                    auto xvals = [&](int c0, float (&xq)[4][4]) {
-#pragma unroll
-                        for (int c = 0; c < 4; ++c) {
-                            const uint16_t* xr = xb + (size_t)s_J[w][min(c0 + 4 * q4 + c, nJ - 1)] * xrow;
-#pragma unroll
-                            for (int pt = 0; pt < 4; ++pt) xq[c][pt] = bf16_bits_to_f32(xr[16 * pt + l16]);
-                        }
-                    };
-                    float xq[4][4];
-                    xvals(0, xq);
-                    for (int c0 = 0; c0 < nJ; c0 += 16) {
-                        // G^T block: rows J[c0 + l16] (A operand: B rows), columns the tile (C rows)
-                        const uint16_t* brow = Bm + (((size_t)b * T + s_J[w][min(c0 + l16, nJ - 1)]) * G + g) * N;
-                        uint4 bq[KS];
-#pragma unroll
-                        for (int ks = 0; ks < KS; ++ks) bq[ks] = *(const uint4*)(brow + 32 * ks + 8 * q4);
-                        float xn[4][4];
-                        xvals(c0 + 16, xn);
-                        f32x4 gt = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int ks = 0; ks < KS; ++ks)
-                            gt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bq[ks]), cf[ks], gt, 0, 0, 0);
-#pragma unroll
-                        for (int c = 0; c < 4; ++c) {
-                            const int jpos = c0 + 4 * q4 + c;
-                            const int j = s_J[w][min(jpos, nJ - 1)];
-                            float wgt = 0.f;
-                            const int t = di - s_dep[j] - kLmDist * k;
-                            if (jpos < nJ && inode < T && t >= 0 && t < s_plen[w][l16] && s_path[w][l16][t] == j)
-                                wgt = s_dec[w][l16][t];
-                            const float sv = gt[c] * wgt;
-#pragma unroll
-                            for (int pt = 0; pt < 4; ++pt)
-                                yw[pt] = __builtin_amdgcn_mfma_f32_16x16x4f32(sv, xq[c][pt], yw[pt], 0, 0, 0);
-                        }
-#pragma unroll
-                        for (int c = 0; c < 4; ++c)
-#pragma unroll
-                            for (int pt = 0; pt < 4; ++pt) xq[c][pt] = xn[c][pt];
-                    }
-                    if (!__ballot(lane < 16 && jw >= 0)) break;
-                    wave_sync();  // lists and columns of this pass consumed
+        for (int pt = 0; pt < 4; ++pt) yw[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // the walk, 32 path steps a pass
+        int jw = lane < 16 && i0 + lane < T ? i0 + lane : -1;
+        float sw = 0.f;
+        const int inode = i0 + l16;
+        const int di = s_dep[min(inode, T - 1)];
+        for (int k = 0;; ++k) {
+            if (lane < 16) {
+                int t = 0;
+                for (; t < kLmDist && jw >= 0; ++t) {
+                    const float dtj = s_a[jw];
+                    s_path[w][lane][t] = (uint16_t)jw;
+                    s_dec[w][lane][t] = __expf(sw) * dtj;
+                    sw += dtj * Ah;
+                    atomicOr(&s_bits[w][jw >> 6], 1ull << (jw & 63));
+                    jw = s_par[jw];
                 }
-                // own x values for the D term, requested before the read-out
-                float xi[4][4];
+                s_plen[w][lane] = t;
+                s_cum[w][lane] = sw;
+            }
+            wave_sync();
+            // compact the flagged ancestors (they precede the tile's last node)
+            int nJ = 0;  // wave-uniform
+            const int nwords = (min(T, i0 + 16) + 63) >> 6;
+            for (int wd = 0; wd < nwords; ++wd) {
+                const unsigned long long m = s_bits[w][wd];
+                if (!m) continue;  // wave-uniform
+                if ((m >> lane) & 1ull) s_J[w][nJ + __popcll(m & ((1ull << lane) - 1))] = (uint16_t)(64 * wd + lane);
+                nJ += __popcll(m);
+                if (lane == 0) s_bits[w][wd] = 0ull;
+            }
+            wave_sync();
+            // per column block of 16: the X values this lane feeds to the S X
+            // steps (row J[c0 + 4 q4 + c], column 16 pt + l16), requested one
+            // block ahead (clamped rows past the list: loaded, unused)
+            auto xvals = [&](int c0, float (&xq)[4][4]) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    const int i = min(i0 + 4 * q4 + c, T - 1);
+                    const uint16_t* xr = xb + (size_t)s_J[w][min(c0 + 4 * q4 + c, nJ - 1)] * xrow;
 #pragma unroll
-                    for (int pt = 0; pt < 4; ++pt) xi[c][pt] = bf16_bits_to_f32(xb[(size_t)i * xrow + 16 * pt + l16]);
+                    for (int pt = 0; pt < 4; ++pt) xq[c][pt] = bf16_bits_to_f32(xr[16 * pt + l16]);
                 }
-                // read-out h0 . C of the tile, same layout as the walk term
-                f32x4 y0[4];
+            };
+            float xq[4][4];
+            xvals(0, xq);
+            for (int c0 = 0; c0 < nJ; c0 += 16) {
+                // G^T block: rows J[c0 + l16] (A operand: B rows), columns the tile (C rows)
+                const uint16_t* brow = Bm + (((size_t)b * T + s_J[w][min(c0 + l16, nJ - 1)]) * G + g) * N;
+                uint4 bq[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) bq[ks] = *(const uint4*)(brow + 32 * ks + 8 * q4);
+                float xn[4][4];
+                xvals(c0 + 16, xn);
+                f32x4 gt = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    gt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bq[ks]), cf[ks], gt, 0, 0, 0);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int jpos = c0 + 4 * q4 + c;
+                    const int j = s_J[w][min(jpos, nJ - 1)];
+                    float wgt = 0.f;
+                    const int t = di - s_dep[j] - kLmDist * k;
+                    if (jpos < nJ && inode < T && t >= 0 && t < s_plen[w][l16] && s_path[w][l16][t] == j)
+                        wgt = s_dec[w][l16][t];
+                    const float sv = gt[c] * wgt;
+#pragma unroll
+                    for (int pt = 0; pt < 4; ++pt)
+                        yw[pt] = __builtin_amdgcn_mfma_f32_16x16x4f32(sv, xq[c][pt], yw[pt], 0, 0, 0);
+                }
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+#pragma unroll
+                    for (int pt = 0; pt < 4; ++pt) xq[c][pt] = xn[c][pt];
+            }
+            if (!__ballot(lane < 16 && jw >= 0)) break;
+            wave_sync();  // lists and columns of this pass consumed
+        }
+        // own x values for the D term, requested before the read-out
+        float xi[4][4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int i = min(i0 + 4 * q4 + c, T - 1);
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) xi[c][pt] = bf16_bits_to_f32(xb[(size_t)i * xrow + 16 * pt + l16]);
+        }
+        // read-out h0 . C of the tile, same layout as the walk term
+        f32x4 y0[4];
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+            y0[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int o = (16 * pt + l16) * RH + 32 * ks + 8 * q4;
+                y0[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf[ks], *(const bf16x8*)&s_h0l[o], y0[pt], 0, 0, 0);
+                y0[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf[ks], *(const bf16x8*)&s_h0h[o], y0[pt], 0, 0, 0);
+            }
+        }
+        wave_sync();  // s_cum
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int i = i0 + 4 * q4 + c;
+            if (i < T) {
+                const float ec = expf(s_cum[w][4 * q4 + c]);
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt) {
-                    y0[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) {
-                        const int o = (16 * pt + l16) * RH + 32 * ks + 8 * q4;
-                        y0[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf[ks], *(const bf16x8*)&s_h0l[o], y0[pt], 0, 0, 0);
-                        y0[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf[ks], *(const bf16x8*)&s_h0h[o], y0[pt], 0, 0, 0);
-                    }
+                    const size_t o = (size_t)i * xrow + 16 * pt + l16;
+                    yb[o] = f32_to_bf16_bits(ec * y0[pt][c] + yw[pt][c] + Dh * xi[c][pt]);
                 }
-                wave_sync();  // s_cum
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int i = i0 + 4 * q4 + c;
-                    if (i < T) {
-                        const float ec = expf(s_cum[w][4 * q4 + c]);
-#pragma unroll
-                        for (int pt = 0; pt < 4; ++pt) {
-                            const size_t o = (size_t)i * xrow + 16 * pt + l16;
-                            yb[o] = f32_to_bf16_bits(ec * y0[pt][c] + yw[pt][c] + Dh * xi[c][pt]);
-                        }
-                    }
-                }
-                wave_sync();  // s_cum, lists of this tile consumed
             }
-        }  // valid tree
-        // the next unit's operands leave as soon as this wave is done
-        if (u + 1 < u_end) {
-            const int nb = (u + 1) / S / H, nh = (u + 1) / S % H;
-            if (nb != cur_b) par_i = load_parent(parent + (size_t)nb * T, T);
-            dt_i = gload(dt + ((size_t)nb * T + min(tid, T - 1)) * H + nh);
-            const float4* H0 = (const float4*)(h0 + ((size_t)nb * H + nh) * P * N);
-#pragma unroll
-            for (int m = 0; m < HF4; ++m) hv[m] = gload(H0 + tid + kLargeThreads * m);
         }
-        __syncthreads();  // the unit's LDS reads are done before the next one stages
-    }  // units
+        wave_sync();  // s_cum, lists of this tile consumed
+    }
 }
 
-// Parts per (item, head) of the MFMA kernel. The launch is persistent: at
-// most one work-group per compute unit (a work-group fills one), each taking
-// per_wg = ceil(units S / CUs) consecutive units. The busiest work-group's time
-// is per_wg (unit overhead + tile work / S) plus one tree set-up; the unit
-// overhead (the h0 planes and step sizes staged, the wait for the unit's
-// slowest wave) is taken as a twentieth of an unsplit unit's tile work.
-// Measured on batch 4 x 80 heads of 1023-node trees: S = 4 (five units per
-// work-group) 103.8 us, S = 2 108.2 us, S = 1 128.8 us; the same launch
-// without the unit loop (every part repeating the tree set-up, S = 2) took
-// 104.8 us, so the repeated set-up was not what bounds it.
-constexpr double kLargeUnitShare = 0.05;
-static int large_split(int units, int T, int cus) {
+// Work-groups per (item, head) of the MFMA kernel: a work-group fills a
+// compute unit, so the launch runs in rounds of one work-group per unit. Each
+// of the S parts takes every S-th 16-node tile (at least one per wave) and
+// repeats the set-up (tree, depth, h0 planes), which costs about a fifth of
+// an unsplit work-group's tile work on the 1023-node trees. S minimises
+// rounds x (set-up + tile work / S) = ceil(units S / CUs) (0.2 + 1 / S).
+constexpr double kLargeSetupShare = 0.2;
+static int large_split(int units, int T) {
+    int cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
     const int tiles = (T + 15) / 16;
     int best = 1;
     double best_cost = 1e30;
     for (int S = 1; S <= 8 && S * kLargeWaves <= tiles; S *= 2) {
-        const double cost = (double)(((long)units * S + cus - 1) / cus) * (kLargeUnitShare + 1.0 / S);
+        const double cost = (double)(((long)units * S + cus - 1) / cus) * (kLargeSetupShare + 1.0 / S);
         if (cost < best_cost) best_cost = cost, best = S;
     }
     return best;
@@ -413,21 +385,18 @@ static int large_split(int units, int T, int cus) {
 hipError_t launch_verify_large(const VerifyArgs& a, bool bf16, hipStream_t stream) {
     dim3 grid((unsigned)(a.batch * a.H));
     if (bf16 && a.P == 64 && (a.N == 64 || a.N == 128)) {
-        const int cus = compute_units();
-        const int S = large_split(a.batch * a.H, a.T, cus);
-        const int units = a.batch * a.H * S;
-        const int per_wg = (units + cus - 1) / cus;
-        dim3 gs((unsigned)((units + per_wg - 1) / per_wg));
+        const int S = large_split(a.batch * a.H, a.T);
+        dim3 gs((unsigned)(a.batch * a.H * S));
         if (a.N == 128)
             hipLaunchKernelGGL(verify_large_mfma_kernel<4>, gs, dim3(kLargeThreads), 0, stream,
                                (const uint16_t*)a.x, (const uint16_t*)a.dt, a.A, (const uint16_t*)a.B,
                                (const uint16_t*)a.C, a.D, a.h0, a.parent, (uint16_t*)a.y,
-                               a.tree_status, a.T, a.H, a.G, S, units, per_wg);
+                               a.tree_status, a.T, a.H, a.G, S);
         else
             hipLaunchKernelGGL(verify_large_mfma_kernel<2>, gs, dim3(kLargeThreads), 0, stream,
                                (const uint16_t*)a.x, (const uint16_t*)a.dt, a.A, (const uint16_t*)a.B,
                                (const uint16_t*)a.C, a.D, a.h0, a.parent, (uint16_t*)a.y,
-                               a.tree_status, a.T, a.H, a.G, S, units, per_wg);
+                               a.tree_status, a.T, a.H, a.G, S);
         return hipGetLastError();
     }
     const bool lds = a.P * (((a.N + 3) & ~3) + 4) <= kLargeH0Lds;

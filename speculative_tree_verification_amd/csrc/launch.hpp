@@ -57,9 +57,6 @@ hipError_t launch_verify_tiny(const VerifyArgs& a, hipStream_t stream);
 hipError_t launch_commit(const CommitArgs& a, bool bf16, hipStream_t stream);
 
 // trees of 257 to 1024 nodes: plain fp32 VALU verify and commit (any P, N <= 256)
-// compute units of the current device (256 if the runtime cannot tell)
-int compute_units();
-
 hipError_t launch_verify_large(const VerifyArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_commit_large(const CommitArgs& a, bool bf16, hipStream_t stream);
 

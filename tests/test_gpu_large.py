@@ -107,11 +107,9 @@ def test_large_workload_full_size_sampled(bnd, oracle_mod):
 
 
 def test_large_mfma_units_across_items(bnd, oracle_mod):
-    """The MFMA kernel's persistent launch: 4 items x 95 heads of 300-node trees
-    are more (item, head) units than compute units, so work-groups take two
-    consecutive units, and two of them step from one item to the next (units
-    94-95 and 284-285). Items 1 and 2 have invalid trees: their outputs stay
-    untouched, and the units of items 0 and 3 next to them are computed."""
+    """The MFMA kernel over more (item, head) units than compute units: 4 items
+    x 95 heads of 300-node trees, items 1 and 2 with invalid trees, whose
+    outputs stay untouched while every head of items 0 and 3 is computed."""
     import torch
     inp = W.make_custom(77, batch=4, n_nodes=300, n_heads=95, head_dim=64, d_state=64, n_groups=1,
                         dtype=W.BF16, tree="recursive", max_depth=12, max_path_len=9)
