@@ -201,10 +201,9 @@ tsv_status tree_ssd_commit_layers(const tsv_shape* s, int32_t n_layers,
  * in_dtype is the type of q, k, v and o: TSV_F32 or TSV_BF16 (bf16 bit
  * patterns); g, beta, S0 and e are fp32 either way. n_nodes <= 256, dk and
  * dv <= 128 (TSV_E_UNSUPPORTED otherwise). Trees of 65 to 256 nodes take a
- * plain kernel that solves the pseudo-values in place in e, so e is required
- * there (TSV_E_NULL otherwise), and a tree with more than 4096
- * ancestor-or-self pairs (the sum over nodes of depth + 1) sets status bit 8
- * and is left untouched.
+ * second kernel, which holds the tree's pair tables in LDS: a tree with more
+ * than 4096 ancestor-or-self pairs (the sum over nodes of depth + 1) sets
+ * status bit 8 and is left untouched.
  *   q, k   [Bt][T][H][dk]   queries and keys (keys normally of unit length)
  *   v      [Bt][T][H][dv]   values
  *   g      [Bt][T][H]       log gate (<= 0)

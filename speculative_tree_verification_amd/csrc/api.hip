@@ -146,7 +146,6 @@ tsv_status tree_gdn_verify(const tsv_shape* s, const void* q, const void* k, con
     if (s->batch == 0 || s->n_nodes == 0) return TSV_OK;
     if (!q || !k || !v || !g || !beta || !S0 || !parent || !o) return TSV_E_NULL;
     if (tsv::gdn_large_supported(s->n_nodes)) {
-        if (!e) return TSV_E_NULL;  // the pseudo-values are solved in place in e
         hipError_t err = tsv::launch_gdn_large(s->batch, s->n_nodes, s->n_heads, s->d_state, s->head_dim,
                                                s->in_dtype == TSV_BF16, q, k, v, g, beta, S0, parent, o, e,
                                                tree_status, (hipStream_t)stream);

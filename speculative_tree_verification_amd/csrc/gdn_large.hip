@@ -10,6 +10,7 @@
 // With M = (I + A)^{-1} and N = W M, both nonzero on ancestor-or-self pairs
 // only, e = M r and o = exp(G) S0 q + N r: the solve moves from the value rows
 // onto one scalar per pair, and both outputs come from one gather over r.
+// e is written only if the caller asks for it.
 //
 // One work-group of 16 waves per (item, head); wave w owns nodes [16 w, 16 w + 16):
 //  1. tree check, depth and every node's ancestor list (itself first, then up
@@ -17,20 +18,20 @@
 //     ancestor-or-self pairs is reported with status 8 and left untouched.
 //     S0 is staged in LDS as bf16 high and low parts, in the order the MFMA B
 //     operand reads it (one linear 1 KB read per wave and step).
-//  2. K S0^T for the wave's 16 nodes on MFMA (three-term bf16 splits, fp32
-//     accumulation; two terms for bf16 inputs, whose low parts are zero), then
-//     r into the caller's e buffer. The column order of the product tiles
-//     gives each lane four consecutive value rows twice, so v, r, e and o move
-//     as 16-byte vectors.
-//  3. pair scores of the wave's nodes from the k and q columns its lanes hold
-//     as A operands (only the ancestors' k rows are loaded), then Q S0^T,
-//     kept in registers; M by substitution one depth level at a time, one
-//     pair entry per thread:
+//  2. pair scores of the wave's nodes from the k and q columns its lanes
+//     hold as MFMA A operands (only the ancestors' k rows are loaded);
+//  3. Q S0^T and K S0^T for the wave's 16 nodes on MFMA (three-term bf16
+//     splits, fp32 accumulation; two terms for bf16 inputs, whose low parts
+//     are zero), and r in registers. The column order of the product tiles
+//     gives each lane four consecutive value rows twice, so v, r, e and o
+//     move as 16-byte vectors;
+//  4. M by substitution one depth level at a time, one pair entry per thread:
 //        M_ij = -A_ij - sum_{x strictly between j and i} A_ix M_xj;
-//     then N_ij = sum_{x from i down to j} W_ix M_xj, all entries at once.
-//  4. e_i = sum_j M_ij r_j and o_i = exp(G_i) (S0 q_i) + sum_j N_ij r_j over the
-//     root path of i, reading r back from e; e is written once every wave has
-//     read r.
+//     then N_ij = sum_{x from i down to j} W_ix M_xj, all entries at once;
+//  5. e_i = sum_j M_ij r_j and o_i = exp(G_i) (S0 q_i) + sum_j N_ij r_j over the
+//     root path of i, one half of the value rows at a time: that half of r
+//     (64 floats per node, 64 KB) sits in LDS where the S0 planes were, so r
+//     never goes to memory.
 // q, k, v and o are fp32 or bf16 (bits); g, beta, S0 and e fp32.
 #include "common.hpp"
 #include "launch.hpp"
@@ -239,8 +240,9 @@ __global__ __launch_bounds__(kGdnLargeNT) void gdn_large_kernel(
     }
     const int ia = 16 * w + l16;  // A-operand row of this lane
     const bool alive = rows && ia < T;
-    ARow<TIO> ka;
+    ARow<TIO> ka, qa;
     load_a<TIO, VEC>(k + (row0 + (size_t)min(ia, T - 1) * H) * dk, alive, q4, dk, ka);
+    load_a<TIO, VEC>(q + (row0 + (size_t)min(ia, T - 1) * H) * dk, alive, q4, dk, qa);
     const int i4 = 16 * w + 4 * q4;  // nodes i4 .. i4 + 3 of this lane's accumulators
 
     const int st = check_tree_lds<NT>(par_i, T, s_par, s_red);
@@ -298,51 +300,12 @@ __global__ __launch_bounds__(kGdnLargeNT) void gdn_large_kernel(
     lds_barrier();
     if (tid < T) s_lvl[atomicAdd(&s_cnt[s_dep[tid]], 1)] = tid;
 
-    // ---- 2. K S0^T, then r = beta (v - exp(G) K S0^T) into e (all stores
-    // issued together, after the last load they depend on)
+    // ---- 2. pair scores of the wave's nodes: lane (l16, q4) holds the
+    // product columns of k_i and q_i (i = ia); for each ancestor j it loads
+    // the same columns of k_j, and the four lanes of node i add up
     f32x4 qs[kLNB];
-    ARow<TIO> qa;
+    float4 rr[8];  // r at the accumulator positions: node i4 + r, value rows 64 hf + 4 l16 .. + 3
     if (rows) {
-        f32x4 ks_[kLNB];
-        s0_product<TIO>(ka, s_S0, lane, dk, dv, ks_);
-        __builtin_amdgcn_sched_barrier(0);
-        // v at the accumulator positions: node i4 + r, value rows p0 .. p0 + 3
-        float4 vv[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const int i = i4 + r, p0 = 64 * hf + 4 * l16;
-                vv[2 * r + hf] = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (i < T && p0 < dv) vv[2 * r + hf] = ld4io<TIO, VEC>(v + (row0 + (size_t)i * H) * dv + p0, dv - p0);
-            }
-        // every value first, then the stores: no wait between two stores
-        float4 rr[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = min(i4 + r, T - 1);
-            const float bt = s_bt[i], gm = s_gam[i];
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const float4 x = vv[2 * r + hf];
-                rr[2 * r + hf] = make_float4(bt * (x.x - gm * ks_[4 * hf][r]), bt * (x.y - gm * ks_[4 * hf + 1][r]),
-                                             bt * (x.z - gm * ks_[4 * hf + 2][r]),
-                                             bt * (x.w - gm * ks_[4 * hf + 3][r]));
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const int i = i4 + r, p0 = 64 * hf + 4 * l16;
-                if (i < T && p0 < dv) st4io<float, VEC>(e + (row0 + (size_t)i * H) * dv + p0, rr[2 * r + hf], dv - p0);
-            }
-        __builtin_amdgcn_sched_barrier(0);  // q is loaded only once v and the products are consumed
-        load_a<TIO, VEC>(q + (row0 + (size_t)min(ia, T - 1) * H) * dk, alive, q4, dk, qa);
-
-        // ---- 3. pair scores of the wave's nodes: lane (l16, q4) holds the
-        // product columns of k_i and q_i (i = ia); for each ancestor j it loads
-        // the same columns of k_j, and the four lanes of node i add up
         const int cnt = alive ? s_dep[ia] + 1 : 0, base = alive ? s_off[ia] : 0;
         for (int m = 0; m < cnt; ++m) {
             ARow<TIO> kj = ka;
@@ -358,11 +321,46 @@ __global__ __launch_bounds__(kGdnLargeNT) void gdn_large_kernel(
                 s_W[base + m] = D * qk;
             }
         }
-        s0_product<TIO>(qa, s_S0, lane, dk, dv, qs);
-    }
-    lds_barrier();
 
-    // M, one depth level at a time: entry (i, m) for the ancestor m steps up
+        // ---- 3. Q S0^T (kept), K S0^T, and r = beta (v - exp(G) K S0^T)
+        s0_product<TIO>(qa, s_S0, lane, dk, dv, qs);
+        f32x4 ks_[kLNB];
+        s0_product<TIO>(ka, s_S0, lane, dk, dv, ks_);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int i = i4 + r, p0 = 64 * hf + 4 * l16;
+                rr[2 * r + hf] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (i < T && p0 < dv) rr[2 * r + hf] = ld4io<TIO, VEC>(v + (row0 + (size_t)i * H) * dv + p0, dv - p0);
+            }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = min(i4 + r, T - 1);
+            const float bt = s_bt[i], gm = s_gam[i];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const float4 x = rr[2 * r + hf];
+                rr[2 * r + hf] = make_float4(bt * (x.x - gm * ks_[4 * hf][r]), bt * (x.y - gm * ks_[4 * hf + 1][r]),
+                                             bt * (x.z - gm * ks_[4 * hf + 2][r]),
+                                             bt * (x.w - gm * ks_[4 * hf + 3][r]));
+            }
+        }
+    }
+    lds_barrier();  // the pair scores are complete, and no wave reads the S0 planes any more
+
+    // r of value rows 0..63 goes where the S0 planes were: a 64-float row per node
+    float* const s_r = (float*)s_S0;
+    auto stage_r = [&](int hf) {
+        if (!rows) return;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (i4 + r < T) *(float4*)&s_r[(i4 + r) * 64 + 4 * l16] = rr[2 * r + hf];
+    };
+    stage_r(0);
+
+    // ---- 4. M, one depth level at a time: entry (i, m) for the ancestor m steps up
     for (int d = 1; d <= maxdep; ++d) {
         const int lo = s_lvs[d], entries = (s_lvs[d + 1] - lo) * d;
         for (int x = tid; x < entries; x += NT) {
@@ -403,74 +401,55 @@ __global__ __launch_bounds__(kGdnLargeNT) void gdn_large_kernel(
         }
         s_A[x] = acc;
     }
-    __syncthreads();  // N complete, and every wave's r is in e
+    lds_barrier();  // N and the first half of r are complete
 
-    // ---- 4. e = M r, o = exp(G) (Q S0^T) + N r over each root path; the
-    // stores follow the last load
-    float4 ea[8], oa[8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const float gm = rows ? s_gam[min(i4 + r, T - 1)] : 0.f;
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            ea[2 * r + hf] = make_float4(0.f, 0.f, 0.f, 0.f);
-            oa[2 * r + hf] = make_float4(gm * qs[4 * hf][r], gm * qs[4 * hf + 1][r], gm * qs[4 * hf + 2][r],
-                                         gm * qs[4 * hf + 3][r]);
+    // ---- 5. e = M r and o = exp(G) (Q S0^T) + N r over each root path, one
+    // half of the value rows at a time (r from LDS)
+    for (int hf = 0; hf < 2; ++hf) {
+        if (64 * hf >= dv) break;
+        if (hf == 1) {
+            lds_barrier();  // every wave is done with the first half
+            stage_r(1);
+            lds_barrier();
         }
-    }
+        const int p0 = 64 * hf + 4 * l16;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int i = i4 + r;
-        if (!rows || i >= T) continue;
-        const int base = s_off[i], cnt = s_dep[i] + 1;
-        for (int m0 = 0; m0 < cnt; m0 += 4) {
-            float4 rv[4][2];
+        for (int r = 0; r < 4; ++r) {
+            const int i = i4 + r;
+            if (!rows || i >= T) continue;
+            const float gm = s_gam[i];
+            float4 ea = make_float4(0.f, 0.f, 0.f, 0.f);
+            float4 oa = make_float4(gm * qs[4 * hf][r], gm * qs[4 * hf + 1][r], gm * qs[4 * hf + 2][r],
+                                    gm * qs[4 * hf + 3][r]);
+            const int base = s_off[i], cnt = s_dep[i] + 1;
+            for (int m0 = 0; m0 < cnt; m0 += 4) {
+                float4 rv[4];
+                float mv[4], nv[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int j = s_pair[base + min(m0 + u, cnt - 1)] >> 8;
+                for (int u = 0; u < 4; ++u) {
+                    const int mm = min(m0 + u, cnt - 1);
+                    rv[u] = *(const float4*)&s_r[(s_pair[base + mm] >> 8) * 64 + 4 * l16];
+                    mv[u] = m0 + u < cnt ? s_M[base + mm] : 0.f;
+                    nv[u] = m0 + u < cnt ? s_A[base + mm] : 0.f;
+                }
 #pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const int p0 = 64 * hf + 4 * l16;
-                    rv[u][hf] = make_float4(0.f, 0.f, 0.f, 0.f);
-                    if (p0 < dv) rv[u][hf] = ld4<VEC>(e + (row0 + (size_t)j * H) * dv + p0, dv - p0);
+                for (int u = 0; u < 4; ++u) {
+                    ea.x += mv[u] * rv[u].x;
+                    ea.y += mv[u] * rv[u].y;
+                    ea.z += mv[u] * rv[u].z;
+                    ea.w += mv[u] * rv[u].w;
+                    oa.x += nv[u] * rv[u].x;
+                    oa.y += nv[u] * rv[u].y;
+                    oa.z += nv[u] * rv[u].z;
+                    oa.w += nv[u] * rv[u].w;
                 }
             }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (m0 + u >= cnt) break;
-                const float mv = s_M[base + m0 + u], nv = s_A[base + m0 + u];
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const float4 x = rv[u][hf];
-                    float4& ev = ea[2 * r + hf];
-                    float4& ov = oa[2 * r + hf];
-                    ev.x += mv * x.x;
-                    ev.y += mv * x.y;
-                    ev.z += mv * x.z;
-                    ev.w += mv * x.w;
-                    ov.x += nv * x.x;
-                    ov.y += nv * x.y;
-                    ov.z += nv * x.z;
-                    ov.w += nv * x.w;
-                }
+            if (p0 < dv) {
+                st4io<TIO, VEC>(o + (row0 + (size_t)i * H) * dv + p0, oa, dv - p0);
+                if (e) st4io<float, VEC>(e + (row0 + (size_t)i * H) * dv + p0, ea, dv - p0);
             }
         }
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const int i = i4 + r, p0 = 64 * hf + 4 * l16;
-            if (rows && i < T && p0 < dv) st4io<TIO, VEC>(o + (row0 + (size_t)i * H) * dv + p0, oa[2 * r + hf], dv - p0);
-        }
-    __syncthreads();  // every wave has read r
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const int i = i4 + r, p0 = 64 * hf + 4 * l16;
-            if (rows && i < T && p0 < dv) st4io<float, VEC>(e + (row0 + (size_t)i * H) * dv + p0, ea[2 * r + hf], dv - p0);
-        }
 }
 
 }  // namespace

@@ -219,10 +219,10 @@ def test_gdn_large_trees(bnd, B, T, H, dk, dv, tree, dtype):
         (err_o, err_e, err_S)
 
 
-def test_gdn_large_capacity_invalid_and_null_e(bnd):
+def test_gdn_large_capacity_invalid_and_optional_e(bnd):
     """A tree with more ancestor pairs than the kernel holds (a 200-node
-    chain) gets status 8 and untouched outputs; invalid trees 1/2; the plain
-    kernel needs e (NULL is TSV_E_NULL); a path row longer than 64 is
+    chain) gets status 8 and untouched outputs; invalid trees 1/2; e is
+    optional (NULL gives the same o); a path row longer than 64 is
     TSV_E_UNSUPPORTED for trees past 64 nodes."""
     import ctypes
     import torch
@@ -243,9 +243,11 @@ def test_gdn_large_capacity_invalid_and_null_e(bnd):
     assert not (o[3] == 5.0).any()
     shape = bnd._gdn_shape(dev["k"], dev["v"])
     args = [dev[x] for x in ("q", "k", "v", "g", "beta", "S0", "parent")]
-    rc = bnd.lib.tree_gdn_verify(ctypes.byref(shape), *[bnd._ptr(t) for t in args], bnd._ptr(o), None,
+    o2 = torch.full_like(dev["v"], 5.0)
+    rc = bnd.lib.tree_gdn_verify(ctypes.byref(shape), *[bnd._ptr(t) for t in args], bnd._ptr(o2), None,
                                  None, bnd._stream(None))
-    assert rc == 1
+    torch.cuda.synchronize()
+    assert rc == 0 and torch.equal(o2, o)
     acc = torch.full((4, 65), -1, dtype=torch.int32, device="cuda")
     rc = bnd.lib.tree_gdn_commit(ctypes.byref(shape), bnd._ptr(dev["k"]), bnd._ptr(dev["g"]),
                                  bnd._ptr(o), bnd._ptr(dev["S0"]), bnd._ptr(dev["parent"]), bnd._ptr(acc),
