@@ -17,9 +17,12 @@
 //     to the root) in LDS; a tree with more than kGdnLargePairs
 //     ancestor-or-self pairs is reported with status 8 and left untouched.
 //     S0 is staged in LDS as bf16 high and low parts, in the order the MFMA B
-//     operand reads it (one linear 1 KB read per wave and step).
+//     operand reads it (one linear 1 KB read per wave and step; for bf16
+//     rows once the pair scores are done with the same LDS).
 //  2. pair scores of the wave's nodes from the k and q columns its lanes
-//     hold as MFMA A operands (only the ancestors' k rows are loaded);
+//     hold as MFMA A operands and the same columns of each ancestor's k row
+//     (bf16 rows: from LDS, where every wave puts its nodes' rows, so k is
+//     read from memory once; fp32 rows: from memory);
 //  3. Q S0^T and K S0^T for the wave's 16 nodes on MFMA (three-term bf16
 //     splits, fp32 accumulation; two terms for bf16 inputs, whose low parts
 //     are zero), and r in registers. The column order of the product tiles
@@ -192,7 +195,6 @@ __global__ __launch_bounds__(kGdnLargeNT) void gdn_large_kernel(
     const int32_t* __restrict__ parent, TIO* __restrict__ o, float* __restrict__ e,
     int32_t* __restrict__ tree_status, int T, int H, int dk, int dv) {
     constexpr int NT = kGdnLargeNT, MAXP = kGdnLargePairs;
-    constexpr bool BF = sizeof(TIO) == 2;
     __shared__ int s_par[kMaxNodes];
     __shared__ int s_dep[kMaxNodes];
     __shared__ int s_off[kMaxNodes];
@@ -262,13 +264,19 @@ __global__ __launch_bounds__(kGdnLargeNT) void gdn_large_kernel(
         s_cnt[tid] = 0;
     }
     if (tid == 0) s_maxdep = 0;
+    constexpr bool BF = sizeof(TIO) == 2;
+    // S0 into its planes: now for fp32 rows, after the pair scores for bf16
+    // rows (whose pair scores use the same LDS first)
+    auto stage_s0 = [&]() {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        bf16x8 hi, lo;
-        split_hi_lo(s0v[2 * u], s0v[2 * u + 1], hi, lo);
-        s_S0[tid + NT * u] = hi;
-        s_S0[kS0Ent + tid + NT * u] = lo;
-    }
+        for (int u = 0; u < 2; ++u) {
+            bf16x8 hi, lo;
+            split_hi_lo(s0v[2 * u], s0v[2 * u + 1], hi, lo);
+            s_S0[tid + NT * u] = hi;
+            s_S0[kS0Ent + tid + NT * u] = lo;
+        }
+    };
+    if constexpr (!BF) stage_s0();
     lds_barrier();
 
     // partial log decays along each list, exp(G_i), list starts, M_ii, depth counts
@@ -300,16 +308,34 @@ __global__ __launch_bounds__(kGdnLargeNT) void gdn_large_kernel(
     lds_barrier();
     if (tid < T) s_lvl[atomicAdd(&s_cnt[s_dep[tid]], 1)] = tid;
 
-    // ---- 2. pair scores of the wave's nodes: lane (l16, q4) holds the
-    // product columns of k_i and q_i (i = ia); for each ancestor j it loads
-    // the same columns of k_j, and the four lanes of node i add up
+    // ---- 2. pair scores: lane (l16, q4) dots the columns it holds of k_i and
+    // q_i (i = ia, its A-operand row) with the same columns of each
+    // ancestor's k_j, and the four lanes of node i add up. bf16 rows: every
+    // wave first puts its nodes' k rows into LDS (where the S0 planes go
+    // later: 128 bits a node, 64 KB), so k_j comes from LDS; fp32 rows (twice
+    // the bytes) load k_j from memory.
     f32x4 qs[kLNB];
     float4 rr[8];  // r at the accumulator positions: node i4 + r, value rows 64 hf + 4 l16 .. + 3
+    const int cnt = alive ? s_dep[ia] + 1 : 0, base = alive ? s_off[ia] : 0;
+    uint16_t* const s_k = (uint16_t*)s_S0;  // bf16 rows: [node][128]
+    if constexpr (BF) {
+        if (alive) {
+#pragma unroll
+            for (int ks = 0; ks < kLKS; ++ks) *(uint4*)&s_k[ia * 128 + 32 * ks + 8 * q4] = ka.v[ks];
+        }
+        lds_barrier();
+    }
     if (rows) {
-        const int cnt = alive ? s_dep[ia] + 1 : 0, base = alive ? s_off[ia] : 0;
         for (int m = 0; m < cnt; ++m) {
-            ARow<TIO> kj = ka;
-            if (m > 0) load_a<TIO, VEC>(k + (row0 + (size_t)(s_pair[base + m] >> 8) * H) * dk, true, q4, dk, kj);
+            const int j = s_pair[base + m] >> 8;
+            ARow<TIO> kj;
+            if constexpr (BF) {
+#pragma unroll
+                for (int ks = 0; ks < kLKS; ++ks) kj.v[ks] = *(const uint4*)&s_k[j * 128 + 32 * ks + 8 * q4];
+            } else {
+                kj = ka;
+                if (m > 0) load_a<TIO, VEC>(k + (row0 + (size_t)j * H) * dk, true, q4, dk, kj);
+            }
             float kk = a_dot<TIO>(ka, kj), qk = a_dot<TIO>(qa, kj);
             kk += __shfl_xor(kk, 16, kWave);
             qk += __shfl_xor(qk, 16, kWave);
@@ -321,7 +347,14 @@ __global__ __launch_bounds__(kGdnLargeNT) void gdn_large_kernel(
                 s_W[base + m] = D * qk;
             }
         }
+    }
+    if constexpr (BF) {
+        lds_barrier();  // every k row has been read: the S0 planes go in
+        stage_s0();
+        lds_barrier();
+    }
 
+    if (rows) {
         // ---- 3. Q S0^T (kept), K S0^T, and r = beta (v - exp(G) K S0^T)
         s0_product<TIO>(qa, s_S0, lane, dk, dv, qs);
         f32x4 ks_[kLNB];
