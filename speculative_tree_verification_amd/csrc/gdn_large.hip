@@ -17,12 +17,12 @@
 //     to the root) in LDS; a tree with more than kGdnLargePairs
 //     ancestor-or-self pairs is reported with status 8 and left untouched.
 //     S0 is staged in LDS as bf16 high and low parts, in the order the MFMA B
-//     operand reads it (one linear 1 KB read per wave and step; for bf16
-//     rows once the pair scores are done with the same LDS).
+//     operand reads it (one linear 1 KB read per wave and step), once the
+//     pair scores are done with the same LDS.
 //  2. pair scores of the wave's nodes from the k and q columns its lanes
-//     hold as MFMA A operands and the same columns of each ancestor's k row
-//     (bf16 rows: from LDS, where every wave puts its nodes' rows, so k is
-//     read from memory once; fp32 rows: from memory);
+//     hold as MFMA A operands and the same columns of each ancestor's k row,
+//     from LDS, where every wave puts its nodes' rows (fp32 rows half of the
+//     columns at a time), so k is read from memory once;
 //  3. Q S0^T and K S0^T for the wave's 16 nodes on MFMA (three-term bf16
 //     splits, fp32 accumulation; two terms for bf16 inputs, whose low parts
 //     are zero), and r in registers. The column order of the product tiles
@@ -265,8 +265,7 @@ __global__ __launch_bounds__(kGdnLargeNT) void gdn_large_kernel(
     }
     if (tid == 0) s_maxdep = 0;
     constexpr bool BF = sizeof(TIO) == 2;
-    // S0 into its planes: now for fp32 rows, after the pair scores for bf16
-    // rows (whose pair scores use the same LDS first)
+    // S0 into its planes, after the pair scores (which use the same LDS first)
     auto stage_s0 = [&]() {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -276,7 +275,6 @@ __global__ __launch_bounds__(kGdnLargeNT) void gdn_large_kernel(
             s_S0[kS0Ent + tid + NT * u] = lo;
         }
     };
-    if constexpr (!BF) stage_s0();
     lds_barrier();
 
     // partial log decays along each list, exp(G_i), list starts, M_ii, depth counts
@@ -310,49 +308,84 @@ __global__ __launch_bounds__(kGdnLargeNT) void gdn_large_kernel(
 
     // ---- 2. pair scores: lane (l16, q4) dots the columns it holds of k_i and
     // q_i (i = ia, its A-operand row) with the same columns of each
-    // ancestor's k_j, and the four lanes of node i add up. bf16 rows: every
-    // wave first puts its nodes' k rows into LDS (where the S0 planes go
-    // later: 128 bits a node, 64 KB), so k_j comes from LDS; fp32 rows (twice
-    // the bytes) load k_j from memory.
+    // ancestor's k_j, and the four lanes of node i add up. Every wave first
+    // puts its nodes' k rows into LDS, where the S0 planes go later (256
+    // bytes a node: bf16 rows whole, fp32 rows 64 columns a pass, the first
+    // pass's partial sums parked in W and in M's strict-ancestor entries,
+    // which the solve writes later), so k is read from memory once. A row's
+    // 16-byte chunks are XOR-swizzled with the node index: the 16 lanes that
+    // read the same column of 16 different rows then hit different banks.
     f32x4 qs[kLNB];
     float4 rr[8];  // r at the accumulator positions: node i4 + r, value rows 64 hf + 4 l16 .. + 3
     const int cnt = alive ? s_dep[ia] + 1 : 0, base = alive ? s_off[ia] : 0;
-    uint16_t* const s_k = (uint16_t*)s_S0;  // bf16 rows: [node][128]
-    if constexpr (BF) {
+    constexpr int PASSES = BF ? 1 : 2;
+    constexpr int KSP = kLKS / PASSES;  // contraction steps per pass
+    constexpr int EPC = 16 / sizeof(TIO);  // elements per 16-byte chunk
+    TIO* const s_k = (TIO*)s_S0;           // [node][16 chunks]
+    // element offset of chunk ch of node n's row
+    auto kchunk = [&](int n, int ch) { return (n * 16 + (ch ^ (n & 15))) * EPC; };
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+        if (ps > 0) lds_barrier();  // the first pass's reads are done
         if (alive) {
 #pragma unroll
-            for (int ks = 0; ks < kLKS; ++ks) *(uint4*)&s_k[ia * 128 + 32 * ks + 8 * q4] = ka.v[ks];
+            for (int t = 0; t < KSP; ++t) {
+                const int ks = ps * KSP + t;
+                if constexpr (BF) {
+                    *(uint4*)&s_k[kchunk(ia, 4 * t + q4)] = ka.v[ks];
+                } else {
+                    *(float4*)&s_k[kchunk(ia, 8 * t + 2 * q4)] = ka.v[2 * ks];
+                    *(float4*)&s_k[kchunk(ia, 8 * t + 2 * q4 + 1)] = ka.v[2 * ks + 1];
+                }
+            }
         }
         lds_barrier();
-    }
-    if (rows) {
-        for (int m = 0; m < cnt; ++m) {
-            const int j = s_pair[base + m] >> 8;
-            ARow<TIO> kj;
-            if constexpr (BF) {
+        if (rows) {
+            for (int m = 0; m < cnt; ++m) {
+                const int j = s_pair[base + m] >> 8;
+                float kk = 0.f, qk = 0.f;
 #pragma unroll
-                for (int ks = 0; ks < kLKS; ++ks) kj.v[ks] = *(const uint4*)&s_k[j * 128 + 32 * ks + 8 * q4];
-            } else {
-                kj = ka;
-                if (m > 0) load_a<TIO, VEC>(k + (row0 + (size_t)j * H) * dk, true, q4, dk, kj);
-            }
-            float kk = a_dot<TIO>(ka, kj), qk = a_dot<TIO>(qa, kj);
-            kk += __shfl_xor(kk, 16, kWave);
-            qk += __shfl_xor(qk, 16, kWave);
-            kk += __shfl_xor(kk, 32, kWave);
-            qk += __shfl_xor(qk, 32, kWave);
-            if (q4 == 0) {
-                const float D = __expf(s_A[base + m]);
-                s_A[base + m] = m > 0 ? s_bt[ia] * D * kk : 0.f;
-                s_W[base + m] = D * qk;
+                for (int t = 0; t < KSP; ++t) {
+                    const int ks = ps * KSP + t;
+                    if constexpr (BF) {
+                        const uint4 kj = *(const uint4*)&s_k[kchunk(j, 4 * t + q4)];
+                        kk = dot8_bf16(ka.v[ks], kj, kk);
+                        qk = dot8_bf16(qa.v[ks], kj, qk);
+                    } else {
+                        const float4 k0 = *(const float4*)&s_k[kchunk(j, 8 * t + 2 * q4)];
+                        const float4 k1 = *(const float4*)&s_k[kchunk(j, 8 * t + 2 * q4 + 1)];
+                        const float4 a0 = ka.v[2 * ks], a1 = ka.v[2 * ks + 1];
+                        const float4 q0 = qa.v[2 * ks], q1 = qa.v[2 * ks + 1];
+                        kk += (a0.x * k0.x + a0.y * k0.y) + (a0.z * k0.z + a0.w * k0.w) +
+                              ((a1.x * k1.x + a1.y * k1.y) + (a1.z * k1.z + a1.w * k1.w));
+                        qk += (q0.x * k0.x + q0.y * k0.y) + (q0.z * k0.z + q0.w * k0.w) +
+                              ((q1.x * k1.x + q1.y * k1.y) + (q1.z * k1.z + q1.w * k1.w));
+                    }
+                }
+                kk += __shfl_xor(kk, 16, kWave);
+                qk += __shfl_xor(qk, 16, kWave);
+                kk += __shfl_xor(kk, 32, kWave);
+                qk += __shfl_xor(qk, 32, kWave);
+                if (q4 == 0) {
+                    if (ps + 1 < PASSES) {
+                        if (m > 0) s_M[base + m] = kk;
+                        s_W[base + m] = qk;
+                    } else {
+                        if (ps > 0) {
+                            kk += m > 0 ? s_M[base + m] : 0.f;
+                            qk += s_W[base + m];
+                        }
+                        const float D = __expf(s_A[base + m]);
+                        s_A[base + m] = m > 0 ? s_bt[ia] * D * kk : 0.f;
+                        s_W[base + m] = D * qk;
+                    }
+                }
             }
         }
     }
-    if constexpr (BF) {
-        lds_barrier();  // every k row has been read: the S0 planes go in
-        stage_s0();
-        lds_barrier();
-    }
+    lds_barrier();  // every k row has been read: the S0 planes go in
+    stage_s0();
+    lds_barrier();
 
     if (rows) {
         // ---- 3. Q S0^T (kept), K S0^T, and r = beta (v - exp(G) K S0^T)
