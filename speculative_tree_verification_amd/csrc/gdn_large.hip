@@ -105,28 +105,33 @@ struct ARow<uint16_t> {
     uint4 v[kLKS];
 };
 
+// With VEC (rows of a multiple of four elements) the loads are unconditional,
+// from columns clamped into the row, and the values past dk or past the tree
+// are zeroed afterwards: the compiler can then count how many of them are
+// still in flight at a wait (branches around loads make it wait for all).
 template <typename TIO, bool VEC>
 __device__ __forceinline__ void load_a(const TIO* __restrict__ row, bool live, int q4, int dk, ARow<TIO>& a) {
 #pragma unroll
     for (int ks = 0; ks < kLKS; ++ks) {
         const int c = 32 * ks + 8 * q4;
+        const bool in0 = live && c < dk, in1 = live && c + 4 < dk;
         if constexpr (sizeof(TIO) == 4) {
-            a.v[2 * ks] = a.v[2 * ks + 1] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (live && c < dk) a.v[2 * ks] = ld4<VEC>(row + c, dk - c);
-            if (live && c + 4 < dk) a.v[2 * ks + 1] = ld4<VEC>(row + c + 4, dk - c - 4);
+            if (VEC) {
+                const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+                const float4 x0 = ld4<true>(row + min(c, dk - 4), 4), x1 = ld4<true>(row + min(c + 4, dk - 4), 4);
+                a.v[2 * ks] = in0 ? x0 : z;
+                a.v[2 * ks + 1] = in1 ? x1 : z;
+            } else {
+                a.v[2 * ks] = a.v[2 * ks + 1] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (in0) a.v[2 * ks] = ld4<false>(row + c, dk - c);
+                if (in1) a.v[2 * ks + 1] = ld4<false>(row + c + 4, dk - c - 4);
+            }
         } else {
             a.v[ks] = make_uint4(0u, 0u, 0u, 0u);
             if (VEC) {
-                if (live && c < dk) {
-                    const uint2 x = gload((const uint2*)(row + c));
-                    a.v[ks].x = x.x;
-                    a.v[ks].y = x.y;
-                }
-                if (live && c + 4 < dk) {
-                    const uint2 x = gload((const uint2*)(row + c + 4));
-                    a.v[ks].z = x.x;
-                    a.v[ks].w = x.y;
-                }
+                const uint2 x0 = gload((const uint2*)(row + min(c, dk - 4)));
+                const uint2 x1 = gload((const uint2*)(row + min(c + 4, dk - 4)));
+                a.v[ks] = make_uint4(in0 ? x0.x : 0u, in0 ? x0.y : 0u, in1 ? x1.x : 0u, in1 ? x1.y : 0u);
             } else {
                 uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -226,19 +231,30 @@ __global__ __launch_bounds__(kGdnLargeNT) void gdn_large_kernel(
 
     // ---- 1. loads, tree
     const int par_i = load_parent(parent + (size_t)b * T, T);
-    float gi = 0.f, bi = 0.f;
-    if (tid < T) {
-        gi = g[row0 + (size_t)tid * H];
-        bi = beta[row0 + (size_t)tid * H];
-    }
+    const float gi = g[row0 + (size_t)min(tid, T - 1) * H];
+    const float bi = beta[row0 + (size_t)min(tid, T - 1) * H];
+    // S0 and the wave's k and q rows leave with the parents. The loads are
+    // unconditional, from clamped addresses where the shapes allow, so that
+    // the tree check waits for the parents only (branches around loads make
+    // the compiler wait for all of them); the parents still come back behind
+    // much of every work-group's burst. Issuing the burst after the check
+    // instead moved the same wait into the pair lists (a wave stalls on
+    // issuing loads whose queue is full): no faster.
     float4 s0v[4];  // B-operand entries tid and tid + NT: S0[vrow(nb, l16')][32 ks + 8 q4' .. + 7]
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int x = tid + NT * u, ln = x & (kWave - 1), ks = (x / kWave) % kLKS, nb = x / (kWave * kLKS);
         const int p = vrow(nb, ln & 15), c = 32 * ks + 8 * (ln >> 4);
-        s0v[2 * u] = s0v[2 * u + 1] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (p < dv && c < dk) s0v[2 * u] = ld4<VEC>(S0h + (size_t)p * dk + c, dk - c);
-        if (p < dv && c + 4 < dk) s0v[2 * u + 1] = ld4<VEC>(S0h + (size_t)p * dk + c + 4, dk - c - 4);
+        const bool in0 = p < dv && c < dk, in1 = p < dv && c + 4 < dk;
+        if (VEC) {  // zeroed past the matrix when staged
+            const float* src = S0h + (size_t)min(p, dv - 1) * dk;
+            s0v[2 * u] = ld4<true>(src + min(c, dk - 4), 4);
+            s0v[2 * u + 1] = ld4<true>(src + min(c + 4, dk - 4), 4);
+        } else {
+            s0v[2 * u] = s0v[2 * u + 1] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (in0) s0v[2 * u] = ld4<false>(S0h + (size_t)p * dk + c, dk - c);
+            if (in1) s0v[2 * u + 1] = ld4<false>(S0h + (size_t)p * dk + c + 4, dk - c - 4);
+        }
     }
     const int ia = 16 * w + l16;  // A-operand row of this lane
     const bool alive = rows && ia < T;
@@ -265,16 +281,6 @@ __global__ __launch_bounds__(kGdnLargeNT) void gdn_large_kernel(
     }
     if (tid == 0) s_maxdep = 0;
     constexpr bool BF = sizeof(TIO) == 2;
-    // S0 into its planes, after the pair scores (which use the same LDS first)
-    auto stage_s0 = [&]() {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            bf16x8 hi, lo;
-            split_hi_lo(s0v[2 * u], s0v[2 * u + 1], hi, lo);
-            s_S0[tid + NT * u] = hi;
-            s_S0[kS0Ent + tid + NT * u] = lo;
-        }
-    };
     lds_barrier();
 
     // partial log decays along each list, exp(G_i), list starts, M_ii, depth counts
@@ -384,7 +390,20 @@ __global__ __launch_bounds__(kGdnLargeNT) void gdn_large_kernel(
         }
     }
     lds_barrier();  // every k row has been read: the S0 planes go in
-    stage_s0();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        if (VEC) {
+            const int x = tid + NT * u, ln = x & (kWave - 1), ks = (x / kWave) % kLKS, nb = x / (kWave * kLKS);
+            const int p = vrow(nb, ln & 15), c = 32 * ks + 8 * (ln >> 4);
+            const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (!(p < dv && c < dk)) s0v[2 * u] = z;
+            if (!(p < dv && c + 4 < dk)) s0v[2 * u + 1] = z;
+        }
+        bf16x8 hi, lo;
+        split_hi_lo(s0v[2 * u], s0v[2 * u + 1], hi, lo);
+        s_S0[tid + NT * u] = hi;
+        s_S0[kS0Ent + tid + NT * u] = lo;
+    }
     lds_barrier();
 
     if (rows) {
