@@ -28,9 +28,10 @@
 //     are zero), and r in registers. The column order of the product tiles
 //     gives each lane four consecutive value rows twice, so v, r, e and o
 //     move as 16-byte vectors;
-//  4. M by substitution one depth level at a time, one pair entry per thread:
-//        M_ij = -A_ij - sum_{x strictly between j and i} A_ix M_xj;
-//     then N_ij = sum_{x from i down to j} W_ix M_xj, all entries at once;
+//  4. M row by row, one thread a row, from M (I + A) = I:
+//        M_ij = -sum_{x from i down to j, x != j} M_ix A_xj   (M_ii = 1),
+//     each entry from the row's entries before it (no barrier per depth
+//     level); then N_ij = sum_{x from i down to j} W_ix M_xj, all at once;
 //  5. e_i = sum_j M_ij r_j and o_i = exp(G_i) (S0 q_i) + sum_j N_ij r_j over the
 //     root path of i, one half of the value rows at a time: that half of r
 //     (64 floats per node, 64 KB) sits in LDS where the S0 planes were, so r
@@ -213,10 +214,6 @@ __global__ __launch_bounds__(kGdnLargeNT) void gdn_large_kernel(
     __shared__ float s_gv[kMaxNodes];  // g of each node
     __shared__ float s_bt[kMaxNodes];  // beta of each node
     __shared__ float s_gam[kMaxNodes]; // exp(G_i)
-    __shared__ int s_lvl[kMaxNodes];   // nodes ordered by depth
-    __shared__ int s_lvs[kMaxNodes + 1];
-    __shared__ int s_cnt[kMaxNodes];
-    __shared__ int s_maxdep;
     __shared__ bf16x8 s_S0[2 * kS0Ent];  // S0 high parts, then low parts, in B-operand order
 
     const int b = blockIdx.x / H;
@@ -277,13 +274,11 @@ __global__ __launch_bounds__(kGdnLargeNT) void gdn_large_kernel(
     if (tid < T) {
         s_gv[tid] = gi;
         s_bt[tid] = bi;
-        s_cnt[tid] = 0;
     }
-    if (tid == 0) s_maxdep = 0;
     constexpr bool BF = sizeof(TIO) == 2;
     lds_barrier();
 
-    // partial log decays along each list, exp(G_i), list starts, M_ii, depth counts
+    // partial log decays along each list, exp(G_i), list starts, M_ii
     if (tid < T) {
         const int base = s_off[tid], cnt = s_dep[tid] + 1;
         float part = 0.f;
@@ -295,22 +290,8 @@ __global__ __launch_bounds__(kGdnLargeNT) void gdn_large_kernel(
         }
         s_M[base] = 1.f;
         s_gam[tid] = __expf(part);
-        atomicAdd(&s_cnt[cnt - 1], 1);
-        atomicMax(&s_maxdep, cnt - 1);
     }
     lds_barrier();
-    const int maxdep = s_maxdep;
-    if (tid == 0) {
-        int run = 0;
-        for (int d = 0; d <= maxdep; ++d) {
-            s_lvs[d] = run;
-            run += s_cnt[d];
-            s_cnt[d] = s_lvs[d];  // next free slot of level d
-        }
-        s_lvs[maxdep + 1] = run;
-    }
-    lds_barrier();
-    if (tid < T) s_lvl[atomicAdd(&s_cnt[s_dep[tid]], 1)] = tid;
 
     // ---- 2. pair scores: lane (l16, q4) dots the columns it holds of k_i and
     // q_i (i = ia, its A-operand row) with the same columns of each
@@ -445,29 +426,31 @@ __global__ __launch_bounds__(kGdnLargeNT) void gdn_large_kernel(
     };
     stage_r(0);
 
-    // ---- 4. M, one depth level at a time: entry (i, m) for the ancestor m steps up
-    for (int d = 1; d <= maxdep; ++d) {
-        const int lo = s_lvs[d], entries = (s_lvs[d + 1] - lo) * d;
-        for (int x = tid; x < entries; x += NT) {
-            const int ni = x / d, m = 1 + x - ni * d;
-            const int base = s_off[s_lvl[lo + ni]];
-            float acc = -s_A[base + m];
-            for (int m0 = 1; m0 < m; m0 += 4) {
-                float a[4], mv[4];
+    // ---- 4. M = (I + A)^{-1} row by row, from M (I + A) = I: entry m of node
+    // i's list (its ancestor m steps up) follows from the entries before it in
+    // the same row, M_{i,m} = -sum_{m' < m} M_{i,m'} A_{x(m'), m - m'}, with
+    // x(m') the ancestor m' steps up and M_{i,0} = 1. One thread a row and no
+    // barrier between depth levels.
+    if (tid < T) {
+        const int base = s_off[tid], cnt = s_dep[tid] + 1;
+        for (int m = 1; m < cnt; ++m) {
+            float acc = 0.f;
+            for (int m0 = 0; m0 < m; m0 += 4) {
+                float mv[4], av[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const int mm = min(m0 + u, m - 1);  // x = the ancestor mm steps up
-                    a[u] = s_A[base + mm];
-                    mv[u] = s_M[s_aof[base + mm] + m - mm];
+                    const int mm = min(m0 + u, m - 1);
+                    mv[u] = s_M[base + mm];
+                    av[u] = s_A[s_aof[base + mm] + m - mm];
                 }
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    if (m0 + u < m) acc -= a[u] * mv[u];
+                    if (m0 + u < m) acc -= mv[u] * av[u];
             }
             s_M[base + m] = acc;
         }
-        lds_barrier();
     }
+    lds_barrier();
     // N = W M over every pair (A is no longer needed)
     for (int x = tid; x < total; x += NT) {
         const int base = s_off[s_pair[x] & 255], m = x - base;
