@@ -25,17 +25,17 @@
 //     registers (the B operand of its products), k and q for LDS (split into
 //     bf16 high and low parts), v in the layout of the product accumulators.
 //     Meanwhile the tree wave (one lane per node) checks the tree and finds by
-//     pointer jumping each node's ancestor set (a 64-bit mask) and G_i, lists
-//     the nodes by depth and each node's strict ancestors by depth.
+//     pointer jumping each node's ancestor set (a 64-bit mask) and G_i, and
+//     lists each node's strict ancestors by depth.
 //  2. Row waves: K S0^T and Q S0^T (nodes x its value rows) on MFMA with
 //     three-term bf16 splits (hi*hi + hi*lo + lo*hi, fp32 accumulation), then the
 //     right-hand sides r_i = beta_i (v_i - exp(G_i) S0 k_i) in registers.
 //     Tree wave, at the same time: the pair scores K K^T and Q K^T on the
 //     lower-triangle 16x16 tiles (same splits), A_ij = beta_i D_ij (k_i . k_j) on
 //     strict ancestors, W_ij = D_ij (q_i . k_j) on the path (D_ij = exp(G_i - G_j)),
-//     and M = (I + A)^{-1} by substitution one depth level at a time, one
-//     (node, ancestor) entry per lane: M is ancestor-masked like A, and it is
-//     shared by every value row.
+//     and M = (I + A)^{-1} row by row from M (I + A) = I, one lane a row, each
+//     entry from the row's entries nearer to its node (no sync per depth
+//     level): M is ancestor-masked like A, and it is shared by every value row.
 //  3. Row waves: e = M r and o = exp(G) * (Q S0^T) + W e on fp32 MFMA; the
 //     accumulators of r and e are laid out as the B operand of the next product,
 //     so they never leave registers.
@@ -116,9 +116,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(
     __shared__ float s_gam[NN];  // exp(G_i)
     __shared__ float s_beta[NN];
     __shared__ int s_dep[NN];
-    __shared__ int s_lvl[NN];      // nodes by depth
-    __shared__ int s_lvs[NN + 1];  // start of each depth in s_lvl
-    __shared__ int s_info[2];      // tree status, maximum depth
+    __shared__ int s_info[1];      // tree status
     uint16_t* const s_kh = s_stage;
     uint16_t* const s_kl = s_kh + NN * RS;
     uint16_t* const s_qh = s_kl + NN * RS;
@@ -200,17 +198,6 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(
             int maxdep = dep;
 #pragma unroll
             for (int off = 32; off > 0; off >>= 1) maxdep = max(maxdep, __shfl_xor(maxdep, off, kWave));
-            int start = 0;
-            for (int d = 0; d <= maxdep; ++d) {
-                const unsigned long long bm = __ballot(dep == d);
-                if (dep == d) s_lvl[start + __popcll(bm & ((1ull << lane) - 1))] = lane;
-                if (lane == 0) s_lvs[d] = start;
-                start += __popcll(bm);
-            }
-            if (lane == 0) {
-                s_lvs[maxdep + 1] = start;
-                s_info[1] = maxdep;
-            }
             // the strict ancestors of each node by depth: climb one step a round
             const int up = live && lane > 0 ? par : 0;
             int cur = lane;
@@ -316,33 +303,30 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(
 #pragma unroll
     for (int ti = 0; ti < NN / 16; ++ti) R4[ti] = Q4[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (tree_wave) {
-        // ---- 3b. M, by the tree wave while the row waves form their products
-        // (I + A) M = I: for c a strict ancestor of i at depth m,
-        // M_ic = -A_ic - sum over the path nodes x strictly between c and i of A_ix M_xc
-        const int maxdep = s_info[1];
-        for (int d = 1; d <= maxdep; ++d) {
-            const int lo = s_lvs[d], entries = (s_lvs[d + 1] - lo) * d;
-            for (int L = lane; L < entries; L += kWave) {
-                const int ni = L / d, m = L - ni * d;
-                const int i = s_lvl[lo + ni];
-                const uint8_t* an = s_anc + i * NN;
-                const float* ac = s_A + i * NN;
-                const int c = an[m];
-                float acc = -ac[m];
-                for (int t0 = m + 1; t0 < d; t0 += 4) {
-                    float a[4], x[4];
+        // ---- 3b. M, by the tree wave while the row waves form their products.
+        // M (I + A) = I row by row: lane i takes row i, from its parent's depth
+        // up to the root; for c the strict ancestor of i at depth t,
+        //   M_ic = -A_ic - sum over the path nodes x strictly between c and i of M_ix A_xc,
+        // each entry from the row's entries nearer to i (no sync per depth level)
+        if (lane < T) {
+            const int i = lane, d = s_dep[i];
+            const uint8_t* an = s_anc + i * NN;
+            const float* ai = s_A + i * NN;
+            for (int t = d - 1; t >= 0; --t) {
+                float acc = -ai[t];
+                for (int s0 = t + 1; s0 < d; s0 += 4) {
+                    float mv[4], av[4];
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
-                        const int t = min(t0 + u, d - 1);
-                        a[u] = ac[t];
-                        x[u] = s_M[an[t] * CS + c];
+                        const int x = an[min(s0 + u, d - 1)];
+                        mv[u] = s_M[i * CS + x];
+                        av[u] = s_A[x * NN + t];
                     }
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) acc = t0 + u < d ? acc - a[u] * x[u] : acc;
+                    for (int u = 0; u < 4; ++u) acc = s0 + u < d ? acc - mv[u] * av[u] : acc;
                 }
-                s_M[i * CS + c] = acc;
+                s_M[i * CS + an[t]] = acc;
             }
-            wave_sync();
         }
     } else if (wave_rows) {
         // ---- 3a. products (three-term bf16 splits, fp32 accumulation)
