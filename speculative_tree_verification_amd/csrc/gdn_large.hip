@@ -25,7 +25,7 @@
 //     columns at a time), so k is read from memory once;
 //  3. Q S0^T and K S0^T for the wave's 16 nodes on MFMA (three-term bf16
 //     splits, fp32 accumulation; two terms for bf16 inputs, whose low parts
-//     are zero), and r in registers. The column order of the product tiles
+//     are zero; bf16 v already on its way), and r in registers. The column order of the product tiles
 //     gives each lane four consecutive value rows twice, so v, r, e and o
 //     move as 16-byte vectors;
 //  4. M row by row, one thread a row, from M (I + A) = I:
@@ -370,6 +370,31 @@ __global__ __launch_bounds__(kGdnLargeNT) void gdn_large_kernel(
             }
         }
     }
+    // v at the accumulator positions (node i4 + r, value rows 64 hf + 4 l16 .. + 3;
+    // VEC: unconditional, from clamped addresses, zeroed past the matrix).
+    // bf16 rows (whole 8-byte vectors) leave now, to arrive while S0 is
+    // staged and the products run; fp32 rows only after the products (holding
+    // them through the products would spill)
+    auto load_v = [&]() {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int i = i4 + r, p0 = 64 * hf + 4 * l16;
+                if (VEC) {
+                    const float4 x = ld4io<TIO, true>(v + (row0 + (size_t)min(i, T - 1) * H) * dv + min(p0, dv - 4), 4);
+                    rr[2 * r + hf] = i < T && p0 < dv ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+                } else {
+                    rr[2 * r + hf] = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (i < T && p0 < dv) rr[2 * r + hf] = ld4io<TIO, false>(v + (row0 + (size_t)i * H) * dv + p0, dv - p0);
+                }
+            }
+    };
+    constexpr bool EARLY_V = BF && VEC;
+    if constexpr (EARLY_V) {
+        if (rows) load_v();
+        __builtin_amdgcn_sched_barrier(0);
+    }
     lds_barrier();  // every k row has been read: the S0 planes go in
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -392,15 +417,10 @@ __global__ __launch_bounds__(kGdnLargeNT) void gdn_large_kernel(
         s0_product<TIO>(qa, s_S0, lane, dk, dv, qs);
         f32x4 ks_[kLNB];
         s0_product<TIO>(ka, s_S0, lane, dk, dv, ks_);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const int i = i4 + r, p0 = 64 * hf + 4 * l16;
-                rr[2 * r + hf] = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (i < T && p0 < dv) rr[2 * r + hf] = ld4io<TIO, VEC>(v + (row0 + (size_t)i * H) * dv + p0, dv - p0);
-            }
+        if constexpr (!EARLY_V) {
+            __builtin_amdgcn_sched_barrier(0);
+            load_v();
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = min(i4 + r, T - 1);
