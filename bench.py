@@ -69,6 +69,16 @@ def parse():
 # ---------------------------------------------------------------------------
 # algorithmic bytes per launch (what the method must move; no per-node state)
 # ---------------------------------------------------------------------------
+def step_hbm(v, c, ms_per_step):
+    """The whole layer's algorithmic HBM rate: the bytes of every verify and
+    commit launch of one step over the step time (verify and commit run back
+    to back, launch gaps included)."""
+    nbytes = v["algorithmic_bytes"] * v["launches_per_step"] + c["algorithmic_bytes"] * c["launches_per_step"]
+    gbs = nbytes / (ms_per_step * 1e-3) / 1e9
+    return {"algorithmic_bytes": nbytes, "achieved": round(gbs, 1), "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "timing": "step time: every verify and commit launch back to back"}
+
+
 def verify_bytes(B, T, H, P, N, G, io):
     return (io * (2 * B * T * H * P + B * T * H + 2 * B * T * G * N) + 4 * B * H * P * N
             + 8 * H + 4 * B * T)
@@ -742,9 +752,11 @@ def run_workload(torch, bnd, W, cid, steps, warmup, hpb, keep_host, reps=50):
     t["accept"] = accept_timing(torch, bnd, W, wl, steps)
     t["accept_stochastic"] = accept_stochastic_timing(torch, bnd, W, wl, reps)
     nodes_s = wl.nodes_per_step / (t["ms_per_step"] * 1e-3)
+    sh = step_hbm(v, c, t["ms_per_step"])
     log(f"[bench] workload {cid}: {t['ms_per_step']:.4f} ms/step, {nodes_s:.4g} nodes/s; "
         f"verify {t['verify_us']:.2f} us ({v['achieved']:.0f} GB/s), "
-        f"commit {t['commit_us']:.2f} us ({c['achieved']:.0f} GB/s); host {t['host_ms']:.3f} ms/step")
+        f"commit {t['commit_us']:.2f} us ({c['achieved']:.0f} GB/s); whole step {sh['achieved']:.0f} GB/s "
+        f"({sh['frac']:.1%}); host {t['host_ms']:.3f} ms/step")
     return wl, t, v, c, nodes_s
 
 
@@ -804,6 +816,7 @@ def main():
                             + (f" ({layers} layers)" if layers > 1 else "")),
                    "rotating_sets": wl.n_sets},
         "roofline": roofline,
+        "step_hbm": step_hbm(v, c, t["ms_per_step"]),
         "step_stats_ms": {k: (round(vv, 5) if isinstance(vv, float) else vv)
                           for k, vv in t["step_stats"].items()},
         "kernels": {"verify": v, "commit": c},
@@ -823,6 +836,7 @@ def main():
                                             0, keep_host=False, reps=args.reps)
         secondary.append({"workload": wl2.cfg.name, "nodes_per_s": round(ns2, 1),
                           "ms_per_step": round(t2["ms_per_step"], 5),
+                          "step_hbm": step_hbm(v2, c2, t2["ms_per_step"]),
                           "verify": v2, "commit": c2, "accept": t2["accept"],
                           "accept_stochastic": t2["accept_stochastic"]})
         del wl2
