@@ -219,6 +219,56 @@ def test_gdn_large_trees(bnd, B, T, H, dk, dv, tree, dtype):
         (err_o, err_e, err_S)
 
 
+def _random_case(seed):
+    """A seeded shape across both kernels: T in 1..256, dk and dv in 1..128
+    (sizes that are not multiples of 4 included), fp32 or bf16 rows, random
+    recursive, geometric, star or chain trees."""
+    rng = np.random.default_rng([4242, seed])
+    T = int(rng.choice([int(rng.integers(1, 65)), int(rng.integers(65, 257))]))
+    tree = str(rng.choice(["recursive", "geometric", "star"] + (["chain"] if T <= 90 else [])))
+    dk, dv = (int(rng.choice([int(rng.integers(1, 129)), 128, 64])) for _ in range(2))
+    dtype = W.BF16 if rng.random() < 0.4 else W.F32
+    return dict(B=int(rng.integers(1, 3)), T=T, H=int(rng.integers(1, 4)), dk=dk, dv=dv, tree=tree,
+                dtype=dtype)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_gdn_random_shapes(bnd, seed):
+    """Seeded random shapes through both kernels: o, e and the committed state
+    against the unrolled recurrence (o of bf16 rows at the fp32 bar plus one
+    bf16 rounding), status bits against the oracle's."""
+    import torch
+    c = _random_case(seed)
+    B, T, H, dk, dv, tree, dtype = (c[k] for k in ("B", "T", "H", "dk", "dv", "tree", "dtype"))
+    d = W.make_gdn(5000 + seed, batch=B, n_nodes=T, n_heads=H, dk=dk, dv=dv, tree=tree,
+                   max_depth=T if tree == "chain" else 8, max_path_len=min(T, 9), dtype=dtype)
+    say(f"[gdn random {seed}] B={B} T={T} H={H} dk={dk} dv={dv} {tree} {dtype}")
+    dev = _dev_io(d)
+    st = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    o, e = bnd.gdn_verify(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], dev["S0"], dev["parent"],
+                          tree_status=st)
+    S = dev["S0"].clone()
+    st2 = torch.full_like(st, -7)
+    bnd.gdn_commit(dev["k"], dev["g"], e, S, dev["parent"], dev["accepted"], dev["accepted_len"],
+                   tree_status=st2)
+    torch.cuda.synchronize()
+    x = {k: (W.to_f64(v, W.BF16) if v.dtype == np.uint16 else
+             (v.astype(np.float64) if v.dtype == np.float32 else v)) for k, v in d.items()}
+    ref, rst = O.verify_unrolled(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], x["parent"])
+    _, eref = O.verify_wy(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], x["parent"])
+    Sref, cst = O.commit_unrolled(x["k"], x["v"], x["g"], x["beta"], x["S0"], x["parent"],
+                                  x["accepted"], x["accepted_len"])
+    assert st.cpu().tolist() == rst.tolist() == [0] * B and st2.cpu().tolist() == cst.tolist()
+    on, en, Sn = (t.float().cpu().double().numpy() for t in (o, e, S))
+    err = lambda a, r, sl: np.max(np.abs(a[sl] - r[sl])) / max(np.max(np.abs(r[sl])), 1e-30)
+    err_o = max(err(on, ref, (b, slice(None), h)) for b in range(B) for h in range(H))
+    err_e = max(err(en, eref, (b, slice(None), h)) for b in range(B) for h in range(H))
+    err_S = max(err(Sn, Sref, (b, h)) for b in range(B) for h in range(H))
+    say(f"    o err {err_o:.2e}  e err {err_e:.2e}  S' err {err_S:.2e}")
+    assert err_o <= (2.0 ** -8 + TOL if dtype == W.BF16 else TOL) and err_e <= TOL and err_S <= TOL, \
+        (c, err_o, err_e, err_S)
+
+
 def test_gdn_large_capacity_invalid_and_optional_e(bnd):
     """A tree with more ancestor pairs than the kernel holds (a 200-node
     chain) gets status 8 and untouched outputs; invalid trees 1/2; e is
