@@ -227,7 +227,7 @@ tsv_status tree_gdn_verify(const tsv_shape* s, const void* q, const void* k, con
  * k (in_dtype), g, parent as for tree_gdn_verify; e (fp32) from it; accepted, accepted_len,
  * max_path_len and tree_status (bits 1|2|4) as for tree_ssd_commit. len == 0
  * leaves S0 unchanged; invalid items leave it untouched. Past 64 nodes,
- * max_path_len must be at most 64 (TSV_E_UNSUPPORTED otherwise): the path's
+ * max_path_len must be at most 128 (TSV_E_UNSUPPORTED otherwise): the path's
  * rows are staged whole in LDS.
  */
 tsv_status tree_gdn_commit(const tsv_shape* s, const void* k, const float* g, const float* e,

@@ -165,7 +165,7 @@ tsv_status tree_gdn_commit(const tsv_shape* s, const void* k, const float* g, co
     tsv_status st = check_gdn_shape(s);
     if (st != TSV_OK) return st;
     if (max_path_len < 0 || max_path_len > kMaxNodes) return TSV_E_SHAPE;
-    if (s->n_nodes > 64 && max_path_len > 64) return TSV_E_UNSUPPORTED;  // paths staged whole in LDS
+    if (s->n_nodes > 64 && max_path_len > tsv::kGdnMaxPath) return TSV_E_UNSUPPORTED;  // paths staged whole in LDS
     if (s->batch == 0 || s->n_nodes == 0) return TSV_OK;
     if (!k || !g || !e || !S0_inout || !parent || !accepted_len) return TSV_E_NULL;
     if (max_path_len > 0 && !accepted) return TSV_E_NULL;

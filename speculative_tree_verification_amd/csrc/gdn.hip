@@ -427,10 +427,11 @@ __global__ __launch_bounds__(kBlock) void gdn_commit_kernel(
     float* __restrict__ S, const int32_t* __restrict__ parent, const int32_t* __restrict__ accepted,
     const int32_t* __restrict__ accepted_len, int32_t* __restrict__ tree_status, int T, int H,
     int dk, int dv, int Lmax, int EW, int KW, int groups) {
-    __shared__ int s_par[kMaxNodes];   // trees of up to 256 nodes
-    __shared__ int s_path[kGdnNodes];  // paths of up to 64 nodes
+    __shared__ int s_par[kMaxNodes];     // trees of up to 256 nodes
+    __shared__ int s_path[kGdnMaxPath];  // paths of up to 128 nodes
     __shared__ int s_bad[kBlock / kWave];
-    __shared__ float s_w[kGdnNodes];
+    __shared__ float s_w[kGdnMaxPath];
+    __shared__ float s_g[kGdnMaxPath];   // g of the path (paths past 64 nodes)
     __shared__ float s_w0;
     // [min(Lmax, T)][EW] e rows of the path, then [min(Lmax, T)][KW] k rows
     extern __shared__ __attribute__((aligned(16))) float s_dyn[];
@@ -535,18 +536,30 @@ __global__ __launch_bounds__(kBlock) void gdn_commit_kernel(
             }
         }
     }
-    if (tid < kWave) {
-        // w_t = exp(sum of g over entries after t): inclusive suffix scan of the
-        // sequence shifted by one entry (len <= T <= 64 lanes)
-        float x = __shfl_down(gt, 1, kWave);
-        if (tid == kWave - 1) x = 0.f;
+    if (len <= kWave) {
+        if (tid < kWave) {
+            // w_t = exp(sum of g over entries after t): inclusive suffix scan of
+            // the sequence shifted by one entry (len <= 64 lanes)
+            float x = __shfl_down(gt, 1, kWave);
+            if (tid == kWave - 1) x = 0.f;
 #pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const float y = __shfl_down(x, off, kWave);
-            if (tid + off < kWave) x += y;
+            for (int off = 1; off < kWave; off <<= 1) {
+                const float y = __shfl_down(x, off, kWave);
+                if (tid + off < kWave) x += y;
+            }
+            if (tid < len) s_w[tid] = __expf(x);
+            if (tid == 0) s_w0 = __expf(x + gt);
         }
-        if (tid < len) s_w[tid] = __expf(x);
-        if (tid == 0) s_w0 = __expf(x + gt);
+    } else {
+        // longer paths: each entry adds up the g after it
+        if (tid < len) s_g[tid] = gt;
+        lds_barrier();
+        if (tid < len) {
+            float x = 0.f;
+            for (int t = tid + 1; t < len; ++t) x += s_g[t];
+            s_w[tid] = __expf(x);
+            if (tid == 0) s_w0 = __expf(x + gt);
+        }
     }
     lds_barrier();
     const float w0 = s_w0;
@@ -651,7 +664,7 @@ hipError_t launch_gdn_commit(int batch, int T, int H, int dk, int dv, bool bf16,
                             : (vec ? (const void*)gdn_commit_kernel<float, true, CPW>
                                    : (const void*)gdn_commit_kernel<float, false, CPW>);
     if (shmem > 48 * 1024) {
-        // paths of up to 64 entries with 128-wide rows take up to 64 KiB
+        // paths of up to 128 entries with 128-wide rows take up to 128 KiB
         const hipError_t err = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
         if (err != hipSuccess) return err;
     }

@@ -70,6 +70,9 @@ bool gdn_large_supported(int T);
 hipError_t launch_gdn_large(int batch, int T, int H, int dk, int dv, bool bf16, const void* q, const void* k,
                             const void* v, const float* g, const float* beta, const float* S0,
                             const int32_t* parent, void* o, float* e, int32_t* tree_status, hipStream_t stream);
+// longest accepted path the gated-delta-rule commit takes past 64 nodes:
+// the path's e and k rows are staged whole in LDS (up to 128 KiB)
+constexpr int kGdnMaxPath = 128;
 hipError_t launch_gdn_commit(int batch, int T, int H, int dk, int dv, bool bf16, const void* k,
                              const float* g, const float* e, float* S, const int32_t* parent,
                              const int32_t* accepted, const int32_t* accepted_len, int Lmax,

@@ -298,8 +298,36 @@ def test_gdn_large_capacity_invalid_and_optional_e(bnd):
                                  None, bnd._stream(None))
     torch.cuda.synchronize()
     assert rc == 0 and torch.equal(o2, o)
-    acc = torch.full((4, 65), -1, dtype=torch.int32, device="cuda")
+    acc = torch.full((4, 129), -1, dtype=torch.int32, device="cuda")
     rc = bnd.lib.tree_gdn_commit(ctypes.byref(shape), bnd._ptr(dev["k"]), bnd._ptr(dev["g"]),
                                  bnd._ptr(o), bnd._ptr(dev["S0"]), bnd._ptr(dev["parent"]), bnd._ptr(acc),
-                                 bnd._ptr(dev["accepted_len"]), 65, None, bnd._stream(None))
+                                 bnd._ptr(dev["accepted_len"]), 129, None, bnd._stream(None))
     assert rc == 4
+
+
+@pytest.mark.parametrize("L,dtype", [(65, W.F32), (80, W.BF16), (90, W.F32)])
+def test_gdn_commit_long_paths(bnd, L, dtype):
+    """Accepted paths past 64 nodes (90-node chains, the paths 0 .. L-1): the
+    committed state against the unrolled recurrence."""
+    import torch
+    T = 90
+    d = W.make_gdn(7000 + L, batch=2, n_nodes=T, n_heads=2, dk=64, dv=96, tree="chain", max_depth=T,
+                   max_path_len=L, dtype=dtype)
+    d["accepted"] = np.tile(np.arange(L, dtype=np.int32), (2, 1))
+    d["accepted_len"] = np.array([L, L - 7], np.int32)
+    say(f"[gdn long path] T={T} L={L} {dtype}")
+    dev = _dev_io(d)
+    _, e = bnd.gdn_verify(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], dev["S0"], dev["parent"])
+    S = dev["S0"].clone()
+    st = torch.full((2,), -7, dtype=torch.int32, device="cuda")
+    bnd.gdn_commit(dev["k"], dev["g"], e, S, dev["parent"], dev["accepted"], dev["accepted_len"], tree_status=st)
+    torch.cuda.synchronize()
+    x = {k: (W.to_f64(v, W.BF16) if v.dtype == np.uint16 else
+             (v.astype(np.float64) if v.dtype == np.float32 else v)) for k, v in d.items()}
+    Sref, cst = O.commit_unrolled(x["k"], x["v"], x["g"], x["beta"], x["S0"], x["parent"],
+                                  x["accepted"], x["accepted_len"])
+    assert st.cpu().tolist() == cst.tolist() == [0, 0]
+    Sn = S.cpu().double().numpy()
+    err = max(np.max(np.abs(Sn[b, h] - Sref[b, h])) / np.max(np.abs(Sref[b, h])) for b in range(2) for h in range(2))
+    say(f"    S' err {err:.2e}")
+    assert err <= TOL, err
