@@ -466,10 +466,10 @@ def large_cpu_baseline(base, seconds):
 
 
 def gdn_timing(torch, bnd, W, rounds, oracle_seconds=0.0, dtype="f32", shape=None, tree="recursive"):
-    """Gated-delta-rule tree verify and commit on a batch-16 layer over the
-    31-node random trees (16 heads, dk = dv = 128; q, k, v and o fp32 or
-    bf16), rotating input sets; average durations of back-to-back launches of
-    each kernel alone."""
+    """Gated-delta-rule tree verify and commit on a batch-16 layer (16 heads,
+    dk = dv = 128; q, k, v and o fp32 or bf16) over 31-node random trees, or
+    the shape and trees given, rotating input sets; average durations of
+    back-to-back launches of each kernel alone."""
     import numpy as np
     sh = shape or GDN_SHAPE
     base = W.make_gdn(31, **sh, max_path_len=5, dtype=dtype, tree=tree)
@@ -858,7 +858,9 @@ def main():
         out["gdn_bf16"] = gdn_timing(torch, bnd, W, args.secondary_steps, 0.0, dtype=W.BF16)
         out["gdn_large"] = gdn_timing(torch, bnd, W, args.secondary_steps, 0.0,
                                       shape=dict(GDN_SHAPE, n_nodes=255), tree="level")
-        for key in ("gdn", "gdn_bf16", "gdn_large"):
+        out["gdn_large_bf16"] = gdn_timing(torch, bnd, W, args.secondary_steps, 0.0, dtype=W.BF16,
+                                           shape=dict(GDN_SHAPE, n_nodes=255), tree="level")
+        for key in ("gdn", "gdn_bf16", "gdn_large", "gdn_large_bf16"):
             r = out[key]
             log(f"[bench] gated delta rule {r['workload']} {r['dtype']}: verify {r['verify']['avg_us']:.2f} us "
                 f"({r['verify']['frac']:.1%}), commit {r['commit']['avg_us']:.2f} us ({r['commit']['frac']:.1%})")
