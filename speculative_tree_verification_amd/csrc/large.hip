@@ -177,8 +177,8 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
     __shared__ float s_a[kMaxNodesLarge];  // dt of each node
     __shared__ __attribute__((aligned(16))) uint16_t s_h0h[P * RH];
     __shared__ __attribute__((aligned(16))) uint16_t s_h0l[P * RH];
-    __shared__ uint16_t s_path[NW][16][kLmDist];  // ancestor at distance 32 k + t of tile node r
-    __shared__ float s_dec[NW][16][kLmDist];      // its decay times its dt
+    __shared__ uint16_t s_path[NW][kLmDist][16];  // ancestor at distance 32 k + t of tile node r
+    __shared__ float s_dec[NW][kLmDist][16];      // its decay times its dt
     __shared__ float s_cum[NW][16];               // cum of tile node r
     __shared__ int s_plen[NW][16];                // entries of this pass for tile node r
     __shared__ unsigned long long s_bits[NW][kMaxNodesLarge / 64];  // ancestors flagged this pass
@@ -256,8 +256,8 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
                 int t = 0;
                 for (; t < kLmDist && jw >= 0; ++t) {
                     const float dtj = s_a[jw];
-                    s_path[w][lane][t] = (uint16_t)jw;
-                    s_dec[w][lane][t] = __expf(sw) * dtj;
+                    s_path[w][t][lane] = (uint16_t)jw;
+                    s_dec[w][t][lane] = __expf(sw) * dtj;
                     sw += dtj * Ah;
                     atomicOr(&s_bits[w][jw >> 6], 1ull << (jw & 63));
                     jw = s_par[jw];
@@ -308,8 +308,8 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
                     const int j = s_J[w][min(jpos, nJ - 1)];
                     float wgt = 0.f;
                     const int t = di - s_dep[j] - kLmDist * k;
-                    if (jpos < nJ && inode < T && t >= 0 && t < s_plen[w][l16] && s_path[w][l16][t] == j)
-                        wgt = s_dec[w][l16][t];
+                    if (jpos < nJ && inode < T && t >= 0 && t < s_plen[w][l16] && s_path[w][t][l16] == j)
+                        wgt = s_dec[w][t][l16];
                     const float sv = gt[c] * wgt;
 #pragma unroll
                     for (int pt = 0; pt < 4; ++pt)
