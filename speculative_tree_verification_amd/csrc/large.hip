@@ -177,6 +177,8 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
     __shared__ float s_a[kMaxNodesLarge];  // dt of each node
     __shared__ __attribute__((aligned(16))) uint16_t s_h0h[P * RH];
     __shared__ __attribute__((aligned(16))) uint16_t s_h0l[P * RH];
+    // distance-major, so that the 16 node lanes of a walk step write 16
+    // neighbouring entries (rows per node put 4 or 8 of them on one LDS bank)
     __shared__ uint16_t s_path[NW][kLmDist][16];  // ancestor at distance 32 k + t of tile node r
     __shared__ float s_dec[NW][kLmDist][16];      // its decay times its dt
     __shared__ float s_cum[NW][16];               // cum of tile node r
