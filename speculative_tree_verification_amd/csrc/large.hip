@@ -235,14 +235,18 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
     for (int e = tid; e < NW * kMaxNodesLarge / 64; e += kLargeThreads) (&s_bits[0][0])[e] = 0ull;
     __syncthreads();
 
-    const size_t xrow = (size_t)H * P;  // x / y stride between nodes
+    // rows within an item are addressed by 32-bit offsets from the item's base
+    const uint32_t xrow = (uint32_t)(H * P);  // x / y stride between nodes
+    const uint32_t bcrow = (uint32_t)(G * N);
     const uint16_t* xb = x + ((size_t)b * T * H + h) * P;
     uint16_t* yb = y + ((size_t)b * T * H + h) * P;
+    const uint16_t* Bb = Bm + ((size_t)b * T * G + g) * N;
+    const uint16_t* Cb = Cm + ((size_t)b * T * G + g) * N;
     for (int tt = w; 16 * (tt * S + part) < T; tt += NW) {
         const int i0 = 16 * (tt * S + part);
         // C rows of the tile: node i0 + l16, columns 32 ks + 8 q4 ..
         bf16x8 cf[KS];
-        const uint16_t* crow = Cm + (((size_t)b * T + min(i0 + l16, T - 1)) * G + g) * N;
+        const uint16_t* crow = Cb + (uint32_t)min(i0 + l16, T - 1) * bcrow;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) cf[ks] = __builtin_bit_cast(bf16x8, *(const uint4*)(crow + 32 * ks + 8 * q4));
         f32x4 yw[4];  // walk term: rows i0 + 4 q4 + c, columns p = 16 pt + l16
@@ -268,15 +272,23 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
                 s_cum[w][lane] = sw;
             }
             wave_sync();
-            // compact the flagged ancestors (they precede the tile's last node)
+            // compact the flagged ancestors (they precede the tile's last node):
+            // lane wd reads word wd (one LDS round trip for all) and clears it
+            // for the next pass; the non-empty words are then taken in order
             int nJ = 0;  // wave-uniform
-            const int nwords = (min(T, i0 + 16) + 63) >> 6;
-            for (int wd = 0; wd < nwords; ++wd) {
-                const unsigned long long m = s_bits[w][wd];
-                if (!m) continue;  // wave-uniform
+            const int nwords = (min(T, i0 + 16) + 63) >> 6;  // at most 16
+            unsigned long long myw = 0ull;
+            if (lane < nwords) {
+                myw = s_bits[w][lane];
+                s_bits[w][lane] = 0ull;
+            }
+            for (unsigned long long nz = __ballot(myw != 0ull); nz; nz &= nz - 1) {
+                const int wd = __builtin_ctzll(nz);  // wave-uniform
+                const unsigned long long m =
+                    (unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)myw, wd) |
+                    ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(myw >> 32), wd) << 32);
                 if ((m >> lane) & 1ull) s_J[w][nJ + __popcll(m & ((1ull << lane) - 1))] = (uint16_t)(64 * wd + lane);
                 nJ += __popcll(m);
-                if (lane == 0) s_bits[w][wd] = 0ull;
             }
             wave_sync();
             // per column block of 16: the X values this lane feeds to the S X
@@ -285,7 +297,7 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
             auto xvals = [&](int c0, float (&xq)[4][4]) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    const uint16_t* xr = xb + (size_t)s_J[w][min(c0 + 4 * q4 + c, nJ - 1)] * xrow;
+                    const uint16_t* xr = xb + (uint32_t)s_J[w][min(c0 + 4 * q4 + c, nJ - 1)] * xrow;
 #pragma unroll
                     for (int pt = 0; pt < 4; ++pt) xq[c][pt] = bf16_bits_to_f32(xr[16 * pt + l16]);
                 }
@@ -294,7 +306,7 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
             xvals(0, xq);
             for (int c0 = 0; c0 < nJ; c0 += 16) {
                 // G^T block: rows J[c0 + l16] (A operand: B rows), columns the tile (C rows)
-                const uint16_t* brow = Bm + (((size_t)b * T + s_J[w][min(c0 + l16, nJ - 1)]) * G + g) * N;
+                const uint16_t* brow = Bb + (uint32_t)s_J[w][min(c0 + l16, nJ - 1)] * bcrow;
                 uint4 bq[KS];
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) bq[ks] = *(const uint4*)(brow + 32 * ks + 8 * q4);
@@ -331,7 +343,7 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
         for (int c = 0; c < 4; ++c) {
             const int i = min(i0 + 4 * q4 + c, T - 1);
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt) xi[c][pt] = bf16_bits_to_f32(xb[(size_t)i * xrow + 16 * pt + l16]);
+            for (int pt = 0; pt < 4; ++pt) xi[c][pt] = bf16_bits_to_f32(xb[(uint32_t)i * xrow + 16 * pt + l16]);
         }
         // read-out h0 . C of the tile, same layout as the walk term
         f32x4 y0[4];
@@ -353,7 +365,7 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
                 const float ec = expf(s_cum[w][4 * q4 + c]);
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt) {
-                    const size_t o = (size_t)i * xrow + 16 * pt + l16;
+                    const uint32_t o = (uint32_t)i * xrow + 16 * pt + l16;
                     yb[o] = f32_to_bf16_bits(ec * y0[pt][c] + yw[pt][c] + Dh * xi[c][pt]);
                 }
             }
