@@ -98,9 +98,7 @@ tsv_status tree_ssd_commit(const tsv_shape* s, const void* x, const void* dt, co
     tsv::CommitArgs a{x,        dt,          A,           B,           h0_inout,   nullptr,
                       1,        parent,      accepted,    accepted_len, tree_status, s->batch,
                       s->n_nodes, s->n_heads, s->head_dim, s->d_state,  s->n_groups, max_path_len};
-    hipError_t e = s->n_nodes > kMaxNodesMfma
-                       ? tsv::launch_commit_large(a, s->in_dtype == TSV_BF16, (hipStream_t)stream)
-                       : tsv::launch_commit(a, s->in_dtype == TSV_BF16, (hipStream_t)stream);
+    hipError_t e = tsv::launch_commit(a, s->in_dtype == TSV_BF16, (hipStream_t)stream);
     return e == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
 }
 
@@ -119,9 +117,7 @@ tsv_status tree_ssd_commit_layers(const tsv_shape* s, int32_t n_layers,
     tsv::CommitArgs a{nullptr,  nullptr,     nullptr,     nullptr,      nullptr,     layers,
                       n_layers, parent,      accepted,    accepted_len, tree_status, s->batch,
                       s->n_nodes, s->n_heads, s->head_dim, s->d_state,  s->n_groups, max_path_len};
-    hipError_t e = s->n_nodes > kMaxNodesMfma
-                       ? tsv::launch_commit_large(a, s->in_dtype == TSV_BF16, (hipStream_t)stream)
-                       : tsv::launch_commit(a, s->in_dtype == TSV_BF16, (hipStream_t)stream);
+    hipError_t e = tsv::launch_commit(a, s->in_dtype == TSV_BF16, (hipStream_t)stream);
     return e == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
 }
 

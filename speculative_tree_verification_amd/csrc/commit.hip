@@ -44,17 +44,21 @@ __device__ __forceinline__ void put8(float* dst, uint4 v) {
                                       bf16_bits_to_f32(v.w & 0xffff), bf16_bits_to_f32(v.w >> 16));
 }
 
-template <typename TIO, bool VEC, bool PRE>
+// NPT: tree nodes (and path entries) per thread, 1 for trees of up to 256
+// nodes, 4 for up to 1024
+template <typename TIO, bool VEC, bool PRE, int NPT>
 __global__ __launch_bounds__(kBlock) void commit_kernel(
     const TIO* __restrict__ x_arg, const TIO* __restrict__ dt_arg, const float* __restrict__ A_arg,
     const TIO* __restrict__ B_arg, float* __restrict__ h_arg, const tsv_commit_layer* __restrict__ layers,
     const int32_t* __restrict__ parent, const int32_t* __restrict__ accepted,
     const int32_t* __restrict__ accepted_len, int32_t* __restrict__ tree_status, int BH, int T,
     int H, int P, int N, int G, int Lmax, int chunks) {
-    __shared__ int s_par[kMaxNodes];
-    __shared__ int s_path[kMaxNodes];
-    __shared__ int s_pos[kMaxNodes];  // path position of each node, or -1 (PRE)
-    __shared__ float s_w[kMaxNodes];
+    constexpr int NMAX = kBlock * NPT;
+    static_assert(!PRE || NPT == 1, "preloaded rows need one node per thread");
+    __shared__ int s_par[NMAX];
+    __shared__ int s_path[NMAX];
+    __shared__ int s_pos[PRE ? kMaxNodes : 1];  // path position of each node, or -1 (PRE)
+    __shared__ float s_w[NMAX];
     __shared__ float s_w0;
     __shared__ int s_red[kBlock / kWave];
     // [kPathChunk][P] x rows, then [kPathChunk][N] B rows, of the path
@@ -89,8 +93,16 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
     // then the path's rows), so they leave first, the accepted row without
     // waiting for its length
     const int len = accepted_len[b];
-    const int acc_i = Lmax > 0 ? accepted[(size_t)b * Lmax + min(tid, Lmax - 1)] : 0;
-    const int par_i = load_parent(parent + (size_t)b * T, T);
+    int acc_i[NPT], par_i[NPT];
+#pragma unroll
+    for (int m = 0; m < NPT; ++m)
+        acc_i[m] = Lmax > 0 ? accepted[(size_t)b * Lmax + min(tid + kBlock * m, Lmax - 1)] : 0;
+    if (NPT == 1) {
+        par_i[0] = load_parent(parent + (size_t)b * T, T);
+    } else {
+#pragma unroll
+        for (int m = 0; m < NPT; ++m) par_i[m] = gload(parent + (size_t)b * T + min(tid + kBlock * m, T - 1));
+    }
     // PRE: piece tid of every node's x rows and of every node's B rows, and
     // node tid's dt, ahead of the state (waiting for them leaves the state in
     // flight); clamped, so every thread issues the same loads
@@ -131,22 +143,51 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
     // a valid path steps from parent to child, so its indices increase and
     // len <= T (this also keeps every path index inside s_path)
     const bool len_ok = len >= 0 && len <= Lmax && len <= T;
-    if (len_ok && tid < len) s_path[tid] = acc_i;
+#pragma unroll
+    for (int m = 0; m < NPT; ++m)
+        if (len_ok && tid + kBlock * m < len) s_path[tid + kBlock * m] = acc_i[m];
     if (pre && tid < T) s_pos[tid] = -1;
     // LDS-only barriers from here on: the state chunk stays in flight while the
     // tree and path are checked and the path rows are requested
-    int st = check_tree_lds<kBlock>(par_i, T, s_par, s_red);  // barrier: s_path visible too
+    int st;
+    if (NPT == 1) {
+        st = check_tree_lds<kBlock>(par_i[0], T, s_par, s_red);  // barrier: s_path visible too
+    } else {
+        int bad_root = 0, bad_par = 0;
+#pragma unroll
+        for (int m = 0; m < NPT; ++m) {
+            const int i = tid + kBlock * m, p = par_i[m];
+            if (i < T) {
+                s_par[i] = p;
+                if (i == 0)
+                    bad_root = p != -1;
+                else
+                    bad_par |= p < 0 || p >= i;
+            }
+        }
+        st = 0;
+        if (lds_sync_or<kBlock>(bad_root | bad_par, s_red)) {  // barrier: s_par, s_path visible
+            st = lds_sync_or<kBlock>(bad_root, s_red) ? kStBadRoot : 0;
+            st |= lds_sync_or<kBlock>(bad_par, s_red) ? kStBadParent : 0;
+        }
+    }
     int bad_path = 0;
     if (!st) {
         if (!len_ok) {
             bad_path = 1;
-        } else if (tid < len) {
-            const int node = s_path[tid];
-            if (tid == 0)
-                bad_path = node != 0;
-            else
-                bad_path = node < 0 || node >= T || s_par[node] != s_path[tid - 1];
-            if (pre && node >= 0 && node < T) s_pos[node] = tid;  // used only for a valid path
+        } else {
+#pragma unroll
+            for (int m = 0; m < NPT; ++m) {
+                const int k = tid + kBlock * m;
+                if (k < len) {
+                    const int node = s_path[k];
+                    if (k == 0)
+                        bad_path |= node != 0;
+                    else
+                        bad_path |= node < 0 || node >= T || s_par[node] != s_path[k - 1];
+                    if (pre && node >= 0 && node < T) s_pos[node] = k;  // used only for a valid path
+                }
+            }
         }
     }
     if (lds_sync_or<kBlock>(bad_path, s_red)) st |= kStBadPath;
@@ -196,7 +237,11 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
             if (tid < T * px && s_pos[tid / px] >= 0) put8(s_wx + 8 * (s_pos[tid / px] * px + tid % px), rx);
             if (tid < T * pb && s_pos[tid / pb] >= 0) put8(s_B + 8 * (s_pos[tid / pb] * pb + tid % pb), rb);
         } else {
-            if (k0 == 0 && tid < len) s_w[tid] = Elem<TIO>::ld(dt, ((size_t)b * T + s_path[tid]) * H + hd);
+            if (k0 == 0)
+#pragma unroll
+                for (int m = 0; m < NPT; ++m)
+                    if (tid + kBlock * m < len)
+                        s_w[tid + kBlock * m] = Elem<TIO>::ld(dt, ((size_t)b * T + s_path[tid + kBlock * m]) * H + hd);
             stage_rows(k0, kn);
         }
         lds_barrier();
@@ -289,7 +334,8 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
     }
 }
 
-hipError_t launch_commit(const CommitArgs& a, bool bf16, hipStream_t stream) {
+template <int NPT>
+static hipError_t launch_commit_npt(const CommitArgs& a, bool bf16, hipStream_t stream) {
     const int per_wg = kBlock * kVec * 4;
     const int chunks = (a.P * a.N + per_wg - 1) / per_wg;
     const int BH = a.batch * a.H;
@@ -297,10 +343,10 @@ hipError_t launch_commit(const CommitArgs& a, bool bf16, hipStream_t stream) {
     const size_t lds = sizeof(float) * kPathChunk * (size_t)(a.P + a.N);
     const bool vec = (a.N % 4) == 0;
     // one piece of every node's x and B rows per thread, the path in one chunk
-    const bool pre = bf16 && vec && a.P % 8 == 0 && a.N % 8 == 0 && a.T * (a.P / 8) <= kBlock &&
+    const bool pre = NPT == 1 && bf16 && vec && a.P % 8 == 0 && a.N % 8 == 0 && a.T * (a.P / 8) <= kBlock &&
                      a.T * (a.N / 8) <= kBlock && 4 * a.T <= a.N && a.Lmax <= kPathChunk;
 #define TSV_COMMIT(TIO, V, PR)                                                               \
-    hipLaunchKernelGGL((commit_kernel<TIO, V, PR>), grid, dim3(kBlock), lds, stream,         \
+    hipLaunchKernelGGL((commit_kernel<TIO, V, PR && NPT == 1, NPT>), grid, dim3(kBlock), lds, stream, \
                        (const TIO*)a.x, (const TIO*)a.dt, a.A, (const TIO*)a.B, a.h, a.layers, \
                        a.parent, a.accepted, a.accepted_len, a.tree_status, BH, a.T, a.H, a.P, \
                        a.N, a.G, a.Lmax, chunks)
@@ -314,6 +360,10 @@ hipError_t launch_commit(const CommitArgs& a, bool bf16, hipStream_t stream) {
     }
 #undef TSV_COMMIT
     return hipGetLastError();
+}
+
+hipError_t launch_commit(const CommitArgs& a, bool bf16, hipStream_t stream) {
+    return a.T <= kMaxNodes ? launch_commit_npt<1>(a, bf16, stream) : launch_commit_npt<4>(a, bf16, stream);
 }
 
 }  // namespace tsv

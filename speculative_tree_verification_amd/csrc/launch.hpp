@@ -54,11 +54,12 @@ hipError_t launch_verify_wide(const VerifyArgs& a, int heads_per_block, hipStrea
 // 16-row slice of head_dim), no LDS, no barrier (heads_per_block does not apply)
 hipError_t launch_verify_tiny(const VerifyArgs& a, hipStream_t stream);
 
+// any tree of up to 1024 nodes (four nodes per thread past 256)
 hipError_t launch_commit(const CommitArgs& a, bool bf16, hipStream_t stream);
 
-// trees of 257 to 1024 nodes: plain fp32 VALU verify and commit (any P, N <= 256)
+// trees of 257 to 1024 nodes: MFMA verify for bf16 with head_dim 64 and
+// d_state 64 or 128, plain fp32 VALU verify otherwise (any P, N <= 256)
 hipError_t launch_verify_large(const VerifyArgs& a, bool bf16, hipStream_t stream);
-hipError_t launch_commit_large(const CommitArgs& a, bool bf16, hipStream_t stream);
 
 // gated delta rule over packed trees (q, k, v, o fp32 or bf16; T <= 64, dk and dv <= 128)
 hipError_t launch_gdn_verify(int batch, int T, int H, int dk, int dv, bool bf16, const void* q,
