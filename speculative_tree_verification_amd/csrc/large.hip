@@ -172,6 +172,7 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
     __shared__ int s_par[kMaxNodesLarge];
     __shared__ int s_dep[kMaxNodesLarge];
     __shared__ int s_nxt[kMaxNodesLarge];
+    __shared__ int s_red[kLargeWaves];
     __shared__ float s_a[kMaxNodesLarge];  // dt of each node
     __shared__ __attribute__((aligned(16))) uint16_t s_h0h[P * RH];
     __shared__ __attribute__((aligned(16))) uint16_t s_h0l[P * RH];
@@ -197,8 +198,8 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
     const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int l16 = lane & 15, q4 = lane >> 4;
     // the parents, this thread's step size and its share of h0 leave together
-    // (one thread per node, T <= 1024 = threads), so the tree check and the
-    // pointer jumping overlap the other two round trips
+    // (one thread per node, T <= 1024 = threads); the tree check and the depths
+    // use LDS-only barriers, so they overlap the other two round trips
     const int par_i = load_parent(parent + (size_t)b * T, T);
     const uint32_t dt_i = gload(dt + ((size_t)b * T + min(tid, T - 1)) * H + h);
     constexpr int HF4 = P * N / 4 / kLargeThreads;  // float4 of h0 per thread
@@ -207,10 +208,12 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
     const float4* H0 = (const float4*)(h0 + ((size_t)b * H + h) * P * N);
 #pragma unroll
     for (int m = 0; m < HF4; ++m) hv[m] = gload(H0 + tid + kLargeThreads * m);
-    const int st = check_tree(par_i, T, s_par);
+    const int st = check_tree_lds<kLargeThreads>(par_i, T, s_par, s_red);
     if (h == 0 && part == 0 && tid == 0 && tree_status) tree_status[b] = st;
     if (st) return;
-    tree_depth(s_par, T, s_nxt, s_dep);
+    // depths: a walk to the root per node, pointer jumping past 16 levels
+    const int dep_i = tree_depth_shallow<kLargeThreads>(s_par, T, s_nxt, s_dep, s_red);
+    if (tid < T) s_dep[tid] = dep_i;
 
     const float Ah = A[h];
     const float Dh = D[h];
