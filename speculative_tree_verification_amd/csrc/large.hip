@@ -293,8 +293,11 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
             }
             wave_sync();
             // per column block of 16: the X values this lane feeds to the S X
-            // steps (row J[c0 + 4 q4 + c], column 16 pt + l16), requested one
-            // block ahead (clamped rows past the list: loaded, unused)
+            // steps (row J[c0 + 4 q4 + c], column 16 pt + l16), requested with
+            // the block's B rows (clamped rows past the list: loaded, unused).
+            // Requesting them a block ahead needs a copy at the end of each
+            // block, which waits for them there: 90.3 against 87.9 us on the
+            // 1023-node trees.
             auto xvals = [&](int c0, float (&xq)[4][4]) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
@@ -303,16 +306,14 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
                     for (int pt = 0; pt < 4; ++pt) xq[c][pt] = bf16_bits_to_f32(xr[16 * pt + l16]);
                 }
             };
-            float xq[4][4];
-            xvals(0, xq);
             for (int c0 = 0; c0 < nJ; c0 += 16) {
                 // G^T block: rows J[c0 + l16] (A operand: B rows), columns the tile (C rows)
                 const uint16_t* brow = Bb + (uint32_t)s_J[w][min(c0 + l16, nJ - 1)] * bcrow;
                 uint4 bq[KS];
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) bq[ks] = *(const uint4*)(brow + 32 * ks + 8 * q4);
-                float xn[4][4];
-                xvals(c0 + 16, xn);
+                float xq[4][4];
+                xvals(c0, xq);
                 f32x4 gt = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
@@ -330,10 +331,6 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
                     for (int pt = 0; pt < 4; ++pt)
                         yw[pt] = __builtin_amdgcn_mfma_f32_16x16x4f32(sv, xq[c][pt], yw[pt], 0, 0, 0);
                 }
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-#pragma unroll
-                    for (int pt = 0; pt < 4; ++pt) xq[c][pt] = xn[c][pt];
             }
             if (!__ballot(lane < 16 && jw >= 0)) break;
             wave_sync();  // lists and columns of this pass consumed
