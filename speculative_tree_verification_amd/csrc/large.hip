@@ -266,7 +266,11 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
                     s_path[w][t][lane] = (uint16_t)jw;
                     s_dec[w][t][lane] = __expf(sw) * dtj;
                     sw += dtj * Ah;
-                    atomicOr(&s_bits[w][jw >> 6], 1ull << (jw & 63));
+                    // flag jw unless the lane to the left (same step) has it
+                    // already: neighbouring nodes share most ancestors, and
+                    // atomics on one word from many lanes are serialised
+                    const int left = __builtin_amdgcn_update_dpp(-2, jw, 0x111, 0xf, 0xf, false);  // row_shr:1
+                    if (jw != left) atomicOr(&s_bits[w][jw >> 6], 1ull << (jw & 63));
                     jw = s_par[jw];
                 }
                 s_plen[w][lane] = t;
