@@ -310,6 +310,7 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
                     for (int pt = 0; pt < 4; ++pt) xq[c][pt] = bf16_bits_to_f32(xr[16 * pt + l16]);
                 }
             };
+            const int plen = s_plen[w][l16];  // entries of this pass for node l16
             for (int c0 = 0; c0 < nJ; c0 += 16) {
                 // G^T block: rows J[c0 + l16] (A operand: B rows), columns the tile (C rows)
                 const uint16_t* brow = Bb + (uint32_t)s_J[w][min(c0 + l16, nJ - 1)] * bcrow;
@@ -318,18 +319,36 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
                 for (int ks = 0; ks < KS; ++ks) bq[ks] = *(const uint4*)(brow + 32 * ks + 8 * q4);
                 float xq[4][4];
                 xvals(c0, xq);
+                // this lane's four columns j are kept where j is node l16's
+                // ancestor at distance t of this pass, weighted by its decay;
+                // each stage's LDS reads leave for all four columns together
+                // (from clamped positions) and the test is a select
+                int jt[4];  // j | clamped t << 16, bit 31 where t is an entry of this pass
+#pragma unroll
+                for (int c = 0; c < 4; ++c) jt[c] = s_J[w][min(c0 + 4 * q4 + c, nJ - 1)];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int t = di - s_dep[jt[c]] - kLmDist * k;
+                    const bool ok = c0 + 4 * q4 + c < nJ && inode < T && t >= 0 && t < plen;
+                    jt[c] |= (min(max(t, 0), kLmDist - 1) << 16) | (ok ? (int)0x80000000 : 0);
+                }
+                int pj[4];
+                float dj[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int t = (jt[c] >> 16) & (kLmDist - 1);
+                    pj[c] = s_path[w][t][l16];
+                    dj[c] = s_dec[w][t][l16];
+                }
+#pragma unroll
+                for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(pj[c]), "+v"(dj[c]));  // all reads before the tests
                 f32x4 gt = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
                     gt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bq[ks]), cf[ks], gt, 0, 0, 0);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    const int jpos = c0 + 4 * q4 + c;
-                    const int j = s_J[w][min(jpos, nJ - 1)];
-                    float wgt = 0.f;
-                    const int t = di - s_dep[j] - kLmDist * k;
-                    if (jpos < nJ && inode < T && t >= 0 && t < s_plen[w][l16] && s_path[w][t][l16] == j)
-                        wgt = s_dec[w][t][l16];
+                    const float wgt = (jt[c] < 0 && pj[c] == (jt[c] & 0xffff)) ? dj[c] : 0.f;
                     const float sv = gt[c] * wgt;
 #pragma unroll
                     for (int pt = 0; pt < 4; ++pt)
