@@ -383,7 +383,7 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
         for (int c = 0; c < 4; ++c) {
             const int i = i0 + 4 * q4 + c;
             if (i < T) {
-                const float ec = expf(s_cum[w][4 * q4 + c]);
+                const float ec = __expf(s_cum[w][4 * q4 + c]);
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt) {
                     const uint32_t o = (uint32_t)i * xrow + 16 * pt + l16;
