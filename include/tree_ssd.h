@@ -32,9 +32,10 @@
  *     tree_status[b] (a bit set, see TSV_ST_*). The outputs of an item with any
  *     bit set are left bitwise untouched. tree_status may be NULL (no report;
  *     invalid items are still skipped).
- *   - Nodes are limited to T <= 1024. Trees of up to 256 nodes take the MFMA
- *     kernels where the shape allows; larger trees take plain fp32 kernels
- *     (same results, lower throughput).
+ *   - Nodes are limited to T <= 1024. bf16 inputs with head_dim 64 and
+ *     d_state 64 or 128 take MFMA verify kernels at every tree size; other
+ *     shapes and fp32 inputs take plain fp32 kernels (same results, lower
+ *     throughput).
  *   - The launch runs on the device current to the calling thread.
  */
 #ifndef TREE_SSD_H
