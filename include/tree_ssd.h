@@ -23,7 +23,10 @@
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller, contiguous
  *     row-major. The library allocates nothing, keeps no state between calls,
- *     and is reentrant. Work is enqueued on `stream` (a hipStream_t; NULL means
+ *     and is reentrant, with one exception: tree_ssd_commit_layers_static
+ *     keeps its layer table in a fixed device array of the library's (one per
+ *     GPU), so its calls that overlap on one GPU race. Work is enqueued on
+ *     `stream` (a hipStream_t; NULL means
  *     the null stream) without synchronising; results are ready when the
  *     stream reaches that point.
  *   - Host-detectable errors (NULL pointers, bad sizes, bad dtype) return a
@@ -184,6 +187,39 @@ tsv_status tree_ssd_commit_layers(const tsv_shape* s, int32_t n_layers,
                                   const tsv_commit_layer* layers, const int32_t* parent,
                                   const int32_t* accepted, const int32_t* accepted_len,
                                   int32_t max_path_len, int32_t* tree_status, void* stream);
+
+/* Most layers tree_ssd_commit_layers_static takes in one call. */
+#define TSV_STATIC_MAX_LAYERS 1024
+
+/*
+ * tree_ssd_commit_layers_static -- tree_ssd_commit_layers for callers that
+ * cannot allocate device memory: code under HIP graph capture, serving loops
+ * that must not call hipMalloc, harnesses that forbid it. The layer table is
+ * passed in HOST memory; the call stages it into a fixed device array that
+ * the library holds for the life of the process (TSV_STATIC_MAX_LAYERS
+ * entries of 40 bytes, one copy per GPU, its address looked up on the first
+ * call made on that GPU) and then runs the commit kernel of
+ * tree_ssd_commit_layers on it, so the results are bitwise those of that
+ * call. Nothing is allocated or freed.
+ *
+ *   layers_host  host array [n_layers] of tsv_commit_layer (device pointers
+ *                inside, as for tree_ssd_commit_layers); read during the
+ *                call, which passes it to the GPU as kernel arguments (64
+ *                entries per staging launch), so it may be freed or reused as
+ *                soon as the call returns
+ *   every other argument as for tree_ssd_commit_layers.
+ *
+ * Returns TSV_E_UNSUPPORTED for n_layers > TSV_STATIC_MAX_LAYERS, TSV_E_NULL
+ * for a NULL layers_host with n_layers > 0, TSV_E_LAUNCH if the device array
+ * cannot be resolved, and otherwise what tree_ssd_commit_layers returns.
+ * Every call on one GPU shares that GPU's array and overwrites the entries it
+ * uses: two calls whose work overlaps on one GPU (different streams, no
+ * ordering between them) race. Calls ordered on one stream do not.
+ */
+tsv_status tree_ssd_commit_layers_static(const tsv_shape* s, int32_t n_layers,
+                                         const tsv_commit_layer* layers_host, const int32_t* parent,
+                                         const int32_t* accepted, const int32_t* accepted_len,
+                                         int32_t max_path_len, int32_t* tree_status, void* stream);
 
 /*
  * tree_gdn_verify -- every node's output of one gated-delta-rule layer over a

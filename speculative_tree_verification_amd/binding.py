@@ -34,7 +34,9 @@ STATUS_NAMES = {0: "TSV_OK", 1: "TSV_E_NULL", 2: "TSV_E_SHAPE", 3: "TSV_E_DTYPE"
 EXPORTS = ("tree_ssd_verify", "tree_ssd_commit", "tree_ssd_commit_layers", "tree_ssd_accept_greedy",
            "tree_ssd_tree_info", "tree_ssd_status_string", "tree_ssd_abi_version", "tree_gdn_verify",
            "tree_gdn_commit", "tree_ssd_unroll_plan", "tree_ssd_unroll_gather", "tree_ssd_seq_scan",
-           "tree_ssd_snapshot_verify", "tree_ssd_snapshot_commit", "tree_ssd_accept_stochastic")
+           "tree_ssd_snapshot_verify", "tree_ssd_snapshot_commit", "tree_ssd_accept_stochastic",
+           "tree_ssd_commit_layers_static")
+STATIC_MAX_LAYERS = 1024  # TSV_STATIC_MAX_LAYERS
 ST_OVER_CAPACITY = 8
 ST_BAD_TOKEN = 16
 
@@ -75,6 +77,9 @@ def _load():
     L.tree_ssd_commit_layers.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32] + [_VP] * 4 + \
         [ctypes.c_int32, _VP, _VP]
     L.tree_ssd_commit_layers.restype = ctypes.c_int
+    L.tree_ssd_commit_layers_static.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32] + [_VP] * 4 + \
+        [ctypes.c_int32, _VP, _VP]
+    L.tree_ssd_commit_layers_static.restype = ctypes.c_int
     L.tree_ssd_accept_greedy.argtypes = [ctypes.c_int32, ctypes.c_int32] + [_VP] * 3 + \
         [ctypes.c_int32] + [_VP] * 5
     L.tree_ssd_accept_greedy.restype = ctypes.c_int
@@ -282,6 +287,37 @@ def commit_layers(layers, parent, accepted, accepted_len, tree_status=None, stre
                                         _ptr(tree_status), _stream(stream))
     if rc != 0:
         raise TreeSSDError(rc, "tree_ssd_commit_layers")
+
+
+def commit_layers_static(layers, parent, accepted, accepted_len, tree_status=None, stream=None):
+    """commit_layers without any device allocation: the layer table goes to
+    tree_ssd_commit_layers_static as a host array, which the library stages
+    into its own fixed device array (at most STATIC_MAX_LAYERS layers; calls
+    that overlap on one GPU race). Results are bitwise those of commit_layers."""
+    n = len(layers)
+    if n == 0:
+        return
+    x0, _, _, B0, _ = layers[0]
+    Bt, T = parent.shape
+    dev = x0.device
+    Lmax = accepted.shape[1] if accepted.dim() == 2 else 0
+    for i, (x, dt, A, B, h0) in enumerate(layers):
+        _check_commit_layer(x, dt, A, B, h0, x0, B0, i)
+    _check(parent, "parent", (x0.shape[0], x0.shape[1]), torch.int32, dev)
+    _check(accepted, "accepted", (Bt, Lmax), torch.int32, dev)
+    _check(accepted_len, "accepted_len", (Bt,), torch.int32, dev)
+    if tree_status is not None:
+        _check(tree_status, "tree_status", (Bt,), torch.int32, dev)
+    table = (CommitLayer * n)()
+    for i, (x, dt, A, B, h0) in enumerate(layers):
+        table[i] = CommitLayer(x.data_ptr(), dt.data_ptr(), A.data_ptr(), B.data_ptr(), h0.data_ptr())
+    shape = make_shape(x0, B0)
+    with torch.cuda.device(dev):
+        rc = lib.tree_ssd_commit_layers_static(ctypes.byref(shape), int(n), ctypes.cast(table, _VP),
+                                               _ptr(parent), _ptr(accepted), _ptr(accepted_len), int(Lmax),
+                                               _ptr(tree_status), _stream(stream))
+    if rc != 0:
+        raise TreeSSDError(rc, "tree_ssd_commit_layers_static")
 
 
 def accept_greedy(parent, draft_tokens, target_tokens, max_path_len: int, accepted=None,

@@ -106,20 +106,49 @@ tsv_status tree_ssd_commit_layers(const tsv_shape* s, int32_t n_layers,
                                   const tsv_commit_layer* layers, const int32_t* parent,
                                   const int32_t* accepted, const int32_t* accepted_len,
                                   int32_t max_path_len, int32_t* tree_status, void* stream) {
+    bool nothing = false;
+    tsv_status st = tsv::check_commit_layers(s, n_layers, parent, accepted, accepted_len, max_path_len, &nothing);
+    if (st != TSV_OK || nothing) return st;
+    if (!layers) return TSV_E_NULL;
+    hipError_t e = tsv::launch_commit(tsv::layers_args(s, n_layers, layers, parent, accepted, accepted_len,
+                                                       max_path_len, tree_status),
+                                      s->in_dtype == TSV_BF16, (hipStream_t)stream);
+    return e == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
+}
+
+}  // extern "C"
+
+namespace tsv {
+
+tsv_status check_commit_layers(const tsv_shape* s, int32_t n_layers, const int32_t* parent,
+                               const int32_t* accepted, const int32_t* accepted_len, int32_t max_path_len,
+                               bool* nothing) {
+    *nothing = false;
     tsv_status st = check_shape(s);
     if (st != TSV_OK) return st;
     if (n_layers < 0 || max_path_len < 0 || max_path_len > kMaxNodes) return TSV_E_SHAPE;
-    if (n_layers == 0 || s->batch == 0 || s->n_nodes == 0) return TSV_OK;
-    if (!layers || !parent || !accepted_len) return TSV_E_NULL;
+    if (n_layers == 0 || s->batch == 0 || s->n_nodes == 0) {
+        *nothing = true;
+        return TSV_OK;
+    }
+    if (!parent || !accepted_len) return TSV_E_NULL;
     if (max_path_len > 0 && !accepted) return TSV_E_NULL;
     // the grid (layers x items x heads x state chunks) stays inside 2^31 work-groups
     if ((long long)n_layers * s->batch * s->n_heads * 64 > 0x7fffffffLL) return TSV_E_UNSUPPORTED;
-    tsv::CommitArgs a{nullptr,  nullptr,     nullptr,     nullptr,      nullptr,     layers,
+    return TSV_OK;
+}
+
+CommitArgs layers_args(const tsv_shape* s, int32_t n_layers, const tsv_commit_layer* layers,
+                       const int32_t* parent, const int32_t* accepted, const int32_t* accepted_len,
+                       int32_t max_path_len, int32_t* tree_status) {
+    return CommitArgs{nullptr,  nullptr,     nullptr,     nullptr,      nullptr,     layers,
                       n_layers, parent,      accepted,    accepted_len, tree_status, s->batch,
                       s->n_nodes, s->n_heads, s->head_dim, s->d_state,  s->n_groups, max_path_len};
-    hipError_t e = tsv::launch_commit(a, s->in_dtype == TSV_BF16, (hipStream_t)stream);
-    return e == hipSuccess ? TSV_OK : TSV_E_LAUNCH;
 }
+
+}  // namespace tsv
+
+extern "C" {
 
 namespace {
 // gated-delta-rule shapes: fp32, one group, T <= 64, dk = d_state and

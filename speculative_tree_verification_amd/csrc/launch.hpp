@@ -56,6 +56,15 @@ hipError_t launch_verify_tiny(const VerifyArgs& a, hipStream_t stream);
 
 // any tree of up to 1024 nodes (four nodes per thread past 256)
 hipError_t launch_commit(const CommitArgs& a, bool bf16, hipStream_t stream);
+// host-side checks of tree_ssd_commit_layers other than the table pointer;
+// *nothing is set when the call has no work (no layers, items or nodes)
+tsv_status check_commit_layers(const tsv_shape* s, int32_t n_layers, const int32_t* parent,
+                               const int32_t* accepted, const int32_t* accepted_len, int32_t max_path_len,
+                               bool* nothing);
+// launch arguments of a multi-layer commit reading its table at `layers`
+CommitArgs layers_args(const tsv_shape* s, int32_t n_layers, const tsv_commit_layer* layers,
+                       const int32_t* parent, const int32_t* accepted, const int32_t* accepted_len,
+                       int32_t max_path_len, int32_t* tree_status);
 
 // trees of 257 to 1024 nodes: MFMA verify for bf16 with head_dim 64 and
 // d_state 64 or 128, plain fp32 VALU verify otherwise (any P, N <= 256)

@@ -232,3 +232,22 @@ def test_gdn_null_and_empty(L):
     s = gdn_good()
     s.batch = 0
     assert call_gdn_verify(L, s) == 0 and call_gdn_commit(L, s) == 0
+
+
+def test_commit_layers_static_host_checks(L):
+    """The allocation-free multi-layer commit rejects a table past its fixed
+    capacity, a NULL table and a negative layer count before any HIP call."""
+    vp = ctypes.c_void_p
+    f = L.tree_ssd_commit_layers_static
+    f.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32] + [vp] * 4 + [ctypes.c_int32, vp, vp]
+    f.restype = ctypes.c_int
+    fake = vp(0x1000)  # never dereferenced: every call below returns on the host
+    table = (ctypes.c_void_p * (5 * 1025))()
+    s = good()
+    assert f(ctypes.byref(s), 1025, ctypes.cast(table, vp), fake, fake, fake, 4, None, None) == 4
+    assert f(ctypes.byref(s), 2, None, fake, fake, fake, 4, None, None) == 1
+    assert f(ctypes.byref(s), -1, ctypes.cast(table, vp), fake, fake, fake, 4, None, None) == 2
+    assert f(ctypes.byref(s), 0, None, fake, fake, fake, 4, None, None) == 0
+    bad = good()
+    bad.n_groups = 3
+    assert f(ctypes.byref(bad), 2, ctypes.cast(table, vp), fake, fake, fake, 4, None, None) == 2
