@@ -57,6 +57,9 @@ void verify_mfma_kernel(
     const float* __restrict__ D, const float* __restrict__ h0, const int32_t* __restrict__ parent,
     uint16_t* __restrict__ y, int32_t* __restrict__ tree_status, int T, int H, int G) {
     using Cfg = MfmaCfg<TI, HW>;
+    // one-head work-groups read h0 in whole 1 KB runs per instruction and
+    // store y as whole rows; wider ones read h0 in MFMA operand order
+    constexpr bool LIN = HW == 1;
     constexpr int NT = Cfg::NT;
     constexpr int N = 32 * KS;
     constexpr int TP = Cfg::TP;
@@ -66,10 +69,19 @@ void verify_mfma_kernel(
     __shared__ float s_G[TP * TP];
     __shared__ __attribute__((aligned(16))) uint16_t s_x[4 * HW][TP * kXStride];
     __shared__ uint16_t s_dth[HW * TP];  // dt of the work-group's heads, bf16 [slot][node]
-    // B and C rows of the item's group, padded by 16 bytes per row
+    // B and C rows of the item's group, padded by 16 bytes per row; once the
+    // pair scores and the C operands are taken, the same memory stages h0
+    // (one-head work-groups: each wave's 16 x N slice, one bf16 plane at a time)
     constexpr int BCS = N + 8;
-    __shared__ __attribute__((aligned(16))) uint16_t s_Bt[TP * BCS];
-    __shared__ __attribute__((aligned(16))) uint16_t s_Ct[TP * BCS];
+    constexpr int kStage = LIN ? 4 * 16 * N : 0;
+    constexpr int kBC = 2 * TP * BCS > kStage ? 2 * TP * BCS : kStage;
+    __shared__ __attribute__((aligned(16))) uint16_t s_BC[kBC];
+    uint16_t* const s_Bt = s_BC;
+    uint16_t* const s_Ct = s_BC + TP * BCS;
+    // y rows of the work-group's head (one-head work-groups), 16 bytes of padding
+    // per row, so that y leaves as whole 128-byte rows
+    constexpr int kYS = kP + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t s_y[LIN ? TP * kYS : 8];
 
     const int nblk = H / HW;
     const int blk = xcd_block(blockIdx.x, gridDim.x);
@@ -108,9 +120,19 @@ void verify_mfma_kernel(
         const int n = e / HW, hh = e - n * HW;  // consecutive threads: consecutive heads of node n
         dtr[m] = dt[((size_t)b * T + n) * H + h_first + hh];
     }
-    // this wave's 16 x N slice of h0 (rows 16 wl + r16) and its 16 columns of x
+    // this wave's 16 x N slice of h0 (rows 16 wl .. 16 wl + 15) and its 16
+    // columns of x. One-head work-groups read the slice as 2 KS consecutive
+    // 1 KB runs (float4 m of lane l is element 4 (l + 64 m) of the slice),
+    // streamed past the caches: this access pattern alone took the launch's
+    // memory skeleton (loads and stores, no arithmetic) from 15.0 to 13.8 us,
+    // 12.4 us with the nontemporal hint, at batch 16 x 31 nodes x 80 heads.
+    // The slice reaches MFMA operand order through LDS after the set-up.
     float4 hr[KS][2];
-    {
+    if (LIN) {
+        const float4* hblk = (const float4*)(h0 + (((size_t)b * H + h) * kP + 16 * wl) * N);
+#pragma unroll
+        for (int m = 0; m < 2 * KS; ++m) hr[m >> 1][m & 1] = gload_nt(hblk + lane + kWave * m);
+    } else {
         const float* hrow = h0 + (((size_t)b * H + h) * kP + 16 * wl + r16) * N + 8 * q;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -189,18 +211,55 @@ void verify_mfma_kernel(
 
     // ---------------------------------------------------------------- head
     // state read-out: acc[it] = (h0 C^T) tile, rows p = 16 wl + 4q + r, column
-    // i; h0 is split into bf16 high and low halves one k-step at a time
+    // i; h0 is split into bf16 high and low halves, the A operand of k-step ks
+    // being columns 32 ks + 8q .. + 7 of row 16 wl + r16
+    bf16x8 hop[KS], lop[KS];
+    if (LIN) {
+        // each wave turns its runs into operands through its own 16 x N bf16
+        // plane in the B/C tile memory (free since the barrier above): 16-byte
+        // chunk c of row r sits at chunk c ^ (r mod chunks-per-row), so the 16
+        // rows one operand read touches fall on different banks
+        constexpr int CH = N / 8;  // 16-byte chunks per row of a plane
+        unsigned char* plane = (unsigned char*)(s_BC + w * 16 * N);
+        auto stage = [&](bool low) {
+#pragma unroll
+            for (int m = 0; m < 2 * KS; ++m) {
+                const int e = 4 * (lane + kWave * m);  // element of the slice
+                const int r = e / N, c = e % N;
+                const float4 v = hr[m >> 1][m & 1];
+                const float f[4] = {v.x, v.y, v.z, v.w};
+                uint16_t u[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const __bf16 hb = (__bf16)f[k];
+                    u[k] = __builtin_bit_cast(uint16_t, low ? (__bf16)(f[k] - (float)hb) : hb);
+                }
+                *(uint2*)(plane + r * 2 * N + (((c >> 3) ^ (r & (CH - 1))) << 4) + 8 * ((c >> 2) & 1)) =
+                    make_uint2(u[0] | (uint32_t)u[1] << 16, u[2] | (uint32_t)u[3] << 16);
+            }
+            wave_sync();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 o = *(const bf16x8*)(plane + r16 * 2 * N + (((4 * ks + q) ^ (r16 & (CH - 1))) << 4));
+                if (low) lop[ks] = o; else hop[ks] = o;
+            }
+            wave_sync();
+        };
+        stage(false);
+        stage(true);
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) split_hi_lo(hr[ks][0], hr[ks][1], hop[ks], lop[ks]);
+    }
     f32x4 acc[TI];
 #pragma unroll
     for (int it = 0; it < TI; ++it) acc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 hi, lo;
-        split_hi_lo(hr[ks][0], hr[ks][1], hi, lo);
 #pragma unroll
         for (int it = 0; it < TI; ++it) {
-            acc[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, creg[it][ks], acc[it], 0, 0, 0);
-            acc[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, creg[it][ks], acc[it], 0, 0, 0);
+            acc[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hop[ks], creg[it][ks], acc[it], 0, 0, 0);
+            acc[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lop[ks], creg[it][ks], acc[it], 0, 0, 0);
         }
     }
 
@@ -234,8 +293,22 @@ void verify_mfma_kernel(
         const float o1 = acc[it][1] * sc + t1 + Dh * hi_bf16(xi.x);
         const float o2 = acc[it][2] * sc + t2 + Dh * lo_bf16(xi.y);
         const float o3 = acc[it][3] * sc + t3 + Dh * hi_bf16(xi.y);
-        *(uint2*)(y + (((size_t)b * T + i) * H + h) * kP + 16 * wl + 4 * q) =
-            make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+        const uint2 ov = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+        if (LIN) *(uint2*)(s_y + i * kYS + 16 * wl + 4 * q) = ov;
+        else *(uint2*)(y + (((size_t)b * T + i) * H + h) * kP + 16 * wl + 4 * q) = ov;
+    }
+    if (LIN) {
+        // y as whole rows: eight consecutive threads store one node's 128 bytes
+        // (the per-wave 8-byte pieces cost about 2 us of the launch's memory
+        // skeleton at batch 16 x 31 nodes x 80 heads)
+        lds_barrier();
+#pragma unroll
+        for (int k = 0; k < (TP * 8 + NT - 1) / NT; ++k) {
+            const int idx = tid + NT * k;
+            const int row = idx >> 3, ch = idx & 7;
+            if (row < T)
+                *(uint4*)(y + (((size_t)b * T + row) * H + h) * kP + 8 * ch) = *(const uint4*)(s_y + row * kYS + 8 * ch);
+        }
     }
 }
 
