@@ -62,7 +62,7 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--heads-per-block", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain device copy of known size (HBM counter calibration)")
+                    help="only run a plain device copy and a sum of known size (HBM counter calibration)")
     return ap.parse_args()
 
 
@@ -766,8 +766,13 @@ def copy_calibration(torch):
     b = torch.empty_like(a)
     for _ in range(5):
         b.copy_(a)
+    # a read-only kernel of the same size as a second reference for FETCH_SIZE
+    # (a reduction: it reads every byte once and writes a few bytes)
+    s = torch.zeros((), dtype=torch.float32, device="cuda")
+    for _ in range(5):
+        s += a.sum()
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_each_way": n, "launches": 5}))
+    print(json.dumps({"copy_bytes_each_way": n, "launches": 5, "sum_bytes_read": n, "sum_launches": 5}))
 
 
 def main():
