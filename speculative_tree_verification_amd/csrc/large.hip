@@ -379,19 +379,29 @@ __global__ __launch_bounds__(kLargeThreads) void verify_large_mfma_kernel(
             }
         }
         wave_sync();  // s_cum
+        // y of the tile leaves through this wave's decay table (free once the
+        // walk is done; 16 rows x 128 bytes, row-major, so every write below
+        // is the lane's base plus a constant) as two 16-byte stores per lane
+        // instead of sixteen 2-byte ones
+        uint16_t* ty = (uint16_t*)&s_dec[w][0][0];
+        uint16_t* tyl = ty + 4 * q4 * P + l16;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const int i = i0 + 4 * q4 + c;
-            if (i < T) {
+            if (i0 + 4 * q4 + c < T) {
                 const float ec = __expf(s_cum[w][4 * q4 + c]);
 #pragma unroll
-                for (int pt = 0; pt < 4; ++pt) {
-                    const uint32_t o = (uint32_t)i * xrow + 16 * pt + l16;
-                    yb[o] = f32_to_bf16_bits(ec * y0[pt][c] + yw[pt][c] + Dh * xi[c][pt]);
-                }
+                for (int pt = 0; pt < 4; ++pt)
+                    tyl[c * P + 16 * pt] = f32_to_bf16_bits(ec * y0[pt][c] + yw[pt][c] + Dh * xi[c][pt]);
             }
         }
-        wave_sync();  // s_cum, lists of this tile consumed
+        wave_sync();
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const int k = lane + kWave * k2;
+            const int r = k >> 3, ch = k & 7;
+            if (i0 + r < T) *(uint4*)(yb + (uint32_t)(i0 + r) * xrow + 8 * ch) = *(const uint4*)(ty + 8 * k);
+        }
+        wave_sync();  // s_cum, lists and the y tile of this tile consumed
     }
 }
 
